@@ -1,0 +1,6 @@
+"""Float64 CPU oracle (test infrastructure only; see attention_oracle's header)."""
+from .attention_oracle import (attention, attention_head, block_means, block_scores,  # noqa: F401
+                               block_token_ids, keep_count, n_blocks_of, near_tie_rows,
+                               qk_norm_rope, rms_norm, rope3d, rope_frequencies,
+                               sparse_attention, sparse_attention_rows, subblock_select,
+                               token_positions, topk_blocks)

@@ -1,0 +1,236 @@
+"""Plain float64 CPU oracle for the video-DiT attention hot path.
+
+TEST INFRASTRUCTURE. Only the tests, the package entry's smoke check and the benchmark's CPU
+baseline leg may import this module. The product path never calls it, and it shares no code,
+tables or constants with the HIP kernels.
+
+Each function is the plain definition of one step, written in numpy float64, slow and direct.
+Inputs are the bf16 tensors the GPU consumed, converted exactly to float64; weights are float32
+converted to float64; theta, eps and sparsity are the values passed through the C ABI.
+
+Sources (web pages on MiniMax-H3 video generation; cited by page title and section):
+  [P3] "MiniMax-H3 的 6.24 倍，不能直接算成六倍产能" (xiaodao.ai/posts/minimax-h3-speed-quality)
+       section "先把近两倍的免费收益拿走": the lossless runtime fuses QK RMSNorm and 3D RoPE into
+       one kernel; fusion does not change the math.
+       section "6.24 倍里，真正有损的部分大约是三倍": SubBlock cuts queries and keys into
+       64-token blocks, estimates which key blocks contribute little, keeps only high-score key
+       blocks for a block-sparse attention kernel; sparsity is the fraction of key blocks dropped.
+  [P4] "MiniMax-H3 在 8×H200 上基准测试：无损加速 1.95×，最高 6.24×" (chat-gpts.plus/?p=43161)
+       section "为什么重要": attention over very long latent sequences is one of the two costs.
+
+Where the pages leave a step open, the reading taken is stated at the function. Parity pins
+for every function live in the CPU tests; the numeric conventions of RoPE (pair layout,
+frequencies, positions) are self-consistent readings and, for the absolute convention,
+parity unpinned by the pages.
+
+Layout: q, k, v are [B, N, Hd, D] (tokens, then heads, then channels), token n of a T x H x W
+latent grid sits at n = (t*H + h)*W + w.
+"""
+from __future__ import annotations
+
+import math
+from typing import Sequence, Tuple
+
+import numpy as np
+
+# --------------------------------------------------------------------------------------------
+# (1) QK RMSNorm + 3D RoPE   [P3, section 先把近两倍的免费收益拿走]
+# --------------------------------------------------------------------------------------------
+
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """y = x * w / sqrt(mean(x^2) + eps), over the last axis (one head's D channels).
+
+    Reading: the norm is per head over D with one weight vector shared by all heads; eps is
+    added inside the square root."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + float(eps)) * w
+
+
+def token_positions(grid: Tuple[int, int, int]) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Integer (t, h, w) coordinates of every token of a T x H x W grid, flattened t-major."""
+    t_len, h_len, w_len = grid
+    n = np.arange(t_len * h_len * w_len, dtype=np.int64)
+    return n // (h_len * w_len), (n // w_len) % h_len, n % w_len
+
+
+def rope_frequencies(d_section: int, theta: float) -> np.ndarray:
+    """theta^(-2j/d) for j < d/2: the rotation rate of pair j inside one axis section."""
+    j = np.arange(d_section // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * j / d_section)
+
+
+def rope3d(x: np.ndarray, grid: Tuple[int, int, int], sections: Sequence[int], theta: float) -> np.ndarray:
+    """3-axis rotary embedding.
+
+    Reading: the head dimension is cut into contiguous [t | h | w] sections of sizes
+    (d_t, d_h, d_w). Inside section a, channels (2j, 2j+1) form a pair rotated by the angle
+    p_a * theta^(-2j/d_a), where p_a is the token's integer coordinate on axis a."""
+    x = np.asarray(x, dtype=np.float64)
+    if sum(sections) != x.shape[-1]:
+        raise ValueError("sections must add up to head_dim")
+    n_tok = x.shape[1]
+    pos = token_positions(grid)
+    if pos[0].shape[0] != n_tok:
+        raise ValueError("grid does not match the token count")
+    out = x.copy()
+    off = 0
+    for p, d_a in zip(pos, sections):
+        ang = p[:, None].astype(np.float64) * rope_frequencies(d_a, theta)[None, :]   # [N, d_a/2]
+        c = np.cos(ang)[None, :, None, :]
+        s = np.sin(ang)[None, :, None, :]
+        x0 = x[..., off:off + d_a:2]
+        x1 = x[..., off + 1:off + d_a:2]
+        out[..., off:off + d_a:2] = x0 * c - x1 * s
+        out[..., off + 1:off + d_a:2] = x0 * s + x1 * c
+        off += d_a
+    return out
+
+
+def qk_norm_rope(q, k, w_q, w_k, grid, sections, theta, eps):
+    """RMSNorm then RoPE, for q and k (the fused kernel computes the same composition)."""
+    return (rope3d(rms_norm(q, w_q, eps), grid, sections, theta),
+            rope3d(rms_norm(k, w_k, eps), grid, sections, theta))
+
+
+# --------------------------------------------------------------------------------------------
+# (2) Dense self-attention   [P4, section 为什么重要]
+# --------------------------------------------------------------------------------------------
+
+
+def _softmax_rows(s: np.ndarray):
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l = np.sum(e, axis=-1, keepdims=True)
+    return e / l, (m + np.log(l))[..., 0]
+
+
+def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, row_chunk: int = 256):
+    """softmax(q k^T / sqrt(D)) v for one head: q [M, D], k [N, D], v [N, D].
+    Returns (O [M, D], lse [M]) with lse = ln sum_j exp(s_ij). Rows are independent; they are
+    processed in chunks only to bound memory."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d = q.shape[-1]
+    out = np.empty((q.shape[0], v.shape[1]), dtype=np.float64)
+    lse = np.empty((q.shape[0],), dtype=np.float64)
+    scale = 1.0 / math.sqrt(d)
+    for r0 in range(0, q.shape[0], row_chunk):
+        s = (q[r0:r0 + row_chunk] @ k.T) * scale
+        p, lse[r0:r0 + row_chunk] = _softmax_rows(s)
+        out[r0:r0 + row_chunk] = p @ v
+    return out, lse
+
+
+def attention(q, k, v):
+    """Non-causal, unmasked multi-head attention on [B, N, Hd, D] tensors.
+    Returns (O [B, N, Hd, D], lse [B, Hd, N])."""
+    b_len, n_len, h_len, d = q.shape
+    out = np.empty((b_len, n_len, h_len, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((b_len, h_len, n_len), dtype=np.float64)
+    for b in range(b_len):
+        for h in range(h_len):
+            out[b, :, h, :], lse[b, h] = attention_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :])
+    return out, lse
+
+
+# --------------------------------------------------------------------------------------------
+# (3) SubBlock selection and block-sparse attention   [P3, section 6.24 倍里，真正有损的部分大约是三倍]
+# --------------------------------------------------------------------------------------------
+
+
+def keep_count(n_blocks: int, sparsity: float) -> int:
+    """Key blocks kept per query block: ceil((1 - s) * n), at least 1 and at most n.
+
+    Sparsity is the fraction of key blocks dropped. A 1e-9 guard keeps float noise such as
+    (1 - 0.7) * 10 = 3.0000000000000004 from rounding up."""
+    if not (0.0 <= sparsity < 1.0) or n_blocks <= 0:
+        raise ValueError("need 0 <= sparsity < 1 and n_blocks > 0")
+    return int(min(n_blocks, max(1, math.ceil((1.0 - sparsity) * n_blocks - 1e-9))))
+
+
+def n_blocks_of(n_tokens: int, block_size: int) -> int:
+    return -(-n_tokens // block_size)
+
+
+def block_means(x: np.ndarray, block_size: int) -> np.ndarray:
+    """Mean of each run of block_size consecutive tokens, per (batch, head): [B, Hd, nB, D].
+    A partial last block averages over its valid tokens."""
+    x = np.asarray(x, dtype=np.float64)
+    b_len, n_len, h_len, d = x.shape
+    nb = n_blocks_of(n_len, block_size)
+    out = np.empty((b_len, h_len, nb, d), dtype=np.float64)
+    for i in range(nb):
+        seg = x[:, i * block_size:min((i + 1) * block_size, n_len)]      # [B, len, Hd, D]
+        out[:, :, i, :] = seg.mean(axis=1)
+    return out
+
+
+def block_scores(q: np.ndarray, k: np.ndarray, block_size: int) -> np.ndarray:
+    """S_bar[b, h, i, j] = mean(q in block i) . mean(k in block j) / sqrt(D).
+
+    The pages leave the importance estimate open; this library fixes it as the scaled dot product
+    of mean-pooled query and key blocks."""
+    qm = block_means(q, block_size)
+    km = block_means(k, block_size)
+    d = q.shape[-1]
+    return np.einsum("bhid,bhjd->bhij", qm, km) / math.sqrt(d)
+
+
+def topk_blocks(scores: np.ndarray, keep: int) -> np.ndarray:
+    """Per row, the keep largest scores; equal scores rank the lower key index first (a stable
+    sort on -score). Returned indices are ascending, int32, shape [..., keep]."""
+    scores = np.asarray(scores, dtype=np.float64)
+    order = np.argsort(-scores, axis=-1, kind="stable")[..., :keep]
+    return np.sort(order, axis=-1).astype(np.int32)
+
+
+def subblock_select(q, k, block_size: int, sparsity: float) -> np.ndarray:
+    """Kept key-block indices [B, Hd, nB, keep] for every query block."""
+    nb = n_blocks_of(q.shape[1], block_size)
+    return topk_blocks(block_scores(q, k, block_size), keep_count(nb, sparsity))
+
+
+def near_tie_rows(scores: np.ndarray, keep: int, rel: float = 1e-5) -> np.ndarray:
+    """Boolean mask of rows whose keep-th and (keep+1)-th largest scores differ by at most
+    rel * max(|a|, |b|); only such rows may legitimately select a different set."""
+    scores = np.asarray(scores, dtype=np.float64)
+    n = scores.shape[-1]
+    if keep >= n:
+        return np.zeros(scores.shape[:-1], dtype=bool)
+    srt = -np.sort(-scores, axis=-1)
+    a = srt[..., keep - 1]
+    b = srt[..., keep]
+    return np.abs(a - b) <= rel * np.maximum(np.abs(a), np.abs(b))
+
+
+def block_token_ids(blocks: Sequence[int], block_size: int, n_tokens: int) -> np.ndarray:
+    ids = [np.arange(j * block_size, min((j + 1) * block_size, n_tokens)) for j in blocks]
+    return np.concatenate(ids) if ids else np.zeros((0,), dtype=np.int64)
+
+
+def sparse_attention_rows(q, k, v, block_idx, block_size: int, b: int, h: int, qblock: int):
+    """Output rows of query block `qblock` of (batch b, head h): attention restricted to the
+    tokens of its kept key blocks, softmax renormalised over those tokens."""
+    n_len = q.shape[1]
+    rows = np.arange(qblock * block_size, min((qblock + 1) * block_size, n_len))
+    keys = block_token_ids(block_idx[b, h, qblock], block_size, k.shape[1])
+    return attention_head(q[b, rows, h, :], k[b, keys, h, :], v[b, keys, h, :])
+
+
+def sparse_attention(q, k, v, block_idx, block_size: int):
+    """Block-sparse attention on [B, N, Hd, D] tensors; block_idx is [B, Hd, nB, keep].
+    Returns (O [B, N, Hd, D], lse [B, Hd, N])."""
+    b_len, n_len, h_len, d = q.shape
+    nb = n_blocks_of(n_len, block_size)
+    out = np.empty((b_len, n_len, h_len, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((b_len, h_len, n_len), dtype=np.float64)
+    for b in range(b_len):
+        for h in range(h_len):
+            for i in range(nb):
+                r0, r1 = i * block_size, min((i + 1) * block_size, n_len)
+                out[b, r0:r1, h, :], lse[b, h, r0:r1] = sparse_attention_rows(q, k, v, block_idx, block_size, b, h, i)
+    return out, lse

@@ -1,0 +1,390 @@
+"""Pins for the float64 oracle: closed forms, invariants, library special cases, brute force and
+hand-worked fixtures. Each pin is chosen so that a plausible slip in the oracle (a dropped term,
+a wrong axis, sign or index, a transposed operand) fails at least one of them. CPU only."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(12345)
+
+
+def rnd(*shape, scale=1.0):
+    return RNG.standard_normal(shape) * scale
+
+
+# ----------------------------------------------------------------------------------- rms_norm
+
+def test_rms_norm_matches_torch_library_routine():
+    x = rnd(2, 5, 3, 16)
+    w = RNG.uniform(0.5, 1.5, 16)
+    for eps in (1e-6, 0.3):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (16,), torch.from_numpy(w), eps).numpy()
+        np.testing.assert_allclose(O.rms_norm(x, w, eps), ref, rtol=1e-14, atol=1e-14)
+
+
+def test_rms_norm_closed_form_rms_and_eps_inside_sqrt():
+    x = rnd(4, 7, 2, 32)
+    w = RNG.uniform(0.5, 1.5, 32)
+    eps = 0.5  # large, so eps placement matters
+    y = O.rms_norm(x, w, eps)
+    ms = np.mean(x * x, axis=-1)
+    rms_unweighted = np.sqrt(np.mean((y / w) ** 2, axis=-1))
+    np.testing.assert_allclose(rms_unweighted, np.sqrt(ms / (ms + eps)), rtol=1e-13)
+    # a constant weight c gives output rms c * sqrt(ms/(ms+eps)): "output rms equals its weight"
+    c = 1.7
+    y2 = O.rms_norm(x, np.full(32, c), 1e-300)
+    np.testing.assert_allclose(np.sqrt(np.mean(y2 ** 2, axis=-1)), c, rtol=1e-13)
+
+
+def test_rms_norm_special_cases():
+    w = RNG.uniform(0.5, 1.5, 8)
+    for c, eps in ((2.0, 1e-6), (-0.25, 0.1), (3.0, 0.0)):
+        x = np.full((1, 1, 1, 8), c)
+        np.testing.assert_allclose(O.rms_norm(x, w, eps)[0, 0, 0], w * c / math.sqrt(c * c + eps), rtol=1e-14)
+    x = rnd(3, 4, 2, 16)
+    w = RNG.uniform(0.5, 1.5, 16)
+    # eps = 0: scale invariant, odd
+    np.testing.assert_allclose(O.rms_norm(3.5 * x, w, 0.0), O.rms_norm(x, w, 0.0), rtol=1e-13)
+    np.testing.assert_allclose(O.rms_norm(-x, w, 0.0), -O.rms_norm(x, w, 0.0), rtol=1e-14)
+
+
+def test_rms_norm_is_per_head():
+    x = rnd(1, 3, 4, 16)
+    w = RNG.uniform(0.5, 1.5, 16)
+    y = O.rms_norm(x, w, 1e-6)
+    x2 = x.copy()
+    x2[:, :, 2, :] *= 100.0  # another head changes
+    y2 = O.rms_norm(x2, w, 1e-6)
+    np.testing.assert_array_equal(y[:, :, [0, 1, 3]], y2[:, :, [0, 1, 3]])
+
+
+# ----------------------------------------------------------------------------------- rope3d
+
+def _complex_rope_1d(x_section, p, theta):
+    """1-D rotary embedding written as complex multiplication z_j * exp(i p theta^(-2j/d))."""
+    d = x_section.shape[-1]
+    z = x_section[..., 0::2] + 1j * x_section[..., 1::2]
+    j = np.arange(d // 2)
+    rot = np.exp(1j * np.multiply.outer(p, theta ** (-2.0 * j / d)))  # [N, d/2]
+    z = z * rot[None, :, None, :]
+    out = np.empty_like(x_section)
+    out[..., 0::2] = z.real
+    out[..., 1::2] = z.imag
+    return out
+
+
+def test_rope_worked_example_golden():
+    lines = [l.split() for l in open(os.path.join(GOLDEN, "rope_worked_example.txt")) if l.strip() and not l.startswith("#")]
+    token = int(lines[0][1])
+    expect = np.array([[float(a), float(b)] for _, _, a, b in lines[1:]]).reshape(-1)
+    x = np.zeros((1, 24, 1, 8))
+    x[..., 0::2] = 1.0
+    y = O.rope3d(x, (2, 3, 4), (2, 2, 4), 100.0)
+    np.testing.assert_allclose(y[0, token, 0], expect, rtol=0, atol=2e-16)
+
+
+def test_rope_preserves_norms_and_is_identity_at_origin():
+    grid, sec = (3, 4, 5), (16, 24, 24)
+    x = rnd(2, 60, 3, 64)
+    y = O.rope3d(x, grid, sec, 1e4)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    pair_x = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    pair_y = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    np.testing.assert_allclose(pair_y, pair_x, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(y[:, 0], x[:, 0])  # token 0 sits at (0, 0, 0)
+
+
+def test_rope_single_axis_grids_equal_complex_1d_rope():
+    theta = 1e4
+    sec = (16, 24, 24)
+    for axis, grid in ((0, (9, 1, 1)), (1, (1, 9, 1)), (2, (1, 1, 9))):
+        x = rnd(1, 9, 2, 64)
+        y = O.rope3d(x, grid, sec, theta)
+        offs = (0, 16, 40, 64)
+        for a in range(3):
+            sl = slice(offs[a], offs[a + 1])
+            if a == axis:
+                np.testing.assert_allclose(y[..., sl], _complex_rope_1d(x[..., sl], np.arange(9.0), theta), atol=1e-13)
+            else:
+                np.testing.assert_array_equal(y[..., sl], x[..., sl])
+
+
+def test_rope_token_flattening_matches_per_axis_coordinates():
+    grid, sec, theta = (3, 4, 5), (16, 24, 24), 1e4
+    x = rnd(1, 60, 2, 64)
+    y = O.rope3d(x, grid, sec, theta)
+    n = np.arange(60)
+    coords = (n // 20, (n // 5) % 4, n % 5)
+    offs = (0, 16, 40, 64)
+    for a in range(3):
+        sl = slice(offs[a], offs[a + 1])
+        np.testing.assert_allclose(y[..., sl], _complex_rope_1d(x[..., sl], coords[a].astype(float), theta), atol=1e-13)
+
+
+def test_rope_relative_position_property():
+    """q.k after RoPE depends only on the (t, h, w) offset between the two tokens."""
+    grid, sec, theta = (4, 5, 6), (16, 24, 24), 1e4
+    t_, h_, w_ = grid
+    tok = lambda t, h, w: (t * h_ + h) * w_ + w
+    q = rnd(64)
+    k = rnd(64)
+    x = np.zeros((1, t_ * h_ * w_, 2, 64))
+    x[0, :, 0, :] = q
+    x[0, :, 1, :] = k
+    y = O.rope3d(x, grid, sec, theta)
+    dot = lambda a, b: float(y[0, a, 0] @ y[0, b, 1])
+    base = dot(tok(0, 1, 2), tok(2, 3, 1))
+    shifted = dot(tok(1, 2, 5 - 1), tok(3, 4, 3))  # both tokens moved by (+1, +1, +2)
+    assert abs(base - shifted) < 1e-12 * (1 + abs(base))
+    other = dot(tok(0, 1, 2), tok(2, 3, 2))  # different offset: differs
+    assert abs(base - other) > 1e-6
+
+
+def test_rope_group_law_double_application():
+    """R(p) R(p) = R(2p): rope twice on a 1x1xW grid equals rope once at even positions of 1x1x2W."""
+    theta, sec = 1e4, (16, 24, 24)
+    x = rnd(1, 7, 2, 64)
+    twice = O.rope3d(O.rope3d(x, (1, 1, 7), sec, theta), (1, 1, 7), sec, theta)
+    x2 = np.zeros((1, 14, 2, 64))
+    x2[:, 0::2] = x
+    once = O.rope3d(x2, (1, 1, 14), sec, theta)[:, 0::2]
+    np.testing.assert_allclose(twice, once, atol=1e-12)
+
+
+def test_rope_frequency_closed_form():
+    # section of width 4, theta 100: pair 1 turns at 100^(-1/2) = 0.1 rad per position
+    x = np.zeros((1, 6, 1, 8))
+    x[..., 0::2] = 1.0
+    y = O.rope3d(x, (1, 1, 6), (2, 2, 4), 100.0)
+    p = np.arange(6.0)
+    np.testing.assert_allclose(y[0, :, 0, 6], np.cos(0.1 * p), atol=1e-15)
+    np.testing.assert_allclose(y[0, :, 0, 7], np.sin(0.1 * p), atol=1e-15)
+    np.testing.assert_allclose(y[0, :, 0, 4], np.cos(p), atol=1e-15)
+
+
+def test_fused_norm_rope_is_the_composition():
+    grid, sec = (2, 3, 4), (16, 24, 24)
+    q, k = rnd(1, 24, 3, 64), rnd(1, 24, 3, 64)
+    wq, wk = RNG.uniform(0.5, 1.5, 64), RNG.uniform(0.5, 1.5, 64)
+    qo, ko = O.qk_norm_rope(q, k, wq, wk, grid, sec, 1e4, 1e-6)
+    np.testing.assert_array_equal(qo, O.rope3d(O.rms_norm(q, wq, 1e-6), grid, sec, 1e4))
+    np.testing.assert_array_equal(ko, O.rope3d(O.rms_norm(k, wk, 1e-6), grid, sec, 1e4))
+    # norm preserved by RoPE => rms of output over head_dim equals rms of the normed input
+    n = O.rms_norm(q, wq, 1e-6)
+    np.testing.assert_allclose(np.linalg.norm(qo, axis=-1), np.linalg.norm(n, axis=-1), rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------------- attention
+
+def test_attention_matches_torch_sdpa_float64():
+    q, k, v = rnd(2, 37, 3, 16), rnd(2, 37, 3, 16), rnd(2, 37, 3, 16)
+    out, lse = O.attention(q, k, v)
+    t = lambda a: torch.from_numpy(a).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v)).permute(0, 2, 1, 3).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    s = torch.einsum("bhqd,bhkd->bhqk", t(q), t(k)) / 4.0
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-13)
+
+
+def test_attention_brute_force_loops():
+    q, k, v = rnd(5, 8), rnd(6, 8), rnd(6, 8)
+    out, lse = O.attention_head(q, k, v)
+    for i in range(5):
+        s = [sum(q[i, d] * k[j, d] for d in range(8)) / math.sqrt(8) for j in range(6)]
+        e = [math.exp(x) for x in s]
+        z = sum(e)
+        for d in range(8):
+            assert abs(out[i, d] - sum(e[j] * v[j, d] for j in range(6)) / z) < 1e-13
+        assert abs(lse[i] - math.log(z)) < 1e-13
+
+
+def test_attention_invariants():
+    q, k, v = rnd(9, 16), rnd(11, 16), rnd(11, 16)
+    out, _ = O.attention_head(q, k, v)
+    # constant V -> constant output
+    c = np.tile(rnd(16), (11, 1))
+    np.testing.assert_allclose(O.attention_head(q, k, c)[0], np.tile(c[0], (9, 1)), atol=1e-13)
+    # q = 0 -> uniform weights -> mean of V
+    np.testing.assert_allclose(O.attention_head(np.zeros((2, 16)), k, v)[0], np.tile(v.mean(0), (2, 1)), atol=1e-13)
+    # single key -> its value
+    np.testing.assert_allclose(O.attention_head(q, k[:1], v[:1])[0], np.tile(v[0], (9, 1)), atol=1e-14)
+    # shifting every key by the same vector leaves O unchanged
+    u = rnd(16)
+    np.testing.assert_allclose(O.attention_head(q, k + u, v)[0], out, atol=1e-12)
+    # jointly permuting keys and values leaves O unchanged
+    perm = RNG.permutation(11)
+    np.testing.assert_allclose(O.attention_head(q, k[perm], v[perm])[0], out, atol=1e-13)
+    # with V = identity the output is the probability matrix: rows sum to 1, entries >= 0
+    p, _ = O.attention_head(q, k, np.eye(11))
+    assert (p >= 0).all()
+    np.testing.assert_allclose(p.sum(1), 1.0, atol=1e-14)
+
+
+def test_attention_two_key_closed_form():
+    q = np.array([[2.0, 0.0, 0.0, 0.0]])
+    k = np.array([[1.0, 0.0, 0.0, 0.0], [-1.0, 0.0, 0.0, 0.0]])
+    v = np.array([[1.0, 2.0, 3.0, 4.0], [5.0, 6.0, 7.0, 8.0]])
+    out, lse = O.attention_head(q, k, v)
+    s1, s2 = 1.0, -1.0  # (2 * +-1) / sqrt(4)
+    a = math.exp(s1) / (math.exp(s1) + math.exp(s2))
+    np.testing.assert_allclose(out[0], a * v[0] + (1 - a) * v[1], rtol=1e-15)
+    assert abs(lse[0] - math.log(math.exp(s1) + math.exp(s2))) < 1e-15
+
+
+def test_attention_large_logits_are_stable():
+    q = rnd(3, 16) * 40
+    k = rnd(20, 16) * 40
+    out, lse = O.attention_head(q, k, rnd(20, 16))
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+# ----------------------------------------------------------------------------------- selection
+
+def _golden_keep_counts():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "keep_counts.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            n, s, k = line.split()
+            rows.append((int(n), float(s), int(k)))
+    return rows
+
+
+def test_keep_count_golden():
+    rows = _golden_keep_counts()
+    assert len(rows) >= 8
+    for n, s, k in rows:
+        assert O.keep_count(n, s) == k, (n, s)
+
+
+def test_keep_count_monotone_and_bounds():
+    for n in (1, 2, 5, 63, 1953):
+        prev = n + 1
+        for s in np.linspace(0, 0.999, 200):
+            k = O.keep_count(n, float(s))
+            assert 1 <= k <= n and k <= prev
+            prev = k
+        assert O.keep_count(n, 0.0) == n
+    for bad in (-0.1, 1.0, 1.5):
+        with pytest.raises(ValueError):
+            O.keep_count(10, bad)
+
+
+def test_block_means_partial_block_and_closed_form():
+    n = 150  # blocks of 64: [0,64), [64,128), [128,150)
+    x = np.zeros((1, n, 2, 3))
+    x[0, :, 0, 0] = np.arange(n)
+    x[0, :, 1, 2] = 1.0
+    m = O.block_means(x, 64)
+    assert m.shape == (1, 2, 3, 3)
+    np.testing.assert_allclose(m[0, 0, :, 0], [31.5, 95.5, (128 + 149) / 2.0])
+    np.testing.assert_allclose(m[0, 1, :, 2], [1.0, 1.0, 1.0])
+
+
+def test_block_scores_equal_block_mean_of_dense_logits():
+    n, d = 200, 16
+    q, k = rnd(1, n, 2, d), rnd(1, n, 2, d)
+    s = O.block_scores(q, k, 64)
+    nb = 4
+    for h in range(2):
+        logits = q[0, :, h, :] @ k[0, :, h, :].T / math.sqrt(d)
+        for i in range(nb):
+            for j in range(nb):
+                blk = logits[i * 64:min(n, (i + 1) * 64), j * 64:min(n, (j + 1) * 64)]
+                assert abs(s[0, h, i, j] - blk.mean()) < 1e-12
+
+
+def _brute_topk(row, keep):
+    idx = list(range(len(row)))
+    idx.sort(key=lambda j: (-row[j], j))
+    return sorted(idx[:keep])
+
+
+def test_topk_brute_force_with_ties():
+    for trial in range(200):
+        n = int(RNG.integers(1, 30))
+        keep = int(RNG.integers(1, n + 1))
+        row = RNG.integers(-3, 4, n).astype(float)  # many exact ties
+        got = O.topk_blocks(row[None, :], keep)[0].tolist()
+        assert got == _brute_topk(row, keep)
+
+
+def test_topk_invariants_and_planted_duplicate_blocks():
+    n, d = 8 * 64, 16
+    q, k = rnd(1, n, 1, d), rnd(1, n, 1, d)
+    k[0, 5 * 64:6 * 64] = k[0, 2 * 64:3 * 64]  # key block 5 duplicates block 2
+    s = O.block_scores(q, k, 64)
+    assert (s[..., 5] == s[..., 2]).all()
+    for keep in range(1, 9):
+        idx = O.topk_blocks(s, keep)
+        assert idx.shape == (1, 1, 8, keep) and idx.dtype == np.int32
+        for row, sc in zip(idx[0, 0], s[0, 0]):
+            assert len(set(row.tolist())) == keep and (np.diff(row) > 0).all()
+            assert row.min() >= 0 and row.max() < 8
+            if 5 in row.tolist():
+                assert 2 in row.tolist()  # tie resolves to the lower index first
+            kept_min = sc[row].min()
+            dropped = np.setdiff1d(np.arange(8), row)
+            if dropped.size:
+                assert sc[dropped].max() <= kept_min
+    full = O.subblock_select(q, k, 64, 0.0)
+    assert (full == np.arange(8)).all()
+
+
+def test_near_tie_rows():
+    s = np.array([[5.0, 4.0, 3.0, 2.0],
+                  [1.0, 1.0 + 5e-6, 0.0, 0.0],
+                  [1.0, 1.0 + 2e-5, 0.0, 0.0],
+                  [0.0, 0.0, 0.0, 0.0]])
+    np.testing.assert_array_equal(O.near_tie_rows(s, 1), [False, True, False, True])
+    assert not O.near_tie_rows(s, 4).any()
+
+
+# ----------------------------------------------------------------------------------- sparse attention
+
+def test_sparse_keep_all_equals_dense():
+    n, d = 3 * 64 + 17, 16
+    q, k, v = rnd(1, n, 2, d), rnd(1, n, 2, d), rnd(1, n, 2, d)
+    nb = 4
+    idx = np.tile(np.arange(nb, dtype=np.int32), (1, 2, nb, 1))
+    so, sl = O.sparse_attention(q, k, v, idx, 64)
+    do, dl = O.attention(q, k, v)
+    np.testing.assert_allclose(so, do, atol=1e-12)
+    np.testing.assert_allclose(sl, dl, atol=1e-12)
+
+
+def test_sparse_single_block_and_masked_formulation():
+    n, d, nb = 4 * 64, 16, 4
+    q, k, v = rnd(1, n, 1, d), rnd(1, n, 1, d), rnd(1, n, 1, d)
+    # keep = 1 with block j: plain attention over that block's tokens only
+    idx = np.full((1, 1, nb, 1), 2, dtype=np.int32)
+    so, _ = O.sparse_attention(q, k, v, idx, 64)
+    ref, _ = O.attention_head(q[0, :, 0], k[0, 128:192, 0], v[0, 128:192, 0])
+    np.testing.assert_allclose(so[0, :, 0], ref, atol=1e-13)
+    # general keep: equal to dense logits with dropped blocks masked to -inf (independent form)
+    idx = O.subblock_select(q, k, 64, 0.5)
+    so, _ = O.sparse_attention(q, k, v, idx, 64)
+    logits = q[0, :, 0] @ k[0, :, 0].T / math.sqrt(d)
+    for i in range(nb):
+        mask = np.full(nb, -np.inf)
+        mask[idx[0, 0, i]] = 0.0
+        lg = logits[i * 64:(i + 1) * 64] + np.repeat(mask, 64)[None, :]
+        p = np.exp(lg - lg.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        np.testing.assert_allclose(so[0, i * 64:(i + 1) * 64, 0], p @ v[0, :, 0], atol=1e-13)
+
+
+def test_sparse_index_order_does_not_matter():
+    n, d, nb = 5 * 64, 16, 5
+    q, k, v = rnd(1, n, 1, d), rnd(1, n, 1, d), rnd(1, n, 1, d)
+    idx = O.subblock_select(q, k, 64, 0.4)
+    shuffled = idx[..., ::-1].copy()
+    a, _ = O.sparse_attention(q, k, v, idx, 64)
+    b, _ = O.sparse_attention(q, k, v, shuffled, 64)
+    np.testing.assert_allclose(a, b, atol=1e-13)
