@@ -1,0 +1,229 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = the whole path on one batch of the 5 s 1344x768 video workload (latent grid
+31 x 48 x 84 = 124,992 tokens, 48 heads, head_dim 128, smooth-field q/k, N(0,1) v, bf16):
+  qk_norm_rope -> dense_fwd -> subblock_select (sparsity 0.75) -> block_sparse_fwd.
+Inputs are resident in HBM before the timed region; outputs and workspaces are preallocated.
+
+Printed JSON line: value = attention TFLOP/s of the step (dense 4*B*H*N^2*D plus block-sparse
+4*B*H*nB*keep*64^2*D flops, divided by the whole step's time, norm+RoPE and selection included).
+Per-kernel times come from HIP events recorded on the launch stream between the calls of every
+timed step; `roofline` describes the dense kernel (the dominant one) against the bf16 MFMA peak.
+`cpu_baseline` times the float64 oracle's dense attention on a bounded sample of query rows of
+the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn TFLOP/s (% MFMA peak) dense+SubBlock 0.75; QK-norm+RoPE HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--config", type=int, default=3, help="workload id (3 = 5 s video)")
+    p.add_argument("--sparsity", type=float, default=0.75)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-extra", action="store_true", help="skip the flushed norm+RoPE runs")
+    return p.parse_args()
+
+
+def flush_caches(buf: torch.Tensor):
+    buf.add_(1)  # rewrites 512 MB: evicts the 256 MB MALL and every L2
+
+
+def elapsed_ms(a, b):
+    return a.elapsed_time(b)
+
+
+def cpu_baseline(q, k, v, cfg, target_s):
+    """Float64 oracle dense attention on a sample of query blocks of head 0 (and more heads if
+    time allows), timed on the host; returns TFLOP/s and what the sample was."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    n = q.shape[1]
+    d = q.shape[3]
+    nb = (n + 63) // 64
+    done_rows = 0
+    spent = 0.0
+    samples = []
+    rng = np.random.default_rng(0)
+    head = 0
+    kh = vh = None
+    while spent < target_s and head < q.shape[2]:
+        if kh is None:
+            kh = k[0, :, head].cpu().to(torch.float64).numpy()
+            vh = v[0, :, head].cpu().to(torch.float64).numpy()
+        blk = int(rng.integers(0, nb))
+        rows = np.arange(blk * 64, min(n, blk * 64 + 64))
+        qh = q[0, rows, head].cpu().to(torch.float64).numpy()
+        t0 = time.perf_counter()
+        oracle.attention_head(qh, kh, vh)
+        spent += time.perf_counter() - t0
+        done_rows += len(rows)
+        samples.append((head, blk))
+        if len(samples) % 16 == 0:
+            head += 1
+            kh = None
+    flops = 4.0 * done_rows * n * d
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 dense attention of {done_rows} query rows ({len(samples)} query blocks of "
+                      f"heads 0..{samples[-1][0]}) against all {n} keys, {spent:.1f} s",
+            "seconds": spent, "cpu_count": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path (asked for {args.gpus}); "
+              "the head-sharded layout it would use is described in the design notes.", file=sys.stderr)
+        sys.exit(2)
+    import video_diffusion_transformer_qk_amd as h3
+    from inputs import CONFIGS, make_inputs
+    h3.load_library()
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating workload {cfg.name} on {torch.cuda.get_device_name(dev)}")
+    x = make_inputs(cfg, dev)
+    q, k, v, wq, wk = x["q"], x["k"], x["v"], x["wq"], x["wk"]
+    b, n, hd, d = q.shape
+    sections = cfg.sections
+    nb = (n + 63) // 64
+    keep = h3.keep_count(nb, args.sparsity)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    out_d = torch.empty_like(q)
+    out_s = torch.empty_like(q)
+    idx = torch.empty((b, hd, nb, keep), dtype=torch.int32, device=dev)
+    ws = torch.empty((h3.select_workspace_bytes(b, hd, n, d),), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None: ev[0].record()
+        h3.qk_norm_rope(q, k, wq, wk, cfg.grid, sections, cfg.theta, cfg.eps, out=(qo, ko))
+        if ev is not None: ev[1].record()
+        h3.dense_fwd(qo, ko, v, out=out_d)
+        if ev is not None: ev[2].record()
+        h3.subblock_select(qo, ko, args.sparsity, workspace=ws, out=idx)
+        if ev is not None: ev[3].record()
+        h3.block_sparse_fwd(qo, ko, v, idx, out=out_s)
+        if ev is not None: ev[4].record()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(args.steps):
+        step(events[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = elapsed_ms(start, end) / args.steps
+    per = {"norm_rope": [], "dense": [], "select": [], "sparse": []}
+    for ev in events:
+        per["norm_rope"].append(elapsed_ms(ev[0], ev[1]))
+        per["dense"].append(elapsed_ms(ev[1], ev[2]))
+        per["select"].append(elapsed_ms(ev[2], ev[3]))
+        per["sparse"].append(elapsed_ms(ev[3], ev[4]))
+    avg = {kname: float(np.mean(vals)) for kname, vals in per.items()}
+    log(f"step {ms_step:.2f} ms (wall {wall / args.steps * 1e3:.2f} ms); per kernel " +
+        ", ".join(f"{kk} {vv:.3f} ms" for kk, vv in avg.items()))
+
+    dense_flops = 4.0 * b * hd * n * n * d
+    sparse_flops = 4.0 * b * hd * nb * keep * 64 * 64 * d
+    nr_bytes = 8.0 * b * n * hd * d
+    dense_tf = dense_flops / (avg["dense"] * 1e-3) / 1e12
+    sparse_tf = sparse_flops / (avg["sparse"] * 1e-3) / 1e12
+    nr_gbs = nr_bytes / (avg["norm_rope"] * 1e-3) / 1e9
+    value = (dense_flops + sparse_flops) / (ms_step * 1e-3) / 1e12
+
+    components = {
+        "dense_ms": avg["dense"], "dense_tflops": dense_tf, "dense_frac_peak": dense_tf / PEAK_BF16_TFLOPS,
+        "sparse_ms": avg["sparse"], "sparse_tflops_kept": sparse_tf, "sparse_frac_peak": sparse_tf / PEAK_BF16_TFLOPS,
+        "select_ms": avg["select"], "norm_rope_ms": avg["norm_rope"], "norm_rope_gbs": nr_gbs,
+        "norm_rope_frac_peak": nr_gbs / PEAK_HBM_GBS, "keep": keep, "n_blocks": nb,
+        "dense_flops": dense_flops, "sparse_flops": sparse_flops, "norm_rope_bytes": nr_bytes,
+    }
+
+    if not args.no_extra:
+        # norm+RoPE alone with MALL/L2 flushed before every run, at the 10 s and frame workloads
+        flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+        for cid in (4, 2):
+            c2 = CONFIGS[cid]
+            x2 = make_inputs(c2, dev)
+            qq, kk2 = x2["q"], x2["k"]
+            o1, o2 = torch.empty_like(qq), torch.empty_like(kk2)
+            times = []
+            for r in range(12):
+                flush_caches(flush)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                h3.qk_norm_rope(qq, kk2, x2["wq"], x2["wk"], c2.grid, c2.sections, c2.theta, c2.eps, out=(o1, o2))
+                e1.record()
+                torch.cuda.synchronize()
+                if r >= 2:
+                    times.append(elapsed_ms(e0, e1))
+            by = 8.0 * qq.numel()
+            med = float(np.median(times))
+            components[f"norm_rope_{c2.name}_us"] = med * 1e3
+            components[f"norm_rope_{c2.name}_gbs"] = by / (med * 1e-3) / 1e9
+            log(f"norm+rope {c2.name}: {med * 1e3:.1f} us median, {by / (med * 1e-3) / 1e9:.0f} GB/s (flushed)")
+            del x2, qq, kk2, o1, o2
+        del flush
+
+    roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,4,false> (dense)",
+                "achieved": dense_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": dense_tf / PEAK_BF16_TFLOPS, "traffic": None,
+                "per_launch_flops": dense_flops, "avg_launch_ms": avg["dense"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a bounded sample (host cores)")
+        cpu = cpu_baseline(qo, ko, v, cfg, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']:.4g} TFLOP/s ({cpu['sample']})")
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": b, "heads": hd, "head_dim": d, "n_tokens": n,
+                   "grid": list(cfg.grid), "sparsity": args.sparsity, "block_size": 64,
+                   "step": "qk_norm_rope + dense_fwd + subblock_select + block_sparse_fwd"},
+        "roofline": roofline, "cpu_baseline": cpu, "components": components,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

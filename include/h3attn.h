@@ -1,0 +1,132 @@
+/*
+ * h3attn — attention hot path of a MiniMax-H3-class video diffusion transformer on AMD MI355X
+ * (gfx950 / CDNA4): fused QK RMSNorm + 3D RoPE, dense bf16 self-attention, SubBlock block
+ * selection and block-sparse attention.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [P3] "MiniMax-H3 的 6.24 倍，不能直接算成六倍产能" (xiaodao.ai/posts/minimax-h3-speed-quality)
+ *       section "先把近两倍的免费收益拿走": the lossless runtime's fused QK RMSNorm + 3D RoPE
+ *       kernel (fusion leaves the math unchanged);
+ *       section "6.24 倍里，真正有损的部分大约是三倍": SubBlock — queries and keys cut into
+ *       64-token blocks, low-contribution key blocks estimated and dropped, the rest fed to a
+ *       block-sparse attention kernel; sparsity = fraction of key blocks dropped.
+ *  [P4] "MiniMax-H3 在 8×H200 上基准测试：无损加速 1.95×，最高 6.24×" (chat-gpts.plus/?p=43161)
+ *       section "为什么重要": attention over very long latent sequences is a main cost.
+ *  [P2] mhpq.cn/news/447544, section 2.1: a video latent holds one 8x-downsampled latent per
+ *       frame, so the token count grows with frame count.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are caller-owned DEVICE pointers, 16-byte aligned. q, k, v and outputs are
+ *    contiguous [batch, n_tokens, heads, head_dim] ("BSHD") bf16 (raw 16-bit patterns).
+ *  - Token n of a T x H x W latent grid sits at n = (t*H + h)*W + w.
+ *  - Every call validates all arguments on the host first; on error it returns a nonzero
+ *    status, writes nothing, launches nothing, and h3attn_last_error() describes the problem.
+ *  - Calls are asynchronous on `stream` (NULL = the default stream); none synchronises, none
+ *    allocates device memory, none changes the current device. After a launch,
+ *    a HIP launch error is reported as H3ATTN_ERR_LAUNCH.
+ *  - head_dim must be 64 or 128; block_size must be 64.
+ *  - The library keeps no global state except a thread-local error string.
+ */
+#ifndef H3ATTN_H_
+#define H3ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t h3attn_bf16; /* raw bfloat16 bits */
+
+typedef struct {
+  int32_t t, h, w; /* latent grid; n_tokens = t*h*w */
+} h3attn_grid;
+
+typedef enum {
+  H3ATTN_OK = 0,
+  H3ATTN_ERR_INVALID_ARGUMENT = 1,
+  H3ATTN_ERR_UNSUPPORTED = 2,
+  H3ATTN_ERR_LAUNCH = 3
+} h3attn_status;
+
+/* Library version string, e.g. "h3attn 0.1.0 gfx950". Never NULL. */
+const char* h3attn_version(void);
+
+/* Message for the last failing call on this thread ("" if none). Never NULL. */
+const char* h3attn_last_error(void);
+
+/* Key blocks kept per query block at a given sparsity (fraction of key blocks dropped)
+ * [P3 "6.24 倍里…"]: min(n, max(1, ceil((1 - s) * n - 1e-9))), computed in double.
+ * Returns -1 if n_kblocks <= 0 or sparsity is outside [0, 1). */
+int32_t h3attn_keep_count(int32_t n_kblocks, double sparsity);
+
+/* Device workspace bytes that h3attn_subblock_select needs: pooled block means of q and k in
+ * float64 ([batch, heads, nB, head_dim] each) plus the float64 block-score matrix
+ * ([batch, heads, nB, nB]), each region 256-byte aligned. Returns 0 on invalid sizes. */
+size_t h3attn_select_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tokens,
+                                     int32_t head_dim, int32_t block_size);
+
+/* Fused per-head RMSNorm then 3D RoPE of q and k [P3 "先把近两倍的免费收益拿走"].
+ * For every (b, n, head) row x of q (resp. k):
+ *   y = x * w / sqrt(mean(x^2) + eps)          (w = q_weight resp. k_weight, float32 [head_dim])
+ *   head_dim is split into contiguous sections [d_t | d_h | d_w] (each even, sum = head_dim);
+ *   inside section a, channel pair (2j, 2j+1) is rotated by angle p_a * rope_theta^(-2j/d_a),
+ *   p_a being the token's integer t, h or w coordinate.
+ * Computed in float32 from the bf16 input, rounded once (nearest-even) to bf16.
+ * q_out / k_out may equal q_in / k_in (in place); otherwise the buffers must not overlap.
+ * Errors: null or misaligned pointer, batch/heads <= 0, grid sizes <= 0, odd or mismatched
+ * sections, eps < 0, theta <= 0 -> INVALID_ARGUMENT; head_dim not 64/128 -> UNSUPPORTED. */
+h3attn_status h3attn_qk_norm_rope(const h3attn_bf16* q_in, const h3attn_bf16* k_in,
+                                  h3attn_bf16* q_out, h3attn_bf16* k_out,
+                                  const float* q_weight, const float* k_weight,
+                                  int32_t batch, int32_t heads, int32_t head_dim, h3attn_grid grid,
+                                  int32_t d_t, int32_t d_h, int32_t d_w,
+                                  float rope_theta, float eps, hipStream_t stream);
+
+/* Dense non-causal self-attention [P4 "为什么重要"]: per (b, head),
+ *   out = softmax(q k^T / sqrt(head_dim)) v,   lse = ln sum_j exp(q.k_j / sqrt(head_dim)).
+ * bf16 MFMA products, float32 accumulation and softmax; P is rounded to bf16 before P.V.
+ * out: bf16 BSHD (must not overlap the inputs). lse: float32 [batch, heads, n_tokens] or NULL.
+ * Errors: null/misaligned pointer, sizes <= 0 -> INVALID_ARGUMENT; head_dim not 64/128 ->
+ * UNSUPPORTED. */
+h3attn_status h3attn_dense_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                               h3attn_bf16* out, float* lse,
+                               int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                               hipStream_t stream);
+
+/* SubBlock key-block selection [P3 "6.24 倍里…"]. Blocks are block_size consecutive tokens
+ * (the last one may be partial). Block importance is estimated, since the pages leave it open,
+ * as the dot product of the mean query of block i and the mean key of block j (over sqrt(D));
+ * per query block i the `keep` highest-scoring key blocks are kept, equal scores ranking the
+ * lower key index first. Means and scores are computed in float64.
+ * block_idx: int32 [batch, heads, nB, keep], each row ascending. keep must equal
+ * h3attn_keep_count(nB, sparsity). workspace: device buffer of at least
+ * h3attn_select_workspace_bytes(...) bytes, 256-byte aligned; its contents are scratch.
+ * Errors: bad pointers/sizes, sparsity outside [0,1), keep mismatch, workspace too small ->
+ * INVALID_ARGUMENT; head_dim not 64/128 or block_size != 64 -> UNSUPPORTED. */
+h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
+                                     int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                     int32_t block_size, double sparsity, int32_t keep,
+                                     int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* Block-sparse attention [P3 "6.24 倍里…"]: the queries of block i attend only to the tokens of
+ * the key blocks block_idx[b, head, i, 0..keep-1], with the softmax renormalised over those
+ * tokens (a partial last key block contributes only its valid tokens). Same numerics and
+ * outputs as h3attn_dense_fwd. block_idx rows must hold `keep` distinct indices in [0, nB);
+ * their order does not matter. Behaviour for other index values is undefined.
+ * Errors: as h3attn_dense_fwd, plus keep outside [1, nB] -> INVALID_ARGUMENT and
+ * block_size != 64 -> UNSUPPORTED. */
+h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                      const int32_t* block_idx, int32_t keep,
+                                      h3attn_bf16* out, float* lse,
+                                      int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                      int32_t block_size, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3ATTN_H_ */

@@ -177,7 +177,7 @@ def block_scores(q: np.ndarray, k: np.ndarray, block_size: int) -> np.ndarray:
     qm = block_means(q, block_size)
     km = block_means(k, block_size)
     d = q.shape[-1]
-    return np.einsum("bhid,bhjd->bhij", qm, km) / math.sqrt(d)
+    return np.matmul(qm, np.swapaxes(km, -1, -2)) / math.sqrt(d)
 
 
 def topk_blocks(scores: np.ndarray, keep: int) -> np.ndarray:

@@ -1,0 +1,125 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared symbol, and host-side
+validation rejects bad arguments before any HIP call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3attn.h")
+LIB = os.path.join(ROOT, "video_diffusion_transformer_qk_amd", "libh3attn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libh3attn.so not built")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(h3attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from video_diffusion_transformer_qk_amd import _lib
+    return _lib.load_library()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    from video_diffusion_transformer_qk_amd import _lib
+    syms = declared_symbols()
+    assert len(syms) >= 8
+    for s in syms:
+        assert hasattr(lib, s), s
+        assert s in _lib.SIGNATURES, f"{s} has no ctypes signature"
+    assert set(_lib.SIGNATURES) == set(syms)
+
+
+def test_version_and_error_string(lib):
+    assert b"gfx950" in lib.h3attn_version()
+    assert lib.h3attn_last_error() is not None
+
+
+def test_keep_count_matches_oracle_and_golden(lib):
+    golden = os.path.join(ROOT, "tests", "golden", "keep_counts.txt")
+    for line in open(golden):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        n, s, k = line.split()
+        assert lib.h3attn_keep_count(int(n), float(s)) == int(k)
+    for n in (1, 7, 63, 1953, 5733):
+        for s in (0.0, 0.1, 0.5, 0.75, 0.8, 0.95):
+            assert lib.h3attn_keep_count(n, s) == oracle.keep_count(n, s)
+    assert lib.h3attn_keep_count(0, 0.5) == -1
+    assert lib.h3attn_keep_count(10, 1.0) == -1
+    assert lib.h3attn_keep_count(10, -0.1) == -1
+
+
+def test_workspace_bytes(lib):
+    nb = 1953
+    means = 48 * nb * 128 * 8
+    scores = 48 * nb * nb * 8
+    r = lambda x: (x + 255) // 256 * 256
+    assert lib.h3attn_select_workspace_bytes(1, 48, 124992, 128, 64) == 2 * r(means) + r(scores)
+    assert lib.h3attn_select_workspace_bytes(0, 48, 124992, 128, 64) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launch
+
+
+def _err(lib):
+    return lib.h3attn_last_error().decode()
+
+
+def test_dense_validation(lib):
+    f = lib.h3attn_dense_fwd
+    assert f(None, FAKE, FAKE, FAKE, None, 1, 2, 64, 64, None) == 1 and "q is NULL" in _err(lib)
+    assert f(FAKE + 2, FAKE, FAKE, FAKE, None, 1, 2, 64, 64, None) == 1 and "aligned" in _err(lib)
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 64, 96, None) == 2 and "head_dim" in _err(lib)
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 0, 2, 64, 64, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 1, 0, 64, 64, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 0, 64, None) == 1
+    assert f(FAKE, 0x20000, 0x30000, FAKE, None, 1, 2, 64, 64, None) == 1 and "alias" in _err(lib)
+    assert f(FAKE, 0x20000, 0x30000, 0x40000, FAKE + 1, 1, 2, 64, 64, None) == 1 and "lse" in _err(lib)
+
+
+def test_norm_rope_validation(lib):
+    from video_diffusion_transformer_qk_amd._lib import Grid
+    f = lib.h3attn_qk_norm_rope
+    P = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000]
+    g = Grid(2, 3, 4)
+    assert f(*P, 1, 2, 64, Grid(0, 3, 4), 16, 24, 24, 1e4, 1e-6, None) == 1
+    assert f(*P, 1, 2, 64, g, 16, 24, 26, 1e4, 1e-6, None) == 1 and "add up" in _err(lib)
+    assert f(*P, 1, 2, 64, g, 15, 25, 24, 1e4, 1e-6, None) == 1 and "even" in _err(lib)
+    assert f(*P, 1, 2, 80, g, 16, 32, 32, 1e4, 1e-6, None) == 2
+    assert f(*P, 1, 2, 64, g, 16, 24, 24, 0.0, 1e-6, None) == 1 and "theta" in _err(lib)
+    assert f(*P, 1, 2, 64, g, 16, 24, 24, 1e4, -1.0, None) == 1 and "eps" in _err(lib)
+    assert f(P[0], P[1], P[2], P[2], P[4], P[5], 1, 2, 64, g, 16, 24, 24, 1e4, 1e-6, None) == 1
+
+
+def test_select_and_sparse_validation(lib):
+    f = lib.h3attn_subblock_select
+    nbytes = lib.h3attn_select_workspace_bytes(1, 2, 640, 64, 64)
+    ws = 0x100000
+    ok_args = dict(q=0x10000, k=0x20000, b=1, h=2, n=640, d=64, bs=64, s=0.5, keep=5, idx=0x30000, ws=ws, wsb=nbytes)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return f(a["q"], a["k"], a["b"], a["h"], a["n"], a["d"], a["bs"], a["s"], a["keep"], a["idx"], a["ws"], a["wsb"], None)
+
+    assert call(bs=32) == 2 and "block_size" in _err(lib)
+    assert call(s=1.0) == 1 and "sparsity" in _err(lib)
+    assert call(s=-0.5) == 1
+    assert call(keep=4) == 1 and "keep" in _err(lib)
+    assert call(wsb=nbytes - 1) == 1 and "workspace" in _err(lib)
+    assert call(ws=ws + 16) == 1 and "256-byte" in _err(lib)
+    assert call(idx=None) == 1
+    assert call(d=72) == 2
+    g = lib.h3attn_block_sparse_fwd
+    P = (0x10000, 0x20000, 0x30000)
+    assert g(*P, 0x40000, 0, 0x50000, None, 1, 2, 640, 64, 64, None) == 1 and "keep" in _err(lib)
+    assert g(*P, 0x40000, 11, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
+    assert g(*P, None, 3, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
+    assert g(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 32, None) == 2

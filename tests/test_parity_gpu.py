@@ -1,0 +1,270 @@
+"""GPU parity: every kernel, called through the C ABI (ctypes binding), against the float64
+oracle on the same seeded bf16 inputs. Small and ragged cases are compared in full; the three
+long-video workloads are compared on every head for a seeded sample of query blocks (each
+sampled row's oracle value is exact: a row depends on all keys but on no other row), while
+block selection and norm+RoPE are compared on the full tensors."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from inputs import CONFIGS, make_inputs, random_case, sample_query_blocks
+from inputs.generate import box_blocks
+from tests.parity_util import (LSE_MAX_ABS, check_attention, check_block_sets, check_norm_rope, f64,
+                               log)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def h3():
+    import video_diffusion_transformer_qk_amd as h3
+    h3.load_library()
+    return h3
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ full comparisons (small)
+
+def _full_norm_rope(h3, q, k, wq, wk, grid, sections, theta=1e4, eps=1e-6, what=""):
+    qo, ko = h3.qk_norm_rope(q, k, wq, wk, grid, sections, theta, eps)
+    _sync()
+    rq, rk = oracle.qk_norm_rope(f64(q), f64(k), f64(wq), f64(wk), tuple(grid), tuple(sections), theta,
+                                 float(np.float32(eps)))
+    for g, r, nm in ((qo, rq, "q"), (ko, rk, "k")):
+        worst, exact = check_norm_rope(f64(g), r)
+        log(f"{what} norm+rope {nm}: worst {worst:.3f} ulp, exact-RNE fraction {exact:.5f}")
+        assert worst <= 1.0, f"{what} {nm}: {worst} ulp"
+        assert exact > 0.99
+    return qo, ko
+
+
+def _full_dense(h3, q, k, v, what=""):
+    o, lse = h3.dense_fwd(q, k, v, return_lse=True)
+    _sync()
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v))
+    check_attention(f64(o), ro, f"{what} dense")
+    assert np.abs(f64(lse) - rl).max() <= LSE_MAX_ABS
+    return o
+
+
+def _full_select_sparse(h3, q, k, v, sparsity, what=""):
+    idx = h3.subblock_select(q, k, sparsity)
+    _sync()
+    qd, kd = f64(q), f64(k)
+    scores = oracle.block_scores(qd, kd, 64)
+    keep = oracle.keep_count(scores.shape[-1], sparsity)
+    ref_idx = oracle.topk_blocks(scores, keep)
+    assert tuple(idx.shape) == ref_idx.shape
+    check_block_sets(idx.cpu().numpy(), ref_idx, scores, keep, f"{what} select s={sparsity}")
+    o, lse = h3.block_sparse_fwd(q, k, v, idx, return_lse=True)
+    _sync()
+    ro, rl = oracle.sparse_attention(qd, kd, f64(v), idx.cpu().numpy(), 64)
+    check_attention(f64(o), ro, f"{what} sparse s={sparsity}")
+    assert np.abs(f64(lse) - rl).max() <= LSE_MAX_ABS
+    return idx, o
+
+
+def test_tiny_workload_all_stages(h3):
+    cfg = CONFIGS[1]
+    x = make_inputs(cfg, DEV)
+    qo, ko = _full_norm_rope(h3, x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps, "tiny")
+    _full_dense(h3, qo, ko, x["v"], "tiny")
+    idx, _ = _full_select_sparse(h3, qo, ko, x["v"], 0.5, "tiny")
+    assert idx.shape[-1] == 2
+
+
+def test_frame_workload_norm_rope(h3):
+    cfg = CONFIGS[2]
+    x = make_inputs(cfg, DEV)
+    _full_norm_rope(h3, x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps, "frame")
+
+
+def test_frame_workload_dense_select_sparse(h3):
+    cfg = CONFIGS[2]
+    x = make_inputs(cfg, DEV)
+    qo, ko = h3.qk_norm_rope(x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps)
+    _full_dense(h3, qo, ko, x["v"], "frame")
+    idx, _ = _full_select_sparse(h3, qo, ko, x["v"], 0.75, "frame")
+    assert idx.shape[-1] == 16
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", [1, 63, 200, 333])
+def test_ragged_shapes_full(h3, n, d):
+    c = random_case(2, n, 3, d, seed=100 + n + d, device=DEV)
+    _full_dense(h3, c["q"], c["k"], c["v"], f"ragged n={n} d={d}")
+    for s in (0.0, 0.5, 0.9):
+        _full_select_sparse(h3, c["q"], c["k"], c["v"], s, f"ragged n={n} d={d}")
+
+
+def test_ragged_norm_rope_grids(h3):
+    for grid, d, sec in (((3, 5, 7), 64, (16, 24, 24)), ((2, 3, 11), 128, (32, 48, 48)),
+                         ((1, 1, 9), 128, (0, 64, 64)), ((5, 2, 3), 64, (64, 0, 0))):
+        n = grid[0] * grid[1] * grid[2]
+        c = random_case(2, n, 5, d, seed=7 + n, device=DEV, scale=3.0)
+        _full_norm_rope(h3, c["q"], c["k"], c["wq"], c["wk"], grid, sec, 1e4, 1e-6, f"grid {grid}")
+
+
+def test_norm_rope_inplace_matches_out_of_place(h3):
+    c = random_case(1, 96, 4, 128, seed=3, device=DEV)
+    a, b = h3.qk_norm_rope(c["q"], c["k"], c["wq"], c["wk"], (2, 6, 8), (32, 48, 48))
+    q2, k2 = c["q"].clone(), c["k"].clone()
+    h3.qk_norm_rope(q2, k2, c["wq"], c["wk"], (2, 6, 8), (32, 48, 48), inplace=True)
+    _sync()
+    assert torch.equal(a, q2) and torch.equal(b, k2)
+
+
+def test_keep_all_sparse_is_bitwise_dense(h3):
+    c = random_case(1, 64 * 9, 2, 128, seed=11, device=DEV)
+    nb = 9
+    idx = torch.arange(nb, dtype=torch.int32, device=DEV).repeat(1, 2, nb, 1).contiguous()
+    dense = h3.dense_fwd(c["q"], c["k"], c["v"])
+    sparse = h3.block_sparse_fwd(c["q"], c["k"], c["v"], idx)
+    sel = h3.subblock_select(c["q"], c["k"], 0.0)
+    _sync()
+    assert torch.equal(sel.cpu(), idx.cpu())
+    assert torch.equal(dense, sparse)
+
+
+def test_sparse_index_order_irrelevant(h3):
+    c = random_case(1, 64 * 8, 2, 64, seed=12, device=DEV)
+    idx = h3.subblock_select(c["q"], c["k"], 0.5)
+    rev = idx.flip(-1).contiguous()
+    a = h3.block_sparse_fwd(c["q"], c["k"], c["v"], idx)
+    b = h3.block_sparse_fwd(c["q"], c["k"], c["v"], rev)
+    _sync()
+    check_attention(f64(a), f64(b).astype(np.float64), "reversed index order")
+
+
+def test_select_ties_resolve_to_lower_index(h3):
+    # all-zero queries: every score is 0 -> the kept set is the lowest `keep` indices
+    c = random_case(1, 64 * 10, 2, 128, seed=13, device=DEV)
+    q0 = torch.zeros_like(c["q"])
+    idx = h3.subblock_select(q0, c["k"], 0.7)
+    _sync()
+    keep = oracle.keep_count(10, 0.7)
+    assert keep == 3
+    assert (idx.cpu().numpy() == np.arange(keep)).all()
+    # duplicated key blocks: block 7 equals block 2, so whenever 7 is kept, 2 is kept too
+    k = c["k"].clone()
+    k[:, 7 * 64:8 * 64] = k[:, 2 * 64:3 * 64]
+    idx = h3.subblock_select(c["q"], k, 0.6)
+    _sync()
+    for row in idx.reshape(-1, idx.shape[-1]).cpu().numpy().tolist():
+        if 7 in row:
+            assert 2 in row
+
+
+def test_python_layer_rejects_bad_inputs(h3):
+    c = random_case(1, 64, 2, 64, seed=1, device=DEV)
+    with pytest.raises(TypeError):
+        h3.dense_fwd(c["q"].float(), c["k"], c["v"])
+    with pytest.raises(ValueError):
+        h3.dense_fwd(c["q"].transpose(1, 2), c["k"], c["v"])
+    with pytest.raises(h3.H3AttnError):
+        c2 = random_case(1, 64, 2, 96, seed=1, device=DEV)
+        h3.dense_fwd(c2["q"], c2["k"], c2["v"])
+    with pytest.raises(ValueError):
+        h3.qk_norm_rope(c["q"], c["k"], c["wq"], c["wk"], (2, 2, 2), (16, 24, 24))
+
+
+# ------------------------------------------------------------------ long-video workloads (sampled)
+
+def _sampled_dense(h3, q, k, v, qblocks_per_head, what):
+    o = h3.dense_fwd(q, k, v)
+    _sync()
+    qh, kh, vh, oh = q.cpu(), k.cpu(), v.cpu(), o.cpu()
+    worst = 0.0
+    for h, blocks in qblocks_per_head.items():
+        rows = np.concatenate([np.arange(i * 64, (i + 1) * 64) for i in blocks])
+        ref, _ = oracle.attention_head(f64(qh[0, rows, h]), f64(kh[0, :, h]), f64(vh[0, :, h]))
+        mx, _ = check_attention(f64(oh[0, rows, h]), ref, f"{what} dense head {h} blocks {blocks}")
+        worst = max(worst, mx)
+    return worst
+
+
+def _full_select_sampled_sparse(h3, q, k, v, sparsity, qblocks_per_head, what, head_chunk=4):
+    idx = h3.subblock_select(q, k, sparsity)
+    o = h3.block_sparse_fwd(q, k, v, idx)
+    _sync()
+    qh, kh, vh, oh, ih = q.cpu(), k.cpu(), v.cpu(), o.cpu(), idx.cpu().numpy()
+    heads = q.shape[2]
+    nb = idx.shape[2]
+    keep = idx.shape[3]
+    assert keep == oracle.keep_count(nb, sparsity)
+    for h0 in range(0, heads, head_chunk):
+        sl = slice(h0, min(heads, h0 + head_chunk))
+        scores = oracle.block_scores(f64(qh[:, :, sl]), f64(kh[:, :, sl]), 64)
+        ref_idx = oracle.topk_blocks(scores, keep)
+        check_block_sets(ih[:, sl], ref_idx, scores, keep, f"{what} select s={sparsity} heads {h0}..")
+    for h, blocks in qblocks_per_head.items():
+        for i in blocks:
+            rows = np.arange(i * 64, (i + 1) * 64)
+            keys = oracle.block_token_ids(ih[0, h, i], 64, q.shape[1])
+            ref, _ = oracle.attention_head(f64(qh[0, rows, h]), f64(kh[0, keys, h]), f64(vh[0, keys, h]))
+            check_attention(f64(oh[0, rows, h]), ref, f"{what} sparse s={sparsity} head {h} block {i}")
+
+
+def _samples(cfg, per_head, extra=()):
+    return {h: sample_query_blocks(cfg.n_blocks, per_head, seed=1000 * cfg.id + h, extra=extra)
+            for h in range(cfg.heads)}
+
+
+@pytest.mark.timeout(900)
+def test_video5s_dense_sampled(h3):
+    cfg = CONFIGS[3]
+    x = make_inputs(cfg, DEV)
+    _sampled_dense(h3, x["q"], x["k"], x["v"], _samples(cfg, 3), "5s")
+
+
+@pytest.mark.timeout(900)
+def test_video5s_select_and_sparse(h3):
+    cfg = CONFIGS[3]
+    x = make_inputs(cfg, DEV)
+    _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, _samples(cfg, 3), "5s", head_chunk=8)
+
+
+@pytest.mark.timeout(900)
+def test_video10s_norm_rope_full(h3):
+    cfg = CONFIGS[4]
+    x = make_inputs(cfg, DEV)
+    qo, ko = h3.qk_norm_rope(x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps)
+    _sync()
+    qh, kh, qoh, koh = x["q"].cpu(), x["k"].cpu(), qo.cpu(), ko.cpu()
+    wq, wk = f64(x["wq"]), f64(x["wk"])
+    eps = float(np.float32(cfg.eps))
+    for h0 in range(0, cfg.heads, 2):
+        sl = slice(h0, h0 + 2)
+        rq, rk = oracle.qk_norm_rope(f64(qh[:, :, sl]), f64(kh[:, :, sl]), wq, wk, cfg.grid, cfg.sections, cfg.theta, eps)
+        for g, r, nm in ((qoh[:, :, sl], rq, "q"), (koh[:, :, sl], rk, "k")):
+            worst, exact = check_norm_rope(f64(g), r)
+            log(f"10s norm+rope {nm} heads {h0}..{h0 + 1}: worst {worst:.3f} ulp, exact {exact:.5f}")
+            assert worst <= 1.0 and exact > 0.99
+
+
+@pytest.mark.timeout(900)
+def test_video10s_dense_select_sparse(h3):
+    cfg = CONFIGS[4]
+    x = make_inputs(cfg, DEV)
+    qo, ko = h3.qk_norm_rope(x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps)
+    _sampled_dense(h3, qo, ko, x["v"], _samples(cfg, 3), "10s")
+    for s in cfg.sparsities:
+        _full_select_sampled_sparse(h3, qo, ko, x["v"], s, _samples(cfg, 3), "10s")
+
+
+@pytest.mark.timeout(900)
+def test_video15s_boxes_select_sparse_dense(h3):
+    cfg = CONFIGS[5]
+    x = make_inputs(cfg, DEV)
+    bb = box_blocks(cfg.grid, x["boxes"])
+    extra = [bb[0], bb[len(bb) // 2], bb[-1]]
+    smp = _samples(cfg, 4, extra=extra)
+    _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, smp, "15s")
+    _sampled_dense(h3, x["q"], x["k"], x["v"], _samples(cfg, 2), "15s")

@@ -1,0 +1,14 @@
+"""h3attn: MI355X-native (gfx950) attention hot path of a MiniMax-H3-class video DiT.
+
+Four calls, each a hand-written HIP kernel behind a C ABI (include/h3attn.h):
+  qk_norm_rope      fused per-head QK RMSNorm + 3D (t/h/w) RoPE
+  dense_fwd         dense bf16 self-attention over the full latent sequence
+  subblock_select   SubBlock 64-token block scores and per-query-block top-k
+  block_sparse_fwd  attention over the kept key blocks only
+"""
+from ._lib import (LIB_PATH, SIGNATURES, H3AttnError, block_sparse_fwd, dense_fwd,  # noqa: F401
+                   keep_count, load_library, qk_norm_rope, select_workspace_bytes,
+                   subblock_select, version)
+
+__all__ = ["qk_norm_rope", "dense_fwd", "subblock_select", "block_sparse_fwd", "keep_count",
+           "select_workspace_bytes", "version", "H3AttnError", "load_library"]

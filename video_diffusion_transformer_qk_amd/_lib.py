@@ -1,0 +1,202 @@
+"""ctypes binding of libh3attn.so (the HIP kernels and their C ABI).
+
+Argument marshalling only: dtype/device/shape checks, raw device pointers and the current HIP
+stream go to the C ABI, and every step runs in the library's kernels. There is no fallback
+path: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libh3attn.so")
+
+STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "LAUNCH"}
+
+# (name, restype, argtypes) of every exported symbol declared in include/h3attn.h
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+
+class Grid(ctypes.Structure):
+    _fields_ = [("t", ctypes.c_int32), ("h", ctypes.c_int32), ("w", ctypes.c_int32)]
+
+
+SIGNATURES = {
+    "h3attn_version": (ctypes.c_char_p, []),
+    "h3attn_last_error": (ctypes.c_char_p, []),
+    "h3attn_keep_count": (_I32, [_I32, ctypes.c_double]),
+    "h3attn_select_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I64, _I32, _I32]),
+    "h3attn_qk_norm_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, Grid,
+                                           _I32, _I32, _I32, ctypes.c_float, ctypes.c_float, _P]),
+    "h3attn_dense_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _P]),
+    "h3attn_subblock_select": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32, _I32, ctypes.c_double,
+                                              _I32, _P, _P, ctypes.c_size_t, _P]),
+    "h3attn_block_sparse_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I64, _I32,
+                                               _I32, _P]),
+}
+
+
+class H3AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"h3attn {STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libh3attn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950); there is no non-HIP fallback")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise H3AttnError(status, load_library().h3attn_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def version() -> str:
+    return load_library().h3attn_version().decode()
+
+
+def keep_count(n_blocks: int, sparsity: float) -> int:
+    k = load_library().h3attn_keep_count(int(n_blocks), float(sparsity))
+    if k < 0:
+        raise ValueError(f"invalid n_blocks={n_blocks} or sparsity={sparsity}")
+    return int(k)
+
+
+def select_workspace_bytes(batch: int, heads: int, n_tokens: int, head_dim: int, block_size: int = 64) -> int:
+    return int(load_library().h3attn_select_workspace_bytes(batch, heads, n_tokens, head_dim, block_size))
+
+
+def qk_norm_rope(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                 grid: Sequence[int], sections: Sequence[int], theta: float = 1e4, eps: float = 1e-6,
+                 out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                 inplace: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fused per-head RMSNorm + 3D RoPE of bf16 q, k [B, N, heads, D]; returns (q', k')."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(w_q, "w_q", torch.float32, 1)
+    _need(w_k, "w_k", torch.float32, 1)
+    if q.shape != k.shape:
+        raise ValueError("q and k must have the same shape")
+    b, n, h, d = q.shape
+    if inplace:
+        qo, ko = q, k
+    elif out is not None:
+        qo, ko = out
+        _need(qo, "q_out", torch.bfloat16, 4)
+        _need(ko, "k_out", torch.bfloat16, 4)
+    else:
+        qo, ko = torch.empty_like(q), torch.empty_like(k)
+    g = Grid(*[int(x) for x in grid])
+    if g.t * g.h * g.w != n:
+        raise ValueError(f"grid {tuple(grid)} does not hold {n} tokens")
+    d_t, d_h, d_w = [int(x) for x in sections]
+    _check(lib.h3attn_qk_norm_rope(q.data_ptr(), k.data_ptr(), qo.data_ptr(), ko.data_ptr(),
+                                   w_q.data_ptr(), w_k.data_ptr(), b, h, d, g, d_t, d_h, d_w,
+                                   float(theta), float(eps), _stream()))
+    return qo, ko
+
+
+def dense_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, return_lse: bool = False,
+              out: Optional[torch.Tensor] = None):
+    """softmax(q k^T / sqrt(D)) v over the whole sequence, bf16 [B, N, heads, D]."""
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 4)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have the same shape")
+    b, n, h, d = q.shape
+    o = torch.empty_like(q) if out is None else out
+    _need(o, "out", torch.bfloat16, 4)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.h3attn_dense_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+                                b, h, n, d, _stream()))
+    return (o, lse) if return_lse else o
+
+
+def subblock_select(q: torch.Tensor, k: torch.Tensor, sparsity: float, block_size: int = 64,
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Kept key-block indices int32 [B, heads, nB, keep], rows ascending."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    if q.shape != k.shape:
+        raise ValueError("q and k must have the same shape")
+    b, n, h, d = q.shape
+    nb = -(-n // block_size)
+    keep = keep_count(nb, sparsity)
+    need = select_workspace_bytes(b, h, n, d, block_size)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    idx = torch.empty((b, h, nb, keep), dtype=torch.int32, device=q.device) if out is None else out
+    _need(idx, "block_idx", torch.int32, 4)
+    _check(lib.h3attn_subblock_select(q.data_ptr(), k.data_ptr(), b, h, n, d, block_size, float(sparsity),
+                                      keep, idx.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()))
+    return idx
+
+
+def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: torch.Tensor,
+                     block_size: int = 64, return_lse: bool = False, out: Optional[torch.Tensor] = None):
+    """Attention of each 64-query block over its kept key blocks only."""
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 4)
+    _need(block_idx, "block_idx", torch.int32, 4)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have the same shape")
+    b, n, h, d = q.shape
+    nb = -(-n // block_size)
+    if tuple(block_idx.shape[:3]) != (b, h, nb):
+        raise ValueError(f"block_idx must be [B, heads, nB, keep] = [{b}, {h}, {nb}, keep]")
+    keep = block_idx.shape[3]
+    o = torch.empty_like(q) if out is None else out
+    _need(o, "out", torch.bfloat16, 4)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.h3attn_block_sparse_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), block_idx.data_ptr(), keep,
+                                       o.data_ptr(), _ptr(lse), b, h, n, d, block_size, _stream()))
+    return (o, lse) if return_lse else o

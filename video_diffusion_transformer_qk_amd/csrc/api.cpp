@@ -1,0 +1,213 @@
+// C ABI of the h3attn library: host-side argument validation, RoPE table construction and
+// kernel dispatch. Every check runs before any HIP call; on failure nothing is launched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <hip/hip_runtime.h>
+
+#include "../../include/h3attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+h3attn_status fail(h3attn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+h3attn_status ok() {
+  g_err[0] = '\0';
+  return H3ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks that p is non-null and 16-byte aligned.
+#define CHECK_PTR(p)                                                                      \
+  do {                                                                                    \
+    if ((p) == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "%s is NULL", #p);       \
+    if (!aligned16(p)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+h3attn_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(H3ATTN_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+h3attn_status check_sizes(int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim) {
+  if (batch <= 0) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "batch must be > 0 (got %d)", batch);
+  if (heads <= 0) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "heads must be > 0 (got %d)", heads);
+  if (n_tokens <= 0) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "n_tokens must be > 0 (got %lld)", (long long)n_tokens);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(H3ATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  // every element offset must fit in int64 and the grid dimensions in 32 bits
+  const double elems = (double)batch * (double)n_tokens * (double)heads * (double)head_dim;
+  if (elems > 9.0e18) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "tensor too large");
+  if (n_tokens > (int64_t)1 << 31) return fail(H3ATTN_ERR_UNSUPPORTED, "n_tokens above 2^31 is not supported");
+  if (heads > 65535 || batch > 65535) return fail(H3ATTN_ERR_UNSUPPORTED, "batch and heads must be <= 65535");
+  return H3ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* h3attn_version(void) { return "h3attn 0.1.0 gfx950"; }
+
+const char* h3attn_last_error(void) { return g_err; }
+
+int32_t h3attn_keep_count(int32_t n_kblocks, double sparsity) {
+  if (n_kblocks <= 0 || !(sparsity >= 0.0 && sparsity < 1.0)) return -1;
+  double k = std::ceil((1.0 - sparsity) * (double)n_kblocks - 1e-9);
+  if (k < 1.0) k = 1.0;
+  if (k > (double)n_kblocks) k = (double)n_kblocks;
+  return (int32_t)k;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t h3attn_select_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tokens,
+                                     int32_t head_dim, int32_t block_size) {
+  if (batch <= 0 || heads <= 0 || n_tokens <= 0 || head_dim <= 0 || block_size <= 0) return 0;
+  const size_t nb = (size_t)((n_tokens + block_size - 1) / block_size);
+  const size_t bh = (size_t)batch * (size_t)heads;
+  const size_t means = align256(bh * nb * (size_t)head_dim * sizeof(double));
+  const size_t scores = align256(bh * nb * nb * sizeof(double));
+  return 2 * means + scores;
+}
+
+h3attn_status h3attn_qk_norm_rope(const h3attn_bf16* q_in, const h3attn_bf16* k_in,
+                                  h3attn_bf16* q_out, h3attn_bf16* k_out,
+                                  const float* q_weight, const float* k_weight,
+                                  int32_t batch, int32_t heads, int32_t head_dim, h3attn_grid grid,
+                                  int32_t d_t, int32_t d_h, int32_t d_w,
+                                  float rope_theta, float eps, hipStream_t stream) {
+  CHECK_PTR(q_in); CHECK_PTR(k_in); CHECK_PTR(q_out); CHECK_PTR(k_out);
+  CHECK_PTR(q_weight); CHECK_PTR(k_weight);
+  if (grid.t <= 0 || grid.h <= 0 || grid.w <= 0)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "grid sizes must be > 0 (got %d x %d x %d)", grid.t, grid.h, grid.w);
+  const int64_t n_tokens = (int64_t)grid.t * grid.h * grid.w;
+  h3attn_status st = check_sizes(batch, heads, n_tokens, head_dim);
+  if (st != H3ATTN_OK) return st;
+  if (d_t < 0 || d_h < 0 || d_w < 0 || (d_t & 1) || (d_h & 1) || (d_w & 1))
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "RoPE sections must be even and >= 0 (got %d/%d/%d)", d_t, d_h, d_w);
+  if (d_t + d_h + d_w != head_dim)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "RoPE sections %d+%d+%d must add up to head_dim %d", d_t, d_h, d_w, head_dim);
+  if (!(rope_theta > 0.0f) || !std::isfinite(rope_theta))
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "rope_theta must be finite and > 0");
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  const bool q_inplace = q_out == q_in, k_inplace = k_out == k_in;
+  if (q_out == k_out || (q_out == k_in && !k_inplace) || (k_out == q_in && !q_inplace))
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "q_out and k_out must be distinct and not alias the other input");
+
+  h3attn::RopeTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  const int32_t secs[3] = {d_t, d_h, d_w};
+  int pair = 0;
+  for (int ax = 0; ax < 3; ++ax) {
+    for (int j = 0; j < secs[ax] / 2; ++j, ++pair) {
+      tab.rate[pair] = std::pow((double)rope_theta, -2.0 * (double)j / (double)secs[ax]);
+      tab.axis[pair] = ax;
+    }
+  }
+  h3attn::NormRopeArgs a{};
+  a.q_in = q_in; a.k_in = k_in; a.q_out = q_out; a.k_out = k_out;
+  a.q_weight = q_weight; a.k_weight = k_weight;
+  a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
+  a.grid_h = grid.h; a.grid_w = grid.w; a.eps = eps;
+  h3attn::launch_qk_norm_rope(a, tab, stream);
+  return check_launch("h3attn_qk_norm_rope");
+}
+
+static h3attn_status check_attn(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                const h3attn_bf16* out, const float* lse,
+                                int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim) {
+  CHECK_PTR(q); CHECK_PTR(k); CHECK_PTR(v); CHECK_PTR(out);
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "lse is not 4-byte aligned");
+  h3attn_status st = check_sizes(batch, heads, n_tokens, head_dim);
+  if (st != H3ATTN_OK) return st;
+  if (out == q || out == k || out == v) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "out must not alias q, k or v");
+  return H3ATTN_OK;
+}
+
+h3attn_status h3attn_dense_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                               h3attn_bf16* out, float* lse,
+                               int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                               hipStream_t stream) {
+  h3attn_status st = check_attn(q, k, v, out, lse, batch, heads, n_tokens, head_dim);
+  if (st != H3ATTN_OK) return st;
+  h3attn::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.block_idx = nullptr;
+  a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
+  a.keep = 0; a.n_blocks = (int32_t)((n_tokens + 63) / 64);
+  h3attn::launch_dense_fwd(a, stream);
+  return check_launch("h3attn_dense_fwd");
+}
+
+h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
+                                     int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                     int32_t block_size, double sparsity, int32_t keep,
+                                     int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  CHECK_PTR(q); CHECK_PTR(k);
+  if (block_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is NULL");
+  if (reinterpret_cast<uintptr_t>(block_idx) & 3u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is not 4-byte aligned");
+  if (workspace == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  h3attn_status st = check_sizes(batch, heads, n_tokens, head_dim);
+  if (st != H3ATTN_OK) return st;
+  if (block_size != 64) return fail(H3ATTN_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", block_size);
+  if (!(sparsity >= 0.0 && sparsity < 1.0)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "sparsity must be in [0, 1) (got %g)", sparsity);
+  if ((int64_t)batch * heads > 65535) return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads must be <= 65535");
+  const int64_t nb = (n_tokens + block_size - 1) / block_size;
+  if (nb * 8 + 4096 > 160 * 1024)
+    return fail(H3ATTN_ERR_UNSUPPORTED, "%lld blocks exceed the per-row LDS budget of the top-k kernel", (long long)nb);
+  const int32_t want = h3attn_keep_count((int32_t)nb, sparsity);
+  if (keep != want) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep %d does not match keep_count(%lld, %g) = %d", keep, (long long)nb, sparsity, want);
+  const size_t need = h3attn_select_workspace_bytes(batch, heads, n_tokens, head_dim, block_size);
+  if (workspace_bytes < need)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  if ((uint64_t)batch * heads * (uint64_t)nb * (uint64_t)keep > ((uint64_t)1 << 62))
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx too large");
+
+  h3attn::SelectArgs a{};
+  a.q = q; a.k = k; a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
+  a.block_size = block_size; a.n_blocks = (int32_t)nb; a.keep = keep; a.block_idx = block_idx;
+  const size_t means = align256((size_t)batch * heads * (size_t)nb * head_dim * sizeof(double));
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.q_mean = reinterpret_cast<double*>(ws);
+  a.k_mean = reinterpret_cast<double*>(ws + means);
+  a.scores = reinterpret_cast<double*>(ws + 2 * means);
+  h3attn::launch_subblock_select(a, stream);
+  return check_launch("h3attn_subblock_select");
+}
+
+h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                      const int32_t* block_idx, int32_t keep,
+                                      h3attn_bf16* out, float* lse,
+                                      int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                      int32_t block_size, hipStream_t stream) {
+  h3attn_status st = check_attn(q, k, v, out, lse, batch, heads, n_tokens, head_dim);
+  if (st != H3ATTN_OK) return st;
+  if (block_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is NULL");
+  if (reinterpret_cast<uintptr_t>(block_idx) & 3u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is not 4-byte aligned");
+  if (block_size != 64) return fail(H3ATTN_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", block_size);
+  const int64_t nb = (n_tokens + block_size - 1) / block_size;
+  if (keep < 1 || keep > nb) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep must be in [1, %lld] (got %d)", (long long)nb, keep);
+  h3attn::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.block_idx = block_idx;
+  a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
+  a.keep = keep; a.n_blocks = (int32_t)nb;
+  h3attn::launch_block_sparse_fwd(a, stream);
+  return check_launch("h3attn_block_sparse_fwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,259 @@
+// Dense and block-sparse flash-style attention forward for gfx950 (bf16 MFMA, fp32 softmax).
+//
+// Sources: "MiniMax-H3 在 8×H200 上基准测试…" (chat-gpts.plus), section "为什么重要" — attention over
+// the long latent sequence is a main cost; "MiniMax-H3 的 6.24 倍，不能直接算成六倍产能"
+// (xiaodao.ai), section "6.24 倍里，真正有损的部分大约是三倍" — SubBlock sends only the kept
+// 64-token key blocks of each query block to a block-sparse attention kernel.
+//
+// Formulation. Each wave owns 32 query rows and computes the transposed score tile
+//   S^T (keys x queries) = K (keys x D) . Q^T (D x queries)
+// with v_mfma_f32_32x32x16_bf16, K as the A operand (read from LDS) and Q^T as the B operand
+// (held in registers for the whole loop). In the MFMA accumulator layout a lane holds one query
+// column and 16 key rows, so the softmax row statistics are mostly per-lane: the max needs one
+// exchange with the lane 32 away, and the row sum stays a per-lane partial until the epilogue.
+// The exponentials P^T are converted to bf16 in place and used directly as the B operand of
+//   O^T (D x queries) += V^T (D x keys) . P^T (keys x queries),
+// whose A operand (V^T) is read from a row-major V tile with the gfx950 LDS transpose read
+// (ds_read_b64_tr_b16). The key order inside each 16-key MFMA step is permuted identically on
+// both operands so that it matches the registers that already hold P^T.
+//
+// Pipeline: K/V tiles of 64 keys are double-buffered in LDS; tile t+1 is fetched from global
+// memory into registers while tile t is computed, then stored to the other LDS buffer; one
+// barrier per tile. The softmax uses exp2 with log2(e)/sqrt(D) folded into one FMA.
+// The sparse variant differs only in where tile t comes from: key block block_idx[.., t].
+#include "device_util.h"
+#include "kernels.h"
+
+namespace h3attn {
+namespace {
+
+constexpr int kBN = 64;  // keys per tile (= SubBlock block size)
+
+template <int D>
+struct Tile {
+  static constexpr int KS = 2 * D + 16;   // K row stride in LDS (bytes): conflict-free b128 reads
+  static constexpr int VS = 2 * D + 64;   // V row stride in LDS (bytes) for the transpose reads
+  static constexpr int K_BYTES = kBN * KS;
+  static constexpr int V_BYTES = kBN * VS;
+  static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
+  static constexpr int CHUNKS = kBN * D / 8;  // 16-byte chunks per tensor tile
+};
+
+template <int D, int WAVES, bool SPARSE>
+__global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnArgs a) {
+  using T = Tile<D>;
+  constexpr int NT = WAVES * 64;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int LOADS = T::CHUNKS / NT;  // 16-byte loads per thread per tensor
+  static_assert(T::CHUNKS % NT == 0, "tile must split evenly");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int head = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t N = a.n_tokens;
+  const int64_t row_stride = (int64_t)a.heads * D;  // elements between consecutive tokens
+  const int64_t base = ((int64_t)b * N) * row_stride + (int64_t)head * D;
+
+  const int64_t qtile0 = (int64_t)blockIdx.x * (WAVES * 32);
+  const int64_t q0 = qtile0 + wave * 32;
+  const int64_t my_q = q0 + l32;
+  const int64_t my_q_c = my_q < N ? my_q : N - 1;
+
+  // Q^T fragments (B operand), one bf16x8 per 16-wide k step.
+  bf16x8 qf[KSTEPS];
+  {
+    const uint16_t* qp = a.q + base + my_q_c * row_stride + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
+  }
+
+  int n_tiles;
+  const int32_t* idx_row = nullptr;
+  if constexpr (SPARSE) {
+    n_tiles = a.keep;
+    idx_row = a.block_idx + (((int64_t)b * a.heads + head) * a.n_blocks + blockIdx.x) * a.keep;
+  } else {
+    n_tiles = (int)((N + kBN - 1) / kBN);
+  }
+  auto tile_key0 = [&](int t) -> int64_t {
+    if constexpr (SPARSE) return (int64_t)idx_row[t] * kBN;
+    else return (int64_t)t * kBN;
+  };
+
+  // global -> register staging of one K/V tile
+  u32x4 kst[LOADS], vst[LOADS];
+  auto fetch = [&](int t) {
+    const int64_t key0 = tile_key0(t);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int ci = tid + i * NT;
+      const int row = ci / (D / 8);
+      const int col = ci % (D / 8);
+      int64_t key = key0 + row;
+      key = key < N ? key : N - 1;
+      const int64_t off = base + key * row_stride + col * 8;
+      kst[i] = *reinterpret_cast<const u32x4*>(a.k + off);
+      vst[i] = *reinterpret_cast<const u32x4*>(a.v + off);
+    }
+  };
+  auto stash = [&](int buf) {
+    unsigned char* kb = smem + buf * T::BUF_BYTES;
+    unsigned char* vb = kb + T::K_BYTES;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int ci = tid + i * NT;
+      const int row = ci / (D / 8);
+      const int col = ci % (D / 8);
+      *reinterpret_cast<u32x4*>(kb + row * T::KS + col * 16) = kst[i];
+      *reinterpret_cast<u32x4*>(vb + row * T::VS + col * 16) = vst[i];
+    }
+  };
+
+  const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
+  float m_run = -INFINITY;  // running max of s*sc (log2 units), shared by lanes l and l^32
+  float l_run = 0.f;        // per-lane partial row sum
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) fetch(t + 1);
+
+    const unsigned char* kb = smem + buf * T::BUF_BYTES;
+    const unsigned char* vb = kb + T::K_BYTES;
+
+    // S^T = K . Q^T for keys [0,32) and [32,64) of the tile
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + (32 * m + l32) * T::KS + (16 * ks + 8 * hi) * 2);
+        s[m] = mfma32x32x16(kf, qf[ks], s[m]);
+      }
+    }
+
+    // mask keys past the end of the sequence (only the tile that holds the last token)
+    const int64_t key0 = tile_key0(t);
+    if (key0 + kBN > N) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t kidx = key0 + 32 * m + 8 * (r / 4) + 4 * hi + (r % 4);
+          if (kidx >= N) s[m][r] = -INFINITY;
+        }
+    }
+
+    // online softmax (log2 domain)
+    float mx = s[0][0];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[m][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * sc);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    u32x4 pk[4];  // P^T as bf16, 4 x 8 values: step kk covers s[kk/2] regs 8*(kk%2) .. +7
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(fmaf(s[m][r], sc, -m_new));
+        const float p1 = fast_exp2(fmaf(s[m][r + 1], sc, -m_new));
+        psum += p0 + p1;
+        pk[2 * m + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
+      }
+    }
+    l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+
+    // O^T += V^T . P^T
+    const int ig = lane & 15;  // index inside the 16-lane group
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int m = kk >> 1, half = kk & 1;
+      const int k0 = 32 * m + 16 * half + 4 * hi;
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[kk]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
+        const unsigned char* p1 = vb + (k0 + (ig >> 2)) * T::VS + (d0 + 4 * (ig & 3)) * 2;
+        const i16x4 lo = lds_read_tr16(p1);
+        const i16x4 hi4 = lds_read_tr16(p1 + 8 * T::VS);
+        typedef __attribute__((ext_vector_type(8))) short i16x8;
+        const i16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, vv), pb, o[dt]);
+      }
+    }
+
+    if (t + 1 < n_tiles) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: combine the two lane-partial sums, normalise, store
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  if (my_q < N) {
+    uint16_t* op = a.out + base + my_q * row_stride;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * hi;
+        u32x2 w;
+        w[0] = pack_bf16x2(o[dt][4 * g + 0] * inv, o[dt][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + d) = w;
+      }
+    if (a.lse != nullptr && hi == 0)
+      a.lse[((int64_t)b * a.heads + head) * N + my_q] = (m_run + __log2f(l_tot)) * 0.6931471805599453f;
+  }
+}
+
+template <int D, int WAVES, bool SPARSE>
+void launch(const AttnArgs& a, hipStream_t stream) {
+  const size_t lds = 2 * Tile<D>::BUF_BYTES;
+  auto kern = attn_fwd_kernel<D, WAVES, SPARSE>;
+  static const bool lds_ok = [&] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
+  }();
+  (void)lds_ok;
+  dim3 grid;
+  if constexpr (SPARSE) grid = dim3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
+  else grid = dim3((unsigned)((a.n_tokens + WAVES * 32 - 1) / (WAVES * 32)), (unsigned)a.heads, (unsigned)a.batch);
+  hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), lds, stream, a);
+}
+
+}  // namespace
+
+void launch_dense_fwd(const AttnArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) launch<128, 4, false>(a, stream);
+  else launch<64, 4, false>(a, stream);
+}
+
+void launch_block_sparse_fwd(const AttnArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) launch<128, 2, true>(a, stream);
+  else launch<64, 2, true>(a, stream);
+}
+
+}  // namespace h3attn

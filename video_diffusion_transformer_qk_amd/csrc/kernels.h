@@ -1,0 +1,61 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels. Arguments are
+// already validated by the caller; launchers only compute grid shapes and enqueue kernels.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace h3attn {
+
+// Per-pair RoPE table built on the host: rotation rate (rad per position) and axis (0=t,1=h,2=w)
+// of each channel pair. Passed by value as a kernel argument.
+struct RopeTable {
+  double rate[64];
+  int32_t axis[64];
+};
+
+struct NormRopeArgs {
+  const uint16_t* q_in;
+  const uint16_t* k_in;
+  uint16_t* q_out;
+  uint16_t* k_out;
+  const float* q_weight;
+  const float* k_weight;
+  int64_t n_tokens;     // per batch element
+  int32_t batch, heads, head_dim;
+  int32_t grid_h, grid_w;
+  float eps;
+};
+
+void launch_qk_norm_rope(const NormRopeArgs& a, const RopeTable& table, hipStream_t stream);
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* block_idx;  // null for dense
+  uint16_t* out;
+  float* lse;                // may be null
+  int64_t n_tokens;
+  int32_t batch, heads, head_dim;
+  int32_t keep;              // sparse only
+  int32_t n_blocks;          // sparse only
+};
+
+void launch_dense_fwd(const AttnArgs& a, hipStream_t stream);
+void launch_block_sparse_fwd(const AttnArgs& a, hipStream_t stream);
+
+struct SelectArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t n_tokens;
+  int32_t batch, heads, head_dim, block_size, n_blocks, keep;
+  int32_t* block_idx;
+  double* q_mean;   // workspace: [B, H, nB, D]
+  double* k_mean;   // workspace: [B, H, nB, D]
+  double* scores;   // workspace: [B, H, nB, nB]
+};
+
+void launch_subblock_select(const SelectArgs& a, hipStream_t stream);
+
+}  // namespace h3attn

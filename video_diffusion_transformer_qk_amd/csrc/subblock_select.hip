@@ -1,0 +1,250 @@
+// SubBlock key-block selection for gfx950: block pooling, block scores, per-row top-k.
+//
+// Source: "MiniMax-H3 的 6.24 倍，不能直接算成六倍产能" (xiaodao.ai), section
+// "6.24 倍里，真正有损的部分大约是三倍": queries and keys are cut into 64-token blocks, the key
+// blocks that would contribute little are estimated and dropped, and the fraction dropped is
+// the sparsity. The pages leave the estimator open; this library scores key block j for query
+// block i by mean(q over block i) . mean(k over block j) and keeps the keep highest per row,
+// equal scores ranking the lower key index first, indices written in ascending order.
+//
+// Exactness: block sums of bf16 values are exact in float64, and the 1/sqrt(D) scale is
+// dropped (a positive factor does not change the order), so the GPU ranks by a float64 dot
+// product of the same means the float64 definition uses; the top-k itself is an exact radix
+// select over order-preserving 64-bit keys.
+//
+// Kernels:
+//  pool_kernel   grid (nB, heads, batch): 256 threads, 16-byte coalesced row reads, fp64 sums
+//                reduced through LDS in a fixed order -> means [B, H, nB, D] for q and k.
+//  score_kernel  grid (ceil(nB/64), ceil(nB/64), B*H): 64x64 tile of Qm . Km^T in fp64,
+//                D staged through LDS in chunks of 32, 4x4 outputs per thread.
+//  topk_kernel   grid (nB, heads, batch): one row of nB scores -> LDS keys -> 8-pass MSB radix
+//                select of the keep-th largest key -> ordered compaction of the kept indices.
+#include "device_util.h"
+#include "kernels.h"
+
+namespace h3attn {
+namespace {
+
+constexpr int kPoolThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int PAIRS = 2 * CH;        // (tensor, chunk) pairs
+  constexpr int TL = kPoolThreads / PAIRS;  // token lanes
+  __shared__ double red[TL][PAIRS][8];
+
+  const int tid = threadIdx.x;
+  const int pair = tid % PAIRS;
+  const int tl = tid / PAIRS;
+  const int tensor = pair / CH;
+  const int chunk = pair % CH;
+  const int j = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const int64_t N = a.n_tokens;
+  const int64_t row_stride = (int64_t)a.heads * D;
+  const int64_t t0 = (int64_t)j * a.block_size;
+  const int64_t t1 = t0 + a.block_size < N ? t0 + a.block_size : N;
+  const uint16_t* src = (tensor == 0 ? a.q : a.k) + ((int64_t)b * N) * row_stride + (int64_t)head * D + chunk * 8;
+
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t t = t0 + tl; t < t1; t += TL) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(src + t * row_stride);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += (double)bf16_lo(w[e]);
+      acc[2 * e + 1] += (double)bf16_hi(w[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[tl][pair][e] = acc[e];
+  __syncthreads();
+  // tl == 0 lanes finish the sum in a fixed order and write the mean
+  if (tl == 0) {
+    const double cnt = (double)(t1 - t0);
+    double* dst = (tensor == 0 ? a.q_mean : a.k_mean) + (((int64_t)b * a.heads + head) * a.n_blocks + j) * D + chunk * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double s = 0.0;
+      for (int u = 0; u < TL; ++u) s += red[u][pair][e];
+      dst[e] = s / cnt;
+    }
+  }
+}
+
+constexpr int kScoreTile = 64;
+constexpr int kScoreDc = 32;
+
+template <int D>
+__global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
+  __shared__ double qs[kScoreDc][kScoreTile + 1];
+  __shared__ double ks[kScoreDc][kScoreTile + 1];
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;  // 4 rows (i) x 4 cols (j) each
+  const int64_t bh = blockIdx.z;
+  const int nb = a.n_blocks;
+  const int i0 = blockIdx.y * kScoreTile, j0 = blockIdx.x * kScoreTile;
+  const double* qm = a.q_mean + bh * (int64_t)nb * D;
+  const double* km = a.k_mean + bh * (int64_t)nb * D;
+  double acc[4][4] = {};
+  for (int dc = 0; dc < D; dc += kScoreDc) {
+    // load 64 x 32 chunks of Qm and Km, transposed into [d][row]
+    for (int e = tid; e < kScoreTile * kScoreDc; e += 256) {
+      const int r = e / kScoreDc, d = e % kScoreDc;
+      const int qi = i0 + r < nb ? i0 + r : nb - 1;
+      const int kj = j0 + r < nb ? j0 + r : nb - 1;
+      qs[d][r] = qm[(int64_t)qi * D + dc + d];
+      ks[d][r] = km[(int64_t)kj * D + dc + d];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int d = 0; d < kScoreDc; ++d) {
+      double qv[4], kv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { qv[u] = qs[d][ty + 16 * u]; kv[u] = ks[d][tx + 16 * u]; }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[u][w] = fma(qv[u], kv[w], acc[u][w]);
+    }
+    __syncthreads();
+  }
+  double* out = a.scores + bh * (int64_t)nb * nb;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = i0 + ty + 16 * u;
+    if (i >= nb) continue;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int j = j0 + tx + 16 * w;
+      if (j < nb) out[(int64_t)i * nb + j] = acc[u][w];
+    }
+  }
+}
+
+// order-preserving map of a double to uint64 (larger double -> larger key); -0 is folded to +0
+__device__ __forceinline__ uint64_t order_key(double x) {
+  x = x + 0.0;  // -0.0 + 0.0 = +0.0 under round-to-nearest
+  const uint64_t u = __double_as_longlong(x);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+constexpr int kTopkThreads = 256;
+
+// block-wide exclusive prefix sum of one int per thread; returns the block total in *total
+__device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= 4 ints */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    const int s = scratch[w];
+    if (w < wave) before += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
+  __shared__ uint32_t hist[256];
+  __shared__ int scan_scratch[4];
+  __shared__ uint64_t sh_prefix;
+  __shared__ int sh_krem;
+
+  const int tid = threadIdx.x;
+  const int nb = a.n_blocks;
+  const int i = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const int64_t row = ((int64_t)b * a.heads + head) * nb + i;
+  const double* sc = a.scores + row * nb;
+  for (int j = tid; j < nb; j += kTopkThreads) keys[j] = order_key(sc[j]);
+
+  uint64_t prefix = 0, mask = 0;
+  int k_rem = a.keep;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int j = tid; j < nb; j += kTopkThreads) {
+      const uint64_t key = keys[j];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int above = 0, d = 255;
+      for (; d > 0; --d) {
+        const int h = (int)hist[d];
+        if (above + h >= k_rem) break;
+        above += h;
+      }
+      sh_prefix = prefix | ((uint64_t)d << shift);
+      sh_krem = k_rem - above;
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    k_rem = sh_krem;
+    mask |= (uint64_t)0xff << shift;
+    __syncthreads();
+  }
+  const uint64_t thr = prefix;  // the keep-th largest key; take k_rem of its equal keys
+
+  // ordered compaction over contiguous per-thread index ranges
+  const int per = (nb + kTopkThreads - 1) / kTopkThreads;
+  const int j0 = tid * per;
+  const int j1 = j0 + per < nb ? j0 + per : nb;
+  int n_eq = 0;
+  for (int j = j0; j < j1; ++j) n_eq += keys[j] == thr;
+  int tot;
+  const int eq_before = block_exclusive_scan(n_eq, &tot, scan_scratch);
+  int n_sel = 0;
+  {
+    int e = eq_before;
+    for (int j = j0; j < j1; ++j) {
+      const uint64_t key = keys[j];
+      if (key > thr) ++n_sel;
+      else if (key == thr) { if (e < k_rem) ++n_sel; ++e; }
+    }
+  }
+  const int pos0 = block_exclusive_scan(n_sel, &tot, scan_scratch);
+  int32_t* dst = a.block_idx + row * a.keep;
+  {
+    int e = eq_before, p = pos0;
+    for (int j = j0; j < j1; ++j) {
+      const uint64_t key = keys[j];
+      bool take = false;
+      if (key > thr) take = true;
+      else if (key == thr) { take = e < k_rem; ++e; }
+      if (take) dst[p++] = j;
+    }
+  }
+}
+
+}  // namespace
+
+void launch_subblock_select(const SelectArgs& a, hipStream_t stream) {
+  const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
+  if (a.head_dim == 128) hipLaunchKernelGGL(pool_kernel<128>, g3, dim3(kPoolThreads), 0, stream, a);
+  else hipLaunchKernelGGL(pool_kernel<64>, g3, dim3(kPoolThreads), 0, stream, a);
+  const unsigned tiles = (unsigned)((a.n_blocks + kScoreTile - 1) / kScoreTile);
+  const dim3 gs(tiles, tiles, (unsigned)(a.batch * a.heads));
+  if (a.head_dim == 128) hipLaunchKernelGGL(score_kernel<128>, gs, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(score_kernel<64>, gs, dim3(256), 0, stream, a);
+  const size_t lds = (size_t)a.n_blocks * sizeof(uint64_t);
+  static const bool lds_ok = [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024) == hipSuccess;
+  }();
+  (void)lds_ok;
+  hipLaunchKernelGGL(topk_kernel, g3, dim3(kTopkThreads), lds, stream, a);
+}
+
+}  // namespace h3attn
