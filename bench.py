@@ -45,7 +45,29 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-extra", action="store_true", help="skip the flushed norm+RoPE runs")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first copy 1 GiB once, so that memory counters of a known-size copy sit in the same trace")
     return p.parse_args()
+
+
+def measured_traffic(kernel_prefix: str):
+    """Bytes per launch of a kernel from the committed PMC summary, or None when the kernel's
+    source has changed since the counters were taken (sha256 prefix recorded in the summary)."""
+    import hashlib
+    summary = os.path.join(ROOT, "profiles", "pmc_traffic_video5s.txt")
+    src = os.path.join(ROOT, "video_diffusion_transformer_qk_amd", "csrc", "attention.hip")
+    try:
+        lines = open(summary).read().splitlines()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    recorded = [l.split(":", 1)[1].strip() for l in lines if l.startswith("attention_source_sha256:")]
+    if not recorded or recorded[0] != sha:
+        return None
+    for l in lines:
+        if l.startswith(kernel_prefix):
+            return float(l.split("|")[3].strip())
+    return None
 
 
 def flush_caches(buf: torch.Tensor):
@@ -109,6 +131,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"generating workload {cfg.name} on {torch.cuda.get_device_name(dev)}")
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     x = make_inputs(cfg, dev)
     q, k, v, wq, wk = x["q"], x["k"], x["v"], x["wq"], x["wk"]
     b, n, hd, d = q.shape
@@ -202,9 +231,11 @@ def main():
             del x2, qq, kk2, o1, o2
         del flush
 
-    roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,4,false> (dense)",
+    roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,8,2,true,false> (dense)",
                 "achieved": dense_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": dense_tf / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": dense_tf / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic("attn_fwd_kernel<128,8,2,true,false,0> (dense)"),
+                "traffic_unit": "bytes per launch (FETCH_SIZE x2.000 + WRITE_SIZE x1.000, copy-calibrated)",
                 "per_launch_flops": dense_flops, "avg_launch_ms": avg["dense"]}
 
     cpu = None

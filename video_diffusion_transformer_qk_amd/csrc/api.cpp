@@ -107,6 +107,8 @@ h3attn_status h3attn_qk_norm_rope(const h3attn_bf16* q_in, const h3attn_bf16* k_
   if (q_out == k_out || (q_out == k_in && !k_inplace) || (k_out == q_in && !q_inplace))
     return fail(H3ATTN_ERR_INVALID_ARGUMENT, "q_out and k_out must be distinct and not alias the other input");
 
+  if (((int64_t)batch * n_tokens / 8 + 1) * ((2 * (int64_t)heads + 3) / 4) >= ((int64_t)1 << 31))
+    return fail(H3ATTN_ERR_UNSUPPORTED, "batch*n_tokens*heads too large for one launch");
   h3attn::RopeTable tab;
   std::memset(&tab, 0, sizeof(tab));
   const int32_t secs[3] = {d_t, d_h, d_w};
@@ -202,6 +204,8 @@ h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k
   if (block_size != 64) return fail(H3ATTN_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", block_size);
   const int64_t nb = (n_tokens + block_size - 1) / block_size;
   if (keep < 1 || keep > nb) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep must be in [1, %lld] (got %d)", (long long)nb, keep);
+  if (nb * heads * (int64_t)batch >= ((int64_t)1 << 31))
+    return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads*n_blocks must be below 2^31");
   h3attn::AttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.block_idx = block_idx;
   a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;

@@ -17,10 +17,15 @@
 // (ds_read_b64_tr_b16). The key order inside each 16-key MFMA step is permuted identically on
 // both operands so that it matches the registers that already hold P^T.
 //
-// Pipeline: K/V tiles of 64 keys are double-buffered in LDS; tile t+1 is fetched from global
-// memory into registers while tile t is computed, then stored to the other LDS buffer; one
-// barrier per tile. The softmax uses exp2 with log2(e)/sqrt(D) folded into one FMA.
-// The sparse variant differs only in where tile t comes from: key block block_idx[.., t].
+// Pipeline: tile t+1 is fetched from global memory into registers while tile t is computed,
+// then stored to LDS. Dense: 8 waves (256 queries) share each 64-key K/V tile, double-buffered
+// in LDS (one barrier per tile), two waves per SIMD (256-register budget) so one wave's MFMAs
+// overlap the other's softmax. Sparse: the workgroup is one 64-query block (2 waves) with a
+// single LDS tile (two barriers per tile) so four workgroups fit per CU, and workgroups are
+// ordered in windows of 1024 so that the resident ones cover one head (its K/V stays in the
+// MALL) with each XCD on consecutive query blocks. The softmax uses exp2 with
+// log2(e)/sqrt(D) folded into one FMA, and the running max only moves (with a wave-uniform O
+// rescale) when a tile exceeds it by more than 2^8.
 #include "device_util.h"
 #include "kernels.h"
 
@@ -39,8 +44,30 @@ struct Tile {
   static constexpr int CHUNKS = kBN * D / 8;  // 16-byte chunks per tensor tile
 };
 
-template <int D, int WAVES, bool SPARSE>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnArgs a) {
+// Tuning knobs: WAVES waves per workgroup (32 queries each); OCC minimum waves per SIMD (2 caps
+// the kernel at 256 registers so two waves share each SIMD and overlap each other's MFMA and
+// softmax work); DBUF double-buffers the K/V tile in LDS (one barrier per tile) instead of
+// keeping a single LDS tile (two barriers per tile, half the LDS, more workgroups per CU).
+// Maps the linear workgroup id to a work item so that each of the 8 XCDs (which receive
+// workgroups round-robin) processes one contiguous range of (query tile, head, batch) items:
+// neighbouring query tiles of one head then share an XCD and its L2.
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t lin, int64_t total) {
+  const int64_t x = lin % 8, k = lin / 8, q = total / 8, r = total % 8;
+  return x * q + (x < r ? x : r) + k;
+}
+
+// Same idea applied per window of 8*C consecutive workgroups: the workgroups resident at any
+// time then cover one narrow range of items (one head's K/V stays in the 256 MB MALL), and
+// inside the window each XCD gets C consecutive items.
+template <int C>
+__device__ __forceinline__ int64_t xcd_grouped(int64_t lin, int64_t total) {
+  const int64_t base = lin / (8 * C) * (8 * C), k = lin - base, rem = total - base;
+  if (rem >= 8 * C) return base + (k % 8) * C + k / 8;
+  return base + xcd_contiguous(k, rem);
+}
+
+template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0>
+__global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
   using T = Tile<D>;
   constexpr int NT = WAVES * 64;
   constexpr int KSTEPS = D / 16;
@@ -55,13 +82,25 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int head = blockIdx.y;
-  const int b = blockIdx.z;
   const int64_t N = a.n_tokens;
+  int64_t qtile;
+  int head, b;
+  if constexpr (XCD != 0) {
+    const int64_t n_qt = SPARSE ? a.n_blocks : (N + WAVES * 32 - 1) / (WAVES * 32);
+    const int64_t total = n_qt * a.heads * a.batch;
+    const int64_t item = XCD == 1 ? xcd_contiguous(blockIdx.x, total) : xcd_grouped<XCD>(blockIdx.x, total);
+    qtile = item % n_qt;
+    head = (int)((item / n_qt) % a.heads);
+    b = (int)(item / (n_qt * a.heads));
+  } else {
+    qtile = blockIdx.x;
+    head = blockIdx.y;
+    b = blockIdx.z;
+  }
   const int64_t row_stride = (int64_t)a.heads * D;  // elements between consecutive tokens
   const int64_t base = ((int64_t)b * N) * row_stride + (int64_t)head * D;
 
-  const int64_t qtile0 = (int64_t)blockIdx.x * (WAVES * 32);
+  const int64_t qtile0 = qtile * (WAVES * 32);
   const int64_t q0 = qtile0 + wave * 32;
   const int64_t my_q = q0 + l32;
   const int64_t my_q_c = my_q < N ? my_q : N - 1;
@@ -79,7 +118,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   const int32_t* idx_row = nullptr;
   if constexpr (SPARSE) {
     n_tiles = a.keep;
-    idx_row = a.block_idx + (((int64_t)b * a.heads + head) * a.n_blocks + blockIdx.x) * a.keep;
+    idx_row = a.block_idx + (((int64_t)b * a.heads + head) * a.n_blocks + qtile) * a.keep;
   } else {
     n_tiles = (int)((N + kBN - 1) / kBN);
   }
@@ -129,7 +168,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+    const int buf = DBUF ? (t & 1) : 0;
     if (t + 1 < n_tiles) fetch(t + 1);
 
     const unsigned char* kb = smem + buf * T::BUF_BYTES;
@@ -158,33 +197,38 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnArgs a) {
         }
     }
 
-    // online softmax (log2 domain)
+    // online softmax (log2 domain). The running max only moves when the tile max exceeds it by
+    // more than 8 (a factor 256): until then exp2 values stay <= 256, which fp32 sums and bf16 P
+    // hold exactly enough, and the O/l rescale (a wave-uniform branch) is skipped.
     float mx = s[0][0];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[m][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sc);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+    if (__any(mx > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
     float psum = 0.f;
     u32x4 pk[4];  // P^T as bf16, 4 x 8 values: step kk covers s[kk/2] regs 8*(kk%2) .. +7
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(s[m][r], sc, -m_new));
-        const float p1 = fast_exp2(fmaf(s[m][r + 1], sc, -m_new));
+        const float p0 = fast_exp2(fmaf(s[m][r], sc, -m_run));
+        const float p1 = fast_exp2(fmaf(s[m][r + 1], sc, -m_run));
         psum += p0 + p1;
         pk[2 * m + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
       }
     }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    l_run += psum;
 
     // O^T += V^T . P^T
     const int ig = lane & 15;  // index inside the 16-lane group
@@ -205,8 +249,16 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnArgs a) {
       }
     }
 
-    if (t + 1 < n_tiles) stash(buf ^ 1);
-    __syncthreads();
+    if constexpr (DBUF) {
+      if (t + 1 < n_tiles) stash(buf ^ 1);
+      __syncthreads();
+    } else {
+      __syncthreads();  // every wave is done reading the single tile
+      if (t + 1 < n_tiles) {
+        stash(0);
+        __syncthreads();
+      }
+    }
   }
 
   // epilogue: combine the two lane-partial sums, normalise, store
@@ -229,31 +281,43 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int WAVES, bool SPARSE>
+
+template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0>
 void launch(const AttnArgs& a, hipStream_t stream) {
-  const size_t lds = 2 * Tile<D>::BUF_BYTES;
-  auto kern = attn_fwd_kernel<D, WAVES, SPARSE>;
+  const size_t lds = (DBUF ? 2 : 1) * Tile<D>::BUF_BYTES;
+  auto kern = attn_fwd_kernel<D, WAVES, OCC, DBUF, SPARSE, XCD>;
   static const bool lds_ok = [&] {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
   }();
   (void)lds_ok;
   dim3 grid;
-  if constexpr (SPARSE) grid = dim3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
-  else grid = dim3((unsigned)((a.n_tokens + WAVES * 32 - 1) / (WAVES * 32)), (unsigned)a.heads, (unsigned)a.batch);
+  const int64_t n_qt = SPARSE ? a.n_blocks : (a.n_tokens + WAVES * 32 - 1) / (WAVES * 32);
+  if constexpr (XCD != 0) grid = dim3((unsigned)(n_qt * a.heads * a.batch));
+  else grid = dim3((unsigned)n_qt, (unsigned)a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), lds, stream, a);
 }
 
 }  // namespace
 
+#ifndef H3ATTN_DENSE_CFG
+#define H3ATTN_DENSE_CFG 8, 2, true
+#endif
+#ifndef H3ATTN_SPARSE_CFG
+#define H3ATTN_SPARSE_CFG 2, 2, false
+#endif
+#ifndef H3ATTN_SPARSE_XCD
+#define H3ATTN_SPARSE_XCD 128
+#endif
+
 void launch_dense_fwd(const AttnArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) launch<128, 4, false>(a, stream);
-  else launch<64, 4, false>(a, stream);
+  if (a.head_dim == 128) launch<128, H3ATTN_DENSE_CFG, false>(a, stream);
+  else launch<64, H3ATTN_DENSE_CFG, false>(a, stream);
 }
 
 void launch_block_sparse_fwd(const AttnArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) launch<128, 2, true>(a, stream);
-  else launch<64, 2, true>(a, stream);
+  if (a.head_dim == 128) launch<128, H3ATTN_SPARSE_CFG, true, H3ATTN_SPARSE_XCD>(a, stream);
+  else launch<64, H3ATTN_SPARSE_CFG, true, H3ATTN_SPARSE_XCD>(a, stream);
 }
 
 }  // namespace h3attn

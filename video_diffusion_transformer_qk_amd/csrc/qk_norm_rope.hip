@@ -18,19 +18,40 @@ namespace h3attn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 8;  // rows (heads of q, then of k) handled by one thread
+#ifndef H3ATTN_NR_ROWS
+#define H3ATTN_NR_ROWS 8
+#endif
+#ifndef H3ATTN_NR_NT
+#define H3ATTN_NR_NT 1
+#endif
+constexpr int kRows = H3ATTN_NR_ROWS;  // rows (heads of q, then of k) handled by one thread
+
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p) {
+  if constexpr (H3ATTN_NR_NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <typename T>
+__device__ __forceinline__ void store_stream(T* p, T v) {
+  if constexpr (H3ATTN_NR_NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(NormRopeArgs a, RopeTable tab) {
   constexpr int TPR = D / 8;                 // lanes per row
   constexpr int TOK_PER_BLOCK = kThreads / TPR;
   const int c = threadIdx.x % TPR;           // chunk index inside the row: channels 8c .. 8c+7
-  const int64_t tok = (int64_t)blockIdx.x * TOK_PER_BLOCK + threadIdx.x / TPR;  // over batch*n_tokens
+  // consecutive workgroups take the row groups of the same tokens, so one token's q and k rows
+  // are read close together in time
+  const int n_rg = (2 * a.heads + kRows - 1) / kRows;
+  const int rg = (int)(blockIdx.x % n_rg);
+  const int64_t tok = (int64_t)(blockIdx.x / n_rg) * TOK_PER_BLOCK + threadIdx.x / TPR;  // over batch*n_tokens
   const int64_t total_tok = (int64_t)a.batch * a.n_tokens;
   if (tok >= total_tok) return;              // whole row groups exit together (TPR divides 64)
 
   const int rows_total = 2 * a.heads;
-  const int r0 = blockIdx.y * kRows;
+  const int r0 = rg * kRows;
 
   // Issue all loads first.
   u32x4 x[kRows];
@@ -41,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(NormRopeArgs a, 
       const bool is_k = r >= a.heads;
       const int head = is_k ? r - a.heads : r;
       const uint16_t* src = (is_k ? a.k_in : a.q_in) + ((tok * a.heads + head) * D + 8 * c);
-      x[i] = *reinterpret_cast<const u32x4*>(src);
+      x[i] = load_stream(reinterpret_cast<const u32x4*>(src));
     }
   }
 
@@ -96,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(NormRopeArgs a, 
     }
     const int head = is_k ? r - a.heads : r;
     uint16_t* dst = (is_k ? a.k_out : a.q_out) + ((tok * a.heads + head) * D + 8 * c);
-    *reinterpret_cast<u32x4*>(dst) = o;
+    store_stream(reinterpret_cast<u32x4*>(dst), o);
   }
 }
 
@@ -104,14 +125,14 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(NormRopeArgs a, 
 
 void launch_qk_norm_rope(const NormRopeArgs& a, const RopeTable& table, hipStream_t stream) {
   const int64_t total_tok = (int64_t)a.batch * a.n_tokens;
-  const int row_groups = (2 * a.heads + kRows - 1) / kRows;
+  const int64_t row_groups = (2 * a.heads + kRows - 1) / kRows;
   if (a.head_dim == 128) {
     constexpr int tpb = kThreads / 16;
-    dim3 grid((unsigned)((total_tok + tpb - 1) / tpb), (unsigned)row_groups);
+    const dim3 grid((unsigned)((total_tok + tpb - 1) / tpb * row_groups));
     hipLaunchKernelGGL(qk_norm_rope_kernel<128>, grid, dim3(kThreads), 0, stream, a, table);
   } else {
     constexpr int tpb = kThreads / 8;
-    dim3 grid((unsigned)((total_tok + tpb - 1) / tpb), (unsigned)row_groups);
+    const dim3 grid((unsigned)((total_tok + tpb - 1) / tpb * row_groups));
     hipLaunchKernelGGL(qk_norm_rope_kernel<64>, grid, dim3(kThreads), 0, stream, a, table);
   }
 }
