@@ -33,21 +33,18 @@ namespace h3attn {
 namespace {
 
 constexpr int kBN = 64;  // keys per tile (= SubBlock block size)
+#define kOnes2 (__builtin_bit_cast(bf16x2, 0x3f803f80u))  // bf16 pair (1.0, 1.0)
 
-template <int D>
+template <int D, int BN>
 struct Tile {
   static constexpr int KS = 2 * D + 16;   // K row stride in LDS (bytes): conflict-free b128 reads
   static constexpr int VS = 2 * D + 64;   // V row stride in LDS (bytes) for the transpose reads
-  static constexpr int K_BYTES = kBN * KS;
-  static constexpr int V_BYTES = kBN * VS;
+  static constexpr int K_BYTES = BN * KS;
+  static constexpr int V_BYTES = BN * VS;
   static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
-  static constexpr int CHUNKS = kBN * D / 8;  // 16-byte chunks per tensor tile
+  static constexpr int CHUNKS = BN * D / 8;  // 16-byte chunks per tensor tile
 };
 
-// Tuning knobs: WAVES waves per workgroup (32 queries each); OCC minimum waves per SIMD (2 caps
-// the kernel at 256 registers so two waves share each SIMD and overlap each other's MFMA and
-// softmax work); DBUF double-buffers the K/V tile in LDS (one barrier per tile) instead of
-// keeping a single LDS tile (two barriers per tile, half the LDS, more workgroups per CU).
 // Maps the linear workgroup id to a work item so that each of the 8 XCDs (which receive
 // workgroups round-robin) processes one contiguous range of (query tile, head, batch) items:
 // neighbouring query tiles of one head then share an XCD and its L2.
@@ -66,9 +63,18 @@ __device__ __forceinline__ int64_t xcd_grouped(int64_t lin, int64_t total) {
   return base + xcd_contiguous(k, rem);
 }
 
-template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0>
+// Tuning knobs: WAVES waves per workgroup (32 queries each); OCC minimum waves per SIMD (2 caps
+// the kernel at 256 registers so two waves share each SIMD and overlap each other's MFMA and
+// softmax work); DBUF double-buffers the K/V tile in LDS (one barrier per tile) instead of
+// keeping a single LDS tile (two barriers per tile, half the LDS, more workgroups per CU); XCD
+// selects the workgroup order (0: grid order, 1: one contiguous range per XCD, C > 1: windows
+// of 8*C workgroups); BN keys per tile (64, or 128 for dense: fewer barriers and less per-tile
+// bookkeeping per MFMA).
+template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0, int BN = 64>
 __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
-  using T = Tile<D>;
+  using T = Tile<D, BN>;
+  static_assert(!SPARSE || BN == kBN, "block-sparse tiles are single 64-token blocks");
+  constexpr int MT = BN / 32;  // 32-key sub-tiles per tile
   constexpr int NT = WAVES * 64;
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
@@ -120,27 +126,42 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
     n_tiles = a.keep;
     idx_row = a.block_idx + (((int64_t)b * a.heads + head) * a.n_blocks + qtile) * a.keep;
   } else {
-    n_tiles = (int)((N + kBN - 1) / kBN);
+    n_tiles = (int)((N + BN - 1) / BN);
   }
   auto tile_key0 = [&](int t) -> int64_t {
     if constexpr (SPARSE) return (int64_t)idx_row[t] * kBN;
-    else return (int64_t)t * kBN;
+    else return (int64_t)t * BN;
   };
 
-  // global -> register staging of one K/V tile
+  // global -> register staging of one K/V tile. Each thread's chunks sit at fixed offsets from
+  // the tile's first row (32-bit: < 64 rows x row_stride); rows past the end of the sequence are
+  // clamped to the last token, only in the tile that holds it.
+  int toff[LOADS], trow[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int ci = tid + i * NT;
+    trow[i] = ci / (D / 8);
+    toff[i] = trow[i] * (int)row_stride + (ci % (D / 8)) * 8;
+  }
   u32x4 kst[LOADS], vst[LOADS];
   auto fetch = [&](int t) {
     const int64_t key0 = tile_key0(t);
+    const int64_t tile = base + key0 * row_stride;
+    if (key0 + BN <= N) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int ci = tid + i * NT;
-      const int row = ci / (D / 8);
-      const int col = ci % (D / 8);
-      int64_t key = key0 + row;
-      key = key < N ? key : N - 1;
-      const int64_t off = base + key * row_stride + col * 8;
-      kst[i] = *reinterpret_cast<const u32x4*>(a.k + off);
-      vst[i] = *reinterpret_cast<const u32x4*>(a.v + off);
+      for (int i = 0; i < LOADS; ++i) {
+        kst[i] = *reinterpret_cast<const u32x4*>(a.k + tile + toff[i]);
+        vst[i] = *reinterpret_cast<const u32x4*>(a.v + tile + toff[i]);
+      }
+    } else {
+      const int last = (int)(N - 1 - key0);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = trow[i] < last ? trow[i] : last;
+        const int64_t off = tile + toff[i] + (int64_t)(r - trow[i]) * row_stride;
+        kst[i] = *reinterpret_cast<const u32x4*>(a.k + off);
+        vst[i] = *reinterpret_cast<const u32x4*>(a.v + off);
+      }
     }
   };
   auto stash = [&](int buf) {
@@ -174,12 +195,14 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
     const unsigned char* kb = smem + buf * T::BUF_BYTES;
     const unsigned char* vb = kb + T::K_BYTES;
 
-    // S^T = K . Q^T for keys [0,32) and [32,64) of the tile
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    // S^T = K . Q^T for the 32-key sub-tiles of the tile
+    f32x16 s[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) s[m] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < MT; ++m) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + (32 * m + l32) * T::KS + (16 * ks + 8 * hi) * 2);
         s[m] = mfma32x32x16(kf, qf[ks], s[m]);
       }
@@ -187,9 +210,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
 
     // mask keys past the end of the sequence (only the tile that holds the last token)
     const int64_t key0 = tile_key0(t);
-    if (key0 + kBN > N) {
+    if (key0 + BN > N) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t kidx = key0 + 32 * m + 8 * (r / 4) + 4 * hi + (r % 4);
@@ -200,12 +223,17 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
     // online softmax (log2 domain). The running max only moves when the tile max exceeds it by
     // more than 8 (a factor 256): until then exp2 values stay <= 256, which fp32 sums and bf16 P
     // hold exactly enough, and the O/l rescale (a wave-uniform branch) is skipped.
-    float mx = s[0][0];
+    // tile max as a shallow tree (independent partial maxima) rather than one long chain
+    float mp[4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int j = 0; j < 4; ++j) mp[j] = fmaxf(s[0][4 * j], s[0][4 * j + 1]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[m][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (m > 0 || (r % 4) >= 2) mp[r / 4] = fmaxf(mp[r / 4], s[m][r]);
+    float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+    mx = pair_max(mx) * sc;
     if (__any(mx > m_run + 8.0f)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);
@@ -216,24 +244,26 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
-    float psum = 0.f;
-    u32x4 pk[4];  // P^T as bf16, 4 x 8 values: step kk covers s[kk/2] regs 8*(kk%2) .. +7
+    float psum[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial row sums
+    u32x4 pk[2 * MT];  // P^T as bf16, 8 values per 16-key step: step kk covers s[kk/2] regs 8*(kk%2) .. +7
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < MT; ++m) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(fmaf(s[m][r], sc, -m_run));
         const float p1 = fast_exp2(fmaf(s[m][r + 1], sc, -m_run));
-        psum += p0 + p1;
-        pk[2 * m + r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
+        const uint32_t pp = pack_bf16x2(p0, p1);
+        pk[2 * m + r / 8][(r % 8) / 2] = pp;
+        // row sum of the bf16-rounded P that P.V uses: one packed dot product with (1, 1)
+        psum[(r / 2) % 4] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes2, psum[(r / 2) % 4], false);
       }
     }
-    l_run += psum;
+    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
 
     // O^T += V^T . P^T
     const int ig = lane & 15;  // index inside the 16-lane group
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2 * MT; ++kk) {
       const int m = kk >> 1, half = kk & 1;
       const int k0 = 32 * m + 16 * half + 4 * hi;
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[kk]);
@@ -262,7 +292,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
   }
 
   // epilogue: combine the two lane-partial sums, normalise, store
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = 1.0f / l_tot;
   if (my_q < N) {
     uint16_t* op = a.out + base + my_q * row_stride;
@@ -282,10 +312,10 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
 }
 
 
-template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0>
+template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0, int BN = 64>
 void launch(const AttnArgs& a, hipStream_t stream) {
-  const size_t lds = (DBUF ? 2 : 1) * Tile<D>::BUF_BYTES;
-  auto kern = attn_fwd_kernel<D, WAVES, OCC, DBUF, SPARSE, XCD>;
+  const size_t lds = (DBUF ? 2 : 1) * Tile<D, BN>::BUF_BYTES;
+  auto kern = attn_fwd_kernel<D, WAVES, OCC, DBUF, SPARSE, XCD, BN>;
   static const bool lds_ok = [&] {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;

@@ -40,4 +40,16 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_ptr) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Combine the values of lane l and lane l^32 without an LDS round trip, using
+// v_permlane32_swap_b32 on two copies of x: between them the two results hold, in every lane,
+// the lane's own value and its partner's, so a symmetric combine of the pair is exact.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace h3attn
