@@ -3,4 +3,6 @@ from .attention_oracle import (attention, attention_head, block_means, block_sco
                                block_token_ids, keep_count, n_blocks_of, near_tie_rows,
                                qk_norm_rope, rms_norm, rope3d, rope_frequencies,
                                sparse_attention, sparse_attention_rows, subblock_select,
-                               token_positions, topk_blocks)
+                               token_positions, topk_blocks, threshold_blocks,
+                               subblock_select_threshold, near_threshold_entries,
+                               sparse_attention_csr)

@@ -234,3 +234,63 @@ def sparse_attention(q, k, v, block_idx, block_size: int):
                 r0, r1 = i * block_size, min((i + 1) * block_size, n_len)
                 out[b, r0:r1, h, :], lse[b, h, r0:r1] = sparse_attention_rows(q, k, v, block_idx, block_size, b, h, i)
     return out, lse
+
+
+# --------------------------------------------------------------------------------------------
+# (4) Threshold-mode SubBlock selection with a variable number of kept blocks per row
+#     ["MiniMax-H3 在 8×H200 上基准测试…", section 事件核心: SubBlock described as skipping the
+#     attention blocks that fall below a threshold]
+# --------------------------------------------------------------------------------------------
+
+
+def threshold_blocks(scores: np.ndarray, tau: float):
+    """Per row i of scores [..., nB]: keep key block j iff S_ij >= max_j S_ij - tau (tau >= 0, in
+    the units of the scaled block score). Reading: the pages give no threshold rule; this keeps
+    every block within tau of the row's best block, so tau = 0 keeps only the best block(s) and
+    tau = inf keeps all. Returns (row_ptr int64 [R + 1], col_idx int32 [nnz]) in CSR form over
+    the flattened rows, each row's indices ascending."""
+    if not (tau >= 0.0):
+        raise ValueError("tau must be >= 0")
+    scores = np.asarray(scores, dtype=np.float64)
+    flat = scores.reshape(-1, scores.shape[-1])
+    rows = []
+    for r in range(flat.shape[0]):
+        thr = flat[r].max() - tau
+        rows.append(np.nonzero(flat[r] >= thr)[0].astype(np.int32))
+    counts = np.array([len(x) for x in rows], dtype=np.int64)
+    row_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    col_idx = np.concatenate(rows) if rows else np.zeros((0,), dtype=np.int32)
+    return row_ptr, col_idx.astype(np.int32)
+
+
+def subblock_select_threshold(q, k, block_size: int, tau: float):
+    """Threshold-mode kept sets of every query block, CSR over rows (b, head, query block)."""
+    return threshold_blocks(block_scores(q, k, block_size), tau)
+
+
+def near_threshold_entries(scores: np.ndarray, tau: float, rel: float = 1e-9) -> np.ndarray:
+    """Boolean mask of (row, j) entries whose score lies within rel (relative to the row's
+    largest magnitude) of that row's threshold: only these may legitimately flip between two
+    correct float evaluations."""
+    scores = np.asarray(scores, dtype=np.float64)
+    mx = scores.max(axis=-1, keepdims=True)
+    scale = np.maximum(np.abs(scores).max(axis=-1, keepdims=True), 1e-300)
+    return np.abs(scores - (mx - tau)) <= rel * scale
+
+
+def sparse_attention_csr(q, k, v, row_ptr, col_idx, block_size: int):
+    """Block-sparse attention with a variable kept set per query block (CSR over the rows
+    (b, head, query block)). Returns (O [B, N, Hd, D], lse [B, Hd, N])."""
+    b_len, n_len, h_len, d = q.shape
+    nb = n_blocks_of(n_len, block_size)
+    out = np.empty((b_len, n_len, h_len, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((b_len, h_len, n_len), dtype=np.float64)
+    for b in range(b_len):
+        for h in range(h_len):
+            for i in range(nb):
+                r = (b * h_len + h) * nb + i
+                blocks = col_idx[row_ptr[r]:row_ptr[r + 1]]
+                rows = np.arange(i * block_size, min((i + 1) * block_size, n_len))
+                keys = block_token_ids(blocks, block_size, n_len)
+                out[b, rows, h, :], lse[b, h, rows] = attention_head(q[b, rows, h, :], k[b, keys, h, :], v[b, keys, h, :])
+    return out, lse

@@ -388,3 +388,62 @@ def test_sparse_index_order_does_not_matter():
     a, _ = O.sparse_attention(q, k, v, idx, 64)
     b, _ = O.sparse_attention(q, k, v, shuffled, 64)
     np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------------- threshold mode
+
+def _brute_threshold(row, tau):
+    m = max(row)
+    return [j for j in range(len(row)) if row[j] >= m - tau]
+
+
+def test_threshold_blocks_brute_force_and_csr_layout():
+    for trial in range(100):
+        r, n = int(RNG.integers(1, 6)), int(RNG.integers(1, 20))
+        s = RNG.integers(-4, 5, (r, n)).astype(float) * 0.5   # exact ties and exact threshold hits
+        tau = float(RNG.choice([0.0, 0.5, 1.0, 2.5, np.inf]))
+        rp, ci = O.threshold_blocks(s, tau)
+        assert rp.dtype == np.int64 and ci.dtype == np.int32 and rp[0] == 0 and rp[-1] == len(ci)
+        for i in range(r):
+            assert ci[rp[i]:rp[i + 1]].tolist() == _brute_threshold(s[i].tolist(), tau)
+
+
+def test_threshold_special_cases_and_monotonicity():
+    n, d = 6 * 64, 16
+    q, k = rnd(1, n, 2, d), rnd(1, n, 2, d)
+    s = O.block_scores(q, k, 64)
+    rp0, ci0 = O.threshold_blocks(s, 0.0)
+    assert (np.diff(rp0) == 1).all()                       # tau = 0: only the row maximum (no ties here)
+    assert (ci0 == s.reshape(-1, 6).argmax(1)).all()
+    rpi, cii = O.threshold_blocks(s, np.inf)
+    assert (np.diff(rpi) == 6).all() and (cii.reshape(-1, 6) == np.arange(6)).all()
+    prev = np.diff(rp0)
+    for tau in (0.01, 0.05, 0.1, 0.5, 2.0):
+        rp, ci = O.threshold_blocks(s, tau)
+        cnt = np.diff(rp)
+        assert (cnt >= prev).all()
+        prev = cnt
+        # a threshold set is the top-c set of that row for its own count c
+        for row in range(rp.size - 1):
+            c = cnt[row]
+            top = O.topk_blocks(s.reshape(-1, 6)[row:row + 1], int(c))[0]
+            assert sorted(ci[rp[row]:rp[row + 1]].tolist()) == top.tolist()
+    with pytest.raises(ValueError):
+        O.threshold_blocks(s, -1.0)
+
+
+def test_sparse_csr_matches_fixed_keep_form():
+    n, d, nb = 5 * 64, 16, 5
+    q, k, v = rnd(1, n, 2, d), rnd(1, n, 2, d), rnd(1, n, 2, d)
+    idx = O.subblock_select(q, k, 64, 0.6)
+    keep = idx.shape[-1]
+    rp = np.arange(0, 2 * nb * keep + 1, keep, dtype=np.int64)
+    a, la = O.sparse_attention(q, k, v, idx, 64)
+    b, lb = O.sparse_attention_csr(q, k, v, rp, idx.reshape(-1), 64)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)
+    # variable rows: keep-all rows reproduce dense attention
+    rpi, cii = O.subblock_select_threshold(q, k, 64, np.inf)
+    c, _ = O.sparse_attention_csr(q, k, v, rpi, cii, 64)
+    dense, _ = O.attention(q, k, v)
+    np.testing.assert_allclose(c, dense, atol=1e-12)
