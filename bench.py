@@ -231,6 +231,50 @@ def main():
             del x2, qq, kk2, o1, o2
         del flush
 
+    if not args.no_extra:
+        # threshold mode (variable kept set per query block, CSR): tau bisected, outside any timed
+        # region, so that about the same quarter of the key blocks is kept
+        tws = torch.empty((h3.threshold_workspace_bytes(b, hd, n, d),), dtype=torch.uint8, device=dev)
+        lo, hi = 0.0, 1.0
+        while True:
+            rp, _ = h3.subblock_select_threshold(qo, ko, hi, workspace=tws)
+            if int(rp[-1].item()) >= 0.25 * rp.numel() * nb or hi > 1e6:
+                break
+            hi *= 2.0
+        for _ in range(12):
+            mid = 0.5 * (lo + hi)
+            rp, _ = h3.subblock_select_threshold(qo, ko, mid, workspace=tws)
+            if int(rp[-1].item()) > (1.0 - args.sparsity) * (rp.numel() - 1) * nb:
+                hi = mid
+            else:
+                lo = mid
+        tau = hi
+        rp, ci = h3.subblock_select_threshold(qo, ko, tau, workspace=tws)
+        out_c = torch.empty_like(q)
+        h3.block_sparse_csr_fwd(qo, ko, v, rp, ci, out=out_c)
+        torch.cuda.synchronize()
+        nnz = int(rp[-1].item())
+        tsel, tcsr = [], []
+        for r in range(3):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            h3.subblock_select_threshold(qo, ko, tau, workspace=tws)   # includes one host read of nnz
+            e1.record()
+            h3.block_sparse_csr_fwd(qo, ko, v, rp, ci, out=out_c)
+            e2.record()
+            torch.cuda.synchronize()
+            tsel.append(elapsed_ms(e0, e1))
+            tcsr.append(elapsed_ms(e1, e2))
+        csr_flops = 4.0 * nnz * 64 * 64 * d
+        components["threshold_mode"] = {
+            "tau": tau, "kept_fraction": nnz / ((rp.numel() - 1) * nb), "select_ms": float(np.median(tsel)),
+            "csr_sparse_ms": float(np.median(tcsr)),
+            "csr_sparse_tflops_kept": csr_flops / (float(np.median(tcsr)) * 1e-3) / 1e12}
+        log(f"threshold mode: tau {tau:.4g}, kept {components['threshold_mode']['kept_fraction']:.3f}, select "
+            f"{components['threshold_mode']['select_ms']:.2f} ms, csr sparse {components['threshold_mode']['csr_sparse_ms']:.2f} ms "
+            f"({components['threshold_mode']['csr_sparse_tflops_kept']:.0f} TFLOP/s)")
+        del tws, out_c
+
     roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,8,2,true,false> (dense)",
                 "achieved": dense_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": dense_tf / PEAK_BF16_TFLOPS,

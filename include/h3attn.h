@@ -125,6 +125,46 @@ h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k
                                       int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
                                       int32_t block_size, hipStream_t stream);
 
+/* ---- Threshold-mode SubBlock selection with a variable number of kept blocks per row ----
+ * "MiniMax-H3 在 8×H200 上基准测试…" (chat-gpts.plus), section "事件核心" describes SubBlock as
+ * skipping the attention blocks that score below a threshold. The pages give no rule; this mode
+ * keeps, for query block i, every key block j whose score (the same pooled estimate as
+ * h3attn_subblock_select) is at least max_j score(i, j) - tau, tau >= 0 (tau = +inf keeps all).
+ * Kept sets are returned in CSR form over the rows r = (b * heads + head) * nB + i:
+ * row_ptr[r] .. row_ptr[r+1] index ascending key-block ids in col_idx. Selection is two calls on
+ * the same workspace, so the caller can size col_idx between them. */
+
+/* Workspace bytes for the threshold calls: the select workspace plus a per-row threshold
+ * (float64) and count (int64), each region 256-byte aligned. 0 on invalid sizes. */
+size_t h3attn_threshold_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tokens,
+                                        int32_t head_dim, int32_t block_size);
+
+/* Pass 1: pools, scores, per-row thresholds and counts; writes row_ptr (int64, B*heads*nB + 1
+ * entries, row_ptr[0] = 0, last entry = total kept count). Errors: as h3attn_subblock_select,
+ * plus tau < 0 or NaN -> INVALID_ARGUMENT. */
+h3attn_status h3attn_subblock_threshold_count(const h3attn_bf16* q, const h3attn_bf16* k,
+                                              int32_t batch, int32_t heads, int64_t n_tokens,
+                                              int32_t head_dim, int32_t block_size, double tau,
+                                              int64_t* row_ptr, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream);
+
+/* Pass 2: fills col_idx (int32) from the workspace left by pass 1 (same sizes, same workspace,
+ * same stream, nothing in between that writes the workspace). Entries at positions >=
+ * col_capacity are not written: size col_idx from row_ptr's last entry. */
+h3attn_status h3attn_subblock_threshold_fill(int32_t batch, int32_t heads, int64_t n_tokens,
+                                             int32_t head_dim, int32_t block_size,
+                                             const int64_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Block-sparse attention with a CSR kept set per query block (rows as above; indices distinct
+ * and in [0, nB), any order). Same numerics as h3attn_block_sparse_fwd. A row with no kept
+ * block yields zeros and lse = -inf. */
+h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                          const int64_t* row_ptr, const int32_t* col_idx,
+                                          h3attn_bf16* out, float* lse,
+                                          int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                          int32_t block_size, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

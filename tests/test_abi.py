@@ -123,3 +123,25 @@ def test_select_and_sparse_validation(lib):
     assert g(*P, 0x40000, 11, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
     assert g(*P, None, 3, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
     assert g(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 32, None) == 2
+
+
+def test_threshold_validation(lib):
+    ws = 0x100000
+    nbytes = lib.h3attn_threshold_workspace_bytes(1, 2, 640, 64, 64)
+    assert nbytes == lib.h3attn_select_workspace_bytes(1, 2, 640, 64, 64) + 2 * 256
+    f = lib.h3attn_subblock_threshold_count
+    assert f(0x10000, 0x20000, 1, 2, 640, 64, 64, -1.0, 0x30000, ws, nbytes, None) == 1 and "tau" in _err(lib)
+    assert f(0x10000, 0x20000, 1, 2, 640, 64, 64, float("nan"), 0x30000, ws, nbytes, None) == 1
+    assert f(0x10000, 0x20000, 1, 2, 640, 64, 64, 0.5, None, ws, nbytes, None) == 1 and "row_ptr" in _err(lib)
+    assert f(0x10000, 0x20000, 1, 2, 640, 64, 64, 0.5, 0x30004, ws, nbytes, None) == 1
+    assert f(0x10000, 0x20000, 1, 2, 640, 64, 64, 0.5, 0x30000, ws, nbytes - 8, None) == 1 and "workspace" in _err(lib)
+    assert f(0x10000, 0x20000, 1, 2, 640, 64, 32, 0.5, 0x30000, ws, nbytes, None) == 2
+    g = lib.h3attn_subblock_threshold_fill
+    assert g(1, 2, 640, 64, 64, 0x30000, 0x40000, -1, ws, nbytes, None) == 1
+    assert g(1, 2, 640, 64, 64, None, 0x40000, 10, ws, nbytes, None) == 1
+    assert g(1, 2, 640, 64, 64, 0x30000, None, 10, ws, nbytes, None) == 1
+    h = lib.h3attn_block_sparse_csr_fwd
+    P = (0x10000, 0x20000, 0x30000)
+    assert h(*P, None, 0x40000, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
+    assert h(*P, 0x60000, None, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
+    assert h(*P, 0x60000, 0x40000, 0x50000, None, 1, 2, 640, 64, 32, None) == 2

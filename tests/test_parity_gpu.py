@@ -268,3 +268,95 @@ def test_video15s_boxes_select_sparse_dense(h3):
     smp = _samples(cfg, 4, extra=extra)
     _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, smp, "15s")
     _sampled_dense(h3, x["q"], x["k"], x["v"], _samples(cfg, 2), "15s")
+
+
+# ------------------------------------------------------------------ threshold mode (CSR)
+
+def _tau_for(scores, keep_frac=0.25):
+    """A tau that keeps roughly keep_frac of the blocks (median over rows of the gap between the
+    row maximum and the row's keep_frac quantile), computed from the oracle's scores."""
+    flat = scores.reshape(-1, scores.shape[-1])
+    gap = flat.max(1) - np.quantile(flat, 1.0 - keep_frac, axis=1)
+    return float(np.median(gap))
+
+
+def _check_threshold_sets(rp, ci, scores, tau, what):
+    flat = scores.reshape(-1, scores.shape[-1])
+    r, nb = flat.shape
+    rp = rp.cpu().numpy()
+    ci = ci.cpu().numpy()
+    assert rp.shape == (r + 1,) and rp[0] == 0 and rp[-1] == ci.size
+    g = np.zeros((r, nb), dtype=bool)
+    for i in range(r):
+        row = ci[rp[i]:rp[i + 1]]
+        assert (row >= 0).all() and (row < nb).all()
+        if row.size > 1:
+            assert (np.diff(row) > 0).all(), f"{what}: row {i} not ascending"
+        g[i, row] = True
+    rrp, rci = oracle.threshold_blocks(scores, tau)
+    ref = np.zeros((r, nb), dtype=bool)
+    for i in range(r):
+        ref[i, rci[rrp[i]:rrp[i + 1]]] = True
+    diff = g != ref
+    near = oracle.near_threshold_entries(flat, tau)
+    log(f"{what}: tau {tau:.4g}, kept {g.sum()} of {g.size} ({g.mean():.3f}), differing {int(diff.sum())} "
+        f"(near-threshold {int((diff & near).sum())})")
+    assert not (diff & ~near).any(), f"{what}: {int((diff & ~near).sum())} entries differ away from the threshold"
+
+
+@pytest.mark.parametrize("n,d", [(256, 64), (333, 128), (64 * 20, 128)])
+def test_threshold_select_and_csr_attention_full(h3, n, d):
+    c = random_case(2, n, 3, d, seed=500 + n, device=DEV)
+    qd, kd, vd = f64(c["q"]), f64(c["k"]), f64(c["v"])
+    scores = oracle.block_scores(qd, kd, 64)
+    for tau in (0.0, _tau_for(scores), float("inf")):
+        rp, ci = h3.subblock_select_threshold(c["q"], c["k"], tau)
+        _sync()
+        _check_threshold_sets(rp, ci, scores, tau, f"threshold n={n} d={d}")
+        o, lse = h3.block_sparse_csr_fwd(c["q"], c["k"], c["v"], rp, ci, return_lse=True)
+        _sync()
+        ro, rl = oracle.sparse_attention_csr(qd, kd, vd, rp.cpu().numpy(), ci.cpu().numpy(), 64)
+        check_attention(f64(o), ro, f"csr sparse n={n} d={d} tau={tau:.3g}")
+        assert np.abs(f64(lse) - rl).max() <= LSE_MAX_ABS
+
+
+def test_csr_keep_all_is_bitwise_dense_and_empty_rows(h3):
+    c = random_case(1, 64 * 6, 2, 128, seed=21, device=DEV)
+    rp, ci = h3.subblock_select_threshold(c["q"], c["k"], float("inf"))
+    dense = h3.dense_fwd(c["q"], c["k"], c["v"])
+    csr = h3.block_sparse_csr_fwd(c["q"], c["k"], c["v"], rp, ci)
+    _sync()
+    assert torch.equal(dense, csr)
+    # an empty kept set yields zeros and lse = -inf; the other rows are unaffected
+    rp2 = rp.clone()
+    rp2[1:] -= 6          # row 0 empty; rows 1.. shifted onto col_idx[0..]
+    rp2[0] = 0
+    ci2 = ci[6:].contiguous()
+    o, lse = h3.block_sparse_csr_fwd(c["q"], c["k"], c["v"], rp2, ci2, return_lse=True)
+    _sync()
+    assert (o[0, :64, 0].float() == 0).all() and torch.isinf(lse[0, 0, :64]).all()
+    assert torch.equal(o[0, 64:, 0], dense[0, 64:, 0]) and torch.equal(o[0, :, 1], dense[0, :, 1])
+
+
+@pytest.mark.timeout(900)
+def test_video5s_threshold_select_and_csr_sparse(h3):
+    cfg = CONFIGS[3]
+    x = make_inputs(cfg, DEV)
+    q, k, v = x["q"], x["k"], x["v"]
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    scores = np.concatenate([oracle.block_scores(f64(qh[:, :, h0:h0 + 8]), f64(kh[:, :, h0:h0 + 8]), 64)
+                             for h0 in range(0, cfg.heads, 8)], axis=1)
+    tau = _tau_for(scores)
+    rp, ci = h3.subblock_select_threshold(q, k, tau)
+    o = h3.block_sparse_csr_fwd(q, k, v, rp, ci)
+    _sync()
+    _check_threshold_sets(rp, ci, scores, tau, "5s threshold")
+    rpn, cin, oh = rp.cpu().numpy(), ci.cpu().numpy(), o.cpu()
+    nb = cfg.n_blocks
+    for h, blocks in _samples(cfg, 2).items():
+        for i in blocks:
+            r = h * nb + i
+            rows = np.arange(i * 64, (i + 1) * 64)
+            keys = oracle.block_token_ids(cin[rpn[r]:rpn[r + 1]], 64, cfg.n_tokens)
+            ref, _ = oracle.attention_head(f64(qh[0, rows, h]), f64(kh[0, keys, h]), f64(vh[0, keys, h]))
+            check_attention(f64(oh[0, rows, h]), ref, f"5s csr sparse head {h} block {i}")

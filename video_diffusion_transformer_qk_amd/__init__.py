@@ -5,10 +5,13 @@ Four calls, each a hand-written HIP kernel behind a C ABI (include/h3attn.h):
   dense_fwd         dense bf16 self-attention over the full latent sequence
   subblock_select   SubBlock 64-token block scores and per-query-block top-k
   block_sparse_fwd  attention over the kept key blocks only
+Threshold mode: subblock_select_threshold (blocks within tau of the row's best, CSR) and
+block_sparse_csr_fwd (variable kept set per query block).
 """
-from ._lib import (LIB_PATH, SIGNATURES, H3AttnError, block_sparse_fwd, dense_fwd,  # noqa: F401
-                   keep_count, load_library, qk_norm_rope, select_workspace_bytes,
-                   subblock_select, version)
+from ._lib import (LIB_PATH, SIGNATURES, H3AttnError, block_sparse_csr_fwd, block_sparse_fwd,  # noqa: F401
+                   dense_fwd, keep_count, load_library, qk_norm_rope, select_workspace_bytes,
+                   subblock_select, subblock_select_threshold, threshold_workspace_bytes, version)
 
 __all__ = ["qk_norm_rope", "dense_fwd", "subblock_select", "block_sparse_fwd", "keep_count",
-           "select_workspace_bytes", "version", "H3AttnError", "load_library"]
+           "select_workspace_bytes", "subblock_select_threshold", "block_sparse_csr_fwd",
+           "threshold_workspace_bytes", "version", "H3AttnError", "load_library"]

@@ -39,6 +39,12 @@ SIGNATURES = {
                                               _I32, _P, _P, ctypes.c_size_t, _P]),
     "h3attn_block_sparse_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I64, _I32,
                                                _I32, _P]),
+    "h3attn_threshold_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I64, _I32, _I32]),
+    "h3attn_subblock_threshold_count": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32, _I32, ctypes.c_double,
+                                                       _P, _P, ctypes.c_size_t, _P]),
+    "h3attn_subblock_threshold_fill": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, _P, _P, _I64, _P,
+                                                      ctypes.c_size_t, _P]),
+    "h3attn_block_sparse_csr_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P]),
 }
 
 
@@ -199,4 +205,59 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_id
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
     _check(lib.h3attn_block_sparse_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), block_idx.data_ptr(), keep,
                                        o.data_ptr(), _ptr(lse), b, h, n, d, block_size, _stream()))
+    return (o, lse) if return_lse else o
+
+
+def threshold_workspace_bytes(batch: int, heads: int, n_tokens: int, head_dim: int, block_size: int = 64) -> int:
+    return int(load_library().h3attn_threshold_workspace_bytes(batch, heads, n_tokens, head_dim, block_size))
+
+
+def subblock_select_threshold(q: torch.Tensor, k: torch.Tensor, tau: float, block_size: int = 64,
+                              workspace: Optional[torch.Tensor] = None):
+    """Threshold-mode kept sets: every key block within tau of the row's best pooled score.
+    Returns CSR (row_ptr int64 [B*heads*nB + 1], col_idx int32 [nnz]) over rows
+    (b, head, query block). Waits for the count pass to read nnz before sizing col_idx."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    if q.shape != k.shape:
+        raise ValueError("q and k must have the same shape")
+    b, n, h, d = q.shape
+    nb = -(-n // block_size)
+    need = threshold_workspace_bytes(b, h, n, d, block_size)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    row_ptr = torch.empty((b * h * nb + 1,), dtype=torch.int64, device=q.device)
+    st = _stream()
+    _check(lib.h3attn_subblock_threshold_count(q.data_ptr(), k.data_ptr(), b, h, n, d, block_size, float(tau),
+                                               row_ptr.data_ptr(), workspace.data_ptr(), workspace.numel(), st))
+    nnz = int(row_ptr[-1].item())
+    col_idx = torch.empty((max(nnz, 1),), dtype=torch.int32, device=q.device)
+    _check(lib.h3attn_subblock_threshold_fill(b, h, n, d, block_size, row_ptr.data_ptr(), col_idx.data_ptr(), nnz,
+                                              workspace.data_ptr(), workspace.numel(), st))
+    return row_ptr, col_idx[:nnz]
+
+
+def block_sparse_csr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+                         col_idx: torch.Tensor, block_size: int = 64, return_lse: bool = False,
+                         out: Optional[torch.Tensor] = None):
+    """Block-sparse attention with a variable kept set per query block (CSR rows)."""
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 4)
+    _need(row_ptr, "row_ptr", torch.int64, 1)
+    _need(col_idx, "col_idx", torch.int32, 1)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have the same shape")
+    b, n, h, d = q.shape
+    nb = -(-n // block_size)
+    if row_ptr.numel() != b * h * nb + 1:
+        raise ValueError(f"row_ptr must have B*heads*nB + 1 = {b * h * nb + 1} entries")
+    o = torch.empty_like(q) if out is None else out
+    _need(o, "out", torch.bfloat16, 4)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
+    ci = col_idx if col_idx.numel() > 0 else torch.zeros((1,), dtype=torch.int32, device=q.device)
+    _check(lib.h3attn_block_sparse_csr_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), row_ptr.data_ptr(), ci.data_ptr(),
+                                           o.data_ptr(), _ptr(lse), b, h, n, d, block_size, _stream()))
     return (o, lse) if return_lse else o

@@ -214,4 +214,114 @@ h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k
   return check_launch("h3attn_block_sparse_fwd");
 }
 
+static h3attn_status check_select_common(const h3attn_bf16* q, const h3attn_bf16* k, int32_t batch,
+                                         int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                         int32_t block_size, const void* workspace, int64_t* nb_out) {
+  if (q != nullptr || k != nullptr) { CHECK_PTR(q); CHECK_PTR(k); }
+  if (workspace == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  h3attn_status st = check_sizes(batch, heads, n_tokens, head_dim);
+  if (st != H3ATTN_OK) return st;
+  if (block_size != 64) return fail(H3ATTN_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", block_size);
+  if ((int64_t)batch * heads > 65535) return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads must be <= 65535");
+  *nb_out = (n_tokens + block_size - 1) / block_size;
+  return H3ATTN_OK;
+}
+
+size_t h3attn_threshold_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tokens,
+                                        int32_t head_dim, int32_t block_size) {
+  const size_t base = h3attn_select_workspace_bytes(batch, heads, n_tokens, head_dim, block_size);
+  if (base == 0) return 0;
+  const size_t rows = (size_t)batch * heads * (size_t)((n_tokens + block_size - 1) / block_size);
+  return base + 2 * align256(rows * 8);
+}
+
+static void threshold_layout(h3attn::SelectArgs& a, void* workspace, int32_t batch, int32_t heads,
+                             int64_t nb, int32_t head_dim) {
+  const size_t means = align256((size_t)batch * heads * (size_t)nb * head_dim * sizeof(double));
+  const size_t scores = align256((size_t)batch * heads * (size_t)nb * (size_t)nb * sizeof(double));
+  const size_t rows = align256((size_t)batch * heads * (size_t)nb * 8);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.q_mean = reinterpret_cast<double*>(ws);
+  a.k_mean = reinterpret_cast<double*>(ws + means);
+  a.scores = reinterpret_cast<double*>(ws + 2 * means);
+  a.row_thr = reinterpret_cast<double*>(ws + 2 * means + scores);
+  a.row_cnt = reinterpret_cast<int64_t*>(ws + 2 * means + scores + rows);
+}
+
+h3attn_status h3attn_subblock_threshold_count(const h3attn_bf16* q, const h3attn_bf16* k,
+                                              int32_t batch, int32_t heads, int64_t n_tokens,
+                                              int32_t head_dim, int32_t block_size, double tau,
+                                              int64_t* row_ptr, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  if (q == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "q is NULL");
+  if (k == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "k is NULL");
+  int64_t nb = 0;
+  h3attn_status st = check_select_common(q, k, batch, heads, n_tokens, head_dim, block_size, workspace, &nb);
+  if (st != H3ATTN_OK) return st;
+  if (row_ptr == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_ptr is NULL");
+  if (reinterpret_cast<uintptr_t>(row_ptr) & 7u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_ptr is not 8-byte aligned");
+  if (!(tau >= 0.0)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "tau must be >= 0 (got %g)", tau);
+  const size_t need = h3attn_threshold_workspace_bytes(batch, heads, n_tokens, head_dim, block_size);
+  if (workspace_bytes < need)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  h3attn::SelectArgs a{};
+  a.q = q; a.k = k; a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
+  a.block_size = block_size; a.n_blocks = (int32_t)nb; a.keep = 0;
+  threshold_layout(a, workspace, batch, heads, nb, head_dim);
+  a.tau_raw = tau * std::sqrt((double)head_dim);
+  a.row_ptr = row_ptr;
+  h3attn::launch_threshold_count(a, stream);
+  return check_launch("h3attn_subblock_threshold_count");
+}
+
+h3attn_status h3attn_subblock_threshold_fill(int32_t batch, int32_t heads, int64_t n_tokens,
+                                             int32_t head_dim, int32_t block_size,
+                                             const int64_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int64_t nb = 0;
+  h3attn_status st = check_select_common(nullptr, nullptr, batch, heads, n_tokens, head_dim, block_size, workspace, &nb);
+  if (st != H3ATTN_OK) return st;
+  if (row_ptr == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_ptr is NULL");
+  if (reinterpret_cast<uintptr_t>(row_ptr) & 7u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_ptr is not 8-byte aligned");
+  if (col_capacity < 0) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "col_capacity must be >= 0");
+  if (col_capacity > 0 && col_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "col_idx is NULL");
+  if (reinterpret_cast<uintptr_t>(col_idx) & 3u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "col_idx is not 4-byte aligned");
+  const size_t need = h3attn_threshold_workspace_bytes(batch, heads, n_tokens, head_dim, block_size);
+  if (workspace_bytes < need)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  h3attn::SelectArgs a{};
+  a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
+  a.block_size = block_size; a.n_blocks = (int32_t)nb; a.keep = 0;
+  threshold_layout(a, workspace, batch, heads, nb, head_dim);
+  a.row_ptr = const_cast<int64_t*>(row_ptr);
+  a.col_idx = col_idx;
+  a.col_capacity = col_capacity;
+  h3attn::launch_threshold_fill(a, stream);
+  return check_launch("h3attn_subblock_threshold_fill");
+}
+
+h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                          const int64_t* row_ptr, const int32_t* col_idx,
+                                          h3attn_bf16* out, float* lse,
+                                          int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                          int32_t block_size, hipStream_t stream) {
+  h3attn_status st = check_attn(q, k, v, out, lse, batch, heads, n_tokens, head_dim);
+  if (st != H3ATTN_OK) return st;
+  if (row_ptr == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_ptr is NULL");
+  if (reinterpret_cast<uintptr_t>(row_ptr) & 7u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_ptr is not 8-byte aligned");
+  if (col_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "col_idx is NULL");
+  if (reinterpret_cast<uintptr_t>(col_idx) & 3u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "col_idx is not 4-byte aligned");
+  if (block_size != 64) return fail(H3ATTN_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", block_size);
+  const int64_t nb = (n_tokens + block_size - 1) / block_size;
+  if (nb * heads * (int64_t)batch >= ((int64_t)1 << 31))
+    return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads*n_blocks must be below 2^31");
+  h3attn::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.block_idx = col_idx; a.row_ptr = row_ptr;
+  a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
+  a.keep = 0; a.n_blocks = (int32_t)nb;
+  h3attn::launch_block_sparse_csr_fwd(a, stream);
+  return check_launch("h3attn_block_sparse_csr_fwd");
+}
+
 }  // extern "C"

@@ -70,7 +70,7 @@ __device__ __forceinline__ int64_t xcd_grouped(int64_t lin, int64_t total) {
 // selects the workgroup order (0: grid order, 1: one contiguous range per XCD, C > 1: windows
 // of 8*C workgroups); BN keys per tile (64, or 128 for dense: fewer barriers and less per-tile
 // bookkeeping per MFMA).
-template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0, int BN = 64>
+template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0, int BN = 64, bool CSR = false>
 __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
   using T = Tile<D, BN>;
   static_assert(!SPARSE || BN == kBN, "block-sparse tiles are single 64-token blocks");
@@ -122,11 +122,27 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
 
   int n_tiles;
   const int32_t* idx_row = nullptr;
-  if constexpr (SPARSE) {
+  if constexpr (SPARSE && CSR) {
+    const int64_t r = ((int64_t)b * a.heads + head) * a.n_blocks + qtile;
+    const int64_t p0 = a.row_ptr[r];
+    n_tiles = (int)(a.row_ptr[r + 1] - p0);
+    idx_row = a.block_idx + p0;
+  } else if constexpr (SPARSE) {
     n_tiles = a.keep;
     idx_row = a.block_idx + (((int64_t)b * a.heads + head) * a.n_blocks + qtile) * a.keep;
   } else {
     n_tiles = (int)((N + BN - 1) / BN);
+  }
+  if (n_tiles <= 0) {  // an empty kept set (CSR rows only): zero output, lse = -inf
+    if (my_q < N) {
+      uint16_t* op = a.out + base + my_q * row_stride;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hi) = u32x2{0u, 0u};
+      if (a.lse != nullptr && hi == 0) a.lse[((int64_t)b * a.heads + head) * N + my_q] = -INFINITY;
+    }
+    return;
   }
   auto tile_key0 = [&](int t) -> int64_t {
     if constexpr (SPARSE) return (int64_t)idx_row[t] * kBN;
@@ -312,10 +328,10 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
 }
 
 
-template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0, int BN = 64>
+template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0, int BN = 64, bool CSR = false>
 void launch(const AttnArgs& a, hipStream_t stream) {
   const size_t lds = (DBUF ? 2 : 1) * Tile<D, BN>::BUF_BYTES;
-  auto kern = attn_fwd_kernel<D, WAVES, OCC, DBUF, SPARSE, XCD, BN>;
+  auto kern = attn_fwd_kernel<D, WAVES, OCC, DBUF, SPARSE, XCD, BN, CSR>;
   static const bool lds_ok = [&] {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
@@ -348,6 +364,11 @@ void launch_dense_fwd(const AttnArgs& a, hipStream_t stream) {
 void launch_block_sparse_fwd(const AttnArgs& a, hipStream_t stream) {
   if (a.head_dim == 128) launch<128, H3ATTN_SPARSE_CFG, true, H3ATTN_SPARSE_XCD>(a, stream);
   else launch<64, H3ATTN_SPARSE_CFG, true, H3ATTN_SPARSE_XCD>(a, stream);
+}
+
+void launch_block_sparse_csr_fwd(const AttnArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) launch<128, H3ATTN_SPARSE_CFG, true, H3ATTN_SPARSE_XCD, 64, true>(a, stream);
+  else launch<64, H3ATTN_SPARSE_CFG, true, H3ATTN_SPARSE_XCD, 64, true>(a, stream);
 }
 
 }  // namespace h3attn

@@ -33,7 +33,8 @@ struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const int32_t* block_idx;  // null for dense
+  const int32_t* block_idx;  // null for dense; CSR column indices for the CSR variant
+  const int64_t* row_ptr;    // CSR variant only: [B*H*nB + 1]
   uint16_t* out;
   float* lse;                // may be null
   int64_t n_tokens;
@@ -44,6 +45,7 @@ struct AttnArgs {
 
 void launch_dense_fwd(const AttnArgs& a, hipStream_t stream);
 void launch_block_sparse_fwd(const AttnArgs& a, hipStream_t stream);
+void launch_block_sparse_csr_fwd(const AttnArgs& a, hipStream_t stream);
 
 struct SelectArgs {
   const uint16_t* q;
@@ -54,8 +56,17 @@ struct SelectArgs {
   double* q_mean;   // workspace: [B, H, nB, D]
   double* k_mean;   // workspace: [B, H, nB, D]
   double* scores;   // workspace: [B, H, nB, nB]
+  // threshold mode only
+  double tau_raw;           // tau * sqrt(D): threshold offset on the unscaled dot products
+  double* row_thr;          // workspace: [B*H*nB] per-row threshold
+  int64_t* row_cnt;         // workspace: [B*H*nB] per-row kept count
+  int64_t* row_ptr;         // [B*H*nB + 1]
+  int32_t* col_idx;         // [col_capacity]
+  int64_t col_capacity;
 };
 
 void launch_subblock_select(const SelectArgs& a, hipStream_t stream);
+void launch_threshold_count(const SelectArgs& a, hipStream_t stream);
+void launch_threshold_fill(const SelectArgs& a, hipStream_t stream);
 
 }  // namespace h3attn

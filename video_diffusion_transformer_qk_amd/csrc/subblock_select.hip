@@ -153,6 +153,38 @@ __device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= 4 ints
   return before + x - v;
 }
 
+// Writes, in ascending index order, every j with keys[j] > thr plus the first k_rem indices with
+// keys[j] == thr; each thread scans one contiguous index range, two block scans place the runs.
+__device__ void ordered_compact(const uint64_t* keys, int nb, uint64_t thr, int k_rem, int32_t* dst,
+                                int keep, int* scan_scratch) {
+  const int tid = threadIdx.x;
+  const int per = (nb + kTopkThreads - 1) / kTopkThreads;
+  const int j0 = tid * per;
+  const int j1 = j0 + per < nb ? j0 + per : nb;
+  int n_eq = 0;
+  for (int j = j0; j < j1; ++j) n_eq += keys[j] == thr;
+  int tot;
+  const int eq_before = block_exclusive_scan(n_eq, &tot, scan_scratch);
+  int n_sel = 0;
+  {
+    int e = eq_before;
+    for (int j = j0; j < j1; ++j) {
+      const uint64_t key = keys[j];
+      if (key > thr) ++n_sel;
+      else if (key == thr) { if (e < k_rem) ++n_sel; ++e; }
+    }
+  }
+  const int pos0 = block_exclusive_scan(n_sel, &tot, scan_scratch);
+  int e = eq_before, p = pos0;
+  for (int j = j0; j < j1; ++j) {
+    const uint64_t key = keys[j];
+    bool take = false;
+    if (key > thr) take = true;
+    else if (key == thr) { take = e < k_rem; ++e; }
+    if (take && p < keep) dst[p++] = j;
+  }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
@@ -197,47 +229,94 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   }
   const uint64_t thr = prefix;  // the keep-th largest key; take k_rem of its equal keys
 
-  // ordered compaction over contiguous per-thread index ranges
+  ordered_compact(keys, nb, thr, k_rem, a.block_idx + row * a.keep, a.keep, scan_scratch);
+}
+
+// Threshold mode, pass 1: per row, the largest unscaled score m and the kept count
+// #{j : s_j >= m - tau*sqrt(D)}; the threshold is stored so that pass 2 uses the same value.
+__global__ __launch_bounds__(kTopkThreads) void threshold_count_kernel(SelectArgs a) {
+  __shared__ double red[kTopkThreads / 64];
+  __shared__ int cnt_red[kTopkThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = a.n_blocks;
+  const int64_t row = ((int64_t)blockIdx.z * a.heads + blockIdx.y) * nb + blockIdx.x;
+  const double* sc = a.scores + row * nb;
+  double m = -INFINITY;
+  for (int j = tid; j < nb; j += kTopkThreads) m = fmax(m, sc[j]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kTopkThreads / 64; ++w) m = fmax(m, red[w]);
+  const double thr = m - a.tau_raw;
+  int c = 0;
+  for (int j = tid; j < nb; j += kTopkThreads) c += sc[j] >= thr;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  if (lane == 0) cnt_red[wave] = c;
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+    for (int w = 0; w < kTopkThreads / 64; ++w) tot += cnt_red[w];
+    a.row_cnt[row] = tot;
+    a.row_thr[row] = thr;
+  }
+}
+
+// exclusive scan of the per-row counts into row_ptr (one workgroup; rows split in contiguous runs)
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void row_ptr_scan_kernel(SelectArgs a, int64_t rows) {
+  __shared__ int64_t part[kScanThreads];
+  const int tid = threadIdx.x;
+  const int64_t per = (rows + kScanThreads - 1) / kScanThreads;
+  const int64_t r0 = tid * per, r1 = r0 + per < rows ? r0 + per : rows;
+  int64_t s = 0;
+  for (int64_t r = r0; r < r1; ++r) s += a.row_cnt[r];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t acc = 0;
+    for (int i = 0; i < kScanThreads; ++i) { const int64_t v = part[i]; part[i] = acc; acc += v; }
+    a.row_ptr[rows] = acc;
+  }
+  __syncthreads();
+  int64_t acc = part[tid];
+  for (int64_t r = r0; r < r1; ++r) { a.row_ptr[r] = acc; acc += a.row_cnt[r]; }
+}
+
+// Threshold mode, pass 2: ordered compaction of {j : s_j >= thr} into col_idx[row_ptr[row] ..].
+// Writes past col_capacity are dropped (the caller sizes col_idx from row_ptr's last entry).
+__global__ __launch_bounds__(kTopkThreads) void threshold_fill_kernel(SelectArgs a) {
+  __shared__ int scan_scratch[4];
+  const int tid = threadIdx.x;
+  const int nb = a.n_blocks;
+  const int64_t row = ((int64_t)blockIdx.z * a.heads + blockIdx.y) * nb + blockIdx.x;
+  const double* sc = a.scores + row * nb;
+  const double thr = a.row_thr[row];
+  const int64_t start = a.row_ptr[row];
   const int per = (nb + kTopkThreads - 1) / kTopkThreads;
   const int j0 = tid * per;
   const int j1 = j0 + per < nb ? j0 + per : nb;
-  int n_eq = 0;
-  for (int j = j0; j < j1; ++j) n_eq += keys[j] == thr;
-  int tot;
-  const int eq_before = block_exclusive_scan(n_eq, &tot, scan_scratch);
   int n_sel = 0;
-  {
-    int e = eq_before;
-    for (int j = j0; j < j1; ++j) {
-      const uint64_t key = keys[j];
-      if (key > thr) ++n_sel;
-      else if (key == thr) { if (e < k_rem) ++n_sel; ++e; }
+  for (int j = j0; j < j1; ++j) n_sel += sc[j] >= thr;
+  int tot;
+  int64_t p = start + block_exclusive_scan(n_sel, &tot, scan_scratch);
+  for (int j = j0; j < j1; ++j)
+    if (sc[j] >= thr) {
+      if (p < a.col_capacity) a.col_idx[p] = j;
+      ++p;
     }
-  }
-  const int pos0 = block_exclusive_scan(n_sel, &tot, scan_scratch);
-  int32_t* dst = a.block_idx + row * a.keep;
-  {
-    int e = eq_before, p = pos0;
-    for (int j = j0; j < j1; ++j) {
-      const uint64_t key = keys[j];
-      bool take = false;
-      if (key > thr) take = true;
-      else if (key == thr) { take = e < k_rem; ++e; }
-      if (take) dst[p++] = j;
-    }
-  }
 }
 
 }  // namespace
 
+static void launch_pool_and_scores(const SelectArgs& a, hipStream_t stream);
+
 void launch_subblock_select(const SelectArgs& a, hipStream_t stream) {
+  launch_pool_and_scores(a, stream);
   const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
-  if (a.head_dim == 128) hipLaunchKernelGGL(pool_kernel<128>, g3, dim3(kPoolThreads), 0, stream, a);
-  else hipLaunchKernelGGL(pool_kernel<64>, g3, dim3(kPoolThreads), 0, stream, a);
-  const unsigned tiles = (unsigned)((a.n_blocks + kScoreTile - 1) / kScoreTile);
-  const dim3 gs(tiles, tiles, (unsigned)(a.batch * a.heads));
-  if (a.head_dim == 128) hipLaunchKernelGGL(score_kernel<128>, gs, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(score_kernel<64>, gs, dim3(256), 0, stream, a);
   const size_t lds = (size_t)a.n_blocks * sizeof(uint64_t);
   static const bool lds_ok = [] {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel),
@@ -245,6 +324,29 @@ void launch_subblock_select(const SelectArgs& a, hipStream_t stream) {
   }();
   (void)lds_ok;
   hipLaunchKernelGGL(topk_kernel, g3, dim3(kTopkThreads), lds, stream, a);
+}
+
+static void launch_pool_and_scores(const SelectArgs& a, hipStream_t stream) {
+  const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
+  if (a.head_dim == 128) hipLaunchKernelGGL(pool_kernel<128>, g3, dim3(kPoolThreads), 0, stream, a);
+  else hipLaunchKernelGGL(pool_kernel<64>, g3, dim3(kPoolThreads), 0, stream, a);
+  const unsigned tiles = (unsigned)((a.n_blocks + kScoreTile - 1) / kScoreTile);
+  const dim3 gs(tiles, tiles, (unsigned)(a.batch * a.heads));
+  if (a.head_dim == 128) hipLaunchKernelGGL(score_kernel<128>, gs, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(score_kernel<64>, gs, dim3(256), 0, stream, a);
+}
+
+void launch_threshold_count(const SelectArgs& a, hipStream_t stream) {
+  launch_pool_and_scores(a, stream);
+  const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
+  hipLaunchKernelGGL(threshold_count_kernel, g3, dim3(kTopkThreads), 0, stream, a);
+  const int64_t rows = (int64_t)a.batch * a.heads * a.n_blocks;
+  hipLaunchKernelGGL(row_ptr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a, rows);
+}
+
+void launch_threshold_fill(const SelectArgs& a, hipStream_t stream) {
+  const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
+  hipLaunchKernelGGL(threshold_fill_kernel, g3, dim3(kTopkThreads), 0, stream, a);
 }
 
 }  // namespace h3attn
