@@ -294,3 +294,33 @@ def sparse_attention_csr(q, k, v, row_ptr, col_idx, block_size: int):
                 keys = block_token_ids(blocks, block_size, n_len)
                 out[b, rows, h, :], lse[b, h, rows] = attention_head(q[b, rows, h, :], k[b, keys, h, :], v[b, keys, h, :])
     return out, lse
+
+
+# --------------------------------------------------------------------------------------------
+# (5) The other fused block ops of the lossless runtime: AdaLN modulation and SwiGLU
+#     ["MiniMax-H3 的 6.24 倍…", section 先把近两倍的免费收益拿走: the runtime fuses AdaLN and
+#     SwiGLU kernels as well as QK RMSNorm and 3D RoPE]
+# --------------------------------------------------------------------------------------------
+
+
+def adaln_modulate(x: np.ndarray, shift: np.ndarray, scale: np.ndarray, eps: float) -> np.ndarray:
+    """y = LayerNorm(x) * (1 + scale) + shift over the last (hidden) axis.
+
+    Reading: the pages name the fused AdaLN kernel without a formula; this is the usual DiT
+    adaptive LayerNorm: normalisation without its own affine weights (biased variance, eps inside
+    the square root), then a per-(batch, channel) scale and shift from the conditioning.
+    x is [B, N, C]; shift and scale are [B, C]."""
+    x = np.asarray(x, dtype=np.float64)
+    mean = x.mean(axis=-1, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=-1, keepdims=True)
+    xn = (x - mean) / np.sqrt(var + float(eps))
+    shift = np.asarray(shift, dtype=np.float64)[:, None, :]
+    scale = np.asarray(scale, dtype=np.float64)[:, None, :]
+    return xn * (1.0 + scale) + shift
+
+
+def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """silu(gate) * up with silu(a) = a / (1 + exp(-a)) (reading: the usual SwiGLU gating)."""
+    a = np.asarray(gate, dtype=np.float64)
+    b = np.asarray(up, dtype=np.float64)
+    return a / (1.0 + np.exp(-a)) * b

@@ -447,3 +447,37 @@ def test_sparse_csr_matches_fixed_keep_form():
     c, _ = O.sparse_attention_csr(q, k, v, rpi, cii, 64)
     dense, _ = O.attention(q, k, v)
     np.testing.assert_allclose(c, dense, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------- AdaLN, SwiGLU
+
+def test_adaln_matches_torch_layer_norm_and_closed_forms():
+    x = rnd(2, 7, 48, scale=3.0) + 5.0                    # large mean: the centring must be exact
+    shift, scale = rnd(2, 48), rnd(2, 48)
+    for eps in (1e-6, 0.25):
+        ln = torch.nn.functional.layer_norm(torch.from_numpy(x), (48,), eps=eps).numpy()
+        ref = ln * (1.0 + scale[:, None, :]) + shift[:, None, :]
+        np.testing.assert_allclose(O.adaln_modulate(x, shift, scale, eps), ref, rtol=1e-13, atol=1e-13)
+    # zero scale and shift: every row has mean 0 and variance var/(var+eps)
+    y = O.adaln_modulate(x, np.zeros((2, 48)), np.zeros((2, 48)), 0.25)
+    np.testing.assert_allclose(y.mean(-1), 0.0, atol=1e-13)
+    v = x.var(-1)
+    np.testing.assert_allclose(y.var(-1), v / (v + 0.25), rtol=1e-12)
+    # constant rows normalise to zero, leaving the shift; scale = -1 removes the normalised part
+    c = np.full((2, 3, 48), 4.0)
+    np.testing.assert_allclose(O.adaln_modulate(c, shift, scale, 1e-6), np.broadcast_to(shift[:, None, :], c.shape), atol=1e-12)
+    np.testing.assert_allclose(O.adaln_modulate(x, shift, -np.ones((2, 48)), 1e-6), np.broadcast_to(shift[:, None, :], x.shape), atol=1e-12)
+    # invariant to adding a constant to a row, covariant in batch: scale/shift of batch 1 never touch batch 0
+    np.testing.assert_allclose(O.adaln_modulate(x + 7.5, shift, scale, 0.0), O.adaln_modulate(x, shift, scale, 0.0), atol=1e-11)
+    s2 = shift.copy(); s2[1] += 100
+    np.testing.assert_array_equal(O.adaln_modulate(x, s2, scale, 1e-6)[0], O.adaln_modulate(x, shift, scale, 1e-6)[0])
+
+
+def test_swiglu_matches_torch_silu_and_special_values():
+    a, b = rnd(5, 33, scale=4.0), rnd(5, 33)
+    ref = (torch.nn.functional.silu(torch.from_numpy(a)) * torch.from_numpy(b)).numpy()
+    np.testing.assert_allclose(O.swiglu(a, b), ref, rtol=1e-14, atol=1e-15)
+    assert O.swiglu(np.array([0.0]), np.array([3.0]))[0] == 0.0
+    np.testing.assert_allclose(O.swiglu(np.array([40.0]), np.array([2.0])), [80.0], rtol=1e-15)
+    np.testing.assert_allclose(O.swiglu(np.array([-40.0]), np.array([2.0])), [0.0], atol=1e-15)
+    np.testing.assert_allclose(O.swiglu(np.array([1.0]), np.array([1.0])), [1.0 / (1.0 + math.exp(-1.0))], rtol=1e-15)
