@@ -229,7 +229,34 @@ def main():
             components[f"norm_rope_{c2.name}_gbs"] = by / (med * 1e-3) / 1e9
             log(f"norm+rope {c2.name}: {med * 1e3:.1f} us median, {by / (med * 1e-3) / 1e9:.0f} GB/s (flushed)")
             del x2, qq, kk2, o1, o2
-        del flush
+        # the runtime's other fused block ops at this workload's shape: hidden = heads*head_dim
+        # tokens wide, SwiGLU on a 4x-hidden MLP width (an assumed expansion ratio), flushed
+        hidden = hd * d
+        xa = torch.randn((b, n, hidden), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        sh = torch.randn((b, hidden), device=dev)
+        scl = torch.randn((b, hidden), device=dev) * 0.1
+        ya = torch.empty_like(xa)
+        gate = torch.randn((b * n, 4 * hidden), device=dev, dtype=torch.bfloat16)
+        up = torch.randn((b * n, 4 * hidden), device=dev, dtype=torch.bfloat16)
+        ys = torch.empty_like(gate)
+        for name, fn, by in (("adaln", lambda: h3.adaln_modulate(xa, sh, scl, 1e-6, out=ya), 4.0 * xa.numel()),
+                             ("swiglu", lambda: h3.swiglu(gate, up, out=ys), 6.0 * gate.numel())):
+            times = []
+            for r in range(8):
+                flush_caches(flush)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                if r >= 2:
+                    times.append(elapsed_ms(e0, e1))
+            med = float(np.median(times))
+            components[f"{name}_us"] = med * 1e3
+            components[f"{name}_gbs"] = by / (med * 1e-3) / 1e9
+            components[f"{name}_frac_peak"] = by / (med * 1e-3) / 1e9 / PEAK_HBM_GBS
+            log(f"{name}: {med * 1e3:.1f} us median, {by / (med * 1e-3) / 1e9:.0f} GB/s (flushed, {by / 1e9:.2f} GB)")
+        del xa, ya, gate, up, ys, flush
 
     if not args.no_extra:
         # threshold mode (variable kept set per query block, CSR): tau bisected, outside any timed

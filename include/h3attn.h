@@ -165,6 +165,31 @@ h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf1
                                           int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
                                           int32_t block_size, hipStream_t stream);
 
+/* ---- The other fused per-block ops of the lossless runtime ----
+ * "MiniMax-H3 的 6.24 倍，不能直接算成六倍产能" (xiaodao.ai), section "先把近两倍的免费收益拿走":
+ * besides QK RMSNorm + 3D RoPE the runtime fuses AdaLN and SwiGLU. The pages give no formulas;
+ * these are the usual DiT forms. Both compute in float32 from bf16 and round once to bf16. */
+
+/* AdaLN modulation over the hidden axis of x [batch, n_tokens, hidden] (bf16):
+ *   y = (x - mean) / sqrt(var + eps) * (1 + scale[b]) + shift[b]
+ * with the biased variance of the row and no affine weights of its own; shift and scale are
+ * float32 [batch, hidden]. out may equal x. hidden must be a multiple of 8, at most 16384.
+ * Errors: null/misaligned pointers, sizes <= 0, eps < 0 -> INVALID_ARGUMENT; hidden not a
+ * multiple of 8 or above 16384 -> UNSUPPORTED. */
+h3attn_status h3attn_adaln_modulate(const h3attn_bf16* x, const float* shift, const float* scale,
+                                    h3attn_bf16* out, int32_t batch, int64_t n_tokens, int32_t hidden,
+                                    float eps, hipStream_t stream);
+
+/* SwiGLU gating: out[r, c] = silu(gate[r, c]) * up[r, c], silu(a) = a / (1 + exp(-a)), for
+ * rows x width elements; gate and up rows start every gate_row_stride / up_row_stride elements
+ * (so they may be the two halves of one [rows, 2*width] tensor), out is contiguous
+ * [rows, width]. out may equal gate or up when that operand's row stride equals width.
+ * width and both strides must be multiples of 8. Errors: null/misaligned pointers, sizes <= 0,
+ * strides < width -> INVALID_ARGUMENT; width or a stride not a multiple of 8 -> UNSUPPORTED. */
+h3attn_status h3attn_swiglu(const h3attn_bf16* gate, const h3attn_bf16* up, h3attn_bf16* out,
+                            int64_t rows, int32_t width, int64_t gate_row_stride, int64_t up_row_stride,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

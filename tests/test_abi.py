@@ -145,3 +145,19 @@ def test_threshold_validation(lib):
     assert h(*P, None, 0x40000, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
     assert h(*P, 0x60000, None, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
     assert h(*P, 0x60000, 0x40000, 0x50000, None, 1, 2, 640, 64, 32, None) == 2
+
+
+def test_block_ops_validation(lib):
+    f = lib.h3attn_adaln_modulate
+    P = (0x10000, 0x20000, 0x30000, 0x40000)
+    assert f(None, *P[1:], 1, 64, 128, 1e-6, None) == 1
+    assert f(*P, 0, 64, 128, 1e-6, None) == 1
+    assert f(*P, 1, 64, 100, 1e-6, None) == 2 and "hidden" in _err(lib)
+    assert f(*P, 1, 64, 16392, 1e-6, None) == 2
+    assert f(*P, 1, 64, 128, -1.0, None) == 1 and "eps" in _err(lib)
+    g = lib.h3attn_swiglu
+    assert g(0x10000, 0x20000, 0x30000, 0, 128, 128, 128, None) == 1
+    assert g(0x10000, 0x20000, 0x30000, 4, 128, 64, 128, None) == 1 and "stride" in _err(lib)
+    assert g(0x10000, 0x20000, 0x30000, 4, 100, 104, 104, None) == 2
+    assert g(0x10000, 0x20000, 0x10000, 4, 128, 256, 128, None) == 1 and "alias" in _err(lib)
+    assert g(0x10002, 0x20000, 0x30000, 4, 128, 128, 128, None) == 1

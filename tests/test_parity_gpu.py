@@ -360,3 +360,51 @@ def test_video5s_threshold_select_and_csr_sparse(h3):
             keys = oracle.block_token_ids(cin[rpn[r]:rpn[r + 1]], 64, cfg.n_tokens)
             ref, _ = oracle.attention_head(f64(qh[0, rows, h]), f64(kh[0, keys, h]), f64(vh[0, keys, h]))
             check_attention(f64(oh[0, rows, h]), ref, f"5s csr sparse head {h} block {i}")
+
+
+# ------------------------------------------------------------------ AdaLN and SwiGLU
+
+def _check_elementwise(gpu, ref, floor, what):
+    from tests.parity_util import bf16_ulp
+    tol = np.maximum(bf16_ulp(ref), floor)
+    worst = float(np.max(np.abs(gpu - ref) / tol))
+    rne = torch.from_numpy(ref).to(torch.bfloat16).to(torch.float64).numpy()
+    exact = float(np.mean(gpu == rne))
+    log(f"{what}: worst {worst:.3f} ulp, exact-RNE fraction {exact:.5f}")
+    assert worst <= 1.0 and exact > 0.99, what
+
+
+@pytest.mark.parametrize("b,n,c", [(2, 333, 6144), (1, 64, 96), (3, 17, 16384), (1, 1, 8)])
+def test_adaln_modulate_full(h3, b, n, c):
+    g = torch.Generator(device=DEV).manual_seed(b * 1000 + n + c)
+    x = (torch.randn((b, n, c), generator=g, device=DEV) * 2.0 + 3.0).to(torch.bfloat16)
+    shift = torch.randn((b, c), generator=g, device=DEV)
+    scale = torch.randn((b, c), generator=g, device=DEV) * 0.5
+    y = h3.adaln_modulate(x, shift, scale, 1e-6)
+    _sync()
+    xd, sh, scd = f64(x), f64(shift), f64(scale)
+    ref = oracle.adaln_modulate(xd, sh, scd, float(np.float32(1e-6)))
+    xn = oracle.adaln_modulate(xd, np.zeros_like(sh), np.zeros_like(scd), float(np.float32(1e-6)))
+    floor = 2.0 ** -14 * (np.abs(xn * (1 + scd[:, None, :])) + np.abs(sh[:, None, :]))
+    _check_elementwise(f64(y), ref, floor, f"adaln {b}x{n}x{c}")
+    y2 = x.clone()
+    h3.adaln_modulate(y2, shift, scale, 1e-6, out=y2)
+    _sync()
+    assert torch.equal(y2, y)
+
+
+def test_swiglu_full_separate_and_fused_layout(h3):
+    g = torch.Generator(device=DEV).manual_seed(77)
+    a = (torch.randn((3, 129, 4096), generator=g, device=DEV) * 3).to(torch.bfloat16)
+    u = torch.randn((3, 129, 4096), generator=g, device=DEV).to(torch.bfloat16)
+    y = h3.swiglu(a, u)
+    _sync()
+    ref = oracle.swiglu(f64(a), f64(u))
+    _check_elementwise(f64(y), ref, 1e-30, "swiglu separate")
+    both = torch.cat([a, u], dim=-1).contiguous()         # one [.., 2F] tensor: gate half, up half
+    y2 = h3.swiglu(both[..., :4096], both[..., 4096:])
+    _sync()
+    assert torch.equal(y2, y)
+    tiny = h3.swiglu(a[0, :1, :8].contiguous(), u[0, :1, :8].contiguous())
+    _sync()
+    _check_elementwise(f64(tiny), oracle.swiglu(f64(a[0, :1, :8]), f64(u[0, :1, :8])), 1e-30, "swiglu 8")

@@ -7,11 +7,13 @@ Four calls, each a hand-written HIP kernel behind a C ABI (include/h3attn.h):
   block_sparse_fwd  attention over the kept key blocks only
 Threshold mode: subblock_select_threshold (blocks within tau of the row's best, CSR) and
 block_sparse_csr_fwd (variable kept set per query block).
+Other fused block ops of the runtime: adaln_modulate (LayerNorm * (1 + scale) + shift) and swiglu.
 """
 from ._lib import (LIB_PATH, SIGNATURES, H3AttnError, block_sparse_csr_fwd, block_sparse_fwd,  # noqa: F401
                    dense_fwd, keep_count, load_library, qk_norm_rope, select_workspace_bytes,
-                   subblock_select, subblock_select_threshold, threshold_workspace_bytes, version)
+                   subblock_select, subblock_select_threshold, threshold_workspace_bytes, version,
+                   adaln_modulate, swiglu)
 
 __all__ = ["qk_norm_rope", "dense_fwd", "subblock_select", "block_sparse_fwd", "keep_count",
            "select_workspace_bytes", "subblock_select_threshold", "block_sparse_csr_fwd",
-           "threshold_workspace_bytes", "version", "H3AttnError", "load_library"]
+           "threshold_workspace_bytes", "adaln_modulate", "swiglu", "version", "H3AttnError", "load_library"]

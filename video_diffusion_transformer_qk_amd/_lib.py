@@ -45,6 +45,8 @@ SIGNATURES = {
     "h3attn_subblock_threshold_fill": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, _P, _P, _I64, _P,
                                                       ctypes.c_size_t, _P]),
     "h3attn_block_sparse_csr_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P]),
+    "h3attn_adaln_modulate": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, ctypes.c_float, _P]),
+    "h3attn_swiglu": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I64, _I64, _P]),
 }
 
 
@@ -261,3 +263,45 @@ def block_sparse_csr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_
     _check(lib.h3attn_block_sparse_csr_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), row_ptr.data_ptr(), ci.data_ptr(),
                                            o.data_ptr(), _ptr(lse), b, h, n, d, block_size, _stream()))
     return (o, lse) if return_lse else o
+
+
+def adaln_modulate(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor, eps: float = 1e-6,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """LayerNorm(x) * (1 + scale) + shift over the hidden axis; x bf16 [B, N, C], shift/scale fp32 [B, C]."""
+    lib = load_library()
+    _need(x, "x", torch.bfloat16, 3)
+    _need(shift, "shift", torch.float32, 2)
+    _need(scale, "scale", torch.float32, 2)
+    b, n, c = x.shape
+    if tuple(shift.shape) != (b, c) or tuple(scale.shape) != (b, c):
+        raise ValueError("shift and scale must be [B, C]")
+    o = torch.empty_like(x) if out is None else out
+    _need(o, "out", torch.bfloat16, 3)
+    _check(lib.h3attn_adaln_modulate(x.data_ptr(), shift.data_ptr(), scale.data_ptr(), o.data_ptr(), b, n, c,
+                                     float(eps), _stream()))
+    return o
+
+
+def swiglu(gate: torch.Tensor, up: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """silu(gate) * up on bf16 tensors [..., F]. gate and up may be strided row views (e.g. the two
+    halves of one [..., 2F] tensor) as long as the last axis is contiguous."""
+    lib = load_library()
+    for t, nm in ((gate, "gate"), (up, "up")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError(f"{nm} must be a bf16 device tensor")
+        if t.stride(-1) != 1 or t.dim() < 1:
+            raise ValueError(f"{nm} must have a contiguous last axis")
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    f = gate.shape[-1]
+    rows = gate.numel() // f
+    def row_stride(t):
+        if t.dim() == 1:
+            return f
+        t2 = t.reshape(-1, f) if t.is_contiguous() else t.view(-1, f)
+        return t2.stride(0)
+    o = torch.empty(gate.shape, dtype=torch.bfloat16, device=gate.device) if out is None else out
+    _need(o, "out", torch.bfloat16)
+    _check(lib.h3attn_swiglu(gate.data_ptr(), up.data_ptr(), o.data_ptr(), rows, f, row_stride(gate), row_stride(up),
+                             _stream()))
+    return o

@@ -324,4 +324,40 @@ h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf1
   return check_launch("h3attn_block_sparse_csr_fwd");
 }
 
+h3attn_status h3attn_adaln_modulate(const h3attn_bf16* x, const float* shift, const float* scale,
+                                    h3attn_bf16* out, int32_t batch, int64_t n_tokens, int32_t hidden,
+                                    float eps, hipStream_t stream) {
+  CHECK_PTR(x); CHECK_PTR(shift); CHECK_PTR(scale); CHECK_PTR(out);
+  if (batch <= 0 || n_tokens <= 0 || hidden <= 0)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "batch, n_tokens and hidden must be > 0");
+  if (hidden % 8 != 0 || hidden > 16384)
+    return fail(H3ATTN_ERR_UNSUPPORTED, "hidden must be a multiple of 8 and at most 16384 (got %d)", hidden);
+  if ((int64_t)batch * n_tokens >= ((int64_t)1 << 31)) return fail(H3ATTN_ERR_UNSUPPORTED, "batch*n_tokens must be below 2^31");
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  h3attn::AdaLNArgs a{};
+  a.x = x; a.shift = shift; a.scale = scale; a.out = out;
+  a.n_tokens = n_tokens; a.batch = batch; a.hidden = hidden; a.eps = eps;
+  h3attn::launch_adaln(a, stream);
+  return check_launch("h3attn_adaln_modulate");
+}
+
+h3attn_status h3attn_swiglu(const h3attn_bf16* gate, const h3attn_bf16* up, h3attn_bf16* out,
+                            int64_t rows, int32_t width, int64_t gate_row_stride, int64_t up_row_stride,
+                            hipStream_t stream) {
+  CHECK_PTR(gate); CHECK_PTR(up); CHECK_PTR(out);
+  if (rows <= 0 || width <= 0) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "rows and width must be > 0");
+  if (gate_row_stride < width || up_row_stride < width)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row strides must be >= width");
+  if (width % 8 || gate_row_stride % 8 || up_row_stride % 8)
+    return fail(H3ATTN_ERR_UNSUPPORTED, "width and row strides must be multiples of 8");
+  if (rows * (int64_t)(width / 8) / 512 >= ((int64_t)1 << 31)) return fail(H3ATTN_ERR_UNSUPPORTED, "tensor too large for one launch");
+  if ((out == gate && gate_row_stride != width) || (out == up && up_row_stride != width))
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "out may alias gate or up only when that row stride equals width");
+  h3attn::SwiGLUArgs a{};
+  a.gate = gate; a.up = up; a.out = out; a.rows = rows; a.width = width;
+  a.gate_stride = gate_row_stride; a.up_stride = up_row_stride;
+  h3attn::launch_swiglu(a, stream);
+  return check_launch("h3attn_swiglu");
+}
+
 }  // extern "C"

@@ -1,0 +1,147 @@
+// Fused AdaLN modulation and SwiGLU for gfx950 — the other per-block fused ops of the runtime.
+//
+// Source: "MiniMax-H3 的 6.24 倍，不能直接算成六倍产能" (xiaodao.ai), section
+// "先把近两倍的免费收益拿走": besides QK RMSNorm and 3D RoPE, the lossless runtime fuses AdaLN and
+// SwiGLU, removing intermediate tensors and their memory traffic without changing the math.
+//
+// Both kernels are HBM-bound streams:
+//  adaln_kernel   one workgroup per token row: the row (hidden bf16 values, 16 bytes per lane per
+//                 chunk) stays in registers between the mean pass, the centred variance pass and
+//                 the output, so x is read once and y written once; scale/shift are per (batch,
+//                 channel) float32 and stay in L2.
+//  swiglu_kernel  16-byte chunks of the gate and up rows -> silu(gate) * up in float32 -> bf16.
+// Loads and stores use nontemporal hints: every byte is touched exactly once.
+#include "device_util.h"
+#include "kernels.h"
+
+namespace h3attn {
+namespace {
+
+constexpr int kAdaThreads = 256;
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();  // red may still be read by the previous reduction
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <int CPT>  // 16-byte chunks per thread
+__global__ __launch_bounds__(kAdaThreads) void adaln_kernel(AdaLNArgs a) {
+  __shared__ float red[kAdaThreads / 64];
+  const int64_t row = blockIdx.x;            // over batch * n_tokens
+  const int b = (int)(row / a.n_tokens);
+  const int chunks = a.hidden / 8;
+  const uint16_t* xr = a.x + row * a.hidden;
+  uint16_t* yr = a.out + row * a.hidden;
+  u32x4 x[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = threadIdx.x + i * kAdaThreads;
+    if (c < chunks) x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + 8 * c));
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = threadIdx.x + i * kAdaThreads;
+    if (c < chunks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s += bf16_lo(x[i][j]) + bf16_hi(x[i][j]);
+  }
+  const float inv_c = 1.0f / (float)a.hidden;
+  const float mean = block_sum_256(s, red) * inv_c;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = threadIdx.x + i * kAdaThreads;
+    if (c < chunks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d0 = bf16_lo(x[i][j]) - mean, d1 = bf16_hi(x[i][j]) - mean;
+        ss = fmaf(d0, d0, fmaf(d1, d1, ss));
+      }
+  }
+  const float rstd = rsqrtf(fmaf(block_sum_256(ss, red), inv_c, a.eps));
+  const float* sh = a.shift + (int64_t)b * a.hidden;
+  const float* sc = a.scale + (int64_t)b * a.hidden;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = threadIdx.x + i * kAdaThreads;
+    if (c < chunks) {
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(sc + 8 * c), s1 = *reinterpret_cast<const f32x4*>(sc + 8 * c + 4);
+      const f32x4 h0 = *reinterpret_cast<const f32x4*>(sh + 8 * c), h1 = *reinterpret_cast<const f32x4*>(sh + 8 * c + 4);
+      const float scv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      const float shv[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float y0 = fmaf((bf16_lo(x[i][j]) - mean) * rstd, 1.0f + scv[2 * j], shv[2 * j]);
+        const float y1 = fmaf((bf16_hi(x[i][j]) - mean) * rstd, 1.0f + scv[2 * j + 1], shv[2 * j + 1]);
+        o[j] = pack_bf16x2(y0, y1);
+      }
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(yr + 8 * c));
+    }
+  }
+}
+
+constexpr int kSwiThreads = 256;
+constexpr int kSwiChunks = 2;  // 16-byte output chunks per thread
+
+__global__ __launch_bounds__(kSwiThreads) void swiglu_kernel(SwiGLUArgs a) {
+  const int64_t cpr = a.width / 8;  // chunks per row
+  const int64_t total = a.rows * cpr;
+  const int64_t first = ((int64_t)blockIdx.x * kSwiThreads * kSwiChunks) + threadIdx.x;
+  u32x4 g[kSwiChunks], u[kSwiChunks];
+#pragma unroll
+  for (int i = 0; i < kSwiChunks; ++i) {
+    const int64_t ch = first + (int64_t)i * kSwiThreads;
+    if (ch < total) {
+      const int64_t r = ch / cpr, c = ch % cpr;
+      g[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.gate + r * a.gate_stride + 8 * c));
+      u[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.up + r * a.up_stride + 8 * c));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kSwiChunks; ++i) {
+    const int64_t ch = first + (int64_t)i * kSwiThreads;
+    if (ch < total) {
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a0 = bf16_lo(g[i][j]), a1 = bf16_hi(g[i][j]);
+        const float y0 = a0 / (1.0f + __expf(-a0)) * bf16_lo(u[i][j]);
+        const float y1 = a1 / (1.0f + __expf(-a1)) * bf16_hi(u[i][j]);
+        o[j] = pack_bf16x2(y0, y1);
+      }
+      const int64_t r = ch / cpr, c = ch % cpr;
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.out + r * a.width + 8 * c));
+    }
+  }
+}
+
+}  // namespace
+
+void launch_adaln(const AdaLNArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.batch * a.n_tokens;
+  const int cpt = (a.hidden / 8 + kAdaThreads - 1) / kAdaThreads;
+  const dim3 grid((unsigned)rows);
+  switch (cpt) {
+    case 1: hipLaunchKernelGGL(adaln_kernel<1>, grid, dim3(kAdaThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(adaln_kernel<2>, grid, dim3(kAdaThreads), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(adaln_kernel<3>, grid, dim3(kAdaThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(adaln_kernel<4>, grid, dim3(kAdaThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL(adaln_kernel<8>, grid, dim3(kAdaThreads), 0, stream, a); break;
+  }
+}
+
+void launch_swiglu(const SwiGLUArgs& a, hipStream_t stream) {
+  const int64_t chunks = a.rows * (a.width / 8);
+  const int64_t per_block = (int64_t)kSwiThreads * kSwiChunks;
+  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((chunks + per_block - 1) / per_block)), dim3(kSwiThreads), 0,
+                     stream, a);
+}
+
+}  // namespace h3attn

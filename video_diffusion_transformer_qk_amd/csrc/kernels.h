@@ -69,4 +69,25 @@ void launch_subblock_select(const SelectArgs& a, hipStream_t stream);
 void launch_threshold_count(const SelectArgs& a, hipStream_t stream);
 void launch_threshold_fill(const SelectArgs& a, hipStream_t stream);
 
+struct AdaLNArgs {
+  const uint16_t* x;
+  const float* shift;   // [B, C]
+  const float* scale;   // [B, C]
+  uint16_t* out;
+  int64_t n_tokens;
+  int32_t batch, hidden;
+  float eps;
+};
+
+void launch_adaln(const AdaLNArgs& a, hipStream_t stream);
+
+struct SwiGLUArgs {
+  const uint16_t* gate;
+  const uint16_t* up;
+  uint16_t* out;          // [rows, width] contiguous
+  int64_t rows, width, gate_stride, up_stride;  // strides in elements
+};
+
+void launch_swiglu(const SwiGLUArgs& a, hipStream_t stream);
+
 }  // namespace h3attn
