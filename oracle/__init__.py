@@ -5,4 +5,5 @@ from .attention_oracle import (attention, attention_head, block_means, block_sco
                                sparse_attention, sparse_attention_rows, subblock_select,
                                token_positions, topk_blocks, threshold_blocks,
                                subblock_select_threshold, near_threshold_entries,
-                               sparse_attention_csr, adaln_modulate, swiglu)
+                               sparse_attention_csr, adaln_modulate, swiglu, residual_change,
+                               CacheGate)

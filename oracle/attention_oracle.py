@@ -324,3 +324,41 @@ def swiglu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     a = np.asarray(gate, dtype=np.float64)
     b = np.asarray(up, dtype=np.float64)
     return a / (1.0 + np.exp(-a)) * b
+
+
+# --------------------------------------------------------------------------------------------
+# (6) Cache-DiT residual-change gate  ["MiniMax-H3 的 6.24 倍…", section 6.24 倍里…: Cache-DiT
+#     compares the residual change between adjacent denoising steps and, when it is small,
+#     reuses the cached middle-block results; the conservative setting has a tighter threshold
+#     and caches at most one step in a row, the stride setting a looser one and at most three]
+# --------------------------------------------------------------------------------------------
+
+
+def residual_change(cur: np.ndarray, prev: np.ndarray):
+    """(sum |cur - prev|, sum |prev|) over all elements; the relative change is their ratio.
+    Reading: the pages say "residual change" without a norm; the L1 relative change is used."""
+    cur = np.asarray(cur, dtype=np.float64)
+    prev = np.asarray(prev, dtype=np.float64)
+    return float(np.abs(cur - prev).sum()), float(np.abs(prev).sum())
+
+
+class CacheGate:
+    """Per-step reuse decision. The first step always computes (nothing to compare with). A step
+    reuses the cache iff its relative change is below `threshold` and fewer than
+    `max_consecutive` steps in a row have already been reused; a computed step resets the run.
+    The thresholds are not on the pages (decision parity unpinned)."""
+
+    def __init__(self, threshold: float, max_consecutive: int):
+        if not (threshold >= 0.0) or max_consecutive < 0:
+            raise ValueError("threshold >= 0 and max_consecutive >= 0 required")
+        self.threshold = float(threshold)
+        self.max_consecutive = int(max_consecutive)
+        self.consecutive = 0
+        self.steps = 0
+
+    def decide(self, rel_change: float) -> bool:
+        reuse = (self.steps > 0 and rel_change < self.threshold
+                 and self.consecutive < self.max_consecutive)
+        self.consecutive = self.consecutive + 1 if reuse else 0
+        self.steps += 1
+        return reuse

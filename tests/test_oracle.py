@@ -481,3 +481,35 @@ def test_swiglu_matches_torch_silu_and_special_values():
     np.testing.assert_allclose(O.swiglu(np.array([40.0]), np.array([2.0])), [80.0], rtol=1e-15)
     np.testing.assert_allclose(O.swiglu(np.array([-40.0]), np.array([2.0])), [0.0], atol=1e-15)
     np.testing.assert_allclose(O.swiglu(np.array([1.0]), np.array([1.0])), [1.0 / (1.0 + math.exp(-1.0))], rtol=1e-15)
+
+
+# ----------------------------------------------------------------------------------- Cache-DiT gate
+
+def test_residual_change_closed_forms():
+    a = rnd(1000)
+    d, n = O.residual_change(a, a)
+    assert d == 0.0 and n == pytest.approx(np.abs(a).sum(), rel=1e-15)
+    d, n = O.residual_change(2 * a, a)              # |2a - a| = |a|: relative change exactly 1
+    assert d == pytest.approx(n, rel=1e-14)
+    d, n = O.residual_change(a + 0.5, np.zeros(1000))
+    assert n == 0.0 and d == pytest.approx(np.abs(a + 0.5).sum(), rel=1e-15)
+    x = np.array([1.0, -2.0, 3.0]); y = np.array([1.5, -2.0, 2.0])
+    assert O.residual_change(x, y) == (1.5, 5.5)
+
+
+def test_cache_gate_rule():
+    # conservative-style: at most one cached step in a row
+    g = O.CacheGate(0.1, 1)
+    seq = [0.0, 0.01, 0.01, 0.01, 0.5, 0.01, 0.01]
+    assert [g.decide(r) for r in seq] == [False, True, False, True, False, True, False]
+    # stride-style: up to three in a row, reset by a large change
+    g = O.CacheGate(0.2, 3)
+    seq = [0.9, 0.1, 0.1, 0.1, 0.1, 0.1, 0.3, 0.1]
+    assert [g.decide(r) for r in seq] == [False, True, True, True, False, True, False, True]
+    # threshold is strict and 0 consecutive never reuses
+    g = O.CacheGate(0.1, 5)
+    assert [g.decide(r) for r in [0.0, 0.1, 0.0999]] == [False, False, True]
+    g = O.CacheGate(1.0, 0)
+    assert not any(g.decide(0.0) for _ in range(4))
+    with pytest.raises(ValueError):
+        O.CacheGate(-1.0, 1)
