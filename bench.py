@@ -239,8 +239,12 @@ def main():
         gate = torch.randn((b * n, 4 * hidden), device=dev, dtype=torch.bfloat16)
         up = torch.randn((b * n, 4 * hidden), device=dev, dtype=torch.bfloat16)
         ys = torch.empty_like(gate)
+        rws = torch.empty((h3.load_library().h3attn_residual_workspace_bytes(xa.numel()),), dtype=torch.uint8, device=dev)
+        rres = torch.empty((2,), dtype=torch.float64, device=dev)
         for name, fn, by in (("adaln", lambda: h3.adaln_modulate(xa, sh, scl, 1e-6, out=ya), 4.0 * xa.numel()),
-                             ("swiglu", lambda: h3.swiglu(gate, up, out=ys), 6.0 * gate.numel())):
+                             ("swiglu", lambda: h3.swiglu(gate, up, out=ys), 6.0 * gate.numel()),
+                             ("residual_change", lambda: h3.residual_change(xa, ya, workspace=rws, out=rres),
+                              4.0 * xa.numel())):
             times = []
             for r in range(8):
                 flush_caches(flush)

@@ -190,6 +190,41 @@ h3attn_status h3attn_swiglu(const h3attn_bf16* gate, const h3attn_bf16* up, h3at
                             int64_t rows, int32_t width, int64_t gate_row_stride, int64_t up_row_stride,
                             hipStream_t stream);
 
+/* ---- Cache-DiT residual-change gate ----
+ * "MiniMax-H3 的 6.24 倍，不能直接算成六倍产能" (xiaodao.ai), section "6.24 倍里，真正有损的部分大约
+ * 是三倍": Cache-DiT measures the residual change between adjacent denoising steps and, when it is
+ * small, reuses cached middle-block results; the conservative setting has a tighter threshold and
+ * caches at most one step in a row, the stride setting a looser one and at most three. The pages
+ * give neither the norm nor the thresholds: the change is the L1 ratio
+ * sum|cur - prev| / sum|prev|, and thresholds are the caller's. */
+
+/* Workspace bytes for h3attn_residual_change on n elements (two float64 per partial block). */
+size_t h3attn_residual_workspace_bytes(int64_t n);
+
+/* result (DEVICE pointer, 2 doubles) <- { sum |cur - prev|, sum |prev| } over n bf16 elements of
+ * two contiguous tensors. Per-thread sums in float32, everything above in float64, combined in a
+ * fixed order (deterministic). Errors: null/misaligned pointers, n <= 0, small workspace ->
+ * INVALID_ARGUMENT. */
+h3attn_status h3attn_residual_change(const h3attn_bf16* cur, const h3attn_bf16* prev, int64_t n,
+                                     double* result, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* Host-side reuse policy (plain C state; no GPU work). */
+typedef struct {
+  double threshold;        /* reuse only when the relative change is strictly below this */
+  int32_t max_consecutive; /* at most this many reused steps in a row (1: conservative, 3: stride) */
+  int32_t consecutive;     /* reused steps in the current run */
+  int64_t steps;           /* steps decided so far */
+} h3attn_cache_gate;
+
+/* Initialise a gate; INVALID_ARGUMENT if threshold < 0 (or NaN), max_consecutive < 0 or gate is NULL. */
+h3attn_status h3attn_cache_gate_init(h3attn_cache_gate* gate, double threshold, int32_t max_consecutive);
+
+/* Decide one step: returns 1 to reuse the cached result, 0 to compute (always 0 on the first
+ * step, when there is nothing to compare with), -1 if gate is NULL. A computed step resets the
+ * run of reused steps. */
+int32_t h3attn_cache_gate_decide(h3attn_cache_gate* gate, double rel_change);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import oracle
@@ -161,3 +162,34 @@ def test_block_ops_validation(lib):
     assert g(0x10000, 0x20000, 0x30000, 4, 100, 104, 104, None) == 2
     assert g(0x10000, 0x20000, 0x10000, 4, 128, 256, 128, None) == 1 and "alias" in _err(lib)
     assert g(0x10002, 0x20000, 0x30000, 4, 128, 128, 128, None) == 1
+
+
+def test_residual_change_validation(lib):
+    f = lib.h3attn_residual_change
+    nbytes = lib.h3attn_residual_workspace_bytes(1000)
+    assert nbytes >= 16 and nbytes % 256 == 0
+    assert lib.h3attn_residual_workspace_bytes(0) == 0
+    assert f(None, 0x20000, 1000, 0x30000, 0x100000, nbytes, None) == 1
+    assert f(0x10000, 0x20000, 0, 0x30000, 0x100000, nbytes, None) == 1
+    assert f(0x10000, 0x20000, 1000, None, 0x100000, nbytes, None) == 1 and "result" in _err(lib)
+    assert f(0x10000, 0x20000, 1000, 0x30000, 0x100000, nbytes - 1, None) == 1 and "workspace" in _err(lib)
+
+
+def test_cache_gate_policy_matches_oracle_rule(lib):
+    """The C policy (host code, no GPU) against the oracle's statement of the rule."""
+    from video_diffusion_transformer_qk_amd._lib import CacheGateState
+    rng = np.random.default_rng(5)
+    for trial in range(50):
+        thr = float(rng.choice([0.0, 0.05, 0.1, 0.5]))
+        mc = int(rng.integers(0, 5))
+        st = CacheGateState()
+        assert lib.h3attn_cache_gate_init(ctypes.byref(st), thr, mc) == 0
+        ref = oracle.CacheGate(thr, mc)
+        for r in rng.choice([0.0, 0.01, 0.05, 0.099, 0.1, 0.3, 1.0], size=40):
+            assert bool(lib.h3attn_cache_gate_decide(ctypes.byref(st), float(r))) == ref.decide(float(r))
+        assert st.steps == 40
+    st = CacheGateState()
+    assert lib.h3attn_cache_gate_init(ctypes.byref(st), -1.0, 1) == 1
+    assert lib.h3attn_cache_gate_init(ctypes.byref(st), 0.1, -1) == 1
+    assert lib.h3attn_cache_gate_init(None, 0.1, 1) == 1
+    assert lib.h3attn_cache_gate_decide(None, 0.0) == -1

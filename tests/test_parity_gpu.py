@@ -408,3 +408,47 @@ def test_swiglu_full_separate_and_fused_layout(h3):
     tiny = h3.swiglu(a[0, :1, :8].contiguous(), u[0, :1, :8].contiguous())
     _sync()
     _check_elementwise(f64(tiny), oracle.swiglu(f64(a[0, :1, :8]), f64(u[0, :1, :8])), 1e-30, "swiglu 8")
+
+
+# ------------------------------------------------------------------ Cache-DiT residual gate
+
+@pytest.mark.parametrize("n", [1, 7, 8, 1000, 65536 + 3, 2 * 8192 * 8 * 5 + 11])
+def test_residual_change_matches_oracle(h3, n):
+    g = torch.Generator(device=DEV).manual_seed(n)
+    prev = torch.randn((n,), generator=g, device=DEV).to(torch.bfloat16)
+    cur = (prev.float() + 0.05 * torch.randn((n,), generator=g, device=DEV)).to(torch.bfloat16)
+    res = h3.residual_change(cur, prev)
+    _sync()
+    d, p = res.tolist()
+    rd, rp = oracle.residual_change(f64(cur), f64(prev))
+    assert abs(d - rd) <= 1e-6 * max(rd, 1e-30) + 1e-12 and abs(p - rp) <= 1e-6 * rp
+    res2 = h3.residual_change(cur, prev)
+    _sync()
+    assert res2.tolist() == [d, p]        # fixed reduction order: bitwise repeatable
+    same = h3.residual_change(prev, prev)
+    _sync()
+    assert same[0].item() == 0.0
+
+
+def test_cache_gate_drives_a_step_sequence(h3):
+    """The library gate on GPU-measured changes makes the same decisions as the oracle rule on
+    oracle-measured changes (sequence built so no change sits near the threshold)."""
+    g = torch.Generator(device=DEV).manual_seed(3)
+    base = torch.randn((4, 256, 512), generator=g, device=DEV)
+    scales = [0.0, 0.01, 0.01, 0.3, 0.01, 0.01, 0.01, 0.01, 0.5, 0.02]
+    states, prev = [], base
+    for s in scales:
+        cur = prev + s * torch.randn(prev.shape, generator=g, device=DEV)
+        states.append(cur.to(torch.bfloat16))
+        prev = cur
+    for mc in (1, 3):
+        gate = h3.CacheGate(0.1, mc)
+        ref = oracle.CacheGate(0.1, mc)
+        for i, st in enumerate(states):
+            got = gate.step(st, states[i - 1] if i > 0 else None)
+            if i == 0:
+                want = ref.decide(float("inf"))
+            else:
+                d, p = oracle.residual_change(f64(st), f64(states[i - 1]))
+                want = ref.decide(d / p)
+            assert got == want, (mc, i)

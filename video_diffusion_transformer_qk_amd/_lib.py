@@ -47,7 +47,16 @@ SIGNATURES = {
     "h3attn_block_sparse_csr_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P]),
     "h3attn_adaln_modulate": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, ctypes.c_float, _P]),
     "h3attn_swiglu": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I64, _I64, _P]),
+    "h3attn_residual_workspace_bytes": (ctypes.c_size_t, [_I64]),
+    "h3attn_residual_change": (ctypes.c_int, [_P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "h3attn_cache_gate_init": (ctypes.c_int, [_P, ctypes.c_double, _I32]),
+    "h3attn_cache_gate_decide": (_I32, [_P, ctypes.c_double]),
 }
+
+
+class CacheGateState(ctypes.Structure):
+    _fields_ = [("threshold", ctypes.c_double), ("max_consecutive", ctypes.c_int32),
+                ("consecutive", ctypes.c_int32), ("steps", ctypes.c_int64)]
 
 
 class H3AttnError(RuntimeError):
@@ -305,3 +314,47 @@ def swiglu(gate: torch.Tensor, up: torch.Tensor, out: Optional[torch.Tensor] = N
     _check(lib.h3attn_swiglu(gate.data_ptr(), up.data_ptr(), o.data_ptr(), rows, f, row_stride(gate), row_stride(up),
                              _stream()))
     return o
+
+
+def residual_change(cur: torch.Tensor, prev: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """float64 device tensor [2] = (sum |cur - prev|, sum |prev|) for two bf16 tensors."""
+    lib = load_library()
+    _need(cur, "cur", torch.bfloat16)
+    _need(prev, "prev", torch.bfloat16)
+    if cur.shape != prev.shape:
+        raise ValueError("cur and prev must have the same shape")
+    n = cur.numel()
+    need = int(lib.h3attn_residual_workspace_bytes(n))
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=cur.device)
+    res = torch.empty((2,), dtype=torch.float64, device=cur.device) if out is None else out
+    _need(res, "out", torch.float64, 1)
+    _check(lib.h3attn_residual_change(cur.data_ptr(), prev.data_ptr(), n, res.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel(), _stream()))
+    return res
+
+
+class CacheGate:
+    """Cache-DiT reuse policy held in the library's C state (h3attn_cache_gate)."""
+
+    CONSERVATIVE_MAX_CONSECUTIVE = 1
+    STRIDE_MAX_CONSECUTIVE = 3
+
+    def __init__(self, threshold: float, max_consecutive: int):
+        self._lib = load_library()
+        self._state = CacheGateState()
+        _check(self._lib.h3attn_cache_gate_init(ctypes.byref(self._state), float(threshold), int(max_consecutive)))
+
+    def decide(self, rel_change: float) -> bool:
+        r = self._lib.h3attn_cache_gate_decide(ctypes.byref(self._state), float(rel_change))
+        if r < 0:
+            raise RuntimeError("invalid gate state")
+        return bool(r)
+
+    def step(self, cur: torch.Tensor, prev: Optional[torch.Tensor]) -> bool:
+        """Measure the change of cur against prev on the GPU (one host read) and decide."""
+        if prev is None:
+            return self.decide(float("inf"))
+        d, p = residual_change(cur, prev).tolist()
+        return self.decide(d / p if p > 0 else float("inf"))

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libh3attn.so")
-SOURCES = ["qk_norm_rope.hip", "attention.hip", "subblock_select.hip", "block_ops.hip", "api.cpp"]
+SOURCES = ["qk_norm_rope.hip", "attention.hip", "subblock_select.hip", "block_ops.hip", "cache_gate.hip", "api.cpp"]
 ARCH = "gfx950"
 
 
@@ -45,7 +45,7 @@ def _compile(src: str, debug: bool) -> str:
 def build(verbose: bool = True, debug: bool = False) -> str:
     """Compile every source and link libh3attn.so next to this file. Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, debug), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC"] + objs + ["-o", tmp]

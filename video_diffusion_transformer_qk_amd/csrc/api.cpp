@@ -360,4 +360,47 @@ h3attn_status h3attn_swiglu(const h3attn_bf16* gate, const h3attn_bf16* up, h3at
   return check_launch("h3attn_swiglu");
 }
 
+size_t h3attn_residual_workspace_bytes(int64_t n) {
+  if (n <= 0) return 0;
+  return align256((size_t)h3attn::residual_parts(n) * 2 * sizeof(double));
+}
+
+h3attn_status h3attn_residual_change(const h3attn_bf16* cur, const h3attn_bf16* prev, int64_t n,
+                                     double* result, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  CHECK_PTR(cur); CHECK_PTR(prev);
+  if (result == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "result is NULL");
+  if (reinterpret_cast<uintptr_t>(result) & 7u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "result is not 8-byte aligned");
+  if (n <= 0) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "n must be > 0");
+  if (workspace == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  const size_t need = h3attn_residual_workspace_bytes(n);
+  if (workspace_bytes < need)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  if (h3attn::residual_parts(n) >= (1 << 30)) return fail(H3ATTN_ERR_UNSUPPORTED, "tensor too large");
+  h3attn::ResidualArgs a{};
+  a.cur = cur; a.prev = prev; a.n = n; a.partial = static_cast<double*>(workspace); a.result = result;
+  h3attn::launch_residual_change(a, stream);
+  return check_launch("h3attn_residual_change");
+}
+
+h3attn_status h3attn_cache_gate_init(h3attn_cache_gate* gate, double threshold, int32_t max_consecutive) {
+  if (gate == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "gate is NULL");
+  if (!(threshold >= 0.0)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "threshold must be >= 0");
+  if (max_consecutive < 0) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "max_consecutive must be >= 0");
+  gate->threshold = threshold;
+  gate->max_consecutive = max_consecutive;
+  gate->consecutive = 0;
+  gate->steps = 0;
+  return ok();
+}
+
+int32_t h3attn_cache_gate_decide(h3attn_cache_gate* gate, double rel_change) {
+  if (gate == nullptr) return -1;
+  const bool reuse = gate->steps > 0 && rel_change < gate->threshold && gate->consecutive < gate->max_consecutive;
+  gate->consecutive = reuse ? gate->consecutive + 1 : 0;
+  gate->steps += 1;
+  return reuse ? 1 : 0;
+}
+
 }  // extern "C"

@@ -90,4 +90,19 @@ struct SwiGLUArgs {
 
 void launch_swiglu(const SwiGLUArgs& a, hipStream_t stream);
 
+// chunks of 8 elements reduced per workgroup by the residual-change kernel
+constexpr int64_t kResidualChunksPerBlock = 8192;
+
+struct ResidualArgs {
+  const uint16_t* cur;
+  const uint16_t* prev;
+  int64_t n;
+  int64_t chunks_per_block;
+  double* partial;   // workspace: 2 doubles per workgroup
+  double* result;    // 2 doubles: sum |cur - prev|, sum |prev|
+};
+
+int residual_parts(int64_t n);
+void launch_residual_change(const ResidualArgs& a, hipStream_t stream);
+
 }  // namespace h3attn
