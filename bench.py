@@ -306,10 +306,10 @@ def main():
             f"({components['threshold_mode']['csr_sparse_tflops_kept']:.0f} TFLOP/s)")
         del tws, out_c
 
-    roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,8,2,true,false> (dense)",
+    roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,8,2> (dense)",
                 "achieved": dense_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": dense_tf / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic("attn_fwd_kernel<128,8,2,true,false,0> (dense)"),
+                "traffic": measured_traffic("attn_fwd_kernel<128,8,2> (dense)"),
                 "traffic_unit": "bytes per launch (FETCH_SIZE x2.000 + WRITE_SIZE x1.000, copy-calibrated)",
                 "per_launch_flops": dense_flops, "avg_launch_ms": avg["dense"]}
 

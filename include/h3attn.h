@@ -116,7 +116,9 @@ h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
  * the key blocks block_idx[b, head, i, 0..keep-1], with the softmax renormalised over those
  * tokens (a partial last key block contributes only its valid tokens). Same numerics and
  * outputs as h3attn_dense_fwd. block_idx rows must hold `keep` distinct indices in [0, nB);
- * their order does not matter. Behaviour for other index values is undefined.
+ * their order does not matter: each row's kept blocks are visited in ascending key order, so
+ * the result is bit-identical for any order (and, with every block kept, to h3attn_dense_fwd).
+ * Behaviour for other index values is undefined.
  * Errors: as h3attn_dense_fwd, plus keep outside [1, nB] -> INVALID_ARGUMENT and
  * block_size != 64 -> UNSUPPORTED. */
 h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
@@ -157,8 +159,8 @@ h3attn_status h3attn_subblock_threshold_fill(int32_t batch, int32_t heads, int64
                                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Block-sparse attention with a CSR kept set per query block (rows as above; indices distinct
- * and in [0, nB), any order). Same numerics as h3attn_block_sparse_fwd. A row with no kept
- * block yields zeros and lse = -inf. */
+ * and in [0, nB), any order, visited in ascending key order). Same numerics as
+ * h3attn_block_sparse_fwd. A row with no kept block yields zeros and lse = -inf. */
 h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
                                           const int64_t* row_ptr, const int32_t* col_idx,
                                           h3attn_bf16* out, float* lse,

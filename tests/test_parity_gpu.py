@@ -140,7 +140,36 @@ def test_sparse_index_order_irrelevant(h3):
     a = h3.block_sparse_fwd(c["q"], c["k"], c["v"], idx)
     b = h3.block_sparse_fwd(c["q"], c["k"], c["v"], rev)
     _sync()
-    check_attention(f64(a), f64(b).astype(np.float64), "reversed index order")
+    # kept blocks are visited in ascending key order whatever their order in the row
+    assert torch.equal(a, b), "reversed index order changed the result"
+
+
+def test_sparse_union_across_windows_and_ragged_groups(h3):
+    """More key blocks than one union window (4096) and a block count that is not a multiple of
+    the 4 query blocks a workgroup takes: sampled query blocks against the oracle, the CSR form
+    and a shuffled index order bit for bit."""
+    nb = 4098                                   # two union windows, last group of 2 blocks
+    n = nb * 64 - 17                            # partial last key block
+    c = random_case(1, n, 1, 64, seed=4242, device=DEV)
+    idx = h3.subblock_select(c["q"], c["k"], 0.99)
+    keep = idx.shape[-1]
+    o, lse = h3.block_sparse_fwd(c["q"], c["k"], c["v"], idx, return_lse=True)
+    perm = torch.argsort(torch.rand(idx.shape, generator=torch.Generator(device=DEV).manual_seed(7), device=DEV), dim=-1)
+    shuffled = torch.gather(idx, -1, perm).contiguous()
+    o2 = h3.block_sparse_fwd(c["q"], c["k"], c["v"], shuffled)
+    rp = torch.arange(0, nb + 1, dtype=torch.int64, device=DEV) * keep
+    o3 = h3.block_sparse_csr_fwd(c["q"], c["k"], c["v"], rp, shuffled.reshape(-1).contiguous())
+    _sync()
+    assert torch.equal(o, o2) and torch.equal(o, o3)
+    ih = idx.cpu().numpy()
+    assert (ih < 4096).any() and (ih >= 4096).any(), "kept sets should span both windows"
+    qh, kh, vh, oh, lh = c["q"].cpu(), c["k"].cpu(), c["v"].cpu(), o.cpu(), lse.cpu()
+    for i in sample_query_blocks(nb, 12, seed=99, extra=(nb - 2, nb - 3, 4095, 4096)):
+        rows = np.arange(i * 64, min((i + 1) * 64, n))
+        keys = oracle.block_token_ids(ih[0, 0, i], 64, n)
+        ref, rl = oracle.attention_head(f64(qh[0, rows, 0]), f64(kh[0, keys, 0]), f64(vh[0, keys, 0]))
+        check_attention(f64(oh[0, rows, 0]), ref, f"two-window sparse block {i}")
+        assert np.abs(f64(lh[0, 0, rows]) - rl).max() <= LSE_MAX_ABS
 
 
 def test_select_ties_resolve_to_lower_index(h3):

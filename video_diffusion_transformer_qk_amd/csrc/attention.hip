@@ -15,17 +15,15 @@
 //   O^T (D x queries) += V^T (D x keys) . P^T (keys x queries),
 // whose A operand (V^T) is read from a row-major V tile with the gfx950 LDS transpose read
 // (ds_read_b64_tr_b16). The key order inside each 16-key MFMA step is permuted identically on
-// both operands so that it matches the registers that already hold P^T.
+// both operands so that it matches the registers that already hold P^T. The softmax uses exp2
+// with log2(e)/sqrt(D) folded into one FMA, and the running max only moves (with a wave-uniform
+// O rescale) when a tile exceeds it by more than 2^8.
 //
 // Pipeline: tile t+1 is fetched from global memory into registers while tile t is computed,
-// then stored to LDS. Dense: 8 waves (256 queries) share each 64-key K/V tile, double-buffered
-// in LDS (one barrier per tile), two waves per SIMD (256-register budget) so one wave's MFMAs
-// overlap the other's softmax. Sparse: the workgroup is one 64-query block (2 waves) with a
-// single LDS tile (two barriers per tile) so four workgroups fit per CU, and workgroups are
-// ordered in windows of 1024 so that the resident ones cover one head (its K/V stays in the
-// MALL) with each XCD on consecutive query blocks. The softmax uses exp2 with
-// log2(e)/sqrt(D) folded into one FMA, and the running max only moves (with a wave-uniform O
-// rescale) when a tile exceeds it by more than 2^8.
+// then stored to the other half of a double-buffered LDS tile (one barrier per tile). Dense:
+// 8 waves (256 queries) share each 64-key K/V tile, two waves per SIMD (256-register budget) so
+// one wave's MFMAs overlap the other's softmax. Block-sparse: a workgroup takes 4 consecutive
+// query blocks and walks the union of their kept key blocks (see attn_sparse_group_kernel).
 #include "device_util.h"
 #include "kernels.h"
 
@@ -33,6 +31,7 @@ namespace h3attn {
 namespace {
 
 constexpr int kBN = 64;  // keys per tile (= SubBlock block size)
+
 #define kOnes2 (__builtin_bit_cast(bf16x2, 0x3f803f80u))  // bf16 pair (1.0, 1.0)
 
 template <int D, int BN>
@@ -45,41 +44,236 @@ struct Tile {
   static constexpr int CHUNKS = BN * D / 8;  // 16-byte chunks per tensor tile
 };
 
-// Maps the linear workgroup id to a work item so that each of the 8 XCDs (which receive
-// workgroups round-robin) processes one contiguous range of (query tile, head, batch) items:
-// neighbouring query tiles of one head then share an XCD and its L2.
-__device__ __forceinline__ int64_t xcd_contiguous(int64_t lin, int64_t total) {
-  const int64_t x = lin % 8, k = lin / 8, q = total / 8, r = total % 8;
-  return x * q + (x < r ? x : r) + k;
+// One wave's share of the forward pass: 32 query rows, their Q^T fragments (B operand, one
+// bf16x8 per 16-wide k step), the O^T accumulator and the running softmax statistics.
+template <int D>
+struct WaveRows {
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DT = D / 32;
+  bf16x8 qf[KSTEPS];
+  f32x16 o[DT];
+  float m_run;  // running max of s*sc (log2 units), shared by lanes l and l^32
+  float l_run;  // per-lane partial row sum
+};
+
+template <int D>
+__device__ __forceinline__ void rows_begin(WaveRows<D>& w, const uint16_t* qp) {
+#pragma unroll
+  for (int ks = 0; ks < WaveRows<D>::KSTEPS; ++ks)
+    w.qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
+#pragma unroll
+  for (int dt = 0; dt < WaveRows<D>::DT; ++dt) w.o[dt] = f32x16{};
+  w.m_run = -INFINITY;
+  w.l_run = 0.f;
 }
 
-// Same idea applied per window of 8*C consecutive workgroups: the workgroups resident at any
-// time then cover one narrow range of items (one head's K/V stays in the 256 MB MALL), and
-// inside the window each XCD gets C consecutive items.
-template <int C>
-__device__ __forceinline__ int64_t xcd_grouped(int64_t lin, int64_t total) {
-  const int64_t base = lin / (8 * C) * (8 * C), k = lin - base, rem = total - base;
-  if (rem >= 8 * C) return base + (k % 8) * C + k / 8;
-  return base + xcd_contiguous(k, rem);
+// The three parts of one 64-key tile for one wave. qk_tile: S^T = K . Q^T from the K tile at kb.
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const bf16x8 (&qf)[D / 16], const unsigned char* kb,
+                                        int lane) {
+  using T = Tile<D, kBN>;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + (32 * m + l32) * T::KS + (16 * ks + 8 * hi) * 2);
+      s[m] = mfma32x32x16(kf, qf[ks], s[m]);
+    }
+  }
 }
 
-// Tuning knobs: WAVES waves per workgroup (32 queries each); OCC minimum waves per SIMD (2 caps
-// the kernel at 256 registers so two waves share each SIMD and overlap each other's MFMA and
-// softmax work); DBUF double-buffers the K/V tile in LDS (one barrier per tile) instead of
-// keeping a single LDS tile (two barriers per tile, half the LDS, more workgroups per CU); XCD
-// selects the workgroup order (0: grid order, 1: one contiguous range per XCD, C > 1: windows
-// of 8*C workgroups); BN keys per tile (64, or 128 for dense: fewer barriers and less per-tile
-// bookkeeping per MFMA).
-template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0, int BN = 64, bool CSR = false>
-__global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
-  using T = Tile<D, BN>;
-  static_assert(!SPARSE || BN == kBN, "block-sparse tiles are single 64-token blocks");
-  constexpr int MT = BN / 32;  // 32-key sub-tiles per tile
-  constexpr int NT = WAVES * 64;
-  constexpr int KSTEPS = D / 16;
+// Keys at or past N get a score of -inf; only called for the tile that holds the last token,
+// so the number of valid keys in it, N - key0, is below 64.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int64_t key0, int64_t N, int lane) {
+  const int valid = (int)(N - key0) - 4 * (lane >> 5);  // valid keys counted from this lane's first row
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * m + 8 * (r / 4) + (r % 4) >= valid) s[m][r] = -INFINITY;
+}
+
+// Online softmax of one score tile in the log2 domain (sc = log2(e)/sqrt(D)), in two parts.
+// softmax_max moves the running max and rescales O and the row sum. The running max only moves
+// when the tile max exceeds it by more than 8 (a factor 256): until then exp2 values stay <= 256,
+// which fp32 sums and bf16 P hold exactly enough, and the rescale (a wave-uniform branch) is
+// skipped.
+template <int D>
+__device__ __forceinline__ void softmax_max(WaveRows<D>& w, const f32x16 (&s)[2], float sc) {
+  // tile max as a shallow tree (independent partial maxima) rather than one long chain
+  float mp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mp[j] = fmaxf(s[0][4 * j], s[0][4 * j + 1]);
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (m > 0 || (r % 4) >= 2) mp[r / 4] = fmaxf(mp[r / 4], s[m][r]);
+  float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+  mx = pair_max(mx) * sc;
+  if (__any(mx > w.m_run + 8.0f)) {
+    const float m_new = fmaxf(w.m_run, mx);
+    const float alpha = fast_exp2(w.m_run - m_new);
+    w.m_run = m_new;
+    w.l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w.o[dt][r] *= alpha;
+  }
+}
+
+// softmax_exp: P^T = exp2(s*sc - m_run) as bf16 (pk, 8 values per 16-key step: step kk covers
+// s[kk/2] regs 8*(kk%2) .. +7), and the tile's row-sum partial of the bf16-rounded P.
+__device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], u32x4 (&pk)[4], float m_run, float sc) {
+  float psum[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial row sums
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(fmaf(s[m][r], sc, -m_run));
+      const float p1 = fast_exp2(fmaf(s[m][r + 1], sc, -m_run));
+      const uint32_t pp = pack_bf16x2(p0, p1);
+      pk[2 * m + r / 8][(r % 8) / 2] = pp;
+      // row sum of the bf16-rounded P that P.V uses: one packed dot product with (1, 1)
+      psum[(r / 2) % 4] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes2, psum[(r / 2) % 4], false);
+    }
+  }
+  return (psum[0] + psum[1]) + (psum[2] + psum[3]);
+}
+
+// O^T += V^T . P^T with V^T read from the row-major V tile at vb through the LDS transpose read;
+// the key order inside each 16-key step matches the registers that hold P^T.
+template <int D>
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const u32x4 (&pk)[4], const unsigned char* vb,
+                                        int lane) {
+  using T = Tile<D, kBN>;
+  const int hi = lane >> 5;
+  const int ig = lane & 15;  // index inside the 16-lane group
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int m = kk >> 1, half = kk & 1;
+    const int k0 = 32 * m + 16 * half + 4 * hi;
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[kk]);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
+      const unsigned char* p1 = vb + (k0 + (ig >> 2)) * T::VS + (d0 + 4 * (ig & 3)) * 2;
+      const i16x4 lo = lds_read_tr16(p1);
+      const i16x4 hi4 = lds_read_tr16(p1 + 8 * T::VS);
+      typedef __attribute__((ext_vector_type(8))) short i16x8;
+      const i16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, vv), pb, o[dt]);
+    }
+  }
+}
+
+// One K/V tile of 64 keys (K rows at kb, V rows at vb in LDS; first key key0) applied to the
+// wave's rows: S^T = K . Q^T, online softmax, O^T += V^T . P^T.
+template <int D, int BN>
+__device__ __forceinline__ void rows_tile(WaveRows<D>& w, const unsigned char* kb, const unsigned char* vb,
+                                          int64_t key0, int64_t N, int lane, float sc) {
+  static_assert(BN == kBN, "64-key tiles");
+  f32x16 s[2];
+  qk_tile<D>(s, w.qf, kb, lane);
+  if (key0 + BN > N) mask_tile(s, key0, N, lane);
+  softmax_max(w, s, sc);
+  u32x4 pk[4];
+  w.l_run += softmax_exp(s, pk, w.m_run, sc);
+  pv_tile<D>(w.o, pk, vb, lane);
+}
+
+// Epilogue: combine the two lane-partial sums, normalise and store query row my_q if it is
+// inside the sequence (out: the output tensor at the (batch, head) base; lse_row: the LSE row of
+// the (batch, head), or null). A row that saw no key (an empty kept set) is written as zeros
+// with LSE -inf.
+template <int D>
+__device__ __forceinline__ void rows_end(const WaveRows<D>& w, uint16_t* out, float* lse_row, int64_t my_q,
+                                         int64_t N, int64_t row_stride, bool empty, int hi) {
   constexpr int DT = D / 32;
-  constexpr int LOADS = T::CHUNKS / NT;  // 16-byte loads per thread per tensor
+  const float l_tot = pair_sum(w.l_run);
+  const float inv = empty ? 0.f : 1.0f / l_tot;
+  if (my_q >= N) return;
+  uint16_t* op = out + my_q * row_stride;
+  float* lse_p = lse_row != nullptr ? lse_row + my_q : nullptr;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * hi;
+      u32x2 v;
+      v[0] = pack_bf16x2(w.o[dt][4 * g + 0] * inv, w.o[dt][4 * g + 1] * inv);
+      v[1] = pack_bf16x2(w.o[dt][4 * g + 2] * inv, w.o[dt][4 * g + 3] * inv);
+      *reinterpret_cast<u32x2*>(op + d) = v;
+    }
+  if (lse_p != nullptr && hi == 0)
+    *lse_p = empty ? -INFINITY : (w.m_run + __log2f(l_tot)) * 0.6931471805599453f;
+}
+
+// Global -> register staging of one K/V tile by NT threads, and register -> LDS store. Each
+// thread's 16-byte chunks sit at fixed offsets from the tile's first row (32-bit: < BN rows x
+// row_stride); rows past the end of the sequence are clamped to the last token, only in the
+// tile that holds it.
+template <int D, int BN, int NT>
+struct TileStage {
+  using T = Tile<D, BN>;
+  static constexpr int LOADS = T::CHUNKS / NT;  // 16-byte loads per thread per tensor
   static_assert(T::CHUNKS % NT == 0, "tile must split evenly");
+  int toff[LOADS], trow[LOADS];
+  u32x4 kst[LOADS], vst[LOADS];
+
+  __device__ __forceinline__ void init(int tid, int64_t row_stride) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int ci = tid + i * NT;
+      trow[i] = ci / (D / 8);
+      toff[i] = trow[i] * (int)row_stride + (ci % (D / 8)) * 8;
+    }
+  }
+  __device__ __forceinline__ void fetch(const uint16_t* k, const uint16_t* v, int64_t base, int64_t key0,
+                                        int64_t N, int64_t row_stride) {
+    const int64_t tile = base + key0 * row_stride;
+    if (key0 + BN <= N) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        kst[i] = *reinterpret_cast<const u32x4*>(k + tile + toff[i]);
+        vst[i] = *reinterpret_cast<const u32x4*>(v + tile + toff[i]);
+      }
+    } else {
+      const int last = (int)(N - 1 - key0);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = trow[i] < last ? trow[i] : last;
+        const int64_t off = tile + toff[i] + (int64_t)(r - trow[i]) * row_stride;
+        kst[i] = *reinterpret_cast<const u32x4*>(k + off);
+        vst[i] = *reinterpret_cast<const u32x4*>(v + off);
+      }
+    }
+  }
+  __device__ __forceinline__ void stash(unsigned char* kb, int tid) const { stash2(kb, kb + T::K_BYTES, tid); }
+  __device__ __forceinline__ void stash2(unsigned char* kb, unsigned char* vb, int tid) const {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int ci = tid + i * NT;
+      const int row = ci / (D / 8);
+      const int col = ci % (D / 8);
+      *reinterpret_cast<u32x4*>(kb + row * T::KS + col * 16) = kst[i];
+      *reinterpret_cast<u32x4*>(vb + row * T::VS + col * 16) = vst[i];
+    }
+  }
+};
+
+// Dense attention. WAVES waves per workgroup (32 queries each); OCC minimum waves per SIMD (2
+// caps the kernel at 256 registers so that two waves share each SIMD and overlap each other's
+// MFMA and softmax work).
+template <int D, int WAVES, int OCC>
+__global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
+  using T = Tile<D, kBN>;
+  constexpr int NT = WAVES * 64;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -89,286 +283,208 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
   const int hi = lane >> 5;
 
   const int64_t N = a.n_tokens;
-  int64_t qtile;
-  int head, b;
-  if constexpr (XCD != 0) {
-    const int64_t n_qt = SPARSE ? a.n_blocks : (N + WAVES * 32 - 1) / (WAVES * 32);
-    const int64_t total = n_qt * a.heads * a.batch;
-    const int64_t item = XCD == 1 ? xcd_contiguous(blockIdx.x, total) : xcd_grouped<XCD>(blockIdx.x, total);
-    qtile = item % n_qt;
-    head = (int)((item / n_qt) % a.heads);
-    b = (int)(item / (n_qt * a.heads));
-  } else {
-    qtile = blockIdx.x;
-    head = blockIdx.y;
-    b = blockIdx.z;
-  }
+  const int64_t qtile = blockIdx.x;
+  const int head = blockIdx.y, b = blockIdx.z;
   const int64_t row_stride = (int64_t)a.heads * D;  // elements between consecutive tokens
   const int64_t base = ((int64_t)b * N) * row_stride + (int64_t)head * D;
 
-  const int64_t qtile0 = qtile * (WAVES * 32);
-  const int64_t q0 = qtile0 + wave * 32;
-  const int64_t my_q = q0 + l32;
+  const int64_t my_q = qtile * (WAVES * 32) + wave * 32 + l32;
   const int64_t my_q_c = my_q < N ? my_q : N - 1;
+  WaveRows<D> w;
+  rows_begin(w, a.q + base + my_q_c * row_stride + 8 * hi);
 
-  // Q^T fragments (B operand), one bf16x8 per 16-wide k step.
-  bf16x8 qf[KSTEPS];
-  {
-    const uint16_t* qp = a.q + base + my_q_c * row_stride + 8 * hi;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
-  }
-
-  int n_tiles;
-  const int32_t* idx_row = nullptr;
-  if constexpr (SPARSE && CSR) {
-    const int64_t r = ((int64_t)b * a.heads + head) * a.n_blocks + qtile;
-    const int64_t p0 = a.row_ptr[r];
-    n_tiles = (int)(a.row_ptr[r + 1] - p0);
-    idx_row = a.block_idx + p0;
-  } else if constexpr (SPARSE) {
-    n_tiles = a.keep;
-    idx_row = a.block_idx + (((int64_t)b * a.heads + head) * a.n_blocks + qtile) * a.keep;
-  } else {
-    n_tiles = (int)((N + BN - 1) / BN);
-  }
-  if (n_tiles <= 0) {  // an empty kept set (CSR rows only): zero output, lse = -inf
-    if (my_q < N) {
-      uint16_t* op = a.out + base + my_q * row_stride;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * g + 4 * hi) = u32x2{0u, 0u};
-      if (a.lse != nullptr && hi == 0) a.lse[((int64_t)b * a.heads + head) * N + my_q] = -INFINITY;
-    }
-    return;
-  }
-  auto tile_key0 = [&](int t) -> int64_t {
-    if constexpr (SPARSE) return (int64_t)idx_row[t] * kBN;
-    else return (int64_t)t * BN;
-  };
-
-  // global -> register staging of one K/V tile. Each thread's chunks sit at fixed offsets from
-  // the tile's first row (32-bit: < 64 rows x row_stride); rows past the end of the sequence are
-  // clamped to the last token, only in the tile that holds it.
-  int toff[LOADS], trow[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int ci = tid + i * NT;
-    trow[i] = ci / (D / 8);
-    toff[i] = trow[i] * (int)row_stride + (ci % (D / 8)) * 8;
-  }
-  u32x4 kst[LOADS], vst[LOADS];
-  auto fetch = [&](int t) {
-    const int64_t key0 = tile_key0(t);
-    const int64_t tile = base + key0 * row_stride;
-    if (key0 + BN <= N) {
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        kst[i] = *reinterpret_cast<const u32x4*>(a.k + tile + toff[i]);
-        vst[i] = *reinterpret_cast<const u32x4*>(a.v + tile + toff[i]);
-      }
-    } else {
-      const int last = (int)(N - 1 - key0);
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int r = trow[i] < last ? trow[i] : last;
-        const int64_t off = tile + toff[i] + (int64_t)(r - trow[i]) * row_stride;
-        kst[i] = *reinterpret_cast<const u32x4*>(a.k + off);
-        vst[i] = *reinterpret_cast<const u32x4*>(a.v + off);
-      }
-    }
-  };
-  auto stash = [&](int buf) {
-    unsigned char* kb = smem + buf * T::BUF_BYTES;
-    unsigned char* vb = kb + T::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int ci = tid + i * NT;
-      const int row = ci / (D / 8);
-      const int col = ci % (D / 8);
-      *reinterpret_cast<u32x4*>(kb + row * T::KS + col * 16) = kst[i];
-      *reinterpret_cast<u32x4*>(vb + row * T::VS + col * 16) = vst[i];
-    }
-  };
-
+  const int n_tiles = (int)((N + kBN - 1) / kBN);
+  TileStage<D, kBN, NT> st;
+  st.init(tid, row_stride);
   const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
-  float m_run = -INFINITY;  // running max of s*sc (log2 units), shared by lanes l and l^32
-  float l_run = 0.f;        // per-lane partial row sum
-  f32x16 o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
 
-  fetch(0);
-  stash(0);
+  st.fetch(a.k, a.v, base, 0, N, row_stride);
+  st.stash(smem, tid);
   __syncthreads();
-
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = DBUF ? (t & 1) : 0;
-    if (t + 1 < n_tiles) fetch(t + 1);
-
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) st.fetch(a.k, a.v, base, (int64_t)(t + 1) * kBN, N, row_stride);
     const unsigned char* kb = smem + buf * T::BUF_BYTES;
-    const unsigned char* vb = kb + T::K_BYTES;
-
-    // S^T = K . Q^T for the 32-key sub-tiles of the tile
-    f32x16 s[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) s[m] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + (32 * m + l32) * T::KS + (16 * ks + 8 * hi) * 2);
-        s[m] = mfma32x32x16(kf, qf[ks], s[m]);
-      }
-    }
-
-    // mask keys past the end of the sequence (only the tile that holds the last token)
-    const int64_t key0 = tile_key0(t);
-    if (key0 + BN > N) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t kidx = key0 + 32 * m + 8 * (r / 4) + 4 * hi + (r % 4);
-          if (kidx >= N) s[m][r] = -INFINITY;
-        }
-    }
-
-    // online softmax (log2 domain). The running max only moves when the tile max exceeds it by
-    // more than 8 (a factor 256): until then exp2 values stay <= 256, which fp32 sums and bf16 P
-    // hold exactly enough, and the O/l rescale (a wave-uniform branch) is skipped.
-    // tile max as a shallow tree (independent partial maxima) rather than one long chain
-    float mp[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mp[j] = fmaxf(s[0][4 * j], s[0][4 * j + 1]);
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (m > 0 || (r % 4) >= 2) mp[r / 4] = fmaxf(mp[r / 4], s[m][r]);
-    float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-    mx = pair_max(mx) * sc;
-    if (__any(mx > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-    float psum[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial row sums
-    u32x4 pk[2 * MT];  // P^T as bf16, 8 values per 16-key step: step kk covers s[kk/2] regs 8*(kk%2) .. +7
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(s[m][r], sc, -m_run));
-        const float p1 = fast_exp2(fmaf(s[m][r + 1], sc, -m_run));
-        const uint32_t pp = pack_bf16x2(p0, p1);
-        pk[2 * m + r / 8][(r % 8) / 2] = pp;
-        // row sum of the bf16-rounded P that P.V uses: one packed dot product with (1, 1)
-        psum[(r / 2) % 4] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes2, psum[(r / 2) % 4], false);
-      }
-    }
-    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
-
-    // O^T += V^T . P^T
-    const int ig = lane & 15;  // index inside the 16-lane group
-#pragma unroll
-    for (int kk = 0; kk < 2 * MT; ++kk) {
-      const int m = kk >> 1, half = kk & 1;
-      const int k0 = 32 * m + 16 * half + 4 * hi;
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[kk]);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
-        const unsigned char* p1 = vb + (k0 + (ig >> 2)) * T::VS + (d0 + 4 * (ig & 3)) * 2;
-        const i16x4 lo = lds_read_tr16(p1);
-        const i16x4 hi4 = lds_read_tr16(p1 + 8 * T::VS);
-        typedef __attribute__((ext_vector_type(8))) short i16x8;
-        const i16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, vv), pb, o[dt]);
-      }
-    }
-
-    if constexpr (DBUF) {
-      if (t + 1 < n_tiles) stash(buf ^ 1);
-      __syncthreads();
-    } else {
-      __syncthreads();  // every wave is done reading the single tile
-      if (t + 1 < n_tiles) {
-        stash(0);
-        __syncthreads();
-      }
-    }
+    rows_tile<D, kBN>(w, kb, kb + T::K_BYTES, (int64_t)t * kBN, N, lane, sc);
+    if (t + 1 < n_tiles) st.stash(smem + (buf ^ 1) * T::BUF_BYTES, tid);
+    __syncthreads();
   }
-
-  // epilogue: combine the two lane-partial sums, normalise, store
-  const float l_tot = pair_sum(l_run);
-  const float inv = 1.0f / l_tot;
-  if (my_q < N) {
-    uint16_t* op = a.out + base + my_q * row_stride;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hi;
-        u32x2 w;
-        w[0] = pack_bf16x2(o[dt][4 * g + 0] * inv, o[dt][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d) = w;
-      }
-    if (a.lse != nullptr && hi == 0)
-      a.lse[((int64_t)b * a.heads + head) * N + my_q] = (m_run + __log2f(l_tot)) * 0.6931471805599453f;
-  }
+  rows_end(w, a.out + base, a.lse != nullptr ? a.lse + ((int64_t)b * a.heads + head) * N : nullptr, my_q, N,
+           row_stride, false, hi);
 }
 
+// Block-sparse attention over groups of G consecutive query blocks per workgroup (2 waves per
+// block, 32 queries each). Neighbouring query blocks keep largely the same key blocks, so the
+// workgroup merges the G kept lists into their union (ascending key-block order, with a bit per
+// query block that keeps it) and loads each union tile into LDS once; a wave runs the tile only
+// when its own block keeps it (a wave-uniform branch), otherwise it just joins the barrier.
+// Each wave therefore sees exactly its block's kept tiles in ascending order, the same
+// arithmetic as the one-block kernel on ascending lists. The union is built in windows of KW
+// key blocks so that LDS use is bounded for any sequence length. Blocks of a group are spread
+// so that the two waves of a SIMD (w and w+4) belong to different blocks.
+template <int D, int G, int KW, bool CSR>
+__global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs a) {
+  using T = Tile<D, kBN>;
+  static_assert(G == 2 || G == 4, "2 or 4 query blocks per workgroup");
+  constexpr int WAVES = 2 * G;
+  constexpr int NT = WAVES * 64;
+  constexpr int PER = KW / NT;  // window slots per thread in the compaction
+  static_assert(KW % NT == 0 && KW <= (1 << 24), "window must split evenly");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint32_t* ulist = reinterpret_cast<uint32_t*>(smem + 2 * T::BUF_BYTES);  // KW words
+  __shared__ int s_wave_tot[WAVES];
+  __shared__ int s_nu;
 
-template <int D, int WAVES, int OCC, bool DBUF, bool SPARSE, int XCD = 0, int BN = 64, bool CSR = false>
-void launch(const AttnArgs& a, hipStream_t stream) {
-  const size_t lds = (DBUF ? 2 : 1) * Tile<D, BN>::BUF_BYTES;
-  auto kern = attn_fwd_kernel<D, WAVES, OCC, DBUF, SPARSE, XCD, BN, CSR>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int64_t N = a.n_tokens;
+  const int64_t nb = a.n_blocks;
+  const int64_t group = blockIdx.x;
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int64_t row_stride = (int64_t)a.heads * D;
+  const int64_t base = ((int64_t)b * N) * row_stride + (int64_t)head * D;
+
+  const int gblk = (wave & 1) + 2 * (wave >> 2);  // this wave's block inside the group
+  const int half = (wave >> 1) & 1;               // and its 32-query half
+  const int64_t qb = group * G + gblk;
+  const int64_t my_q = qb * kBN + half * 32 + l32;
+  const int64_t my_q_c = my_q < N ? my_q : N - 1;
+
+  // the kept list [beg, end) of each block of the group inside block_idx
+  const int64_t row0 = ((int64_t)b * a.heads + head) * nb + group * G;
+  int64_t beg[G], end[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (group * G + g >= nb) {
+      beg[g] = end[g] = 0;
+    } else if constexpr (CSR) {
+      beg[g] = a.row_ptr[row0 + g];
+      end[g] = a.row_ptr[row0 + g + 1];
+    } else {
+      beg[g] = (row0 + g) * a.keep;
+      end[g] = beg[g] + a.keep;
+    }
+  }
+  int64_t my_count = 0;
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    if (g == gblk) my_count = end[g] - beg[g];
+
+  WaveRows<D> w;
+  rows_begin(w, a.q + base + my_q_c * row_stride + 8 * hi);
+  TileStage<D, kBN, NT> st;
+  st.init(tid, row_stride);
+  const float sc = 1.4426950408889634f / sqrtf((float)D);
+  const uint32_t my_bit = 1u << gblk;
+
+  for (int64_t j0 = 0; j0 < nb; j0 += KW) {
+    const int nw = (int)(nb - j0 < KW ? nb - j0 : KW);
+    // membership bits of the window's key blocks
+    for (int i = tid; i < KW; i += NT) ulist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      for (int64_t e = beg[g] + tid; e < end[g]; e += NT) {
+        const int64_t j = a.block_idx[e] - j0;
+        if (j >= 0 && j < nw) atomicOr(&ulist[j], 1u << g);
+      }
+    __syncthreads();
+    // compaction into (slot << 8 | bits), ascending; each thread owns PER consecutive slots
+    uint32_t mk[PER];
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      mk[i] = ulist[tid * PER + i];
+      c += mk[i] != 0u;
+    }
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_wave_tot[wave] = incl;
+    __syncthreads();  // also orders every read of the bit array before the writes below
+    int pre = 0;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) pre += v < wave ? s_wave_tot[v] : 0;
+    int pos = pre + incl - c;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (mk[i] != 0u) ulist[pos++] = ((uint32_t)(tid * PER + i) << 8) | mk[i];
+    if (tid == NT - 1) s_nu = pos;
+    __syncthreads();
+    const int nu = s_nu;
+    if (nu == 0) continue;
+
+    auto key0_of = [&](int t) -> int64_t { return (j0 + (int64_t)(ulist[t] >> 8)) * kBN; };
+    st.fetch(a.k, a.v, base, key0_of(0), N, row_stride);
+    st.stash(smem, tid);
+    __syncthreads();
+    for (int t = 0; t < nu; ++t) {
+      const int buf = t & 1;
+      const uint32_t e = ulist[t];
+      if (t + 1 < nu) st.fetch(a.k, a.v, base, key0_of(t + 1), N, row_stride);
+      if (e & my_bit) {
+        const unsigned char* kb = smem + buf * T::BUF_BYTES;
+        rows_tile<D, kBN>(w, kb, kb + T::K_BYTES, (j0 + (int64_t)(e >> 8)) * kBN, N, lane, sc);
+      }
+      if (t + 1 < nu) st.stash(smem + (buf ^ 1) * T::BUF_BYTES, tid);
+      __syncthreads();
+    }
+  }
+  if (qb < nb)
+    rows_end(w, a.out + base, a.lse != nullptr ? a.lse + ((int64_t)b * a.heads + head) * N : nullptr, my_q, N,
+             row_stride, my_count <= 0, hi);
+}
+
+template <int D, int WAVES, int OCC>
+void launch_dense(const AttnArgs& a, hipStream_t stream) {
+  const size_t lds = 2 * Tile<D, kBN>::BUF_BYTES;
+  auto kern = attn_fwd_kernel<D, WAVES, OCC>;
   static const bool lds_ok = [&] {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
   }();
   (void)lds_ok;
-  dim3 grid;
-  const int64_t n_qt = SPARSE ? a.n_blocks : (a.n_tokens + WAVES * 32 - 1) / (WAVES * 32);
-  if constexpr (XCD != 0) grid = dim3((unsigned)(n_qt * a.heads * a.batch));
-  else grid = dim3((unsigned)n_qt, (unsigned)a.heads, (unsigned)a.batch);
+  const dim3 grid((unsigned)((a.n_tokens + WAVES * 32 - 1) / (WAVES * 32)), (unsigned)a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), lds, stream, a);
+}
+
+template <int D, int G, int KW, bool CSR>
+void launch_group(const AttnArgs& a, hipStream_t stream) {
+  const size_t lds = 2 * Tile<D, kBN>::BUF_BYTES + (size_t)KW * 4;
+  auto kern = attn_sparse_group_kernel<D, G, KW, CSR>;
+  static const bool lds_ok = [&] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
+  }();
+  (void)lds_ok;
+  const dim3 grid((unsigned)((a.n_blocks + G - 1) / G), (unsigned)a.heads, (unsigned)a.batch);
+  hipLaunchKernelGGL(kern, grid, dim3(G * 128), lds, stream, a);
 }
 
 }  // namespace
 
-#ifndef H3ATTN_DENSE_CFG
-#define H3ATTN_DENSE_CFG 8, 2, true
-#endif
-#ifndef H3ATTN_SPARSE_CFG
-#define H3ATTN_SPARSE_CFG 2, 2, false
-#endif
-#ifndef H3ATTN_SPARSE_XCD
-#define H3ATTN_SPARSE_XCD 128
-#endif
-
+// 8 waves (256 queries) per workgroup, two waves per SIMD
 void launch_dense_fwd(const AttnArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) launch<128, H3ATTN_DENSE_CFG, false>(a, stream);
-  else launch<64, H3ATTN_DENSE_CFG, false>(a, stream);
+  if (a.head_dim == 128) launch_dense<128, 8, 2>(a, stream);
+  else launch_dense<64, 8, 2>(a, stream);
 }
 
+// 4 query blocks per workgroup; union windows of 4096 key blocks (16 KB of LDS)
 void launch_block_sparse_fwd(const AttnArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) launch<128, H3ATTN_SPARSE_CFG, true, H3ATTN_SPARSE_XCD>(a, stream);
-  else launch<64, H3ATTN_SPARSE_CFG, true, H3ATTN_SPARSE_XCD>(a, stream);
+  if (a.head_dim == 128) launch_group<128, 4, 4096, false>(a, stream);
+  else launch_group<64, 4, 4096, false>(a, stream);
 }
 
 void launch_block_sparse_csr_fwd(const AttnArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) launch<128, H3ATTN_SPARSE_CFG, true, H3ATTN_SPARSE_XCD, 64, true>(a, stream);
-  else launch<64, H3ATTN_SPARSE_CFG, true, H3ATTN_SPARSE_XCD, 64, true>(a, stream);
+  if (a.head_dim == 128) launch_group<128, 4, 4096, true>(a, stream);
+  else launch_group<64, 4, 4096, true>(a, stream);
 }
 
 }  // namespace h3attn
