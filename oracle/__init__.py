@@ -6,4 +6,6 @@ from .attention_oracle import (attention, attention_head, block_means, block_sco
                                token_positions, topk_blocks, threshold_blocks,
                                subblock_select_threshold, near_threshold_entries,
                                sparse_attention_csr, adaln_modulate, swiglu, residual_change,
-                               CacheGate)
+                               CacheGate, E4M3_MAX, e4m3_values, e4m3_round, pow2_scale,
+                               quantize_blocks, quantize_channels, attention_fp8,
+                               sparse_attention_fp8, attention_fp8_rows)

@@ -362,3 +362,156 @@ class CacheGate:
         self.consecutive = self.consecutive + 1 if reuse else 0
         self.steps += 1
         return reuse
+
+
+# --------------------------------------------------------------------------------------------
+# (7) FP8 (e4m3) attention
+#     ["智東西…H3 Lightning" (hao.cnyes.com), section "02. 從50步壓到9步三層最佳化實現12倍提速":
+#     SageAttention2 speeds up the attention computation; "VDN-MiniMax-H3：基于MiniMax H3的视频
+#     生成加速开源项目" (aipuzi.cn), sections "二、功能特色" and "三、技术细节": FP8 quantized
+#     inference]. The pages give no quantization rule; the readings taken are stated below.
+# --------------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_values() -> np.ndarray:
+    """The 256 values of the OCP fp8 e4m3 format (1 sign, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent field 0 holds subnormals m/8 * 2^-6; the all-ones exponent with
+    mantissa 7 is NaN and there is no infinity), indexed by the byte code."""
+    out = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            out[code] = np.nan
+        elif e == 0:
+            out[code] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            out[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest e4m3 value, ties to the even mantissa. Magnitudes that round above
+    448 (from 464 exclusive) have no e4m3 value and become NaN (no saturation)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    out = np.empty_like(a)
+    normal = a >= 2.0 ** -6
+    # normal range: a = f * 2^e with f in [1, 2); mantissa steps of 2^(e-3)
+    e = np.floor(np.log2(np.where(normal, a, 1.0)))
+    # guard log2 rounding at exact powers of two
+    e = np.where(np.where(normal, a, 1.0) < 2.0 ** e, e - 1, e)
+    e = np.where(np.where(normal, a, 1.0) >= 2.0 ** (e + 1), e + 1, e)
+    step = 2.0 ** (e - 3)
+    out[normal] = (np.rint(a / step) * step)[normal]          # np.rint: ties to even
+    sub = ~normal
+    out[sub] = np.rint(a[sub] / 2.0 ** -9) * 2.0 ** -9        # subnormal grid 2^-9 (2^-6 exact)
+    out = np.where(out > E4M3_MAX, np.nan, out)
+    return np.copysign(out, x)
+
+
+def pow2_scale(amax: np.ndarray) -> np.ndarray:
+    """Smallest power of two s with amax <= 448 * s (1 where amax is 0). Reading: power-of-two
+    scales keep the scaling exact, so a quantised value is the e4m3 rounding of x / s."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, ex = np.frexp(np.where(amax > 0, amax, 1.0))           # amax = m * 2^ex, m in [0.5, 1)
+    e = ex - 9 + (m > 0.875)                                   # 448 = 0.875 * 2^9
+    return np.where(amax > 0, np.ldexp(1.0, e), 1.0)
+
+
+def quantize_blocks(x: np.ndarray, block_size: int = 64):
+    """Per (batch, head, 64-token block) e4m3 quantisation of q or k [B, N, Hd, D]: returns the
+    e4m3 values x8 (same shape, x ~ x8 * s) and the scales s [B, Hd, nB] (reading: one scale per
+    block, the granularity SubBlock works at)."""
+    x = np.asarray(x, dtype=np.float64)
+    b_len, n, h_len, d = x.shape
+    nb = n_blocks_of(n, block_size)
+    scales = np.empty((b_len, h_len, nb))
+    x8 = np.empty_like(x)
+    for i in range(nb):
+        sl = slice(i * block_size, min((i + 1) * block_size, n))
+        amax = np.abs(x[:, sl]).max(axis=(1, 3))                # [B, Hd]
+        s = pow2_scale(amax)
+        scales[:, :, i] = s
+        x8[:, sl] = e4m3_round(x[:, sl] / s[:, None, :, None])
+    return x8, scales
+
+
+def quantize_channels(v: np.ndarray):
+    """Per (batch, head, channel) e4m3 quantisation of v [B, N, Hd, D] over all tokens: returns
+    v8 (v ~ v8 * s) and s [B, Hd, D] (reading: the P.V product then rescales each output channel
+    once)."""
+    v = np.asarray(v, dtype=np.float64)
+    s = pow2_scale(np.abs(v).max(axis=1))                       # [B, Hd, D]
+    return e4m3_round(v / s[:, None]), s
+
+
+def _fp8_rows(q8, sq, k8, sk, v8, sv, qrows, keys, block_size):
+    """Quantised attention of query rows qrows over key ids keys for one (batch, head):
+    x = (q8 . k8) * s_q * s_k * log2(e) / sqrt(D); m = ceil(max x) per row;
+    P = e4m3(2^(8 + x - m)); O = (P @ v8) * s_v / sum(P); LSE = ln2 * (m - 8 + log2 sum(P))."""
+    d = q8.shape[-1]
+    s = (q8[qrows] @ k8[keys].T) * sq[qrows // block_size][:, None] * sk[keys // block_size][None, :]
+    x = s * (math.log2(math.e) / math.sqrt(d))
+    m = np.ceil(x.max(axis=1, keepdims=True))
+    p = e4m3_round(np.exp2(8.0 + x - m))
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ v8[keys]) * sv[None, :] / l
+    lse = math.log(2.0) * (m[:, 0] - 8.0 + np.log2(l[:, 0]))
+    return o, lse
+
+
+def attention_fp8(q, k, v, block_size: int = 64):
+    """Dense attention on e4m3-quantised q, k (per 64-token block), v (per channel), with the
+    probabilities quantised to e4m3 as 2^(8 + x - m), m the row max rounded up to an integer
+    (reading: the probabilities then fill the e4m3 range [2^-9, 256], and a running max that
+    only takes integer values moves them by exact powers of two). Returns (O, lse)."""
+    q8, sq = quantize_blocks(q, block_size)
+    k8, sk = quantize_blocks(k, block_size)
+    v8, sv = quantize_channels(v)
+    b_len, n, h_len, d = q8.shape
+    out = np.empty((b_len, n, h_len, v8.shape[-1]))
+    lse = np.empty((b_len, h_len, n))
+    allk = np.arange(n)
+    for b in range(b_len):
+        for h in range(h_len):
+            for r0 in range(0, n, 256):
+                rows = np.arange(r0, min(r0 + 256, n))
+                out[b, rows, h], lse[b, h, rows] = _fp8_rows(q8[b, :, h], sq[b, h], k8[b, :, h], sk[b, h],
+                                                           v8[b, :, h], sv[b, h], rows, allk, block_size)
+    return out, lse
+
+
+def sparse_attention_fp8(q, k, v, block_idx, block_size: int = 64):
+    """Block-sparse attention on the same quantised tensors: query block i attends to the key
+    blocks block_idx[b, h, i, :] only (row max over those keys)."""
+    q8, sq = quantize_blocks(q, block_size)
+    k8, sk = quantize_blocks(k, block_size)
+    v8, sv = quantize_channels(v)
+    b_len, n, h_len, d = q8.shape
+    nb = n_blocks_of(n, block_size)
+    out = np.empty((b_len, n, h_len, v8.shape[-1]))
+    lse = np.empty((b_len, h_len, n))
+    for b in range(b_len):
+        for h in range(h_len):
+            for i in range(nb):
+                rows = np.arange(i * block_size, min((i + 1) * block_size, n))
+                keys = block_token_ids(block_idx[b, h, i], block_size, n)
+                out[b, rows, h], lse[b, h, rows] = _fp8_rows(q8[b, :, h], sq[b, h], k8[b, :, h], sk[b, h],
+                                                           v8[b, :, h], sv[b, h], rows, keys, block_size)
+    return out, lse
+
+
+def attention_fp8_rows(q, k, v, b: int, h: int, qblock: int, block_idx=None, block_size: int = 64):
+    """One query block of attention_fp8 (block_idx None) or sparse_attention_fp8, for sampled
+    comparisons on long sequences (the quantisation is the same as on the full tensors)."""
+    q8, sq = quantize_blocks(q[b:b + 1, :, h:h + 1], block_size)
+    k8, sk = quantize_blocks(k[b:b + 1, :, h:h + 1], block_size)
+    v8, sv = quantize_channels(v[b:b + 1, :, h:h + 1])
+    n = q8.shape[1]
+    rows = np.arange(qblock * block_size, min((qblock + 1) * block_size, n))
+    keys = np.arange(n) if block_idx is None else block_token_ids(block_idx, block_size, n)
+    return _fp8_rows(q8[0, :, 0], sq[0, 0], k8[0, :, 0], sk[0, 0], v8[0, :, 0], sv[0, 0], rows, keys, block_size)

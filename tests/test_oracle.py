@@ -513,3 +513,145 @@ def test_cache_gate_rule():
     assert not any(g.decide(0.0) for _ in range(4))
     with pytest.raises(ValueError):
         O.CacheGate(-1.0, 1)
+
+
+# ----------------------------------------------------------------------------------- FP8 (e4m3)
+
+def _nearest_e4m3_by_search(x: float) -> float:
+    """Independent rounding: the nearest finite e4m3 value by exhaustive search over the code
+    table, ties to the even code (even mantissa), NaN above the largest value's rounding range."""
+    vals = O.e4m3_values()
+    codes = [c for c in range(256) if np.isfinite(vals[c]) and not (vals[c] == 0 and c == 0x80)]
+    best, best_d, best_c = None, None, None
+    for c in codes:
+        dist = abs(vals[c] - x)
+        if best_d is None or dist < best_d or (dist == best_d and (c & 1) == 0 and (best_c & 1) == 1):
+            best, best_d, best_c = vals[c], dist, c
+    if abs(x) > 464.0:            # nearer to the missing 480 than to 448: no e4m3 value
+        return float("nan")
+    return math.copysign(abs(best), x) if best == 0 else best
+
+
+def test_e4m3_table_from_the_format_definition():
+    t = O.e4m3_values()
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and np.isfinite(t).sum() == 254
+    # hand-decoded codes: sign | eeee | mmm with bias 7, subnormals m/8 * 2^-6
+    hand = {0x00: 0.0, 0x38: 1.0, 0x30: 0.5, 0x3A: 1.25, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x07: 7 / 8 * 2.0 ** -6,
+            0x08: 2.0 ** -6, 0xB8: -1.0, 0x44: 3.0, 0x79: 288.0, 0x1D: 0.1015625, 0xFE: -448.0}
+    for c, v in hand.items():
+        assert t[c] == v, hex(c)
+    pos = np.sort(t[(t > 0) & np.isfinite(t)])
+    assert len(pos) == 126 and pos[0] == 2.0 ** -9 and pos[-1] == O.E4M3_MAX
+
+
+def test_e4m3_round_against_table_search_and_torch():
+    t = O.e4m3_values()
+    fin = t[np.isfinite(t)]
+    np.testing.assert_array_equal(O.e4m3_round(fin), fin)              # every value is a fixed point
+    pos = np.sort(np.unique(fin[fin >= 0]))
+    mids = (pos[:-1] + pos[1:]) / 2                                     # exact ties
+    probes = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9), [464.0, 465.0, 479.0, 480.0]])
+    probes = np.concatenate([probes, -probes])
+    got = O.e4m3_round(probes)
+    want = np.array([_nearest_e4m3_by_search(float(x)) for x in probes])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    np.testing.assert_array_equal(got[ok], want[ok])
+    # library routine: torch's float8_e4m3fn cast (round to nearest even) inside the finite range
+    x = RNG.uniform(-448, 448, 20000) * np.exp2(RNG.integers(-14, 1, 20000))
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.e4m3_round(x.astype(np.float32).astype(np.float64)), ref)
+
+
+def test_pow2_scale_is_the_smallest_fitting_power_of_two():
+    amax = np.concatenate([[0.0, 448.0, 449.0, 1.0, 224.0, 896.0, 897.0], RNG.uniform(1e-6, 1e6, 500)])
+    s = O.pow2_scale(amax)
+    for a, sc in zip(amax, s):
+        if a == 0:
+            assert sc == 1.0
+            continue
+        e = math.log2(sc)
+        assert e == int(e), "power of two"
+        assert a <= 448.0 * sc and a > 448.0 * sc / 2, (a, sc)        # fits, and half would not
+
+
+def test_quantize_blocks_and_channels_error_bounds_and_scale_invariance():
+    x = rnd(2, 200, 3, 16, scale=3.0)
+    x8, s = O.quantize_blocks(x, 64)
+    assert s.shape == (2, 3, 4)
+    sfull = np.repeat(s.transpose(0, 2, 1), 64, axis=1)[:, :200][:, :, :, None]     # [B, N, Hd, 1]
+    y = x / sfull
+    assert np.abs(y).max() <= 448.0
+    err = np.abs(x8 - y)
+    assert (err <= np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) + 1e-300).all()    # half an ulp
+    assert np.isin(x8, O.e4m3_values()).all()
+    x8b, sb = O.quantize_blocks(x * 2.0 ** 5, 64)                                    # exact rescaling
+    np.testing.assert_array_equal(x8b, x8)
+    np.testing.assert_array_equal(sb, s * 2.0 ** 5)
+    v = rnd(1, 150, 2, 8)
+    v8, sv = O.quantize_channels(v)
+    assert sv.shape == (1, 2, 8)
+    assert np.abs(v8 - v / sv[:, None]).max() <= 448 * 2.0 ** -4
+
+
+def _fp8_brute(q, k, v):
+    """The definition with explicit loops over rows and keys, rounding by table search."""
+    q8, sq = O.quantize_blocks(q, 64)
+    k8, sk = O.quantize_blocks(k, 64)
+    v8, sv = O.quantize_channels(v)
+    n, d = q.shape[1], q.shape[3]
+    out = np.zeros((n, v.shape[3]))
+    lse = np.zeros(n)
+    for i in range(n):
+        xs = []
+        for j in range(n):
+            dot = sum(q8[0, i, 0, c] * k8[0, j, 0, c] for c in range(d))
+            xs.append(dot * sq[0, 0, i // 64] * sk[0, 0, j // 64] * math.log2(math.e) / math.sqrt(d))
+        m = math.ceil(max(xs))
+        ps = [_nearest_e4m3_by_search(2.0 ** (8.0 + xv - m)) for xv in xs]
+        l = sum(ps)
+        for c in range(v.shape[3]):
+            out[i, c] = sum(ps[j] * v8[0, j, 0, c] for j in range(n)) * sv[0, 0, c] / l
+        lse[i] = math.log(2.0) * (m - 8 + math.log2(l))
+    return out, lse
+
+
+def test_attention_fp8_brute_force_and_closed_forms():
+    q, k, v = rnd(1, 70, 1, 8), rnd(1, 70, 1, 8), rnd(1, 70, 1, 4)
+    o, lse = O.attention_fp8(q, k, v)
+    bo, bl = _fp8_brute(q, k, v)
+    np.testing.assert_allclose(o[0, :, 0], bo, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], bl, rtol=1e-12, atol=1e-12)
+    # constant value rows (representable after scaling): output equals that value exactly
+    vc = np.broadcast_to(np.array([0.75, -1.5, 3.0, 0.0]), (1, 70, 1, 4)).copy()
+    oc, _ = O.attention_fp8(q, k, vc)
+    np.testing.assert_allclose(oc[0, :, 0], np.broadcast_to(vc[0, 0, 0], (70, 4)), rtol=1e-15)
+    # identical keys: equal weights, the output is the mean of the quantised values
+    kc = np.broadcast_to(k[:, :1], k.shape).copy()
+    oi, li = O.attention_fp8(q, kc, v)
+    v8, sv = O.quantize_channels(v)
+    np.testing.assert_allclose(oi[0, :, 0], np.broadcast_to((v8[0, :, 0] * sv[0, 0]).mean(0), (70, 4)), rtol=1e-12)
+    # the quantised path stays close to exact attention on these inputs
+    ex, _ = O.attention(q, k, v)
+    assert np.abs(o - ex).max() < 0.15
+
+
+def test_sparse_attention_fp8_special_cases():
+    q, k, v = rnd(1, 192, 2, 16), rnd(1, 192, 2, 16), rnd(1, 192, 2, 8)
+    idx_all = np.broadcast_to(np.arange(3), (1, 2, 3, 3)).copy()
+    so, sl = O.sparse_attention_fp8(q, k, v, idx_all)
+    do, dl = O.attention_fp8(q, k, v)
+    np.testing.assert_allclose(so, do, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(sl, dl, rtol=1e-12, atol=1e-13)
+    # one kept block == dense fp8 attention of that query block over that key block's tokens,
+    # with the quantisation (scales) of the full tensors
+    idx1 = np.full((1, 2, 3, 1), 2)
+    o1, _ = O.sparse_attention_fp8(q, k, v, idx1)
+    q8, sq = O.quantize_blocks(q); k8, sk = O.quantize_blocks(k); v8, sv = O.quantize_channels(v)
+    x = (q8[0, 64:128, 1] @ k8[0, 128:192, 1].T) * sq[0, 1, 1] * sk[0, 1, 2] * math.log2(math.e) / 4.0
+    p = O.e4m3_round(np.exp2(8 + x - np.ceil(x.max(1, keepdims=True))))
+    ref = (p @ v8[0, 128:192, 1]) * sv[0, 1] / p.sum(1, keepdims=True)
+    np.testing.assert_allclose(o1[0, 64:128, 1], ref, rtol=1e-12)
+    # sampled-row helper agrees with the full computation
+    r, rl = O.attention_fp8_rows(q, k, v, 0, 1, 2, block_idx=idx_all[0, 1, 2])
+    np.testing.assert_allclose(r, do[0, 128:192, 1], rtol=1e-12, atol=1e-13)
