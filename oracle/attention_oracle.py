@@ -413,12 +413,17 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
     return np.copysign(out, x)
 
 
+POW2_SCALE_MIN_EXP = -60
+
+
 def pow2_scale(amax: np.ndarray) -> np.ndarray:
-    """Smallest power of two s with amax <= 448 * s (1 where amax is 0). Reading: power-of-two
-    scales keep the scaling exact, so a quantised value is the e4m3 rounding of x / s."""
+    """Smallest power of two s with amax <= 448 * s (1 where amax is 0), but not below 2^-60.
+    Reading: power-of-two scales keep the scaling exact, so a quantised value is the e4m3
+    rounding of x / s; the floor keeps the product of two scales a normal float32 (it only
+    matters for blocks whose largest magnitude is below 448 * 2^-60)."""
     amax = np.asarray(amax, dtype=np.float64)
     m, ex = np.frexp(np.where(amax > 0, amax, 1.0))           # amax = m * 2^ex, m in [0.5, 1)
-    e = ex - 9 + (m > 0.875)                                   # 448 = 0.875 * 2^9
+    e = np.maximum(ex - 9 + (m > 0.875), POW2_SCALE_MIN_EXP)   # 448 = 0.875 * 2^9
     return np.where(amax > 0, np.ldexp(1.0, e), 1.0)
 
 

@@ -566,6 +566,9 @@ def test_e4m3_round_against_table_search_and_torch():
 def test_pow2_scale_is_the_smallest_fitting_power_of_two():
     amax = np.concatenate([[0.0, 448.0, 449.0, 1.0, 224.0, 896.0, 897.0], RNG.uniform(1e-6, 1e6, 500)])
     s = O.pow2_scale(amax)
+    # the floor: tiny maxima get 2^-60, which still fits them
+    np.testing.assert_array_equal(O.pow2_scale(np.array([1e-30, 448 * 2.0 ** -60, 449 * 2.0 ** -60])),
+                                  [2.0 ** -60, 2.0 ** -60, 2.0 ** -59])
     for a, sc in zip(amax, s):
         if a == 0:
             assert sc == 1.0
