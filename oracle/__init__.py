@@ -8,4 +8,5 @@ from .attention_oracle import (attention, attention_head, block_means, block_sco
                                sparse_attention_csr, adaln_modulate, swiglu, residual_change,
                                CacheGate, E4M3_MAX, e4m3_values, e4m3_round, pow2_scale,
                                quantize_blocks, quantize_channels, attention_fp8,
-                               sparse_attention_fp8, attention_fp8_rows)
+                               sparse_attention_fp8, attention_fp8_rows,
+                               attention_fp8_detail)

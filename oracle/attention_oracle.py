@@ -454,10 +454,13 @@ def quantize_channels(v: np.ndarray):
     return e4m3_round(v / s[:, None]), s
 
 
-def _fp8_rows(q8, sq, k8, sk, v8, sv, qrows, keys, block_size):
+def _fp8_rows(q8, sq, k8, sk, v8, sv, qrows, keys, block_size, detail=False):
     """Quantised attention of query rows qrows over key ids keys for one (batch, head):
     x = (q8 . k8) * s_q * s_k * log2(e) / sqrt(D); m = ceil(max x) per row;
-    P = e4m3(2^(8 + x - m)); O = (P @ v8) * s_v / sum(P); LSE = ln2 * (m - 8 + log2 sum(P))."""
+    P = e4m3(2^(8 + x - m)); O = (P @ v8) * s_v / sum(P); LSE = ln2 * (m - 8 + log2 sum(P)).
+    With detail, also the two quantities that bound the effect of one probability taking the
+    neighbouring e4m3 code: the row's largest weight max P / sum(P), and per channel the largest
+    distance max_j |v_j - O| of a value from the output."""
     d = q8.shape[-1]
     s = (q8[qrows] @ k8[keys].T) * sq[qrows // block_size][:, None] * sk[keys // block_size][None, :]
     x = s * (math.log2(math.e) / math.sqrt(d))
@@ -466,7 +469,11 @@ def _fp8_rows(q8, sq, k8, sk, v8, sv, qrows, keys, block_size):
     l = p.sum(axis=1, keepdims=True)
     o = (p @ v8[keys]) * sv[None, :] / l
     lse = math.log(2.0) * (m[:, 0] - 8.0 + np.log2(l[:, 0]))
-    return o, lse
+    if not detail:
+        return o, lse
+    vals = v8[keys] * sv[None, :]                                       # [keys, D]
+    dev = np.maximum(np.abs(vals.max(axis=0)[None, :] - o), np.abs(vals.min(axis=0)[None, :] - o))
+    return o, lse, p.max(axis=1) / l[:, 0], dev
 
 
 def attention_fp8(q, k, v, block_size: int = 64):
@@ -510,7 +517,8 @@ def sparse_attention_fp8(q, k, v, block_idx, block_size: int = 64):
     return out, lse
 
 
-def attention_fp8_rows(q, k, v, b: int, h: int, qblock: int, block_idx=None, block_size: int = 64):
+def attention_fp8_rows(q, k, v, b: int, h: int, qblock: int, block_idx=None, block_size: int = 64,
+                       detail: bool = False):
     """One query block of attention_fp8 (block_idx None) or sparse_attention_fp8, for sampled
     comparisons on long sequences (the quantisation is the same as on the full tensors)."""
     q8, sq = quantize_blocks(q[b:b + 1, :, h:h + 1], block_size)
@@ -519,4 +527,28 @@ def attention_fp8_rows(q, k, v, b: int, h: int, qblock: int, block_idx=None, blo
     n = q8.shape[1]
     rows = np.arange(qblock * block_size, min((qblock + 1) * block_size, n))
     keys = np.arange(n) if block_idx is None else block_token_ids(block_idx, block_size, n)
-    return _fp8_rows(q8[0, :, 0], sq[0, 0], k8[0, :, 0], sk[0, 0], v8[0, :, 0], sv[0, 0], rows, keys, block_size)
+    return _fp8_rows(q8[0, :, 0], sq[0, 0], k8[0, :, 0], sk[0, 0], v8[0, :, 0], sv[0, 0], rows, keys, block_size,
+                     detail)
+
+
+def attention_fp8_detail(q, k, v, block_idx=None, block_size: int = 64):
+    """attention_fp8 (block_idx None) or sparse_attention_fp8 with the per-row bound quantities
+    of _fp8_rows: returns (O, lse, wmax [B, Hd, N], dev [B, N, Hd, D])."""
+    q8, sq = quantize_blocks(q, block_size)
+    k8, sk = quantize_blocks(k, block_size)
+    v8, sv = quantize_channels(v)
+    b_len, n, h_len, d = q8.shape
+    nb = n_blocks_of(n, block_size)
+    out = np.empty((b_len, n, h_len, v8.shape[-1]))
+    dev = np.empty_like(out)
+    lse = np.empty((b_len, h_len, n))
+    wmax = np.empty((b_len, h_len, n))
+    for b in range(b_len):
+        for h in range(h_len):
+            for i in range(nb):
+                rows = np.arange(i * block_size, min((i + 1) * block_size, n))
+                keys = np.arange(n) if block_idx is None else block_token_ids(block_idx[b, h, i], block_size, n)
+                o, l_, w, dv = _fp8_rows(q8[b, :, h], sq[b, h], k8[b, :, h], sk[b, h], v8[b, :, h], sv[b, h],
+                                         rows, keys, block_size, detail=True)
+                out[b, rows, h], lse[b, h, rows], wmax[b, h, rows], dev[b, rows, h] = o, l_, w, dv
+    return out, lse, wmax, dev

@@ -658,3 +658,19 @@ def test_sparse_attention_fp8_special_cases():
     # sampled-row helper agrees with the full computation
     r, rl = O.attention_fp8_rows(q, k, v, 0, 1, 2, block_idx=idx_all[0, 1, 2])
     np.testing.assert_allclose(r, do[0, 128:192, 1], rtol=1e-12, atol=1e-13)
+    # detail: same outputs; one probability moved to a neighbouring e4m3 code (relative change at
+    # most 2^-3 of its value) moves the output by no more than 2^-3 * wmax * dev
+    od, ld, wmax, dev = O.attention_fp8_detail(q, k, v)
+    np.testing.assert_array_equal(od, do)
+    np.testing.assert_array_equal(ld, dl)
+    q8, sq = O.quantize_blocks(q); k8, sk = O.quantize_blocks(k); v8, sv = O.quantize_channels(v)
+    x = (q8[0, :, 0] @ k8[0, :, 0].T) * np.repeat(sq[0, 0], 64)[:, None] * np.repeat(sk[0, 0], 64)[None, :] \
+        * math.log2(math.e) / 4.0
+    p = O.e4m3_round(np.exp2(8 + x - np.ceil(x.max(1, keepdims=True))))
+    vals = v8[0, :, 0] * sv[0, 0]
+    for row in (0, 77, 191):
+        j = int(np.argmax(p[row]))
+        for factor in (1 - 2.0 ** -4, 1 + 2.0 ** -3):                 # the neighbouring codes of a value
+            p2 = p[row].copy(); p2[j] *= factor
+            o2 = p2 @ vals / p2.sum()
+            assert (np.abs(o2 - od[0, row, 0]) <= 2.0 ** -3 * wmax[0, 0, row] * dev[0, row, 0] + 1e-12).all()
