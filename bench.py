@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attn TFLOP/s (% MFMA peak) dense+SubBlock 0.75; QK-norm+RoPE HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 
 
 def log(msg):
@@ -305,6 +306,43 @@ def main():
             f"{components['threshold_mode']['select_ms']:.2f} ms, csr sparse {components['threshold_mode']['csr_sparse_ms']:.2f} ms "
             f"({components['threshold_mode']['csr_sparse_tflops_kept']:.0f} TFLOP/s)")
         del tws, out_c
+
+    if not args.no_extra:
+        # fp8 (e4m3) path on the same inputs and kept sets: quantisation (an HBM stream; 3 bytes
+        # per element of each of q, k, v: bf16 read, e4m3 written) and dense / block-sparse
+        # attention on the quantised tensors, against the fp8 dense MFMA peak
+        fws = torch.empty((h3.fp8_workspace_bytes(b, hd, n, d),), dtype=torch.uint8, device=dev)
+        fq = h3.fp8_quantize(qo, ko, v, workspace=fws)
+        out_f = torch.empty_like(q)
+        h3.fp8_dense_fwd(fq, out=out_f)
+        h3.fp8_block_sparse_fwd(fq, idx, out=out_f)
+        torch.cuda.synchronize()
+        tq, tdn, tsp = [], [], []
+        for r in range(3):
+            ev4 = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev4[0].record()
+            h3.fp8_quantize(qo, ko, v, workspace=fws, out=fq)
+            ev4[1].record()
+            h3.fp8_dense_fwd(fq, out=out_f)
+            ev4[2].record()
+            h3.fp8_block_sparse_fwd(fq, idx, out=out_f)
+            ev4[3].record()
+            torch.cuda.synchronize()
+            tq.append(elapsed_ms(ev4[0], ev4[1]))
+            tdn.append(elapsed_ms(ev4[1], ev4[2]))
+            tsp.append(elapsed_ms(ev4[2], ev4[3]))
+        mq, md, msp = (float(np.median(t)) for t in (tq, tdn, tsp))
+        qbytes = 9.0 * q.numel()
+        components["fp8"] = {
+            "quantize_ms": mq, "quantize_gbs": qbytes / (mq * 1e-3) / 1e9,
+            "dense_ms": md, "dense_tflops": dense_flops / (md * 1e-3) / 1e12,
+            "dense_frac_fp8_peak": dense_flops / (md * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+            "sparse_ms": msp, "sparse_tflops_kept": sparse_flops / (msp * 1e-3) / 1e12,
+            "sparse_frac_fp8_peak": sparse_flops / (msp * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+        log(f"fp8: quantize {mq:.2f} ms ({components['fp8']['quantize_gbs']:.0f} GB/s), dense {md:.1f} ms "
+            f"({components['fp8']['dense_tflops']:.0f} TFLOP/s), sparse {msp:.1f} ms "
+            f"({components['fp8']['sparse_tflops_kept']:.0f} TFLOP/s kept)")
+        del fws, fq, out_f
 
     roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,8,2> (dense)",
                 "achieved": dense_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -227,6 +227,56 @@ h3attn_status h3attn_cache_gate_init(h3attn_cache_gate* gate, double threshold, 
  * run of reused steps. */
 int32_t h3attn_cache_gate_decide(h3attn_cache_gate* gate, double rel_change);
 
+/* ---- FP8 (OCP e4m3) attention ----
+ * "智東西…H3 Lightning" (hao.cnyes.com), section "02. 從50步壓到9步三層最佳化實現12倍提速":
+ * SageAttention2 speeds up the attention computation; "VDN-MiniMax-H3：基于MiniMax H3的视频生成
+ * 加速开源项目" (aipuzi.cn), sections "二、功能特色" / "三、技术细节": FP8 quantised inference. The
+ * pages give no quantisation rule; this one uses power-of-two scales (so scaling is exact):
+ *   q, k: per (batch, head, 64-token block), the smallest power of two s >= 2^-60 with
+ *         max|x| <= 448 s; codes are the round-to-nearest-even e4m3 values of x / s;
+ *   v:    per (batch, head, channel) over all tokens, the same rule;
+ *   attention: x = (q8 . k8) * s_q * s_k * log2(e) / sqrt(D); m = the row max of x rounded up
+ *   to an integer; P = e4m3(2^(8 + x - m)); O = (P . v8) * s_v / sum(P) (bf16 output);
+ *   lse = ln(2) * (m - 8 + log2 sum(P)).
+ * Inputs whose magnitudes exceed 448 * 2^60 are not supported (their codes are NaN).
+ *
+ * Quantised layouts (all bytes are e4m3 codes; every pointer 16-byte aligned):
+ *   q8, k8   [batch, n_tokens, heads, head_dim]
+ *   v8t      [batch, heads, head_dim, nB * 64]: v transposed; within each 64-key block, key
+ *            kappa = 32a + 8b + 4c + d (a, c in {0,1}; b, d in 0..3) is stored at byte
+ *            32c + 16a + 4b + d (the order the P.V product reads it); keys >= n_tokens are 0
+ *   q_scale, k_scale float32 [batch, heads, nB]; v_scale float32 [batch, heads, head_dim]. */
+
+/* Workspace bytes for h3attn_fp8_quantize (channel maxima of v per 1024-token chunk and the
+ * channel scale exponents). 0 on invalid sizes. */
+size_t h3attn_fp8_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                  int32_t block_size);
+
+/* Quantises bf16 q, k, v [batch, n_tokens, heads, head_dim] into the layouts above (four
+ * kernels on `stream`). Errors: null or misaligned pointers, bad sizes, block_size != 64,
+ * workspace smaller than h3attn_fp8_workspace_bytes -> INVALID_ARGUMENT / UNSUPPORTED. */
+h3attn_status h3attn_fp8_quantize(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                  uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                                  float* q_scale, float* k_scale, float* v_scale,
+                                  int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                  int32_t block_size, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Dense attention on the quantised tensors (rule above). out: bf16 [batch, n_tokens, heads,
+ * head_dim]; lse: nullable float32 [batch, heads, n_tokens]. Errors as h3attn_dense_fwd. */
+h3attn_status h3attn_fp8_dense_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
+                                   const float* q_scale, const float* k_scale, const float* v_scale,
+                                   h3attn_bf16* out, float* lse, int32_t batch, int32_t heads, int64_t n_tokens,
+                                   int32_t head_dim, int32_t block_size, hipStream_t stream);
+
+/* Block-sparse attention on the quantised tensors: query block i attends to the key blocks
+ * block_idx[b, head, i, 0..keep-1] only (same index rules as h3attn_block_sparse_fwd; the row
+ * max is taken over the kept keys). */
+h3attn_status h3attn_fp8_block_sparse_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
+                                          const float* q_scale, const float* k_scale, const float* v_scale,
+                                          const int32_t* block_idx, int32_t keep, h3attn_bf16* out, float* lse,
+                                          int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                          int32_t block_size, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -193,3 +193,32 @@ def test_cache_gate_policy_matches_oracle_rule(lib):
     assert lib.h3attn_cache_gate_init(ctypes.byref(st), 0.1, -1) == 1
     assert lib.h3attn_cache_gate_init(None, 0.1, 1) == 1
     assert lib.h3attn_cache_gate_decide(None, 0.0) == -1
+
+
+def test_fp8_workspace_bytes_and_validation(lib):
+    r = lambda x: (x + 255) // 256 * 256
+    chunks = (124992 + 1023) // 1024
+    assert lib.h3attn_fp8_workspace_bytes(1, 48, 124992, 128, 64) == r(48 * chunks * 128 * 4) + r(48 * 128 * 4)
+    assert lib.h3attn_fp8_workspace_bytes(1, 0, 124992, 128, 64) == 0
+    q, k, v, q8, k8, v8t, sq, sk, sv, ws = (0x10000 * (i + 1) for i in range(10))
+    big = 1 << 20
+    f = lib.h3attn_fp8_quantize
+    # every call below fails validation before any launch (pointers are never dereferenced)
+    assert f(None, k, v, q8, k8, v8t, sq, sk, sv, 1, 2, 64, 64, 64, ws, big, None) == 1 and "q is NULL" in _err(lib)
+    assert f(q, k, v, q8 + 8, k8, v8t, sq, sk, sv, 1, 2, 64, 64, 64, ws, big, None) == 1 and "aligned" in _err(lib)
+    assert f(q, k, v, q8, k8, v8t, sq, sk, sv, 1, 2, 64, 96, 64, ws, big, None) == 2 and "head_dim" in _err(lib)
+    assert f(q, k, v, q8, k8, v8t, sq, sk, sv, 1, 2, 64, 64, 32, ws, big, None) == 2 and "block_size" in _err(lib)
+    assert f(q, k, v, q8, k8, v8t, sq, sk, sv, 1, 2, 64, 64, 64, ws, 16, None) == 1 and "workspace" in _err(lib)
+    assert f(q, k, v, q, k8, v8t, sq, sk, sv, 1, 2, 64, 64, 64, ws, big, None) == 1 and "alias" in _err(lib)
+    g = lib.h3attn_fp8_dense_fwd
+    out = 0x200000
+    assert g(None, k8, v8t, sq, sk, sv, out, None, 1, 2, 64, 64, 64, None) == 1 and "q8 is NULL" in _err(lib)
+    assert g(q8, k8, v8t, sq, sk, sv, out, out + 2, 1, 2, 64, 64, 64, None) == 1 and "lse" in _err(lib)
+    assert g(q8, k8, v8t, sq, sk, sv, q8, None, 1, 2, 64, 64, 64, None) == 1 and "alias" in _err(lib)
+    assert g(q8, k8, v8t, sq, sk, sv, out, None, 1, 2, 64, 128, 16, None) == 2 and "block_size" in _err(lib)
+    h = lib.h3attn_fp8_block_sparse_fwd
+    idx = 0x300000
+    assert h(q8, k8, v8t, sq, sk, sv, None, 1, out, None, 1, 2, 128, 64, 64, None) == 1 and "block_idx" in _err(lib)
+    assert h(q8, k8, v8t, sq, sk, sv, idx, 0, out, None, 1, 2, 128, 64, 64, None) == 1 and "keep" in _err(lib)
+    assert h(q8, k8, v8t, sq, sk, sv, idx, 3, out, None, 1, 2, 128, 64, 64, None) == 1 and "keep" in _err(lib)
+    assert h(q8, k8, v8t, sq, sk, sv, idx + 2, 1, out, None, 1, 2, 128, 64, 64, None) == 1 and "aligned" in _err(lib)

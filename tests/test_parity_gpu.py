@@ -12,8 +12,8 @@ import torch
 import oracle
 from inputs import CONFIGS, make_inputs, random_case, sample_query_blocks
 from inputs.generate import box_blocks
-from tests.parity_util import (LSE_MAX_ABS, check_attention, check_block_sets, check_norm_rope, f64,
-                               log)
+from tests.parity_util import (ATTN_MAX_ABS, ATTN_MEAN_ABS, LSE_MAX_ABS, check_attention, check_block_sets,
+                               check_norm_rope, f64, log)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -481,3 +481,134 @@ def test_cache_gate_drives_a_step_sequence(h3):
                 d, p = oracle.residual_change(f64(st), f64(states[i - 1]))
                 want = ref.decide(d / p)
             assert got == want, (mc, i)
+
+
+# ----------------------------------------------------------------- fp8 (e4m3) attention
+
+def _e4m3(t):
+    """Decode uint8 e4m3 codes through the oracle's code table (from the format definition)."""
+    return oracle.e4m3_values()[t.cpu().numpy()]
+
+
+# byte slot of key kappa inside a 64-key block of v8t, as the ABI documents it
+_V8T_SLOT = np.array([32 * ((kk >> 2) & 1) + 16 * (kk >> 5) + 4 * ((kk >> 3) & 3) + (kk & 3) for kk in range(64)])
+
+
+def _v8t_to_tokens(v8t_vals, n):
+    """[B, H, D, nB*64] (slot order) -> [B, N, H, D] values, and the padding slots."""
+    b, h, d, np_ = v8t_vals.shape
+    blocks = v8t_vals.reshape(b, h, d, np_ // 64, 64)[..., _V8T_SLOT]          # key order
+    tok = blocks.reshape(b, h, d, np_).transpose(0, 3, 1, 2)
+    return tok[:, :n], tok[:, n:]
+
+
+def _scaled_case(b, n, h, d, seed):
+    """N(0,1) inputs whose tokens (q, k: factors 2^-3 .. 2^1, so scores stay in the range of
+    real attention) and channels (v: 2^-4 .. 2^4) differ in magnitude, so that the power-of-two
+    scales differ between blocks and channels."""
+    c = random_case(b, n, h, d, seed=seed, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(seed + 1)
+    tok = torch.exp2(torch.randint(-3, 2, (1, n, 1, 1), generator=g, device=DEV).float())
+    ch = torch.exp2(torch.randint(-4, 5, (1, 1, 1, d), generator=g, device=DEV).float())
+    for nm in ("q", "k"):
+        c[nm] = (c[nm].float() * tok).to(torch.bfloat16)
+    c["v"] = (c["v"].float() * ch).to(torch.bfloat16)
+    return c
+
+
+@pytest.mark.parametrize("b,n,h,d", [(1, 256, 2, 64), (2, 333, 3, 128), (1, 1, 1, 64), (1, 4100, 1, 128)])
+def test_fp8_quantize_bit_exact(h3, b, n, h, d):
+    c = _scaled_case(b, n, h, d, 700 + n)
+    fq = h3.fp8_quantize(c["q"], c["k"], c["v"])
+    _sync()
+    for nm, t8, ts in (("q", fq.q8, fq.q_scale), ("k", fq.k8, fq.k_scale)):
+        ref8, refs = oracle.quantize_blocks(f64(c[nm]), 64)
+        np.testing.assert_array_equal(ts.cpu().numpy().astype(np.float64), refs, err_msg=f"{nm} scales")
+        np.testing.assert_array_equal(_e4m3(t8), ref8, err_msg=f"{nm} codes")
+    v8, sv = oracle.quantize_channels(f64(c["v"]))
+    np.testing.assert_array_equal(fq.v_scale.cpu().numpy().astype(np.float64), sv)
+    tok, pad = _v8t_to_tokens(_e4m3(fq.v8t), n)
+    np.testing.assert_array_equal(tok, v8)
+    assert (pad == 0).all()
+    log(f"fp8 quantize {b}x{n}x{h}x{d}: codes and scales bit-exact")
+
+
+def _fp8_compare(o, lse, ref, rl, wmax, dev, what, exact=None):
+    """fp8 path vs its oracle. Where the fp32 score decides an e4m3 probability code next to a
+    rounding boundary, the GPU and the float64 oracle may pick neighbouring codes; one such
+    choice moves a row by at most 2^-3 * wmax * dev (oracle quantities of that row). The bound
+    per element is therefore ATTN_MAX_ABS + 2^-8 |ref| (bf16 output rounding of larger values)
+    + 2^-3 * wmax * dev; the mean error must stay within the bf16 path's bound and at most 2% of
+    the rows may exceed ATTN_MAX_ABS + 2^-8 |ref|."""
+    g = f64(o)
+    err = np.abs(g - ref)
+    w = np.transpose(wmax, (0, 2, 1))[..., None]                       # [B, N, Hd, 1]
+    base = ATTN_MAX_ABS + 2.0 ** -8 * np.abs(ref)
+    bound = base + 2.0 ** -3 * w * dev
+    over = (err > base).any(axis=-1)
+    lerr = np.abs(f64(lse) - rl)
+    lbound = LSE_MAX_ABS + math.log(2.0) * np.log2(1.0 + 2.0 ** -3 * wmax)
+    log(f"{what}: max-abs {err.max():.3g} mean-abs {err.mean():.3g}, rows over base: {int(over.sum())} "
+        f"of {over.size}, worst err/bound {(err / bound).max():.3f}, lse max-abs {lerr.max():.3g}")
+    if exact is not None:
+        log(f"{what}: fp8 path vs exact attention max-abs {np.abs(g - exact).max():.3g}, "
+            f"mean-abs {np.abs(g - exact).mean():.3g} (diagnostic)")
+    assert err.mean() <= ATTN_MEAN_ABS + 2.0 ** -9 * np.abs(ref).mean(), what
+    assert (err <= bound).all(), what
+    assert over.mean() <= 0.02, what
+    assert (lerr <= lbound).all(), what
+
+
+@pytest.mark.parametrize("n,d", [(1, 64), (63, 128), (200, 64), (333, 128), (64 * 20, 128)])
+def test_fp8_dense_and_sparse_full(h3, n, d):
+    c = _scaled_case(1, n, 3, d, 800 + n)
+    qd, kd, vd = f64(c["q"]), f64(c["k"]), f64(c["v"])
+    fq = h3.fp8_quantize(c["q"], c["k"], c["v"])
+    o, lse = h3.fp8_dense_fwd(fq, return_lse=True)
+    _sync()
+    ref, rl, wm, dv = oracle.attention_fp8_detail(qd, kd, vd)
+    _fp8_compare(o, lse, ref, rl, wm, dv, f"fp8 dense n={n} d={d}", exact=oracle.attention(qd, kd, vd)[0])
+    for s in (0.0, 0.5, 0.9):
+        idx = h3.subblock_select(c["q"], c["k"], s)
+        os_, ls = h3.fp8_block_sparse_fwd(fq, idx, return_lse=True)
+        _sync()
+        rs, rls, wms, dvs = oracle.attention_fp8_detail(qd, kd, vd, idx.cpu().numpy())
+        _fp8_compare(os_, ls, rs, rls, wms, dvs, f"fp8 sparse n={n} d={d} s={s}")
+        if s == 0.0:
+            assert torch.equal(os_, o), "keep-all fp8 sparse must equal fp8 dense bit for bit"
+
+
+def test_fp8_frame_workload(h3):
+    x = make_inputs(CONFIGS[2], DEV)
+    qd, kd, vd = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    fq = h3.fp8_quantize(x["q"], x["k"], x["v"])
+    o, lse = h3.fp8_dense_fwd(fq, return_lse=True)
+    idx = h3.subblock_select(x["q"], x["k"], 0.75)
+    os_, ls = h3.fp8_block_sparse_fwd(fq, idx, return_lse=True)
+    _sync()
+    ref, rl, wm, dv = oracle.attention_fp8_detail(qd, kd, vd)
+    _fp8_compare(o, lse, ref, rl, wm, dv, "fp8 dense frame", exact=oracle.attention(qd, kd, vd)[0])
+    rs, rls, wms, dvs = oracle.attention_fp8_detail(qd, kd, vd, idx.cpu().numpy())
+    _fp8_compare(os_, ls, rs, rls, wms, dvs, "fp8 sparse frame s=0.75")
+
+
+@pytest.mark.timeout(900)
+def test_fp8_video5s_sampled(h3):
+    cfg = CONFIGS[3]
+    x = make_inputs(cfg, DEV)
+    fq = h3.fp8_quantize(x["q"], x["k"], x["v"])
+    o = h3.fp8_dense_fwd(fq)
+    idx = h3.subblock_select(x["q"], x["k"], 0.75)
+    os_ = h3.fp8_block_sparse_fwd(fq, idx)
+    _sync()
+    qh, kh, vh, oh, osh, ih = x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), o.cpu(), os_.cpu(), idx.cpu().numpy()
+    for h in (0, 17, 47):
+        qd, kd, vd = f64(qh[:, :, h:h + 1]), f64(kh[:, :, h:h + 1]), f64(vh[:, :, h:h + 1])
+        for i in sample_query_blocks(cfg.n_blocks, 3, seed=3000 + h):
+            rows = np.arange(i * 64, (i + 1) * 64)
+            for what, got, bidx in (("dense", oh, None), ("sparse", osh, ih[0, h, i])):
+                ref, rl, wm, dv = oracle.attention_fp8_rows(qd, kd, vd, 0, 0, i, block_idx=bidx, detail=True)
+                err = np.abs(f64(got[0, rows, h]) - ref)
+                bound = ATTN_MAX_ABS + 2.0 ** -8 * np.abs(ref) + 2.0 ** -3 * wm[:, None] * dv
+                log(f"fp8 {what} 5s head {h} block {i}: max-abs {err.max():.3g} mean-abs {err.mean():.3g}")
+                assert (err <= bound).all() and err.mean() <= ATTN_MEAN_ABS, f"fp8 {what} 5s head {h} block {i}"

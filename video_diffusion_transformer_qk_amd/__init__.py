@@ -9,13 +9,16 @@ Threshold mode: subblock_select_threshold (blocks within tau of the row's best, 
 block_sparse_csr_fwd (variable kept set per query block).
 Other fused block ops of the runtime: adaln_modulate (LayerNorm * (1 + scale) + shift) and swiglu.
 Cache-DiT step reuse: residual_change (L1 change between adjacent steps) and CacheGate (policy).
+FP8 (e4m3) attention: fp8_quantize, fp8_dense_fwd, fp8_block_sparse_fwd.
 """
 from ._lib import (LIB_PATH, SIGNATURES, H3AttnError, block_sparse_csr_fwd, block_sparse_fwd,  # noqa: F401
                    dense_fwd, keep_count, load_library, qk_norm_rope, select_workspace_bytes,
                    subblock_select, subblock_select_threshold, threshold_workspace_bytes, version,
-                   adaln_modulate, swiglu, residual_change, CacheGate)
+                   adaln_modulate, swiglu, residual_change, CacheGate, Fp8QKV, fp8_workspace_bytes,
+                   fp8_quantize, fp8_dense_fwd, fp8_block_sparse_fwd)
 
 __all__ = ["qk_norm_rope", "dense_fwd", "subblock_select", "block_sparse_fwd", "keep_count",
            "select_workspace_bytes", "subblock_select_threshold", "block_sparse_csr_fwd",
            "threshold_workspace_bytes", "adaln_modulate", "swiglu",
-           "residual_change", "CacheGate", "version", "H3AttnError", "load_library"]
+           "residual_change", "CacheGate", "Fp8QKV", "fp8_workspace_bytes", "fp8_quantize",
+           "fp8_dense_fwd", "fp8_block_sparse_fwd", "version", "H3AttnError", "load_library"]

@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Sequence, Tuple
+from typing import NamedTuple, Optional, Sequence, Tuple
 
 import torch
 
@@ -51,6 +51,12 @@ SIGNATURES = {
     "h3attn_residual_change": (ctypes.c_int, [_P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "h3attn_cache_gate_init": (ctypes.c_int, [_P, ctypes.c_double, _I32]),
     "h3attn_cache_gate_decide": (_I32, [_P, ctypes.c_double]),
+    "h3attn_fp8_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I64, _I32, _I32]),
+    "h3attn_fp8_quantize": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32,
+                                           _P, ctypes.c_size_t, _P]),
+    "h3attn_fp8_dense_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P]),
+    "h3attn_fp8_block_sparse_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I64,
+                                                   _I32, _I32, _P]),
 }
 
 
@@ -358,3 +364,98 @@ class CacheGate:
             return self.decide(float("inf"))
         d, p = residual_change(cur, prev).tolist()
         return self.decide(d / p if p > 0 else float("inf"))
+
+
+class Fp8QKV(NamedTuple):
+    """e4m3 codes of q, k ([B, N, heads, D] uint8), of v transposed ([B, heads, D, nB*64] uint8,
+    keys of each 64-key block in the order the P.V product reads them) and their power-of-two
+    scales (float32 [B, heads, nB] for q and k, [B, heads, D] for v)."""
+    q8: torch.Tensor
+    k8: torch.Tensor
+    v8t: torch.Tensor
+    q_scale: torch.Tensor
+    k_scale: torch.Tensor
+    v_scale: torch.Tensor
+
+
+def fp8_workspace_bytes(batch: int, heads: int, n_tokens: int, head_dim: int, block_size: int = 64) -> int:
+    return int(load_library().h3attn_fp8_workspace_bytes(batch, heads, n_tokens, head_dim, block_size))
+
+
+def fp8_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int = 64,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[Fp8QKV] = None) -> Fp8QKV:
+    """e4m3 quantisation of bf16 q, k (per 64-token block) and v (per channel) for the fp8 path."""
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 4)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have the same shape")
+    b, n, h, d = q.shape
+    nb = -(-n // block_size)
+    dev = q.device
+    if out is None:
+        fq = Fp8QKV(torch.empty((b, n, h, d), dtype=torch.uint8, device=dev),
+                    torch.empty((b, n, h, d), dtype=torch.uint8, device=dev),
+                    torch.empty((b, h, d, nb * block_size), dtype=torch.uint8, device=dev),
+                    torch.empty((b, h, nb), dtype=torch.float32, device=dev),
+                    torch.empty((b, h, nb), dtype=torch.float32, device=dev),
+                    torch.empty((b, h, d), dtype=torch.float32, device=dev))
+    else:
+        fq = out
+        if _fp8_check(fq) != (b, n, h, d):
+            raise ValueError("out tensors do not match q's shape")
+    need = fp8_workspace_bytes(b, h, n, d, block_size)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib.h3attn_fp8_quantize(q.data_ptr(), k.data_ptr(), v.data_ptr(), fq.q8.data_ptr(), fq.k8.data_ptr(),
+                                   fq.v8t.data_ptr(), fq.q_scale.data_ptr(), fq.k_scale.data_ptr(),
+                                   fq.v_scale.data_ptr(), b, h, n, d, block_size, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream()))
+    return fq
+
+
+def _fp8_check(fq: Fp8QKV):
+    for t, nm in ((fq.q8, "q8"), (fq.k8, "k8"), (fq.v8t, "v8t")):
+        _need(t, nm, torch.uint8, 4)
+    for t, nm in ((fq.q_scale, "q_scale"), (fq.k_scale, "k_scale"), (fq.v_scale, "v_scale")):
+        _need(t, nm, torch.float32, 3)
+    b, n, h, d = fq.q8.shape
+    nb = -(-n // 64)
+    if fq.k8.shape != fq.q8.shape or tuple(fq.v8t.shape) != (b, h, d, nb * 64) or \
+            tuple(fq.q_scale.shape) != (b, h, nb) or tuple(fq.k_scale.shape) != (b, h, nb) or \
+            tuple(fq.v_scale.shape) != (b, h, d):
+        raise ValueError("inconsistent fp8 tensors")
+    return b, n, h, d
+
+
+def fp8_dense_fwd(fq: Fp8QKV, return_lse: bool = False, out: Optional[torch.Tensor] = None):
+    """Dense attention on e4m3 tensors from fp8_quantize; bf16 output [B, N, heads, D]."""
+    lib = load_library()
+    b, n, h, d = _fp8_check(fq)
+    o = torch.empty((b, n, h, d), dtype=torch.bfloat16, device=fq.q8.device) if out is None else out
+    _need(o, "out", torch.bfloat16, 4)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=o.device) if return_lse else None
+    _check(lib.h3attn_fp8_dense_fwd(fq.q8.data_ptr(), fq.k8.data_ptr(), fq.v8t.data_ptr(), fq.q_scale.data_ptr(),
+                                    fq.k_scale.data_ptr(), fq.v_scale.data_ptr(), o.data_ptr(), _ptr(lse), b, h, n, d,
+                                    64, _stream()))
+    return (o, lse) if return_lse else o
+
+
+def fp8_block_sparse_fwd(fq: Fp8QKV, block_idx: torch.Tensor, return_lse: bool = False,
+                         out: Optional[torch.Tensor] = None):
+    """Block-sparse attention on e4m3 tensors over the kept key blocks block_idx [B, heads, nB, keep]."""
+    lib = load_library()
+    b, n, h, d = _fp8_check(fq)
+    _need(block_idx, "block_idx", torch.int32, 4)
+    nb = -(-n // 64)
+    if tuple(block_idx.shape[:3]) != (b, h, nb):
+        raise ValueError(f"block_idx must be [B, heads, nB, keep] = [{b}, {h}, {nb}, keep]")
+    keep = block_idx.shape[3]
+    o = torch.empty((b, n, h, d), dtype=torch.bfloat16, device=fq.q8.device) if out is None else out
+    _need(o, "out", torch.bfloat16, 4)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=o.device) if return_lse else None
+    _check(lib.h3attn_fp8_block_sparse_fwd(fq.q8.data_ptr(), fq.k8.data_ptr(), fq.v8t.data_ptr(),
+                                           fq.q_scale.data_ptr(), fq.k_scale.data_ptr(), fq.v_scale.data_ptr(),
+                                           block_idx.data_ptr(), keep, o.data_ptr(), _ptr(lse), b, h, n, d, 64,
+                                           _stream()))
+    return (o, lse) if return_lse else o

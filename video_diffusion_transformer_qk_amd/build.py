@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libh3attn.so")
-SOURCES = ["qk_norm_rope.hip", "attention.hip", "subblock_select.hip", "block_ops.hip", "cache_gate.hip", "api.cpp"]
+SOURCES = ["qk_norm_rope.hip", "attention.hip", "attention_fp8.hip", "fp8_quant.hip", "subblock_select.hip",
+           "block_ops.hip", "cache_gate.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

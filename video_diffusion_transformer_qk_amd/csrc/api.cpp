@@ -395,6 +395,105 @@ h3attn_status h3attn_cache_gate_init(h3attn_cache_gate* gate, double threshold, 
   return ok();
 }
 
+size_t h3attn_fp8_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                  int32_t block_size) {
+  if (batch <= 0 || heads <= 0 || n_tokens <= 0 || head_dim <= 0 || block_size <= 0) return 0;
+  const size_t bh = (size_t)batch * (size_t)heads;
+  const size_t chunks = (size_t)((n_tokens + h3attn::kFp8VChunk - 1) / h3attn::kFp8VChunk);
+  return align256(bh * chunks * (size_t)head_dim * sizeof(float)) + align256(bh * (size_t)head_dim * sizeof(int32_t));
+}
+
+h3attn_status h3attn_fp8_quantize(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                  uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                                  float* q_scale, float* k_scale, float* v_scale,
+                                  int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                  int32_t block_size, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  h3attn_status st = check_sizes(batch, heads, n_tokens, head_dim);
+  if (st != H3ATTN_OK) return st;
+  CHECK_PTR(q); CHECK_PTR(k); CHECK_PTR(v); CHECK_PTR(q8); CHECK_PTR(k8); CHECK_PTR(v8t);
+  CHECK_PTR(q_scale); CHECK_PTR(k_scale); CHECK_PTR(v_scale); CHECK_PTR(workspace);
+  {
+    const void* ins[] = {q, k, v};
+    const void* outs[] = {q8, k8, v8t, q_scale, k_scale, v_scale, workspace};
+    for (const void* o : outs)
+      for (const void* i : ins)
+        if (o == i) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "outputs must not alias the inputs");
+  }
+  if (block_size != 64) return fail(H3ATTN_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", block_size);
+  const size_t need = h3attn_fp8_workspace_bytes(batch, heads, n_tokens, head_dim, block_size);
+  if (workspace_bytes < need)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  const int64_t nb = (n_tokens + 63) / 64;
+  if (nb * heads * (int64_t)batch >= ((int64_t)1 << 31))
+    return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads*n_blocks must be below 2^31");
+  h3attn::Fp8QuantArgs a{};
+  a.q = q; a.k = k; a.v = v; a.q8 = q8; a.k8 = k8; a.v8t = v8t;
+  a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.v_partial = static_cast<float*>(workspace);
+  const size_t chunks = (size_t)((n_tokens + h3attn::kFp8VChunk - 1) / h3attn::kFp8VChunk);
+  a.v_exp = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                       align256((size_t)batch * heads * chunks * head_dim * sizeof(float)));
+  a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
+  a.n_blocks = (int32_t)nb; a.n_chunks = (int32_t)chunks;
+  h3attn::launch_fp8_quantize(a, stream);
+  return check_launch("h3attn_fp8_quantize");
+}
+
+namespace {
+h3attn_status fp8_attn_args(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t, const float* q_scale,
+                             const float* k_scale, const float* v_scale, h3attn_bf16* out, float* lse,
+                             int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim, int32_t block_size,
+                             h3attn::Fp8AttnArgs& a) {
+  h3attn_status st = check_sizes(batch, heads, n_tokens, head_dim);
+  if (st != H3ATTN_OK) return st;
+  CHECK_PTR(q8); CHECK_PTR(k8); CHECK_PTR(v8t); CHECK_PTR(q_scale); CHECK_PTR(k_scale); CHECK_PTR(v_scale);
+  CHECK_PTR(out);
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "lse is not 4-byte aligned");
+  if ((const void*)out == q8 || (const void*)out == k8 || (const void*)out == v8t)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "out must not alias the quantised inputs");
+  if (block_size != 64) return fail(H3ATTN_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", block_size);
+  const int64_t nb = (n_tokens + 63) / 64;
+  if (nb * heads * (int64_t)batch >= ((int64_t)1 << 31))
+    return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads*n_blocks must be below 2^31");
+  a = h3attn::Fp8AttnArgs{};
+  a.q8 = q8; a.k8 = k8; a.v8t = v8t; a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.out = out; a.lse = lse; a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
+  a.n_blocks = (int32_t)nb;
+  return H3ATTN_OK;
+}
+}  // namespace
+
+h3attn_status h3attn_fp8_dense_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
+                                   const float* q_scale, const float* k_scale, const float* v_scale,
+                                   h3attn_bf16* out, float* lse, int32_t batch, int32_t heads, int64_t n_tokens,
+                                   int32_t head_dim, int32_t block_size, hipStream_t stream) {
+  h3attn::Fp8AttnArgs a;
+  h3attn_status st = fp8_attn_args(q8, k8, v8t, q_scale, k_scale, v_scale, out, lse, batch, heads, n_tokens,
+                                   head_dim, block_size, a);
+  if (st != H3ATTN_OK) return st;
+  h3attn::launch_fp8_dense_fwd(a, stream);
+  return check_launch("h3attn_fp8_dense_fwd");
+}
+
+h3attn_status h3attn_fp8_block_sparse_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
+                                          const float* q_scale, const float* k_scale, const float* v_scale,
+                                          const int32_t* block_idx, int32_t keep, h3attn_bf16* out, float* lse,
+                                          int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                          int32_t block_size, hipStream_t stream) {
+  h3attn::Fp8AttnArgs a;
+  h3attn_status st = fp8_attn_args(q8, k8, v8t, q_scale, k_scale, v_scale, out, lse, batch, heads, n_tokens,
+                                   head_dim, block_size, a);
+  if (st != H3ATTN_OK) return st;
+  if (block_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is NULL");
+  if (reinterpret_cast<uintptr_t>(block_idx) & 3u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is not 4-byte aligned");
+  if (keep < 1 || keep > a.n_blocks)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep must be in [1, %d] (got %d)", a.n_blocks, keep);
+  a.block_idx = block_idx;
+  a.keep = keep;
+  h3attn::launch_fp8_block_sparse_fwd(a, stream);
+  return check_launch("h3attn_fp8_block_sparse_fwd");
+}
+
 int32_t h3attn_cache_gate_decide(h3attn_cache_gate* gate, double rel_change) {
   if (gate == nullptr) return -1;
   const bool reuse = gate->steps > 0 && rel_change < gate->threshold && gate->consecutive < gate->max_consecutive;

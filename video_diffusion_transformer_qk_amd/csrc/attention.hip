@@ -26,6 +26,7 @@
 // query blocks and walks the union of their kept key blocks (see attn_sparse_group_kernel).
 #include "device_util.h"
 #include "kernels.h"
+#include "sparse_union.h"
 
 namespace h3attn {
 namespace {
@@ -328,8 +329,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
   static_assert(G == 2 || G == 4, "2 or 4 query blocks per workgroup");
   constexpr int WAVES = 2 * G;
   constexpr int NT = WAVES * 64;
-  constexpr int PER = KW / NT;  // window slots per thread in the compaction
-  static_assert(KW % NT == 0 && KW <= (1 << 24), "window must split evenly");
+  static_assert(KW <= (1 << 24), "window slots must fit in 24 bits");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint32_t* ulist = reinterpret_cast<uint32_t*>(smem + 2 * T::BUF_BYTES);  // KW words
   __shared__ int s_wave_tot[WAVES];
@@ -357,18 +357,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
   // the kept list [beg, end) of each block of the group inside block_idx
   const int64_t row0 = ((int64_t)b * a.heads + head) * nb + group * G;
   int64_t beg[G], end[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (group * G + g >= nb) {
-      beg[g] = end[g] = 0;
-    } else if constexpr (CSR) {
-      beg[g] = a.row_ptr[row0 + g];
-      end[g] = a.row_ptr[row0 + g + 1];
-    } else {
-      beg[g] = (row0 + g) * a.keep;
-      end[g] = beg[g] + a.keep;
-    }
-  }
+  group_lists<G, CSR>(a.row_ptr, a.keep, row0, group, nb, beg, end);
   int64_t my_count = 0;
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -383,42 +372,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
 
   for (int64_t j0 = 0; j0 < nb; j0 += KW) {
     const int nw = (int)(nb - j0 < KW ? nb - j0 : KW);
-    // membership bits of the window's key blocks
-    for (int i = tid; i < KW; i += NT) ulist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      for (int64_t e = beg[g] + tid; e < end[g]; e += NT) {
-        const int64_t j = a.block_idx[e] - j0;
-        if (j >= 0 && j < nw) atomicOr(&ulist[j], 1u << g);
-      }
-    __syncthreads();
-    // compaction into (slot << 8 | bits), ascending; each thread owns PER consecutive slots
-    uint32_t mk[PER];
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      mk[i] = ulist[tid * PER + i];
-      c += mk[i] != 0u;
-    }
-    int incl = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    if (lane == 63) s_wave_tot[wave] = incl;
-    __syncthreads();  // also orders every read of the bit array before the writes below
-    int pre = 0;
-#pragma unroll
-    for (int v = 0; v < WAVES; ++v) pre += v < wave ? s_wave_tot[v] : 0;
-    int pos = pre + incl - c;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (mk[i] != 0u) ulist[pos++] = ((uint32_t)(tid * PER + i) << 8) | mk[i];
-    if (tid == NT - 1) s_nu = pos;
-    __syncthreads();
-    const int nu = s_nu;
+    const int nu = build_union_window<G, KW, NT>(ulist, s_wave_tot, &s_nu, a.block_idx, beg, end, j0, nw);
     if (nu == 0) continue;
 
     auto key0_of = [&](int t) -> int64_t { return (j0 + (int64_t)(ulist[t] >> 8)) * kBN; };

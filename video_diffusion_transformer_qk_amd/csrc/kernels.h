@@ -105,4 +105,46 @@ struct ResidualArgs {
 int residual_parts(int64_t n);
 void launch_residual_change(const ResidualArgs& a, hipStream_t stream);
 
+// ---- fp8 (OCP e4m3) attention ----
+// Quantised tensors: q8, k8 are [B, N, H, D] bytes (e4m3 codes of x / s, s the power-of-two
+// scale of the (b, head, 64-token block)); v8t is [B, H, D, nB*64] bytes: V transposed, each
+// 64-key block's keys stored in the order the P.V product consumes them (see fp8_key_slot), and
+// keys past N zero; scales are float32 q_scale/k_scale [B, H, nB], v_scale [B, H, D].
+struct Fp8QuantArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint8_t* q8;
+  uint8_t* k8;
+  uint8_t* v8t;
+  float* q_scale;
+  float* k_scale;
+  float* v_scale;
+  float* v_partial;   // workspace: per (b, head, token chunk) channel maxima
+  int32_t* v_exp;     // workspace: the channel scale exponents [B, H, D]
+  int64_t n_tokens;
+  int32_t batch, heads, head_dim, n_blocks, n_chunks;
+};
+
+constexpr int kFp8VChunk = 1024;  // tokens per V channel-maximum partial
+
+void launch_fp8_quantize(const Fp8QuantArgs& a, hipStream_t stream);
+
+struct Fp8AttnArgs {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8t;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_idx;  // sparse only
+  uint16_t* out;
+  float* lse;                // may be null
+  int64_t n_tokens;
+  int32_t batch, heads, head_dim, n_blocks, keep;
+};
+
+void launch_fp8_dense_fwd(const Fp8AttnArgs& a, hipStream_t stream);
+void launch_fp8_block_sparse_fwd(const Fp8AttnArgs& a, hipStream_t stream);
+
 }  // namespace h3attn
