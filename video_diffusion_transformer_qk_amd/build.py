@@ -33,10 +33,15 @@ def common_flags(debug: bool = False):
     return flags
 
 
+# Per-source flags. The attention kernels never see NaN operands (masked keys are -inf), so
+# max() needs no NaN quieting of MFMA results before the v_max3 tree.
+EXTRA_FLAGS = {"attention.hip": ["-fno-honor-nans"], "attention_fp8.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, debug: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc()] + common_flags(debug) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags(debug) + EXTRA_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
