@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--config", type=int, default=3, help="workload id (3 = 5 s video)")
     p.add_argument("--sparsity", type=float, default=0.75)
+    p.add_argument("--group-stride", type=int, default=0,
+                   help="query-block group stride of the sparse kernels (0: one frame of blocks when frames "
+                        "are whole blocks, else 1)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-extra", action="store_true", help="skip the flushed norm+RoPE runs")
@@ -145,6 +148,7 @@ def main():
     sections = cfg.sections
     nb = (n + 63) // 64
     keep = h3.keep_count(nb, args.sparsity)
+    gs = args.group_stride if args.group_stride > 0 else h3.frame_group_stride(cfg.grid)
     qo, ko = torch.empty_like(q), torch.empty_like(k)
     out_d = torch.empty_like(q)
     out_s = torch.empty_like(q)
@@ -160,7 +164,7 @@ def main():
         if ev is not None: ev[2].record()
         h3.subblock_select(qo, ko, args.sparsity, workspace=ws, out=idx)
         if ev is not None: ev[3].record()
-        h3.block_sparse_fwd(qo, ko, v, idx, out=out_s)
+        h3.block_sparse_fwd(qo, ko, v, idx, out=out_s, group_stride=gs)
         if ev is not None: ev[4].record()
 
     log(f"warmup {args.warmup}")
@@ -283,7 +287,7 @@ def main():
         tau = hi
         rp, ci = h3.subblock_select_threshold(qo, ko, tau, workspace=tws)
         out_c = torch.empty_like(q)
-        h3.block_sparse_csr_fwd(qo, ko, v, rp, ci, out=out_c)
+        h3.block_sparse_csr_fwd(qo, ko, v, rp, ci, out=out_c, group_stride=gs)
         torch.cuda.synchronize()
         nnz = int(rp[-1].item())
         tsel, tcsr = [], []
@@ -292,7 +296,7 @@ def main():
             e0.record()
             h3.subblock_select_threshold(qo, ko, tau, workspace=tws)   # includes one host read of nnz
             e1.record()
-            h3.block_sparse_csr_fwd(qo, ko, v, rp, ci, out=out_c)
+            h3.block_sparse_csr_fwd(qo, ko, v, rp, ci, out=out_c, group_stride=gs)
             e2.record()
             torch.cuda.synchronize()
             tsel.append(elapsed_ms(e0, e1))
@@ -315,7 +319,7 @@ def main():
         fq = h3.fp8_quantize(qo, ko, v, workspace=fws)
         out_f = torch.empty_like(q)
         h3.fp8_dense_fwd(fq, out=out_f)
-        h3.fp8_block_sparse_fwd(fq, idx, out=out_f)
+        h3.fp8_block_sparse_fwd(fq, idx, out=out_f, group_stride=gs)
         torch.cuda.synchronize()
         tq, tdn, tsp = [], [], []
         for r in range(3):
@@ -325,7 +329,7 @@ def main():
             ev4[1].record()
             h3.fp8_dense_fwd(fq, out=out_f)
             ev4[2].record()
-            h3.fp8_block_sparse_fwd(fq, idx, out=out_f)
+            h3.fp8_block_sparse_fwd(fq, idx, out=out_f, group_stride=gs)
             ev4[3].record()
             torch.cuda.synchronize()
             tq.append(elapsed_ms(ev4[0], ev4[1]))
@@ -363,6 +367,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "batch": b, "heads": hd, "head_dim": d, "n_tokens": n,
                    "grid": list(cfg.grid), "sparsity": args.sparsity, "block_size": 64,
+                   "group_stride": gs,
                    "step": "qk_norm_rope + dense_fwd + subblock_select + block_sparse_fwd"},
         "roofline": roofline, "cpu_baseline": cpu, "components": components,
     }

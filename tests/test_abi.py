@@ -120,10 +120,12 @@ def test_select_and_sparse_validation(lib):
     assert call(d=72) == 2
     g = lib.h3attn_block_sparse_fwd
     P = (0x10000, 0x20000, 0x30000)
-    assert g(*P, 0x40000, 0, 0x50000, None, 1, 2, 640, 64, 64, None) == 1 and "keep" in _err(lib)
-    assert g(*P, 0x40000, 11, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
-    assert g(*P, None, 3, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
-    assert g(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 32, None) == 2
+    assert g(*P, 0x40000, 0, 0x50000, None, 1, 2, 640, 64, 64, 1, None) == 1 and "keep" in _err(lib)
+    assert g(*P, 0x40000, 11, 0x50000, None, 1, 2, 640, 64, 64, 1, None) == 1
+    assert g(*P, None, 3, 0x50000, None, 1, 2, 640, 64, 64, 1, None) == 1
+    assert g(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 32, 1, None) == 2
+    assert g(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 64, 0, None) == 1 and "group_stride" in _err(lib)
+    assert g(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 64, 11, None) == 1 and "group_stride" in _err(lib)
 
 
 def test_threshold_validation(lib):
@@ -143,9 +145,10 @@ def test_threshold_validation(lib):
     assert g(1, 2, 640, 64, 64, 0x30000, None, 10, ws, nbytes, None) == 1
     h = lib.h3attn_block_sparse_csr_fwd
     P = (0x10000, 0x20000, 0x30000)
-    assert h(*P, None, 0x40000, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
-    assert h(*P, 0x60000, None, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
-    assert h(*P, 0x60000, 0x40000, 0x50000, None, 1, 2, 640, 64, 32, None) == 2
+    assert h(*P, None, 0x40000, 0x50000, None, 1, 2, 640, 64, 64, 1, None) == 1
+    assert h(*P, 0x60000, None, 0x50000, None, 1, 2, 640, 64, 64, 1, None) == 1
+    assert h(*P, 0x60000, 0x40000, 0x50000, None, 1, 2, 640, 64, 32, 1, None) == 2
+    assert h(*P, 0x60000, 0x40000, 0x50000, None, 1, 2, 640, 64, 64, -1, None) == 1 and "group_stride" in _err(lib)
 
 
 def test_block_ops_validation(lib):
@@ -218,7 +221,8 @@ def test_fp8_workspace_bytes_and_validation(lib):
     assert g(q8, k8, v8t, sq, sk, sv, out, None, 1, 2, 64, 128, 16, None) == 2 and "block_size" in _err(lib)
     h = lib.h3attn_fp8_block_sparse_fwd
     idx = 0x300000
-    assert h(q8, k8, v8t, sq, sk, sv, None, 1, out, None, 1, 2, 128, 64, 64, None) == 1 and "block_idx" in _err(lib)
-    assert h(q8, k8, v8t, sq, sk, sv, idx, 0, out, None, 1, 2, 128, 64, 64, None) == 1 and "keep" in _err(lib)
-    assert h(q8, k8, v8t, sq, sk, sv, idx, 3, out, None, 1, 2, 128, 64, 64, None) == 1 and "keep" in _err(lib)
-    assert h(q8, k8, v8t, sq, sk, sv, idx + 2, 1, out, None, 1, 2, 128, 64, 64, None) == 1 and "aligned" in _err(lib)
+    assert h(q8, k8, v8t, sq, sk, sv, None, 1, out, None, 1, 2, 128, 64, 64, 1, None) == 1 and "block_idx" in _err(lib)
+    assert h(q8, k8, v8t, sq, sk, sv, idx, 0, out, None, 1, 2, 128, 64, 64, 1, None) == 1 and "keep" in _err(lib)
+    assert h(q8, k8, v8t, sq, sk, sv, idx, 3, out, None, 1, 2, 128, 64, 64, 1, None) == 1 and "keep" in _err(lib)
+    assert h(q8, k8, v8t, sq, sk, sv, idx + 2, 1, out, None, 1, 2, 128, 64, 64, 1, None) == 1 and "aligned" in _err(lib)
+    assert h(q8, k8, v8t, sq, sk, sv, idx, 1, out, None, 1, 2, 128, 64, 64, 3, None) == 1 and "group_stride" in _err(lib)

@@ -144,6 +144,40 @@ def test_sparse_index_order_irrelevant(h3):
     assert torch.equal(a, b), "reversed index order changed the result"
 
 
+@pytest.mark.parametrize("n,d,strides", [(64 * 37 - 5, 64, (2, 3, 9, 36, 37)), (64 * 37 - 5, 128, (4, 10, 37)),
+                                         (64 * 9, 128, (2, 9)), (64 * 4098 - 3, 64, (63, 4000))])
+def test_group_stride_is_bitwise_neutral(h3, n, d, strides):
+    """Which four query blocks share a sparse workgroup (i..i+3, or i, i+S, i+2S, i+3S) changes
+    the schedule only: top-k, CSR (with empty rows) and fp8 outputs and lse are bit-identical for
+    every stride, including strides that do not divide the block count and S = nB."""
+    c = random_case(1, n, 2, d, seed=5000 + n + d, device=DEV)
+    nb = -(-n // 64)
+    idx = h3.subblock_select(c["q"], c["k"], 0.5 if nb < 100 else 0.99)
+    keep = idx.shape[-1]
+    rows = 2 * nb
+    counts = (torch.arange(rows) * 7) % (keep + 1)             # 0..keep kept blocks per row
+    rp = torch.zeros(rows + 1, dtype=torch.int64)
+    rp[1:] = torch.cumsum(counts, 0)
+    ih = idx.cpu().reshape(rows, keep)
+    ci = torch.cat([ih[r, :counts[r]] for r in range(rows)]).to(torch.int32)
+    rp, ci = rp.to(DEV), ci.contiguous().to(DEV)
+    fq = h3.fp8_quantize(c["q"], c["k"], c["v"])
+
+    def run(stride):
+        return (h3.block_sparse_fwd(c["q"], c["k"], c["v"], idx, return_lse=True, group_stride=stride),
+                h3.block_sparse_csr_fwd(c["q"], c["k"], c["v"], rp, ci, return_lse=True, group_stride=stride),
+                h3.fp8_block_sparse_fwd(fq, idx, return_lse=True, group_stride=stride))
+
+    base = run(1)
+    _sync()
+    assert bool((base[1][1][0, 0, :64] == -math.inf).all()), "row 0 of the CSR case keeps no block"
+    for stride in strides:
+        got = run(stride)
+        _sync()
+        for (o, lse), (o1, lse1), nm in zip(got, base, ("top-k", "csr", "fp8")):
+            assert torch.equal(o, o1) and torch.equal(lse, lse1), f"{nm} n={n} d={d}: stride {stride} changed the result"
+
+
 def test_sparse_union_across_windows_and_ragged_groups(h3):
     """More key blocks than one union window (4096) and a block count that is not a multiple of
     the 4 query blocks a workgroup takes: sampled query blocks against the oracle, the CSR form
@@ -219,9 +253,14 @@ def _sampled_dense(h3, q, k, v, qblocks_per_head, what):
     return worst
 
 
-def _full_select_sampled_sparse(h3, q, k, v, sparsity, qblocks_per_head, what, head_chunk=4):
+def _full_select_sampled_sparse(h3, q, k, v, sparsity, qblocks_per_head, what, head_chunk=4, group_stride=1):
     idx = h3.subblock_select(q, k, sparsity)
-    o = h3.block_sparse_fwd(q, k, v, idx)
+    o = h3.block_sparse_fwd(q, k, v, idx, group_stride=group_stride)
+    if group_stride != 1:
+        o1 = h3.block_sparse_fwd(q, k, v, idx)
+        _sync()
+        assert torch.equal(o, o1), f"{what}: group stride {group_stride} changed the result"
+        del o1
     _sync()
     qh, kh, vh, oh, ih = q.cpu(), k.cpu(), v.cpu(), o.cpu(), idx.cpu().numpy()
     heads = q.shape[2]
@@ -257,7 +296,8 @@ def test_video5s_dense_sampled(h3):
 def test_video5s_select_and_sparse(h3):
     cfg = CONFIGS[3]
     x = make_inputs(cfg, DEV)
-    _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, _samples(cfg, 3), "5s", head_chunk=8)
+    _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, _samples(cfg, 3), "5s", head_chunk=8,
+                                group_stride=h3.frame_group_stride(cfg.grid))
 
 
 @pytest.mark.timeout(900)
@@ -285,7 +325,8 @@ def test_video10s_dense_select_sparse(h3):
     qo, ko = h3.qk_norm_rope(x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps)
     _sampled_dense(h3, qo, ko, x["v"], _samples(cfg, 3), "10s")
     for s in cfg.sparsities:
-        _full_select_sampled_sparse(h3, qo, ko, x["v"], s, _samples(cfg, 3), "10s")
+        _full_select_sampled_sparse(h3, qo, ko, x["v"], s, _samples(cfg, 3), "10s",
+                                    group_stride=h3.frame_group_stride(cfg.grid))
 
 
 @pytest.mark.timeout(900)
@@ -377,8 +418,11 @@ def test_video5s_threshold_select_and_csr_sparse(h3):
                              for h0 in range(0, cfg.heads, 8)], axis=1)
     tau = _tau_for(scores)
     rp, ci = h3.subblock_select_threshold(q, k, tau)
-    o = h3.block_sparse_csr_fwd(q, k, v, rp, ci)
+    o = h3.block_sparse_csr_fwd(q, k, v, rp, ci, group_stride=h3.frame_group_stride(cfg.grid))
+    o1 = h3.block_sparse_csr_fwd(q, k, v, rp, ci)
     _sync()
+    assert torch.equal(o, o1), "5s csr: frame group stride changed the result"
+    del o1
     _check_threshold_sets(rp, ci, scores, tau, "5s threshold")
     rpn, cin, oh = rp.cpu().numpy(), ci.cpu().numpy(), o.cpu()
     nb = cfg.n_blocks
@@ -599,8 +643,11 @@ def test_fp8_video5s_sampled(h3):
     fq = h3.fp8_quantize(x["q"], x["k"], x["v"])
     o = h3.fp8_dense_fwd(fq)
     idx = h3.subblock_select(x["q"], x["k"], 0.75)
-    os_ = h3.fp8_block_sparse_fwd(fq, idx)
+    os_ = h3.fp8_block_sparse_fwd(fq, idx, group_stride=h3.frame_group_stride(cfg.grid))
+    os1 = h3.fp8_block_sparse_fwd(fq, idx)
     _sync()
+    assert torch.equal(os_, os1), "fp8 5s: frame group stride changed the result"
+    del os1
     qh, kh, vh, oh, osh, ih = x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), o.cpu(), os_.cpu(), idx.cpu().numpy()
     for h in (0, 17, 47):
         qd, kd, vd = f64(qh[:, :, h:h + 1]), f64(kh[:, :, h:h + 1]), f64(vh[:, :, h:h + 1])

@@ -38,13 +38,14 @@ SIGNATURES = {
     "h3attn_subblock_select": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32, _I32, ctypes.c_double,
                                               _I32, _P, _P, ctypes.c_size_t, _P]),
     "h3attn_block_sparse_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I64, _I32,
-                                               _I32, _P]),
+                                               _I32, _I32, _P]),
     "h3attn_threshold_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I64, _I32, _I32]),
     "h3attn_subblock_threshold_count": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32, _I32, ctypes.c_double,
                                                        _P, _P, ctypes.c_size_t, _P]),
     "h3attn_subblock_threshold_fill": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, _P, _P, _I64, _P,
                                                       ctypes.c_size_t, _P]),
-    "h3attn_block_sparse_csr_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P]),
+    "h3attn_block_sparse_csr_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32,
+                                                   _I32, _P]),
     "h3attn_adaln_modulate": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, ctypes.c_float, _P]),
     "h3attn_swiglu": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I64, _I64, _P]),
     "h3attn_residual_workspace_bytes": (ctypes.c_size_t, [_I64]),
@@ -56,7 +57,7 @@ SIGNATURES = {
                                            _P, ctypes.c_size_t, _P]),
     "h3attn_fp8_dense_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32, _P]),
     "h3attn_fp8_block_sparse_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I64,
-                                                   _I32, _I32, _P]),
+                                                   _I32, _I32, _I32, _P]),
 }
 
 
@@ -120,6 +121,16 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 def version() -> str:
     return load_library().h3attn_version().decode()
+
+
+def frame_group_stride(grid, block_size: int = 64) -> int:
+    """Query-block group stride for a T x H x W latent whose frames are whole blocks: H*W/64,
+    so a sparse workgroup takes one spatial position in four consecutive frames. 1 otherwise."""
+    t, h, w = (int(x) for x in grid)
+    frame = h * w
+    if frame % block_size or frame // block_size >= -(-t * frame // block_size):
+        return 1
+    return frame // block_size
 
 
 def keep_count(n_blocks: int, sparsity: float) -> int:
@@ -204,8 +215,10 @@ def subblock_select(q: torch.Tensor, k: torch.Tensor, sparsity: float, block_siz
 
 
 def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: torch.Tensor,
-                     block_size: int = 64, return_lse: bool = False, out: Optional[torch.Tensor] = None):
-    """Attention of each 64-query block over its kept key blocks only."""
+                     block_size: int = 64, return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                     group_stride: int = 1):
+    """Attention of each 64-query block over its kept key blocks only. group_stride picks which
+    four query blocks share a workgroup (i, i+S, i+2S, i+3S); it changes speed, never the result."""
     lib = load_library()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16, 4)
@@ -221,7 +234,7 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_id
     _need(o, "out", torch.bfloat16, 4)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
     _check(lib.h3attn_block_sparse_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), block_idx.data_ptr(), keep,
-                                       o.data_ptr(), _ptr(lse), b, h, n, d, block_size, _stream()))
+                                       o.data_ptr(), _ptr(lse), b, h, n, d, block_size, group_stride, _stream()))
     return (o, lse) if return_lse else o
 
 
@@ -258,7 +271,7 @@ def subblock_select_threshold(q: torch.Tensor, k: torch.Tensor, tau: float, bloc
 
 def block_sparse_csr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
                          col_idx: torch.Tensor, block_size: int = 64, return_lse: bool = False,
-                         out: Optional[torch.Tensor] = None):
+                         out: Optional[torch.Tensor] = None, group_stride: int = 1):
     """Block-sparse attention with a variable kept set per query block (CSR rows)."""
     lib = load_library()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
@@ -276,7 +289,8 @@ def block_sparse_csr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
     ci = col_idx if col_idx.numel() > 0 else torch.zeros((1,), dtype=torch.int32, device=q.device)
     _check(lib.h3attn_block_sparse_csr_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), row_ptr.data_ptr(), ci.data_ptr(),
-                                           o.data_ptr(), _ptr(lse), b, h, n, d, block_size, _stream()))
+                                           o.data_ptr(), _ptr(lse), b, h, n, d, block_size, group_stride,
+                                           _stream()))
     return (o, lse) if return_lse else o
 
 
@@ -442,7 +456,7 @@ def fp8_dense_fwd(fq: Fp8QKV, return_lse: bool = False, out: Optional[torch.Tens
 
 
 def fp8_block_sparse_fwd(fq: Fp8QKV, block_idx: torch.Tensor, return_lse: bool = False,
-                         out: Optional[torch.Tensor] = None):
+                         out: Optional[torch.Tensor] = None, group_stride: int = 1):
     """Block-sparse attention on e4m3 tensors over the kept key blocks block_idx [B, heads, nB, keep]."""
     lib = load_library()
     b, n, h, d = _fp8_check(fq)
@@ -457,5 +471,5 @@ def fp8_block_sparse_fwd(fq: Fp8QKV, block_idx: torch.Tensor, return_lse: bool =
     _check(lib.h3attn_fp8_block_sparse_fwd(fq.q8.data_ptr(), fq.k8.data_ptr(), fq.v8t.data_ptr(),
                                            fq.q_scale.data_ptr(), fq.k_scale.data_ptr(), fq.v_scale.data_ptr(),
                                            block_idx.data_ptr(), keep, o.data_ptr(), _ptr(lse), b, h, n, d, 64,
-                                           _stream()))
+                                           group_stride, _stream()))
     return (o, lse) if return_lse else o

@@ -55,6 +55,14 @@ h3attn_status check_sizes(int32_t batch, int32_t heads, int64_t n_tokens, int32_
   return H3ATTN_OK;
 }
 
+// Query-block grouping of the sparse kernels: 1 (four consecutive blocks) up to n_blocks.
+h3attn_status check_group_stride(int32_t group_stride, int64_t n_blocks) {
+  if (group_stride < 1 || group_stride > n_blocks)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "group_stride must be in [1, %lld] (got %d)", (long long)n_blocks,
+                group_stride);
+  return H3ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -196,7 +204,7 @@ h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k
                                       const int32_t* block_idx, int32_t keep,
                                       h3attn_bf16* out, float* lse,
                                       int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
-                                      int32_t block_size, hipStream_t stream) {
+                                      int32_t block_size, int32_t group_stride, hipStream_t stream) {
   h3attn_status st = check_attn(q, k, v, out, lse, batch, heads, n_tokens, head_dim);
   if (st != H3ATTN_OK) return st;
   if (block_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is NULL");
@@ -206,10 +214,12 @@ h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k
   if (keep < 1 || keep > nb) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep must be in [1, %lld] (got %d)", (long long)nb, keep);
   if (nb * heads * (int64_t)batch >= ((int64_t)1 << 31))
     return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads*n_blocks must be below 2^31");
+  st = check_group_stride(group_stride, nb);
+  if (st != H3ATTN_OK) return st;
   h3attn::AttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.block_idx = block_idx;
   a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
-  a.keep = keep; a.n_blocks = (int32_t)nb;
+  a.keep = keep; a.n_blocks = (int32_t)nb; a.group_stride = group_stride;
   h3attn::launch_block_sparse_fwd(a, stream);
   return check_launch("h3attn_block_sparse_fwd");
 }
@@ -305,7 +315,7 @@ h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf1
                                           const int64_t* row_ptr, const int32_t* col_idx,
                                           h3attn_bf16* out, float* lse,
                                           int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
-                                          int32_t block_size, hipStream_t stream) {
+                                          int32_t block_size, int32_t group_stride, hipStream_t stream) {
   h3attn_status st = check_attn(q, k, v, out, lse, batch, heads, n_tokens, head_dim);
   if (st != H3ATTN_OK) return st;
   if (row_ptr == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_ptr is NULL");
@@ -316,10 +326,12 @@ h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf1
   const int64_t nb = (n_tokens + block_size - 1) / block_size;
   if (nb * heads * (int64_t)batch >= ((int64_t)1 << 31))
     return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads*n_blocks must be below 2^31");
+  st = check_group_stride(group_stride, nb);
+  if (st != H3ATTN_OK) return st;
   h3attn::AttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.block_idx = col_idx; a.row_ptr = row_ptr;
   a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
-  a.keep = 0; a.n_blocks = (int32_t)nb;
+  a.keep = 0; a.n_blocks = (int32_t)nb; a.group_stride = group_stride;
   h3attn::launch_block_sparse_csr_fwd(a, stream);
   return check_launch("h3attn_block_sparse_csr_fwd");
 }
@@ -479,7 +491,7 @@ h3attn_status h3attn_fp8_block_sparse_fwd(const uint8_t* q8, const uint8_t* k8, 
                                           const float* q_scale, const float* k_scale, const float* v_scale,
                                           const int32_t* block_idx, int32_t keep, h3attn_bf16* out, float* lse,
                                           int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
-                                          int32_t block_size, hipStream_t stream) {
+                                          int32_t block_size, int32_t group_stride, hipStream_t stream) {
   h3attn::Fp8AttnArgs a;
   h3attn_status st = fp8_attn_args(q8, k8, v8t, q_scale, k_scale, v_scale, out, lse, batch, heads, n_tokens,
                                    head_dim, block_size, a);
@@ -488,8 +500,11 @@ h3attn_status h3attn_fp8_block_sparse_fwd(const uint8_t* q8, const uint8_t* k8, 
   if (reinterpret_cast<uintptr_t>(block_idx) & 3u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is not 4-byte aligned");
   if (keep < 1 || keep > a.n_blocks)
     return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep must be in [1, %d] (got %d)", a.n_blocks, keep);
+  st = check_group_stride(group_stride, a.n_blocks);
+  if (st != H3ATTN_OK) return st;
   a.block_idx = block_idx;
   a.keep = keep;
+  a.group_stride = group_stride;
   h3attn::launch_fp8_block_sparse_fwd(a, stream);
   return check_launch("h3attn_fp8_block_sparse_fwd");
 }

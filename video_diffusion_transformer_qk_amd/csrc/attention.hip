@@ -343,25 +343,23 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
 
   const int64_t N = a.n_tokens;
   const int64_t nb = a.n_blocks;
-  const int64_t group = blockIdx.x;
   const int head = blockIdx.y, b = blockIdx.z;
   const int64_t row_stride = (int64_t)a.heads * D;
   const int64_t base = ((int64_t)b * N) * row_stride + (int64_t)head * D;
 
-  const int gblk = (wave & 1) + 2 * (wave >> 2);  // this wave's block inside the group
+  const int gblk = __builtin_amdgcn_readfirstlane((wave & 1) + 2 * (wave >> 2));  // this wave's block in the group
   const int half = (wave >> 1) & 1;               // and its 32-query half
-  const int64_t qb = group * G + gblk;
-  const int64_t my_q = qb * kBN + half * 32 + l32;
+  const int64_t row0 = ((int64_t)b * a.heads + head) * nb;
+  const int64_t qb = group_block<G>(blockIdx.x, gblk, a.group_stride, nb);
+  const int64_t my_q = (qb < 0 ? 0 : qb) * kBN + half * 32 + l32;
   const int64_t my_q_c = my_q < N ? my_q : N - 1;
 
-  // the kept list [beg, end) of each block of the group inside block_idx
-  const int64_t row0 = ((int64_t)b * a.heads + head) * nb + group * G;
-  int64_t beg[G], end[G];
-  group_lists<G, CSR>(a.row_ptr, a.keep, row0, group, nb, beg, end);
-  int64_t my_count = 0;
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-    if (g == gblk) my_count = end[g] - beg[g];
+  // the kept list of each block of the group inside block_idx, in LDS; this wave's own length
+  __shared__ int64_t s_range[2 * G];
+  stash_group_ranges<G, CSR>(s_range, a.row_ptr, a.keep, row0, blockIdx.x, a.group_stride, nb);
+  int64_t my_beg, my_end;
+  kept_range<CSR>(a.row_ptr, a.keep, row0, qb, my_beg, my_end);
+  const int64_t my_count = my_end - my_beg;
 
   WaveRows<D> w;
   rows_begin(w, a.q + base + my_q_c * row_stride + 8 * hi);
@@ -372,7 +370,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
 
   for (int64_t j0 = 0; j0 < nb; j0 += KW) {
     const int nw = (int)(nb - j0 < KW ? nb - j0 : KW);
-    const int nu = build_union_window<G, KW, NT>(ulist, s_wave_tot, &s_nu, a.block_idx, beg, end, j0, nw);
+    const int nu = build_union_window<G, KW, NT>(ulist, s_wave_tot, &s_nu, a.block_idx, s_range, j0, nw);
     if (nu == 0) continue;
 
     auto key0_of = [&](int t) -> int64_t { return (j0 + (int64_t)(ulist[t] >> 8)) * kBN; };
@@ -381,7 +379,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
     __syncthreads();
     for (int t = 0; t < nu; ++t) {
       const int buf = t & 1;
-      const uint32_t e = ulist[t];
+      const uint32_t e = __builtin_amdgcn_readfirstlane(ulist[t]);  // uniform: scalar tests and loads
       if (t + 1 < nu) st.fetch(a.k, a.v, base, key0_of(t + 1), N, row_stride);
       if (e & my_bit) {
         const unsigned char* kb = smem + buf * T::BUF_BYTES;
@@ -391,7 +389,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
       __syncthreads();
     }
   }
-  if (qb < nb)
+  if (qb >= 0)
     rows_end(w, a.out + base, a.lse != nullptr ? a.lse + ((int64_t)b * a.heads + head) * N : nullptr, my_q, N,
              row_stride, my_count <= 0, hi);
 }
@@ -418,7 +416,7 @@ void launch_group(const AttnArgs& a, hipStream_t stream) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
   }();
   (void)lds_ok;
-  const dim3 grid((unsigned)((a.n_blocks + G - 1) / G), (unsigned)a.heads, (unsigned)a.batch);
+  const dim3 grid((unsigned)n_groups<G>(a.n_blocks, a.group_stride), (unsigned)a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL(kern, grid, dim3(G * 128), lds, stream, a);
 }
 

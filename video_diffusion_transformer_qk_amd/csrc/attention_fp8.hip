@@ -190,12 +190,17 @@ __device__ __forceinline__ void fp8_rows_end(const Fp8Rows<D>& w, uint16_t* out,
   const float inv = empty ? 0.f : 1.0f / l;
   if (my_q >= N) return;
   uint16_t* op = out + my_q * rs;
+  f32x4 vsc[D / 32][4];  // all channel scales first: the stores below may alias them for the compiler
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) vsc[dt][g] = *reinterpret_cast<const f32x4*>(vscale + 32 * dt + 8 * g + 4 * hi);
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = 32 * dt + 8 * g + 4 * hi;
-      const f32x4 vs = *reinterpret_cast<const f32x4*>(vscale + d);
+      const f32x4 vs = vsc[dt][g];
       u32x2 v;
       v[0] = pack_bf16x2(w.o[dt][4 * g + 0] * vs[0] * inv, w.o[dt][4 * g + 1] * vs[1] * inv);
       v[1] = pack_bf16x2(w.o[dt][4 * g + 2] * vs[2] * inv, w.o[dt][4 * g + 3] * vs[3] * inv);
@@ -255,48 +260,59 @@ __global__ __launch_bounds__(512, 2) void attn_fp8_sparse_kernel(Fp8AttnArgs a) 
   __shared__ int s_nu;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   const int64_t N = a.n_tokens, nb = a.n_blocks;
-  const int64_t group = blockIdx.x;
   const int head = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.heads + head;
   const int64_t rs = (int64_t)a.heads * D;
   const int64_t np = nb * 64;
   const int64_t kbase = ((int64_t)b * N) * rs + (int64_t)head * D;
   const int64_t vbase = bh * D * np;
-  const int gblk = (wave & 1) + 2 * (wave >> 2);  // block inside the group; SIMD-mates differ
+  const int gblk = __builtin_amdgcn_readfirstlane((wave & 1) + 2 * (wave >> 2));  // block in the group; SIMD-mates differ
   const int half = (wave >> 1) & 1;
-  const int64_t qb = group * G + gblk;
-  const int64_t my_q = qb * 64 + half * 32 + l32, my_q_c = my_q < N ? my_q : N - 1;
+  const int64_t qb = group_block<G>(blockIdx.x, gblk, a.group_stride, nb);
+  const int64_t my_q = (qb < 0 ? 0 : qb) * 64 + half * 32 + l32, my_q_c = my_q < N ? my_q : N - 1;
 
-  int64_t beg[G], end[G];
-  group_lists<G, false>(nullptr, a.keep, bh * nb + group * G, group, nb, beg, end);
+  // the kept list of each block of the group inside block_idx, in LDS
+  __shared__ int64_t s_range[2 * G];
+  __shared__ float s_ks[2];  // key scale of the tile in each buffer
+  stash_group_ranges<G, false>(s_range, nullptr, a.keep, bh * nb, blockIdx.x, a.group_stride, nb);
 
   Fp8Rows<D> w;
   fp8_rows_begin(w, a.q8 + kbase + my_q_c * rs, hi,
-                 a.q_scale[bh * nb + (qb < nb ? qb : nb - 1)] * (kLog2e / sqrtf((float)D)));
+                 a.q_scale[bh * nb + (qb < 0 ? 0 : qb)] * (kLog2e / sqrtf((float)D)));
   Fp8Stage<D, NT> st;
   const uint32_t my_bit = 1u << gblk;
   for (int64_t j0 = 0; j0 < nb; j0 += KW) {
     const int nw = (int)(nb - j0 < KW ? nb - j0 : KW);
-    const int nu = build_union_window<G, KW, NT>(ulist, s_wave_tot, &s_nu, a.block_idx, beg, end, j0, nw);
+    const int nu = build_union_window<G, KW, NT>(ulist, s_wave_tot, &s_nu, a.block_idx, s_range, j0, nw);
     if (nu == 0) continue;
-    auto key0_of = [&](int t) -> int64_t { return (j0 + (int64_t)(ulist[t] >> 8)) * 64; };
-    st.fetch(a.k8, a.v8t, kbase, vbase, key0_of(0), N, rs, np, tid);
+    auto kblk_of = [&](int t) -> int64_t { return j0 + (int64_t)(ulist[t] >> 8); };
+    // a tile's key scale is staged in LDS with the tile, so the tile's compute never waits on a
+    // global load (which would also wait for the prefetch of the next tile)
+    float ks = a.k_scale[bh * nb + kblk_of(0)];
+    st.fetch(a.k8, a.v8t, kbase, vbase, kblk_of(0) * 64, N, rs, np, tid);
     st.stash(smem, tid);
+    if (tid == 0) s_ks[0] = ks;
     __syncthreads();
     for (int t = 0; t < nu; ++t) {
       const int buf = t & 1;
-      const uint32_t e = ulist[t];
-      if (t + 1 < nu) st.fetch(a.k8, a.v8t, kbase, vbase, key0_of(t + 1), N, rs, np, tid);
-      if (e & my_bit) {
-        const int64_t kblk = j0 + (int64_t)(e >> 8);
-        const unsigned char* kb = smem + buf * T::BUF_BYTES;
-        fp8_rows_tile<D>(w, kb, kb + T::K_BYTES, kblk * 64, N, lane, a.k_scale[bh * nb + kblk]);
+      const uint32_t e = __builtin_amdgcn_readfirstlane(ulist[t]);  // uniform: scalar tests
+      if (t + 1 < nu) {
+        const int64_t next = kblk_of(t + 1);
+        ks = a.k_scale[bh * nb + next];
+        st.fetch(a.k8, a.v8t, kbase, vbase, next * 64, N, rs, np, tid);
       }
-      if (t + 1 < nu) st.stash(smem + (buf ^ 1) * T::BUF_BYTES, tid);
+      if (e & my_bit) {
+        const unsigned char* kb = smem + buf * T::BUF_BYTES;
+        fp8_rows_tile<D>(w, kb, kb + T::K_BYTES, (j0 + (int64_t)(e >> 8)) * 64, N, lane, s_ks[buf]);
+      }
+      if (t + 1 < nu) {
+        st.stash(smem + (buf ^ 1) * T::BUF_BYTES, tid);
+        if (tid == 0) s_ks[buf ^ 1] = ks;
+      }
       __syncthreads();
     }
   }
-  if (qb < nb)
+  if (qb >= 0)
     fp8_rows_end(w, a.out + ((int64_t)b * N) * rs + (int64_t)head * D,
                  a.lse != nullptr ? a.lse + bh * N : nullptr, a.v_scale + bh * D, my_q, N, rs, hi);
 }
@@ -322,8 +338,8 @@ void launch_sparse(const Fp8AttnArgs& a, hipStream_t stream) {
   auto kern = attn_fp8_sparse_kernel<D, KW>;
   static const bool once = (set_lds(kern, lds), true);
   (void)once;
-  hipLaunchKernelGGL(kern, dim3((unsigned)((a.n_blocks + 3) / 4), (unsigned)a.heads, (unsigned)a.batch), dim3(512),
-                     lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)n_groups<4>(a.n_blocks, a.group_stride), (unsigned)a.heads, (unsigned)a.batch),
+                     dim3(512), lds, stream, a);
 }
 
 }  // namespace

@@ -41,6 +41,7 @@ struct AttnArgs {
   int32_t batch, heads, head_dim;
   int32_t keep;              // sparse only
   int32_t n_blocks;          // sparse only
+  int32_t group_stride;      // sparse only: query blocks of a workgroup are i, i+S, i+2S, i+3S (1: consecutive)
 };
 
 void launch_dense_fwd(const AttnArgs& a, hipStream_t stream);
@@ -142,6 +143,7 @@ struct Fp8AttnArgs {
   float* lse;                // may be null
   int64_t n_tokens;
   int32_t batch, heads, head_dim, n_blocks, keep;
+  int32_t group_stride;      // sparse only, as in AttnArgs
 };
 
 void launch_fp8_dense_fwd(const Fp8AttnArgs& a, hipStream_t stream);
