@@ -102,6 +102,7 @@ struct Fp8Rows {
   f32x16 lsum;   // 1 . P^T: every register holds the row sum of the lane's query
   float m_run;   // integer-valued running max (log2 units), shared by lanes l and l^32
   float cq;      // query block scale * log2(e)/sqrt(D)
+  i32x8 ones;    // e4m3 ones (the row-sum operand), built once
 };
 
 template <int D>
@@ -116,6 +117,9 @@ __device__ __forceinline__ void fp8_rows_begin(Fp8Rows<D>& w, const uint8_t* qro
   for (int dt = 0; dt < D / 32; ++dt) w.o[dt] = f32x16{};
   w.lsum = f32x16{};
   w.m_run = -INFINITY;
+  int one4 = 0x38383838;          // four e4m3 ones
+  asm volatile("" : "+v"(one4));  // opaque: kept in registers, not rebuilt from a constant every tile
+  w.ones = i32x8{one4, one4, one4, one4, one4, one4, one4, one4};
   w.cq = cq;
 }
 
@@ -169,16 +173,17 @@ __device__ __forceinline__ void fp8_rows_tile(Fp8Rows<D>& w, const unsigned char
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int r = 0; r < 16; r += 4) {
-      int v = __builtin_amdgcn_cvt_pk_fp8_f32(fast_exp2(fmaf(s[m][r], c, off)), fast_exp2(fmaf(s[m][r + 1], c, off)), 0, false);
+      // both halves of the word are written, so the first conversion's "old" operand is any
+      // dying register (no zeroing move)
+      const float e1 = fast_exp2(fmaf(s[m][r + 1], c, off));
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(fast_exp2(fmaf(s[m][r], c, off)), e1, __builtin_bit_cast(int, e1), false);
       v = __builtin_amdgcn_cvt_pk_fp8_f32(fast_exp2(fmaf(s[m][r + 2], c, off)), fast_exp2(fmaf(s[m][r + 3], c, off)), v, true);
       pk[4 * m + r / 4] = v;
     }
   const i32x8 pb = {pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) w.o[dt] = mfma_e4m3(lds_read_32b(vb + (32 * dt + l32) * T::VS + 32 * hi), pb, w.o[dt]);
-  const int one4 = 0x38383838;  // four e4m3 ones
-  const i32x8 ones = {one4, one4, one4, one4, one4, one4, one4, one4};
-  w.lsum = mfma_e4m3(ones, pb, w.lsum);
+  w.lsum = mfma_e4m3(w.ones, pb, w.lsum);
 }
 
 // normalise by the row sum, apply the channel scales, store the row of query my_q (if < N)
