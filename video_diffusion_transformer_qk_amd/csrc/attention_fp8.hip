@@ -129,14 +129,26 @@ __device__ __forceinline__ void fp8_rows_tile(Fp8Rows<D>& w, const unsigned char
                                               int64_t key0, int64_t N, int lane, float ck) {
   using T = Fp8Tile<D>;
   const int l32 = lane & 31, hi = lane >> 5;
+  // every K fragment is read before the first MFMA, and every V^T fragment right after the last
+  // one, so the V reads are in flight during the softmax below (left alone, the compiler issues
+  // each read just before its MFMA and waits for it)
+  i32x8 kf[2][D / 64], vf[D / 32];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) kf[m][ks] = lds_read_32b(kb + (32 * m + l32) * T::KS + 64 * ks + 32 * hi);
   f32x16 s[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     s[m] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < D / 64; ++ks)
-      s[m] = mfma_e4m3(lds_read_32b(kb + (32 * m + l32) * T::KS + 64 * ks + 32 * hi), w.qf[ks], s[m]);
+    for (int ks = 0; ks < D / 64; ++ks) s[m] = mfma_e4m3(kf[m][ks], w.qf[ks], s[m]);
   }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) vf[dt] = lds_read_32b(vb + (32 * dt + l32) * T::VS + 32 * hi);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 * (D / 64), 0);  // K reads (two per fragment)
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 64), 0);  // QK MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);  // V reads
   if (key0 + 64 > N) {  // keys past the end of the sequence (the tile that holds the last token)
     const int valid = (int)(N - key0) - 4 * hi;
 #pragma unroll
@@ -182,7 +194,7 @@ __device__ __forceinline__ void fp8_rows_tile(Fp8Rows<D>& w, const unsigned char
     }
   const i32x8 pb = {pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) w.o[dt] = mfma_e4m3(lds_read_32b(vb + (32 * dt + l32) * T::VS + 32 * hi), pb, w.o[dt]);
+  for (int dt = 0; dt < D / 32; ++dt) w.o[dt] = mfma_e4m3(vf[dt], pb, w.o[dt]);
   w.lsum = mfma_e4m3(w.ones, pb, w.lsum);
 }
 
@@ -238,15 +250,25 @@ __global__ __launch_bounds__(512, 2) void attn_fp8_dense_kernel(Fp8AttnArgs a) {
   Fp8Rows<D> w;
   fp8_rows_begin(w, a.q8 + kbase + my_q_c * rs, hi, a.q_scale[bh * nb + qblk] * (kLog2e / sqrtf((float)D)));
   Fp8Stage<D, NT> st;
+  // a tile's key scale is staged in LDS with the tile (see the sparse kernel below)
+  __shared__ float s_ks[2];
+  float ks = a.k_scale[bh * nb];
   st.fetch(a.k8, a.v8t, kbase, vbase, 0, N, rs, np, tid);
   st.stash(smem, tid);
+  if (tid == 0) s_ks[0] = ks;
   __syncthreads();
   for (int t = 0; t < nb; ++t) {
     const int buf = t & 1;
-    if (t + 1 < nb) st.fetch(a.k8, a.v8t, kbase, vbase, (int64_t)(t + 1) * 64, N, rs, np, tid);
+    if (t + 1 < nb) {
+      ks = a.k_scale[bh * nb + t + 1];
+      st.fetch(a.k8, a.v8t, kbase, vbase, (int64_t)(t + 1) * 64, N, rs, np, tid);
+    }
     const unsigned char* kb = smem + buf * T::BUF_BYTES;
-    fp8_rows_tile<D>(w, kb, kb + T::K_BYTES, (int64_t)t * 64, N, lane, a.k_scale[bh * nb + t]);
-    if (t + 1 < nb) st.stash(smem + (buf ^ 1) * T::BUF_BYTES, tid);
+    fp8_rows_tile<D>(w, kb, kb + T::K_BYTES, (int64_t)t * 64, N, lane, s_ks[buf]);
+    if (t + 1 < nb) {
+      st.stash(smem + (buf ^ 1) * T::BUF_BYTES, tid);
+      if (tid == 0) s_ks[buf ^ 1] = ks;
+    }
     __syncthreads();
   }
   fp8_rows_end(w, a.out + ((int64_t)b * N) * rs + (int64_t)head * D,
@@ -292,7 +314,7 @@ __global__ __launch_bounds__(512, 2) void attn_fp8_sparse_kernel(Fp8AttnArgs a) 
     if (nu == 0) continue;
     auto kblk_of = [&](int t) -> int64_t { return j0 + (int64_t)(ulist[t] >> 8); };
     // a tile's key scale is staged in LDS with the tile, so the tile's compute never waits on a
-    // global load (which would also wait for the prefetch of the next tile)
+    // global load (vmcnt counts in issue order: it would also wait for the next tile's prefetch)
     float ks = a.k_scale[bh * nb + kblk_of(0)];
     st.fetch(a.k8, a.v8t, kbase, vbase, kblk_of(0) * 64, N, rs, np, tid);
     st.stash(smem, tid);
