@@ -118,19 +118,28 @@ h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
  * outputs as h3attn_dense_fwd. block_idx rows must hold `keep` distinct indices in [0, nB);
  * their order does not matter: each row's kept blocks are visited in ascending key order, so
  * the result is bit-identical for any order (and, with every block kept, to h3attn_dense_fwd).
- * Behaviour for other index values is undefined.
- * group_stride S (performance only, the result is bit-identical for every S): one workgroup
- * serves four query blocks and streams the union of their kept key blocks once; with S = 1
- * these are four consecutive blocks i..i+3, with S > 1 the blocks i, i+S, i+2S, i+3S. For a
- * video latent of T x H x W tokens whose frames are whole 64-token blocks, S = H*W/64 groups
- * the same spatial position of four consecutive frames, whose kept sets overlap more.
- * Errors: as h3attn_dense_fwd, plus keep outside [1, nB] or group_stride outside [1, nB] ->
- * INVALID_ARGUMENT and block_size != 64 -> UNSUPPORTED. */
+ * Behaviour for other index values is undefined. One workgroup serves four consecutive query
+ * blocks and streams the union of their kept key blocks once.
+ * Errors: as h3attn_dense_fwd, plus keep outside [1, nB] -> INVALID_ARGUMENT and
+ * block_size != 64 -> UNSUPPORTED. */
 h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
                                       const int32_t* block_idx, int32_t keep,
                                       h3attn_bf16* out, float* lse,
                                       int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
-                                      int32_t block_size, int32_t group_stride, hipStream_t stream);
+                                      int32_t block_size, hipStream_t stream);
+
+/* h3attn_block_sparse_fwd with a choice of which four query blocks share a workgroup (a schedule
+ * choice only: the result is bit-identical for every group_stride S). S = 1 is
+ * h3attn_block_sparse_fwd (blocks i..i+3); S > 1 takes the blocks i, i+S, i+2S, i+3S. For a video
+ * latent of T x H x W tokens whose frames are whole 64-token blocks, S = H*W/64 groups the same
+ * spatial position of four consecutive frames, whose kept sets overlap more (79 % against 58 %
+ * for neighbouring blocks on the smooth-field workloads), so fewer union tiles are streamed.
+ * Errors: as h3attn_block_sparse_fwd, plus group_stride outside [1, nB] -> INVALID_ARGUMENT. */
+h3attn_status h3attn_block_sparse_grouped_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                              const int32_t* block_idx, int32_t keep,
+                                              h3attn_bf16* out, float* lse,
+                                              int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                              int32_t block_size, int32_t group_stride, hipStream_t stream);
 
 /* ---- Threshold-mode SubBlock selection with a variable number of kept blocks per row ----
  * "MiniMax-H3 在 8×H200 上基准测试…" (chat-gpts.plus), section "事件核心" describes SubBlock as
@@ -164,13 +173,21 @@ h3attn_status h3attn_subblock_threshold_fill(int32_t batch, int32_t heads, int64
                                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Block-sparse attention with a CSR kept set per query block (rows as above; indices distinct
- * and in [0, nB), any order, visited in ascending key order). Same numerics and group_stride as
+ * and in [0, nB), any order, visited in ascending key order). Same numerics as
  * h3attn_block_sparse_fwd. A row with no kept block yields zeros and lse = -inf. */
 h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
                                           const int64_t* row_ptr, const int32_t* col_idx,
                                           h3attn_bf16* out, float* lse,
                                           int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
-                                          int32_t block_size, int32_t group_stride, hipStream_t stream);
+                                          int32_t block_size, hipStream_t stream);
+
+/* h3attn_block_sparse_csr_fwd with the group_stride of h3attn_block_sparse_grouped_fwd. */
+h3attn_status h3attn_block_sparse_csr_grouped_fwd(const h3attn_bf16* q, const h3attn_bf16* k,
+                                                  const h3attn_bf16* v, const int64_t* row_ptr,
+                                                  const int32_t* col_idx, h3attn_bf16* out, float* lse,
+                                                  int32_t batch, int32_t heads, int64_t n_tokens,
+                                                  int32_t head_dim, int32_t block_size, int32_t group_stride,
+                                                  hipStream_t stream);
 
 /* ---- The other fused per-block ops of the lossless runtime ----
  * "MiniMax-H3 的 6.24 倍，不能直接算成六倍产能" (xiaodao.ai), section "先把近两倍的免费收益拿走":
@@ -274,8 +291,9 @@ h3attn_status h3attn_fp8_dense_fwd(const uint8_t* q8, const uint8_t* k8, const u
                                    int32_t head_dim, int32_t block_size, hipStream_t stream);
 
 /* Block-sparse attention on the quantised tensors: query block i attends to the key blocks
- * block_idx[b, head, i, 0..keep-1] only (same index and group_stride rules as
- * h3attn_block_sparse_fwd; the row max is taken over the kept keys). */
+ * block_idx[b, head, i, 0..keep-1] only (same index rules as h3attn_block_sparse_fwd and
+ * group_stride as h3attn_block_sparse_grouped_fwd, 1 for consecutive blocks; the row max is
+ * taken over the kept keys). */
 h3attn_status h3attn_fp8_block_sparse_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
                                           const float* q_scale, const float* k_scale, const float* v_scale,
                                           const int32_t* block_idx, int32_t keep, h3attn_bf16* out, float* lse,

@@ -120,12 +120,14 @@ def test_select_and_sparse_validation(lib):
     assert call(d=72) == 2
     g = lib.h3attn_block_sparse_fwd
     P = (0x10000, 0x20000, 0x30000)
-    assert g(*P, 0x40000, 0, 0x50000, None, 1, 2, 640, 64, 64, 1, None) == 1 and "keep" in _err(lib)
-    assert g(*P, 0x40000, 11, 0x50000, None, 1, 2, 640, 64, 64, 1, None) == 1
-    assert g(*P, None, 3, 0x50000, None, 1, 2, 640, 64, 64, 1, None) == 1
-    assert g(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 32, 1, None) == 2
-    assert g(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 64, 0, None) == 1 and "group_stride" in _err(lib)
-    assert g(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 64, 11, None) == 1 and "group_stride" in _err(lib)
+    assert g(*P, 0x40000, 0, 0x50000, None, 1, 2, 640, 64, 64, None) == 1 and "keep" in _err(lib)
+    assert g(*P, 0x40000, 11, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
+    assert g(*P, None, 3, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
+    assert g(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 32, None) == 2
+    gg = lib.h3attn_block_sparse_grouped_fwd
+    assert gg(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 64, 0, None) == 1 and "group_stride" in _err(lib)
+    assert gg(*P, 0x40000, 3, 0x50000, None, 1, 2, 640, 64, 64, 11, None) == 1 and "group_stride" in _err(lib)
+    assert gg(*P, 0x40000, 0, 0x50000, None, 1, 2, 640, 64, 64, 2, None) == 1 and "keep" in _err(lib)
 
 
 def test_threshold_validation(lib):
@@ -145,10 +147,12 @@ def test_threshold_validation(lib):
     assert g(1, 2, 640, 64, 64, 0x30000, None, 10, ws, nbytes, None) == 1
     h = lib.h3attn_block_sparse_csr_fwd
     P = (0x10000, 0x20000, 0x30000)
-    assert h(*P, None, 0x40000, 0x50000, None, 1, 2, 640, 64, 64, 1, None) == 1
-    assert h(*P, 0x60000, None, 0x50000, None, 1, 2, 640, 64, 64, 1, None) == 1
-    assert h(*P, 0x60000, 0x40000, 0x50000, None, 1, 2, 640, 64, 32, 1, None) == 2
-    assert h(*P, 0x60000, 0x40000, 0x50000, None, 1, 2, 640, 64, 64, -1, None) == 1 and "group_stride" in _err(lib)
+    assert h(*P, None, 0x40000, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
+    assert h(*P, 0x60000, None, 0x50000, None, 1, 2, 640, 64, 64, None) == 1
+    assert h(*P, 0x60000, 0x40000, 0x50000, None, 1, 2, 640, 64, 32, None) == 2
+    hg = lib.h3attn_block_sparse_csr_grouped_fwd
+    assert hg(*P, 0x60000, 0x40000, 0x50000, None, 1, 2, 640, 64, 64, -1, None) == 1 and "group_stride" in _err(lib)
+    assert hg(*P, None, 0x40000, 0x50000, None, 1, 2, 640, 64, 64, 2, None) == 1 and "row_ptr" in _err(lib)
 
 
 def test_block_ops_validation(lib):

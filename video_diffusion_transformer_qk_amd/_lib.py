@@ -38,14 +38,18 @@ SIGNATURES = {
     "h3attn_subblock_select": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32, _I32, ctypes.c_double,
                                               _I32, _P, _P, ctypes.c_size_t, _P]),
     "h3attn_block_sparse_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I64, _I32,
-                                               _I32, _I32, _P]),
+                                               _I32, _P]),
+    "h3attn_block_sparse_grouped_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I64, _I32,
+                                                       _I32, _I32, _P]),
     "h3attn_threshold_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I64, _I32, _I32]),
     "h3attn_subblock_threshold_count": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32, _I32, ctypes.c_double,
                                                        _P, _P, ctypes.c_size_t, _P]),
     "h3attn_subblock_threshold_fill": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, _P, _P, _I64, _P,
                                                       ctypes.c_size_t, _P]),
     "h3attn_block_sparse_csr_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32,
-                                                   _I32, _P]),
+                                                   _P]),
+    "h3attn_block_sparse_csr_grouped_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32,
+                                                           _I32, _I32, _P]),
     "h3attn_adaln_modulate": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, ctypes.c_float, _P]),
     "h3attn_swiglu": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I64, _I64, _P]),
     "h3attn_residual_workspace_bytes": (ctypes.c_size_t, [_I64]),
@@ -233,8 +237,12 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_id
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", torch.bfloat16, 4)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
-    _check(lib.h3attn_block_sparse_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), block_idx.data_ptr(), keep,
-                                       o.data_ptr(), _ptr(lse), b, h, n, d, block_size, group_stride, _stream()))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), block_idx.data_ptr(), keep, o.data_ptr(), _ptr(lse), b, h, n, d,
+            block_size)
+    if group_stride == 1:
+        _check(lib.h3attn_block_sparse_fwd(*args, _stream()))
+    else:
+        _check(lib.h3attn_block_sparse_grouped_fwd(*args, group_stride, _stream()))
     return (o, lse) if return_lse else o
 
 
@@ -288,9 +296,12 @@ def block_sparse_csr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_
     _need(o, "out", torch.bfloat16, 4)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
     ci = col_idx if col_idx.numel() > 0 else torch.zeros((1,), dtype=torch.int32, device=q.device)
-    _check(lib.h3attn_block_sparse_csr_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), row_ptr.data_ptr(), ci.data_ptr(),
-                                           o.data_ptr(), _ptr(lse), b, h, n, d, block_size, group_stride,
-                                           _stream()))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), row_ptr.data_ptr(), ci.data_ptr(), o.data_ptr(), _ptr(lse), b, h,
+            n, d, block_size)
+    if group_stride == 1:
+        _check(lib.h3attn_block_sparse_csr_fwd(*args, _stream()))
+    else:
+        _check(lib.h3attn_block_sparse_csr_grouped_fwd(*args, group_stride, _stream()))
     return (o, lse) if return_lse else o
 
 

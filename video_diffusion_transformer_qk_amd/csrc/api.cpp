@@ -200,11 +200,11 @@ h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
   return check_launch("h3attn_subblock_select");
 }
 
-h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
-                                      const int32_t* block_idx, int32_t keep,
-                                      h3attn_bf16* out, float* lse,
-                                      int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
-                                      int32_t block_size, int32_t group_stride, hipStream_t stream) {
+static h3attn_status block_sparse_topk(const char* name, const h3attn_bf16* q, const h3attn_bf16* k,
+                                       const h3attn_bf16* v, const int32_t* block_idx, int32_t keep,
+                                       h3attn_bf16* out, float* lse, int32_t batch, int32_t heads,
+                                       int64_t n_tokens, int32_t head_dim, int32_t block_size,
+                                       int32_t group_stride, hipStream_t stream) {
   h3attn_status st = check_attn(q, k, v, out, lse, batch, heads, n_tokens, head_dim);
   if (st != H3ATTN_OK) return st;
   if (block_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is NULL");
@@ -221,7 +221,25 @@ h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k
   a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
   a.keep = keep; a.n_blocks = (int32_t)nb; a.group_stride = group_stride;
   h3attn::launch_block_sparse_fwd(a, stream);
-  return check_launch("h3attn_block_sparse_fwd");
+  return check_launch(name);
+}
+
+h3attn_status h3attn_block_sparse_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                      const int32_t* block_idx, int32_t keep,
+                                      h3attn_bf16* out, float* lse,
+                                      int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                      int32_t block_size, hipStream_t stream) {
+  return block_sparse_topk("h3attn_block_sparse_fwd", q, k, v, block_idx, keep, out, lse, batch, heads, n_tokens,
+                           head_dim, block_size, 1, stream);
+}
+
+h3attn_status h3attn_block_sparse_grouped_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                              const int32_t* block_idx, int32_t keep,
+                                              h3attn_bf16* out, float* lse,
+                                              int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                              int32_t block_size, int32_t group_stride, hipStream_t stream) {
+  return block_sparse_topk("h3attn_block_sparse_grouped_fwd", q, k, v, block_idx, keep, out, lse, batch, heads,
+                           n_tokens, head_dim, block_size, group_stride, stream);
 }
 
 static h3attn_status check_select_common(const h3attn_bf16* q, const h3attn_bf16* k, int32_t batch,
@@ -311,11 +329,11 @@ h3attn_status h3attn_subblock_threshold_fill(int32_t batch, int32_t heads, int64
   return check_launch("h3attn_subblock_threshold_fill");
 }
 
-h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
-                                          const int64_t* row_ptr, const int32_t* col_idx,
-                                          h3attn_bf16* out, float* lse,
-                                          int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
-                                          int32_t block_size, int32_t group_stride, hipStream_t stream) {
+static h3attn_status block_sparse_csr(const char* name, const h3attn_bf16* q, const h3attn_bf16* k,
+                                      const h3attn_bf16* v, const int64_t* row_ptr, const int32_t* col_idx,
+                                      h3attn_bf16* out, float* lse, int32_t batch, int32_t heads,
+                                      int64_t n_tokens, int32_t head_dim, int32_t block_size,
+                                      int32_t group_stride, hipStream_t stream) {
   h3attn_status st = check_attn(q, k, v, out, lse, batch, heads, n_tokens, head_dim);
   if (st != H3ATTN_OK) return st;
   if (row_ptr == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_ptr is NULL");
@@ -333,7 +351,26 @@ h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf1
   a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
   a.keep = 0; a.n_blocks = (int32_t)nb; a.group_stride = group_stride;
   h3attn::launch_block_sparse_csr_fwd(a, stream);
-  return check_launch("h3attn_block_sparse_csr_fwd");
+  return check_launch(name);
+}
+
+h3attn_status h3attn_block_sparse_csr_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const h3attn_bf16* v,
+                                          const int64_t* row_ptr, const int32_t* col_idx,
+                                          h3attn_bf16* out, float* lse,
+                                          int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                          int32_t block_size, hipStream_t stream) {
+  return block_sparse_csr("h3attn_block_sparse_csr_fwd", q, k, v, row_ptr, col_idx, out, lse, batch, heads,
+                          n_tokens, head_dim, block_size, 1, stream);
+}
+
+h3attn_status h3attn_block_sparse_csr_grouped_fwd(const h3attn_bf16* q, const h3attn_bf16* k,
+                                                  const h3attn_bf16* v, const int64_t* row_ptr,
+                                                  const int32_t* col_idx, h3attn_bf16* out, float* lse,
+                                                  int32_t batch, int32_t heads, int64_t n_tokens,
+                                                  int32_t head_dim, int32_t block_size, int32_t group_stride,
+                                                  hipStream_t stream) {
+  return block_sparse_csr("h3attn_block_sparse_csr_grouped_fwd", q, k, v, row_ptr, col_idx, out, lse, batch,
+                          heads, n_tokens, head_dim, block_size, group_stride, stream);
 }
 
 h3attn_status h3attn_adaln_modulate(const h3attn_bf16* x, const float* shift, const float* scale,
