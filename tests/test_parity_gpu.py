@@ -447,7 +447,7 @@ def _check_elementwise(gpu, ref, floor, what):
     assert worst <= 1.0 and exact > 0.99, what
 
 
-@pytest.mark.parametrize("b,n,c", [(2, 333, 6144), (1, 64, 96), (3, 17, 16384), (1, 1, 8)])
+@pytest.mark.parametrize("b,n,c", [(2, 333, 6144), (1, 64, 96), (3, 17, 16384), (1, 1, 8), (1, 5, 8192), (2, 3, 12000)])
 def test_adaln_modulate_full(h3, b, n, c):
     g = torch.Generator(device=DEV).manual_seed(b * 1000 + n + c)
     x = (torch.randn((b, n, c), generator=g, device=DEV) * 2.0 + 3.0).to(torch.bfloat16)
