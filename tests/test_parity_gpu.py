@@ -144,17 +144,18 @@ def test_sparse_index_order_irrelevant(h3):
     assert torch.equal(a, b), "reversed index order changed the result"
 
 
-@pytest.mark.parametrize("n,d,strides", [(64 * 37 - 5, 64, (2, 3, 9, 36, 37)), (64 * 37 - 5, 128, (4, 10, 37)),
-                                         (64 * 9, 128, (2, 9)), (64 * 4098 - 3, 64, (63, 4000))])
-def test_group_stride_is_bitwise_neutral(h3, n, d, strides):
+@pytest.mark.parametrize("b,n,d,strides", [(1, 64 * 37 - 5, 64, (2, 3, 9, 36, 37)), (1, 64 * 37 - 5, 128, (4, 10, 37)),
+                                           (1, 64 * 9, 128, (2, 9)), (1, 64 * 4098 - 3, 64, (63, 4000)),
+                                           (2, 64 * 37 - 5, 128, (9, 37))])
+def test_group_stride_is_bitwise_neutral(h3, b, n, d, strides):
     """Which four query blocks share a sparse workgroup (i..i+3, or i, i+S, i+2S, i+3S) changes
     the schedule only: top-k, CSR (with empty rows) and fp8 outputs and lse are bit-identical for
     every stride, including strides that do not divide the block count and S = nB."""
-    c = random_case(1, n, 2, d, seed=5000 + n + d, device=DEV)
+    c = random_case(b, n, 2, d, seed=5000 + n + d + b, device=DEV)
     nb = -(-n // 64)
     idx = h3.subblock_select(c["q"], c["k"], 0.5 if nb < 100 else 0.99)
     keep = idx.shape[-1]
-    rows = 2 * nb
+    rows = b * 2 * nb
     counts = (torch.arange(rows) * 7) % (keep + 1)             # 0..keep kept blocks per row
     rp = torch.zeros(rows + 1, dtype=torch.int64)
     rp[1:] = torch.cumsum(counts, 0)
@@ -175,7 +176,7 @@ def test_group_stride_is_bitwise_neutral(h3, n, d, strides):
         got = run(stride)
         _sync()
         for (o, lse), (o1, lse1), nm in zip(got, base, ("top-k", "csr", "fp8")):
-            assert torch.equal(o, o1) and torch.equal(lse, lse1), f"{nm} n={n} d={d}: stride {stride} changed the result"
+            assert torch.equal(o, o1) and torch.equal(lse, lse1), f"{nm} b={b} n={n} d={d}: stride {stride} changed the result"
 
 
 def test_sparse_union_across_windows_and_ragged_groups(h3):
@@ -336,7 +337,8 @@ def test_video15s_boxes_select_sparse_dense(h3):
     bb = box_blocks(cfg.grid, x["boxes"])
     extra = [bb[0], bb[len(bb) // 2], bb[-1]]
     smp = _samples(cfg, 4, extra=extra)
-    _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, smp, "15s")
+    _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, smp, "15s",
+                                group_stride=h3.frame_group_stride(cfg.grid))
     _sampled_dense(h3, x["q"], x["k"], x["v"], _samples(cfg, 2), "15s")
 
 
@@ -603,9 +605,10 @@ def _fp8_compare(o, lse, ref, rl, wmax, dev, what, exact=None):
     assert (lerr <= lbound).all(), what
 
 
-@pytest.mark.parametrize("n,d", [(1, 64), (63, 128), (200, 64), (333, 128), (64 * 20, 128)])
-def test_fp8_dense_and_sparse_full(h3, n, d):
-    c = _scaled_case(1, n, 3, d, 800 + n)
+@pytest.mark.parametrize("b,n,d", [(1, 1, 64), (1, 63, 128), (2, 200, 64), (1, 333, 128), (1, 64 * 20, 128),
+                                   (2, 64 * 9 + 7, 128)])
+def test_fp8_dense_and_sparse_full(h3, b, n, d):
+    c = _scaled_case(b, n, 3, d, 800 + n + b)
     qd, kd, vd = f64(c["q"]), f64(c["k"]), f64(c["v"])
     fq = h3.fp8_quantize(c["q"], c["k"], c["v"])
     o, lse = h3.fp8_dense_fwd(fq, return_lse=True)
