@@ -129,6 +129,7 @@ __device__ __forceinline__ uint64_t order_key(double x) {
 }
 
 constexpr int kTopkThreads = 256;
+static_assert(kTopkThreads == 256, "one histogram bin per thread");
 
 // block-wide exclusive prefix sum of one int per thread; returns the block total in *total
 __device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= 4 ints */) {
@@ -153,23 +154,24 @@ __device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= 4 ints
   return before + x - v;
 }
 
-// Writes, in ascending index order, every j with keys[j] > thr plus the first k_rem indices with
-// keys[j] == thr; each thread scans one contiguous index range, two block scans place the runs.
-__device__ void ordered_compact(const uint64_t* keys, int nb, uint64_t thr, int k_rem, int32_t* dst,
+// Writes, in ascending index order, every j with (keys[j] & mask) > thr plus the first k_rem
+// indices with (keys[j] & mask) == thr (thr has no bits outside mask); each thread scans one
+// contiguous index range, two block scans place the runs.
+__device__ void ordered_compact(const uint64_t* keys, int nb, uint64_t thr, uint64_t mask, int k_rem, int32_t* dst,
                                 int keep, int* scan_scratch) {
   const int tid = threadIdx.x;
   const int per = (nb + kTopkThreads - 1) / kTopkThreads;
   const int j0 = tid * per;
   const int j1 = j0 + per < nb ? j0 + per : nb;
   int n_eq = 0;
-  for (int j = j0; j < j1; ++j) n_eq += keys[j] == thr;
+  for (int j = j0; j < j1; ++j) n_eq += (keys[j] & mask) == thr;
   int tot;
   const int eq_before = block_exclusive_scan(n_eq, &tot, scan_scratch);
   int n_sel = 0;
   {
     int e = eq_before;
     for (int j = j0; j < j1; ++j) {
-      const uint64_t key = keys[j];
+      const uint64_t key = keys[j] & mask;
       if (key > thr) ++n_sel;
       else if (key == thr) { if (e < k_rem) ++n_sel; ++e; }
     }
@@ -177,7 +179,7 @@ __device__ void ordered_compact(const uint64_t* keys, int nb, uint64_t thr, int 
   const int pos0 = block_exclusive_scan(n_sel, &tot, scan_scratch);
   int e = eq_before, p = pos0;
   for (int j = j0; j < j1; ++j) {
-    const uint64_t key = keys[j];
+    const uint64_t key = keys[j] & mask;
     bool take = false;
     if (key > thr) take = true;
     else if (key == thr) { take = e < k_rem; ++e; }
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ int scan_scratch[4];
   __shared__ uint64_t sh_prefix;
-  __shared__ int sh_krem;
+  __shared__ int sh_krem, sh_done;
 
   const int tid = threadIdx.x;
   const int nb = a.n_blocks;
@@ -200,6 +202,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   const double* sc = a.scores + row * nb;
   for (int j = tid; j < nb; j += kTopkThreads) keys[j] = order_key(sc[j]);
 
+  // Digit by digit from the top: the 8-bit digit of the keep-th largest key is the bin where the
+  // count of keys in higher bins first reaches k_rem (thread t owns bin 255 - t, so a block
+  // prefix sum gives every bin the count above it and exactly one thread finds the digit). The
+  // select stops early once the chosen bin holds exactly the k_rem keys still wanted: all of
+  // them are kept, so the remaining digits cannot change the kept set.
   uint64_t prefix = 0, mask = 0;
   int k_rem = a.keep;
   for (int pass = 0; pass < 8; ++pass) {
@@ -211,25 +218,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      int above = 0, d = 255;
-      for (; d > 0; --d) {
-        const int h = (int)hist[d];
-        if (above + h >= k_rem) break;
-        above += h;
-      }
+    const int d = 255 - tid;
+    const int h = (int)hist[d];
+    int tot;
+    const int above = block_exclusive_scan(h, &tot, scan_scratch);  // keys in the bins above d
+    if (above < k_rem && k_rem <= above + h) {
       sh_prefix = prefix | ((uint64_t)d << shift);
       sh_krem = k_rem - above;
+      sh_done = h == k_rem - above;
     }
     __syncthreads();
     prefix = sh_prefix;
     k_rem = sh_krem;
     mask |= (uint64_t)0xff << shift;
-    __syncthreads();
+    if (sh_done) break;  // block-uniform
   }
-  const uint64_t thr = prefix;  // the keep-th largest key; take k_rem of its equal keys
 
-  ordered_compact(keys, nb, thr, k_rem, a.block_idx + row * a.keep, a.keep, scan_scratch);
+  // keys whose top digits exceed the prefix are kept, plus k_rem of those equal to it
+  ordered_compact(keys, nb, prefix, mask, k_rem, a.block_idx + row * a.keep, a.keep, scan_scratch);
 }
 
 // Threshold mode, pass 1: per row, the largest unscaled score m and the kept count
