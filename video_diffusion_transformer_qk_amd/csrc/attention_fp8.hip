@@ -123,31 +123,38 @@ __device__ __forceinline__ void fp8_rows_begin(Fp8Rows<D>& w, const uint8_t* qro
   w.cq = cq;
 }
 
-// one 64-key tile (K rows at kb, V^T rows at vb in LDS; first key key0; ck its key-block scale)
+// QK half of one 64-key tile: S^T = K8 . Q8^T from the K tile at kb. Every K fragment is read
+// before the first MFMA (left alone, the compiler issues each read just before its MFMA and
+// waits for it).
 template <int D>
-__device__ __forceinline__ void fp8_rows_tile(Fp8Rows<D>& w, const unsigned char* kb, const unsigned char* vb,
-                                              int64_t key0, int64_t N, int lane, float ck) {
+__device__ __forceinline__ void fp8_qk(const Fp8Rows<D>& w, const unsigned char* kb, int lane, f32x16 (&s)[2]) {
   using T = Fp8Tile<D>;
   const int l32 = lane & 31, hi = lane >> 5;
-  // every K fragment is read before the first MFMA, and every V^T fragment right after the last
-  // one, so the V reads are in flight during the softmax below (left alone, the compiler issues
-  // each read just before its MFMA and waits for it)
-  i32x8 kf[2][D / 64], vf[D / 32];
+  i32x8 kf[2][D / 64];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks) kf[m][ks] = lds_read_32b(kb + (32 * m + l32) * T::KS + 64 * ks + 32 * hi);
-  f32x16 s[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     s[m] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks) s[m] = mfma_e4m3(kf[m][ks], w.qf[ks], s[m]);
   }
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) vf[dt] = lds_read_32b(vb + (32 * dt + l32) * T::VS + 32 * hi);
   __builtin_amdgcn_sched_group_barrier(0x100, 4 * (D / 64), 0);  // K reads (two per fragment)
   __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 64), 0);  // QK MFMAs
+}
+
+// Softmax and P.V half of the tile whose scores are s (V^T rows at vb; first key key0; ck its
+// key-block scale). The V^T fragments are read first, so they arrive during the softmax.
+template <int D>
+__device__ __forceinline__ void fp8_soft_pv(Fp8Rows<D>& w, f32x16 (&s)[2], const unsigned char* vb, int64_t key0,
+                                            int64_t N, int lane, float ck) {
+  using T = Fp8Tile<D>;
+  const int l32 = lane & 31, hi = lane >> 5;
+  i32x8 vf[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) vf[dt] = lds_read_32b(vb + (32 * dt + l32) * T::VS + 32 * hi);
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);  // V reads
   if (key0 + 64 > N) {  // keys past the end of the sequence (the tile that holds the last token)
     const int valid = (int)(N - key0) - 4 * hi;
@@ -196,6 +203,15 @@ __device__ __forceinline__ void fp8_rows_tile(Fp8Rows<D>& w, const unsigned char
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) w.o[dt] = mfma_e4m3(vf[dt], pb, w.o[dt]);
   w.lsum = mfma_e4m3(w.ones, pb, w.lsum);
+}
+
+// one whole 64-key tile (K rows at kb, V^T rows at vb in LDS; first key key0; ck its scale)
+template <int D>
+__device__ __forceinline__ void fp8_rows_tile(Fp8Rows<D>& w, const unsigned char* kb, const unsigned char* vb,
+                                              int64_t key0, int64_t N, int lane, float ck) {
+  f32x16 s[2];
+  fp8_qk(w, kb, lane, s);
+  fp8_soft_pv(w, s, vb, key0, N, lane, ck);
 }
 
 // normalise by the row sum, apply the channel scales, store the row of query my_q (if < N)
