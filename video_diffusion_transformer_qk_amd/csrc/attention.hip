@@ -22,8 +22,9 @@
 // Pipeline: tile t+1 is fetched from global memory into registers while tile t is computed,
 // then stored to the other half of a double-buffered LDS tile (one barrier per tile). Dense:
 // 8 waves (256 queries) share each 64-key K/V tile, two waves per SIMD (256-register budget) so
-// one wave's MFMAs overlap the other's softmax. Block-sparse: a workgroup takes 4 consecutive
-// query blocks and walks the union of their kept key blocks (see attn_sparse_group_kernel).
+// one wave's MFMAs overlap the other's softmax. Block-sparse: a workgroup takes 4 query blocks
+// (consecutive, or one per frame at the same position with a group stride) and walks the union
+// of their kept key blocks (see attn_sparse_group_kernel).
 #include "device_util.h"
 #include "kernels.h"
 #include "sparse_union.h"
@@ -331,10 +332,12 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
            row_stride, false, hi);
 }
 
-// Block-sparse attention over groups of G consecutive query blocks per workgroup (2 waves per
-// block, 32 queries each). Neighbouring query blocks keep largely the same key blocks, so the
-// workgroup merges the G kept lists into their union (ascending key-block order, with a bit per
-// query block that keeps it) and loads each union tile into LDS once; a wave runs the tile only
+// Block-sparse attention over groups of G query blocks per workgroup (2 waves per block, 32
+// queries each; the blocks i, i+S, ..., i+(G-1)S of the group stride S, 1 for consecutive
+// blocks). Neighbouring query blocks (in the sequence or frame to frame) keep largely the same
+// key blocks, so the workgroup merges the G kept lists into their union (ascending key-block
+// order, with a bit per query block that keeps it) and loads each union tile into LDS once; a
+// wave runs the tile only
 // when its own block keeps it (a wave-uniform branch), otherwise it just joins the barrier.
 // Each wave therefore sees exactly its block's kept tiles in ascending order, the same
 // arithmetic as the one-block kernel on ascending lists. The union is built in windows of KW

@@ -291,8 +291,9 @@ __global__ __launch_bounds__(512, 2) void attn_fp8_dense_kernel(Fp8AttnArgs a) {
                a.lse != nullptr ? a.lse + bh * N : nullptr, a.v_scale + bh * D, my_q, N, rs, hi);
 }
 
-// Block-sparse over groups of 4 consecutive query blocks (2 waves each), walking the union of
-// their kept key blocks (see sparse_union.h); a wave runs a union tile only if its block keeps it.
+// Block-sparse over groups of 4 query blocks (2 waves each; blocks i, i+S, i+2S, i+3S of the
+// group stride S), walking the union of their kept key blocks (see sparse_union.h); a wave runs a
+// union tile only if its block keeps it.
 template <int D, int KW>
 __global__ __launch_bounds__(512, 2) void attn_fp8_sparse_kernel(Fp8AttnArgs a) {
   using T = Fp8Tile<D>;
