@@ -48,7 +48,9 @@ def parse():
                         "are whole blocks, else 1)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    p.add_argument("--no-extra", action="store_true", help="skip the flushed norm+RoPE runs")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip everything outside the step: flushed norm+RoPE, block ops, threshold mode, fp8, "
+                        "the 10 s and 15 s workloads and the context rates")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first copy 1 GiB once, so that memory counters of a known-size copy sit in the same trace")
     return p.parse_args()
@@ -347,6 +349,93 @@ def main():
             f"({components['fp8']['dense_tflops']:.0f} TFLOP/s), sparse {msp:.1f} ms "
             f"({components['fp8']['sparse_tflops_kept']:.0f} TFLOP/s kept)")
         del fws, fq, out_f
+
+    if not args.no_extra:
+        # the 10 s (12 heads, sparsity 0.75 and 0.80) and 15 s (12 heads, planted boxes, 0.75)
+        # workloads: dense attention against selection + block-sparse attention, one warm-up and
+        # the median of three runs each. The 10 s path starts with norm+RoPE; the 15 s path feeds
+        # the synthetic q, k straight to attention and selection.
+        del out_s, ws
+        for cid in (4, 5):
+            c2 = CONFIGS[cid]
+            x2 = make_inputs(c2, dev)
+            q2, k2, v2 = x2["q"], x2["k"], x2["v"]
+            b2, n2, h2, d2 = q2.shape
+            nb2 = (n2 + 63) // 64
+            gs2 = h3.frame_group_stride(c2.grid)
+            if cid == 4:
+                q2n, k2n = torch.empty_like(q2), torch.empty_like(k2)
+                h3.qk_norm_rope(q2, k2, x2["wq"], x2["wk"], c2.grid, c2.sections, c2.theta, c2.eps, out=(q2n, k2n))
+                q2, k2 = q2n, k2n
+            o2 = torch.empty_like(q2)
+            ws2 = torch.empty((h3.select_workspace_bytes(b2, h2, n2, d2),), dtype=torch.uint8, device=dev)
+            fl_dense = 4.0 * b2 * h2 * n2 * n2 * d2
+            td = []
+            for r in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                h3.dense_fwd(q2, k2, v2, out=o2)
+                e1.record()
+                torch.cuda.synchronize()
+                if r >= 1:
+                    td.append(elapsed_ms(e0, e1))
+            md = float(np.median(td))
+            rec = {"n_tokens": n2, "heads": h2, "grid": list(c2.grid), "dense_ms": md,
+                   "dense_tflops": fl_dense / (md * 1e-3) / 1e12, "group_stride": gs2}
+            for sp in c2.sparsities:
+                keep2 = h3.keep_count(nb2, sp)
+                idx2 = torch.empty((b2, h2, nb2, keep2), dtype=torch.int32, device=dev)
+                tsel, tsp = [], []
+                for r in range(4):
+                    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                    e0.record()
+                    h3.subblock_select(q2, k2, sp, workspace=ws2, out=idx2)
+                    e1.record()
+                    h3.block_sparse_fwd(q2, k2, v2, idx2, out=o2, group_stride=gs2)
+                    e2.record()
+                    torch.cuda.synchronize()
+                    if r >= 1:
+                        tsel.append(elapsed_ms(e0, e1))
+                        tsp.append(elapsed_ms(e1, e2))
+                msel, msp = float(np.median(tsel)), float(np.median(tsp))
+                fl_sp = 4.0 * b2 * h2 * nb2 * keep2 * 64 * 64 * d2
+                rec[f"s{sp:.2f}"] = {"keep": keep2, "select_ms": msel, "sparse_ms": msp,
+                                     "sparse_tflops_kept": fl_sp / (msp * 1e-3) / 1e12,
+                                     "sparse_frac_peak": fl_sp / (msp * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                     "speedup_vs_dense": md / (msel + msp)}
+                log(f"{c2.name}: dense {md:.1f} ms ({rec['dense_tflops']:.0f} TFLOP/s); sparsity {sp}: select "
+                    f"{msel:.2f} ms + sparse {msp:.1f} ms ({rec[f's{sp:.2f}']['sparse_tflops_kept']:.0f} TFLOP/s "
+                    f"kept), {md / (msel + msp):.2f}x faster than dense")
+                del idx2
+            components[c2.name] = rec
+            del x2, q2, k2, v2, o2, ws2
+        # context rates on the same device: a bf16 GEMM through torch (hipBLASLt) and a device copy
+        a_m = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+        b_m = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+        c_m = torch.empty((8192, 8192), device=dev, dtype=torch.bfloat16)
+        cp_src = torch.ones(1 << 30, dtype=torch.bfloat16, device=dev)   # 2 GiB
+        cp_dst = torch.empty_like(cp_src)
+        tg, tc = [], []
+        for r in range(8):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            torch.matmul(a_m, b_m, out=c_m)
+            e1.record()
+            cp_dst.copy_(cp_src)
+            e2.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                tg.append(elapsed_ms(e0, e1))
+                tc.append(elapsed_ms(e1, e2))
+        gemm_tf = 2.0 * 8192 ** 3 / (float(np.median(tg)) * 1e-3) / 1e12
+        copy_gbs = 2.0 * cp_src.numel() * 2 / (float(np.median(tc)) * 1e-3) / 1e9
+        components["context"] = {"torch_matmul_bf16_8192_tflops": gemm_tf,
+                                 "dense_frac_of_torch_matmul": dense_tf / gemm_tf,
+                                 "device_copy_2gib_gbs": copy_gbs,
+                                 "norm_rope_frac_of_copy": nr_gbs / copy_gbs}
+        log(f"context: torch.matmul bf16 8192^3 {gemm_tf:.0f} TFLOP/s (dense attention at "
+            f"{dense_tf / gemm_tf:.2f} of it); 2 GiB copy_ {copy_gbs:.0f} GB/s")
+        del a_m, b_m, c_m, cp_src, cp_dst
 
     roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel<128,8,2> (dense)",
                 "achieved": dense_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
