@@ -13,10 +13,11 @@
 // select over order-preserving 64-bit keys.
 //
 // Kernels:
-//  pool_kernel   grid (nB, heads, batch): 256 threads, 16-byte coalesced row reads, fp64 sums
-//                reduced through LDS in a fixed order -> means [B, H, nB, D] for q and k.
-//  score_kernel  grid (ceil(nB/64), ceil(nB/64), B*H): 64x64 tile of Qm . Km^T in fp64,
-//                D staged through LDS in chunks of 32, 4x4 outputs per thread.
+//  pool_kernel   grid (heads * nB, 1, batch): 256 threads, 16-byte coalesced row reads (all
+//                issued before the sums), fp64 sums reduced through LDS in a fixed order ->
+//                means [B, H, nB, D] for q and k.
+//  score_kernel  grid (ceil(nB/T), ceil(nB/T), B*H), T = 64 or 128: a T x T tile of Qm . Km^T on
+//                the fp64 MFMA (v_mfma_f64_16x16x4f64), D staged through LDS in chunks of 32.
 //  topk_kernel   grid (nB, heads, batch): one row of nB scores -> LDS keys -> 8-pass MSB radix
 //                select of the keep-th largest key -> ordered compaction of the kept indices.
 #include "device_util.h"
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
   const int tl = tid / PAIRS;
   const int tensor = pair / CH;
   const int chunk = pair % CH;
-  const int j = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const int head = (int)(blockIdx.x % (unsigned)a.heads), j = (int)(blockIdx.x / (unsigned)a.heads), b = blockIdx.z;
   const int64_t N = a.n_tokens;
   const int64_t row_stride = (int64_t)a.heads * D;
   const int64_t t0 = (int64_t)j * a.block_size;
@@ -47,12 +48,21 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
   const uint16_t* src = (tensor == 0 ? a.q : a.k) + ((int64_t)b * N) * row_stride + (int64_t)head * D + chunk * 8;
 
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t t = t0 + tl; t < t1; t += TL) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(src + t * row_stride);
+  constexpr int R = 64 / TL;  // rows per thread: blocks are 64 tokens (the entry points accept no other size)
+  u32x4 w[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int64_t t = t0 + tl + (int64_t)i * TL;
+    w[i] = u32x4{0u, 0u, 0u, 0u};
+    if (t < t1) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + t * row_stride));
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (t0 + tl + (int64_t)i * TL >= t1) break;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += (double)bf16_lo(w[e]);
-      acc[2 * e + 1] += (double)bf16_hi(w[e]);
+      acc[2 * e] += (double)bf16_lo(w[i][e]);
+      acc[2 * e + 1] += (double)bf16_hi(w[i][e]);
     }
   }
 #pragma unroll
@@ -71,54 +81,71 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
   }
 }
 
-constexpr int kScoreTile = 64;
-constexpr int kScoreDc = 32;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
+// Qm . Km^T on the fp64 matrix cores. v_mfma_f64_16x16x4f64 takes A[i][k] from lane i + 16k and
+// B[k][j] from lane j + 16k, and returns D[4r + l/16][l%16] in register r of lane l. A workgroup
+// of 4 waves computes a TILE x TILE block of scores, each wave a (TILE/2)^2 quarter as
+// (TILE/32)^2 16x16 tiles. Both operands are staged through LDS as [row][d] with a row stride of
+// DC + 4 doubles, so the 16 rows x 4 k of an operand read fall in 2 passes over the 64 banks.
+template <int D, int TILE, int DC>
 __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
-  __shared__ double qs[kScoreDc][kScoreTile + 1];
-  __shared__ double ks[kScoreDc][kScoreTile + 1];
-  const int tid = threadIdx.x;
-  const int tx = tid % 16, ty = tid / 16;  // 4 rows (i) x 4 cols (j) each
+  constexpr int LD = DC + 4;
+  constexpr int RT = TILE / 32;  // 16x16 tiles per wave per dimension
+  __shared__ __attribute__((aligned(16))) double qs[TILE * LD];
+  __shared__ __attribute__((aligned(16))) double ks[TILE * LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, kq = lane >> 4;
   const int64_t bh = blockIdx.z;
   const int nb = a.n_blocks;
-  const int i0 = blockIdx.y * kScoreTile, j0 = blockIdx.x * kScoreTile;
+  const int i0 = blockIdx.y * TILE, j0 = blockIdx.x * TILE;
+  const int rb = (wave >> 1) * (TILE / 2), cb = (wave & 1) * (TILE / 2);
   const double* qm = a.q_mean + bh * (int64_t)nb * D;
   const double* km = a.k_mean + bh * (int64_t)nb * D;
-  double acc[4][4] = {};
-  for (int dc = 0; dc < D; dc += kScoreDc) {
-    // load 64 x 32 chunks of Qm and Km, transposed into [d][row]
-    for (int e = tid; e < kScoreTile * kScoreDc; e += 256) {
-      const int r = e / kScoreDc, d = e % kScoreDc;
+  f64x4 acc[RT][RT];
+#pragma unroll
+  for (int u = 0; u < RT; ++u)
+#pragma unroll
+    for (int w = 0; w < RT; ++w) acc[u][w] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int dc = 0; dc < D; dc += DC) {
+    // stage TILE x DC of Qm and Km, 16 bytes per thread and step (rows past nb repeat the last)
+#pragma unroll
+    for (int e = tid; e < TILE * DC / 2; e += 256) {
+      const int r = e / (DC / 2), c2 = e % (DC / 2);
       const int qi = i0 + r < nb ? i0 + r : nb - 1;
       const int kj = j0 + r < nb ? j0 + r : nb - 1;
-      qs[d][r] = qm[(int64_t)qi * D + dc + d];
-      ks[d][r] = km[(int64_t)kj * D + dc + d];
+      *reinterpret_cast<double2*>(&qs[r * LD + 2 * c2]) = *reinterpret_cast<const double2*>(qm + (int64_t)qi * D + dc + 2 * c2);
+      *reinterpret_cast<double2*>(&ks[r * LD + 2 * c2]) = *reinterpret_cast<const double2*>(km + (int64_t)kj * D + dc + 2 * c2);
     }
     __syncthreads();
-#pragma unroll 8
-    for (int d = 0; d < kScoreDc; ++d) {
-      double qv[4], kv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) { qv[u] = qs[d][ty + 16 * u]; kv[u] = ks[d][tx + 16 * u]; }
+    for (int kk = 0; kk < DC / 4; ++kk) {
+      double av[RT], bv[RT];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < RT; ++u) {
+        av[u] = qs[(rb + 16 * u + l16) * LD + 4 * kk + kq];
+        bv[u] = ks[(cb + 16 * u + l16) * LD + 4 * kk + kq];
+      }
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc[u][w] = fma(qv[u], kv[w], acc[u][w]);
+      for (int u = 0; u < RT; ++u)
+#pragma unroll
+        for (int w = 0; w < RT; ++w) acc[u][w] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[w], acc[u][w], 0, 0, 0);
     }
     __syncthreads();
   }
   double* out = a.scores + bh * (int64_t)nb * nb;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = i0 + ty + 16 * u;
-    if (i >= nb) continue;
+  for (int u = 0; u < RT; ++u)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int j = j0 + tx + 16 * w;
-      if (j < nb) out[(int64_t)i * nb + j] = acc[u][w];
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + rb + 16 * u + 4 * r + kq;
+      if (i >= nb) continue;
+#pragma unroll
+      for (int w = 0; w < RT; ++w) {
+        const int j = j0 + cb + 16 * w + l16;
+        if (j < nb) __builtin_nontemporal_store(acc[u][w][r], out + (int64_t)i * nb + j);
+      }
     }
-  }
 }
 
 // order-preserving map of a double to uint64 (larger double -> larger key); -0 is folded to +0
@@ -332,14 +359,22 @@ void launch_subblock_select(const SelectArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(topk_kernel, g3, dim3(kTopkThreads), lds, stream, a);
 }
 
+template <int TILE>
+void launch_scores(const SelectArgs& a, hipStream_t stream) {
+  const unsigned tiles = (unsigned)((a.n_blocks + TILE - 1) / TILE);
+  const dim3 gs(tiles, tiles, (unsigned)(a.batch * a.heads));
+  if (a.head_dim == 128) hipLaunchKernelGGL((score_kernel<128, TILE, 32>), gs, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((score_kernel<64, TILE, 32>), gs, dim3(256), 0, stream, a);
+}
+
 static void launch_pool_and_scores(const SelectArgs& a, hipStream_t stream) {
-  const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
+  const dim3 g3((unsigned)a.n_blocks * (unsigned)a.heads, 1, (unsigned)a.batch);
   if (a.head_dim == 128) hipLaunchKernelGGL(pool_kernel<128>, g3, dim3(kPoolThreads), 0, stream, a);
   else hipLaunchKernelGGL(pool_kernel<64>, g3, dim3(kPoolThreads), 0, stream, a);
-  const unsigned tiles = (unsigned)((a.n_blocks + kScoreTile - 1) / kScoreTile);
-  const dim3 gs(tiles, tiles, (unsigned)(a.batch * a.heads));
-  if (a.head_dim == 128) hipLaunchKernelGGL(score_kernel<128>, gs, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(score_kernel<64>, gs, dim3(256), 0, stream, a);
+  // 128 x 128 score tiles once there are enough of them (half the operand staging per score);
+  // 64 x 64 for short rows, where 128-wide tiles leave most of the chip idle
+  if (a.n_blocks >= 1024) launch_scores<128>(a, stream);
+  else launch_scores<64>(a, stream);
 }
 
 void launch_threshold_count(const SelectArgs& a, hipStream_t stream) {
