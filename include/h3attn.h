@@ -105,7 +105,8 @@ h3attn_status h3attn_dense_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const
  * h3attn_keep_count(nB, sparsity). workspace: device buffer of at least
  * h3attn_select_workspace_bytes(...) bytes, 256-byte aligned; its contents are scratch.
  * Errors: bad pointers/sizes, sparsity outside [0,1), keep mismatch, workspace too small ->
- * INVALID_ARGUMENT; head_dim not 64/128 or block_size != 64 -> UNSUPPORTED. */
+ * INVALID_ARGUMENT; head_dim not 64/128, block_size != 64 or nB > 19968 (a row of float64
+ * scores must fit in one CU's LDS) -> UNSUPPORTED. */
 h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
                                      int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
                                      int32_t block_size, double sparsity, int32_t keep,
@@ -156,8 +157,8 @@ size_t h3attn_threshold_workspace_bytes(int32_t batch, int32_t heads, int64_t n_
                                         int32_t head_dim, int32_t block_size);
 
 /* Pass 1: pools, scores, per-row thresholds and counts; writes row_ptr (int64, B*heads*nB + 1
- * entries, row_ptr[0] = 0, last entry = total kept count). Errors: as h3attn_subblock_select,
- * plus tau < 0 or NaN -> INVALID_ARGUMENT. */
+ * entries, row_ptr[0] = 0, last entry = total kept count). Errors: as h3attn_subblock_select
+ * (nB > 19968 -> UNSUPPORTED included), plus tau < 0 or NaN -> INVALID_ARGUMENT. */
 h3attn_status h3attn_subblock_threshold_count(const h3attn_bf16* q, const h3attn_bf16* k,
                                               int32_t batch, int32_t heads, int64_t n_tokens,
                                               int32_t head_dim, int32_t block_size, double tau,

@@ -118,6 +118,9 @@ def test_select_and_sparse_validation(lib):
     assert call(ws=ws + 16) == 1 and "256-byte" in _err(lib)
     assert call(idx=None) == 1
     assert call(d=72) == 2
+    # a row of nB float64 scores must fit in one CU's LDS: nB <= (160 KiB - 4 KiB) / 8 = 19968
+    assert call(n=19969 * 64) == 2 and "LDS" in _err(lib)
+    assert call(n=19968 * 64) == 1 and "LDS" not in _err(lib)  # passes the row check, fails on keep
     g = lib.h3attn_block_sparse_fwd
     P = (0x10000, 0x20000, 0x30000)
     assert g(*P, 0x40000, 0, 0x50000, None, 1, 2, 640, 64, 64, None) == 1 and "keep" in _err(lib)
@@ -141,7 +144,9 @@ def test_threshold_validation(lib):
     assert f(0x10000, 0x20000, 1, 2, 640, 64, 64, 0.5, 0x30004, ws, nbytes, None) == 1
     assert f(0x10000, 0x20000, 1, 2, 640, 64, 64, 0.5, 0x30000, ws, nbytes - 8, None) == 1 and "workspace" in _err(lib)
     assert f(0x10000, 0x20000, 1, 2, 640, 64, 32, 0.5, 0x30000, ws, nbytes, None) == 2
+    assert f(0x10000, 0x20000, 1, 2, 19969 * 64, 64, 64, 0.5, 0x30000, ws, nbytes, None) == 2 and "LDS" in _err(lib)
     g = lib.h3attn_subblock_threshold_fill
+    assert g(1, 2, 19969 * 64, 64, 64, 0x30000, 0x40000, 10, ws, nbytes, None) == 2 and "LDS" in _err(lib)
     assert g(1, 2, 640, 64, 64, 0x30000, 0x40000, -1, ws, nbytes, None) == 1
     assert g(1, 2, 640, 64, 64, None, 0x40000, 10, ws, nbytes, None) == 1
     assert g(1, 2, 640, 64, 64, 0x30000, None, 10, ws, nbytes, None) == 1

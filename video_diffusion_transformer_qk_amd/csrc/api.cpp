@@ -178,7 +178,7 @@ h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
   if (!(sparsity >= 0.0 && sparsity < 1.0)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "sparsity must be in [0, 1) (got %g)", sparsity);
   if ((int64_t)batch * heads > 65535) return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads must be <= 65535");
   const int64_t nb = (n_tokens + block_size - 1) / block_size;
-  if (nb * 8 + 4096 > 160 * 1024)
+  if (nb * 8 > h3attn::kSelectRowLdsBytes)
     return fail(H3ATTN_ERR_UNSUPPORTED, "%lld blocks exceed the per-row LDS budget of the top-k kernel", (long long)nb);
   const int32_t want = h3attn_keep_count((int32_t)nb, sparsity);
   if (keep != want) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep %d does not match keep_count(%lld, %g) = %d", keep, (long long)nb, sparsity, want);
@@ -253,6 +253,9 @@ static h3attn_status check_select_common(const h3attn_bf16* q, const h3attn_bf16
   if (block_size != 64) return fail(H3ATTN_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", block_size);
   if ((int64_t)batch * heads > 65535) return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads must be <= 65535");
   *nb_out = (n_tokens + block_size - 1) / block_size;
+  if (*nb_out * 8 > h3attn::kSelectRowLdsBytes)
+    return fail(H3ATTN_ERR_UNSUPPORTED, "%lld blocks exceed the per-row LDS budget of the threshold kernels",
+                (long long)*nb_out);
   return H3ATTN_OK;
 }
 

@@ -48,6 +48,10 @@ void launch_dense_fwd(const AttnArgs& a, hipStream_t stream);
 void launch_block_sparse_fwd(const AttnArgs& a, hipStream_t stream);
 void launch_block_sparse_csr_fwd(const AttnArgs& a, hipStream_t stream);
 
+// Dynamic LDS for one row of nB float64 scores (the top-k keys, the threshold fill's staged row):
+// what a CU's 160 KB leaves after the kernels' static LDS; rows longer than this are refused.
+constexpr int64_t kSelectRowLdsBytes = 160 * 1024 - 4096;
+
 struct SelectArgs {
   const uint16_t* q;
   const uint16_t* k;

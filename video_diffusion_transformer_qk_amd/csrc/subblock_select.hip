@@ -158,6 +158,25 @@ __device__ __forceinline__ uint64_t order_key(double x) {
 constexpr int kTopkThreads = 256;
 static_assert(kTopkThreads == 256, "one histogram bin per thread");
 
+// Calls f(j, row[j]) for this thread's j = tid, tid + 256, ... < n, issuing 8 loads at a time so
+// that a thread has several in flight (a plain loop waits for each load before the next).
+template <typename F>
+__device__ __forceinline__ void for_row(const double* row, int n, F f) {
+  for (int j0 = threadIdx.x; j0 < n; j0 += 8 * kTopkThreads) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * kTopkThreads;
+      v[u] = j < n ? __builtin_nontemporal_load(row + j) : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * kTopkThreads;
+      if (j < n) f(j, v[u]);
+    }
+  }
+}
+
 // block-wide exclusive prefix sum of one int per thread; returns the block total in *total
 __device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= 4 ints */) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -227,7 +246,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   const int i = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const int64_t row = ((int64_t)b * a.heads + head) * nb + i;
   const double* sc = a.scores + row * nb;
-  for (int j = tid; j < nb; j += kTopkThreads) keys[j] = order_key(sc[j]);
+  for_row(sc, nb, [&](int j, double x) { keys[j] = order_key(x); });
 
   // Digit by digit from the top: the 8-bit digit of the keep-th largest key is the bin where the
   // count of keys in higher bins first reaches k_rem (thread t owns bin 255 - t, so a block
@@ -275,7 +294,7 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_count_kernel(SelectArg
   const int64_t row = ((int64_t)blockIdx.z * a.heads + blockIdx.y) * nb + blockIdx.x;
   const double* sc = a.scores + row * nb;
   double m = -INFINITY;
-  for (int j = tid; j < nb; j += kTopkThreads) m = fmax(m, sc[j]);
+  for_row(sc, nb, [&](int, double x) { m = fmax(m, x); });
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
   if (lane == 0) red[wave] = m;
@@ -285,7 +304,7 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_count_kernel(SelectArg
   for (int w = 1; w < kTopkThreads / 64; ++w) m = fmax(m, red[w]);
   const double thr = m - a.tau_raw;
   int c = 0;
-  for (int j = tid; j < nb; j += kTopkThreads) c += sc[j] >= thr;
+  for_row(sc, nb, [&](int, double x) { c += x >= thr; });
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
   if (lane == 0) cnt_red[wave] = c;
@@ -326,7 +345,11 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_fill_kernel(SelectArgs
   const int tid = threadIdx.x;
   const int nb = a.n_blocks;
   const int64_t row = ((int64_t)blockIdx.z * a.heads + blockIdx.y) * nb + blockIdx.x;
-  const double* sc = a.scores + row * nb;
+  // the row is staged in LDS with coalesced loads; the ordered scans below walk contiguous runs
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  double* sc = reinterpret_cast<double*>(smem);
+  for_row(a.scores + row * nb, nb, [&](int j, double x) { sc[j] = x; });
+  __syncthreads();
   const double thr = a.row_thr[row];
   const int64_t start = a.row_ptr[row];
   const int per = (nb + kTopkThreads - 1) / kTopkThreads;
@@ -353,7 +376,7 @@ void launch_subblock_select(const SelectArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)a.n_blocks * sizeof(uint64_t);
   static const bool lds_ok = [] {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024) == hipSuccess;
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSelectRowLdsBytes) == hipSuccess;
   }();
   (void)lds_ok;
   hipLaunchKernelGGL(topk_kernel, g3, dim3(kTopkThreads), lds, stream, a);
@@ -387,7 +410,13 @@ void launch_threshold_count(const SelectArgs& a, hipStream_t stream) {
 
 void launch_threshold_fill(const SelectArgs& a, hipStream_t stream) {
   const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
-  hipLaunchKernelGGL(threshold_fill_kernel, g3, dim3(kTopkThreads), 0, stream, a);
+  const size_t lds = (size_t)a.n_blocks * sizeof(double);
+  static const bool lds_ok = [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(threshold_fill_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSelectRowLdsBytes) == hipSuccess;
+  }();
+  (void)lds_ok;
+  hipLaunchKernelGGL(threshold_fill_kernel, g3, dim3(kTopkThreads), lds, stream, a);
 }
 
 }  // namespace h3attn
