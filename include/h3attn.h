@@ -142,6 +142,17 @@ h3attn_status h3attn_block_sparse_grouped_fwd(const h3attn_bf16* q, const h3attn
                                               int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
                                               int32_t block_size, int32_t group_stride, hipStream_t stream);
 
+/* Validation of a caller-built kept set for h3attn_block_sparse_fwd / _grouped_fwd /
+ * h3attn_fp8_block_sparse_fwd, which take it as given (behaviour for bad indices is undefined).
+ * For every row r = (b * heads + head) * n_blocks + i of block_idx ([batch, heads, n_blocks,
+ * keep] int32) writes row_flags[r] (uint8, device, caller-owned): 0 for a valid row, else bit 0
+ * (an index outside [0, n_blocks)) | bit 1 (an index repeated in the row). Asynchronous on
+ * `stream`; the caller reads the flags back. Errors: null or misaligned pointers, sizes <= 0,
+ * keep outside [1, n_blocks] -> INVALID_ARGUMENT; n_blocks > 2^20 or batch*heads*n_blocks >= 2^31
+ * -> UNSUPPORTED. */
+h3attn_status h3attn_check_block_idx(const int32_t* block_idx, int32_t batch, int32_t heads, int32_t n_blocks,
+                                     int32_t keep, uint8_t* row_flags, hipStream_t stream);
+
 /* ---- Threshold-mode SubBlock selection with a variable number of kept blocks per row ----
  * "MiniMax-H3 在 8×H200 上基准测试…" (chat-gpts.plus), section "事件核心" describes SubBlock as
  * skipping the attention blocks that score below a threshold. The pages give no rule; this mode
@@ -189,6 +200,15 @@ h3attn_status h3attn_block_sparse_csr_grouped_fwd(const h3attn_bf16* q, const h3
                                                   int32_t batch, int32_t heads, int64_t n_tokens,
                                                   int32_t head_dim, int32_t block_size, int32_t group_stride,
                                                   hipStream_t stream);
+
+/* Validation of caller-built CSR kept sets for the two CSR calls above: for every row r of the
+ * batch*heads*n_blocks rows writes row_flags[r] (uint8, device, caller-owned): 0 for a valid row,
+ * else bit 0 (an index outside [0, n_blocks)) | bit 1 (an index repeated in the row) | bit 2
+ * (row_ptr[r] < 0, row_ptr[r+1] < row_ptr[r] or row_ptr[r+1] > col_capacity, the number of int32
+ * entries col_idx holds; the row's indices are then not read). Asynchronous on `stream`.
+ * Errors: as h3attn_check_block_idx (col_idx may be NULL only when col_capacity is 0). */
+h3attn_status h3attn_check_csr(const int64_t* row_ptr, const int32_t* col_idx, int64_t col_capacity, int32_t batch,
+                               int32_t heads, int32_t n_blocks, uint8_t* row_flags, hipStream_t stream);
 
 /* ---- The other fused per-block ops of the lossless runtime ----
  * "MiniMax-H3 的 6.24 倍，不能直接算成六倍产能" (xiaodao.ai), section "先把近两倍的免费收益拿走":

@@ -235,3 +235,21 @@ def test_fp8_workspace_bytes_and_validation(lib):
     assert h(q8, k8, v8t, sq, sk, sv, idx, 3, out, None, 1, 2, 128, 64, 64, 1, None) == 1 and "keep" in _err(lib)
     assert h(q8, k8, v8t, sq, sk, sv, idx + 2, 1, out, None, 1, 2, 128, 64, 64, 1, None) == 1 and "aligned" in _err(lib)
     assert h(q8, k8, v8t, sq, sk, sv, idx, 1, out, None, 1, 2, 128, 64, 64, 3, None) == 1 and "group_stride" in _err(lib)
+
+
+def test_kept_set_check_validation(lib):
+    f = lib.h3attn_check_block_idx
+    assert f(None, 1, 2, 10, 3, 0x2000, None) == 1 and "block_idx" in _err(lib)
+    assert f(0x1002, 1, 2, 10, 3, 0x2000, None) == 1 and "aligned" in _err(lib)
+    assert f(0x1000, 1, 2, 10, 3, None, None) == 1 and "row_flags" in _err(lib)
+    assert f(0x1000, 1, 2, 10, 0, 0x2000, None) == 1 and "keep" in _err(lib)
+    assert f(0x1000, 1, 2, 10, 11, 0x2000, None) == 1 and "keep" in _err(lib)
+    assert f(0x1000, 0, 2, 10, 3, 0x2000, None) == 1
+    assert f(0x1000, 1, 2, (1 << 20) + 1, 3, 0x2000, None) == 2 and "n_blocks" in _err(lib)
+    g = lib.h3attn_check_csr
+    assert g(None, 0x1000, 5, 1, 2, 10, 0x2000, None) == 1 and "row_ptr" in _err(lib)
+    assert g(0x1004, 0x1000, 5, 1, 2, 10, 0x2000, None) == 1 and "8-byte" in _err(lib)
+    assert g(0x1000, None, 5, 1, 2, 10, 0x2000, None) == 1 and "col_idx" in _err(lib)
+    assert g(0x1000, 0x1000, -1, 1, 2, 10, 0x2000, None) == 1 and "col_capacity" in _err(lib)
+    assert g(0x1000, 0x1000, 5, 1, 2, 10, None, None) == 1 and "row_flags" in _err(lib)
+    assert g(0x1000, 0x1000, 5, 1, 2, (1 << 20) + 1, 0x2000, None) == 2

@@ -392,6 +392,52 @@ def test_threshold_select_and_csr_attention_full(h3, n, d):
         assert np.abs(f64(lse) - rl).max() <= LSE_MAX_ABS
 
 
+def test_kept_set_check_flags_exactly_the_bad_rows(h3):
+    """Top-k and CSR kept sets from the selection kernels are valid; planted bad rows (an index out
+    of range, a repeated index, a decreasing or overlong CSR range) are flagged with their reason
+    and nothing else is. With validate=True the attention calls raise before any launch."""
+    b, n, h, d = 1, 64 * 10, 2, 64
+    nb = 10
+    c = random_case(b, n, h, d, seed=77, device=DEV)
+    idx = h3.subblock_select(c["q"], c["k"], 0.5)
+    fl = h3.check_block_idx(idx)
+    _sync()
+    assert fl.shape == (b, h, nb) and int(fl.count_nonzero()) == 0
+    bad = idx.clone()
+    bad[0, 1, 3, 0] = nb          # out of range
+    bad[0, 0, 2, 1] = bad[0, 0, 2, 0]  # repeated
+    bad[0, 1, 7, 2] = -1          # out of range
+    bad[0, 0, 9, 0] = nb + 5
+    bad[0, 0, 9, 1] = bad[0, 0, 9, 2]  # both reasons in one row
+    fl = h3.check_block_idx(bad).cpu()
+    want = torch.zeros((b, h, nb), dtype=torch.uint8)
+    want[0, 1, 3] = 1
+    want[0, 0, 2] = 2
+    want[0, 1, 7] = 1
+    want[0, 0, 9] = 3
+    assert torch.equal(fl, want), fl
+    with pytest.raises(h3.H3AttnError):
+        h3.block_sparse_fwd(c["q"], c["k"], c["v"], bad, validate=True)
+    h3.block_sparse_fwd(c["q"], c["k"], c["v"], idx, validate=True)  # valid: runs
+    # CSR: threshold-mode rows are valid
+    rp, ci = h3.subblock_select_threshold(c["q"], c["k"], 0.3)
+    assert int(h3.check_csr(rp, ci, b, h, nb).count_nonzero()) == 0
+    # hand-built rows over b = 1, h = 2, nB = 4 (8 rows), col_idx capacity 9
+    rows = [[1, 3], [], [0, 0, 2], [3], [0, 4], [2, 1, 0], [], [1]]
+    ptr = [0]
+    for r in rows:
+        ptr.append(ptr[-1] + len(r))
+    rp2 = torch.tensor(ptr, dtype=torch.int64)
+    ci2 = torch.tensor([x for r in rows for x in r], dtype=torch.int32)
+    rp2[7] = 20                   # row 6 runs past col_idx (capacity 9), row 7 ends below its start
+    fl = h3.check_csr(rp2.to(DEV), ci2.to(DEV), 1, 2, 4).cpu()
+    assert fl.tolist() == [0, 0, 2, 0, 1, 0, 4, 4], fl.tolist()
+    x = random_case(1, 256, 2, 64, seed=78, device=DEV)
+    with pytest.raises(h3.H3AttnError):
+        h3.block_sparse_csr_fwd(x["q"], x["k"], x["v"], rp2.to(DEV), ci2.to(DEV), validate=True)
+    log("kept-set checks: valid sets pass, every planted bad row flagged with its reason")
+
+
 def test_csr_keep_all_is_bitwise_dense_and_empty_rows(h3):
     c = random_case(1, 64 * 6, 2, 128, seed=21, device=DEV)
     rp, ci = h3.subblock_select_threshold(c["q"], c["k"], float("inf"))

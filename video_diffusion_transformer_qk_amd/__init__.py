@@ -15,10 +15,11 @@ from ._lib import (LIB_PATH, SIGNATURES, H3AttnError, block_sparse_csr_fwd, bloc
                    dense_fwd, keep_count, load_library, qk_norm_rope, select_workspace_bytes,
                    subblock_select, subblock_select_threshold, threshold_workspace_bytes, version,
                    adaln_modulate, swiglu, residual_change, CacheGate, Fp8QKV, fp8_workspace_bytes,
-                   fp8_quantize, fp8_dense_fwd, fp8_block_sparse_fwd, frame_group_stride)
+                   fp8_quantize, fp8_dense_fwd, fp8_block_sparse_fwd, frame_group_stride, check_block_idx, check_csr)
 
 __all__ = ["qk_norm_rope", "dense_fwd", "subblock_select", "block_sparse_fwd", "keep_count",
            "select_workspace_bytes", "subblock_select_threshold", "block_sparse_csr_fwd",
            "threshold_workspace_bytes", "adaln_modulate", "swiglu",
            "residual_change", "CacheGate", "Fp8QKV", "fp8_workspace_bytes", "fp8_quantize",
-           "fp8_dense_fwd", "fp8_block_sparse_fwd", "frame_group_stride", "version", "H3AttnError", "load_library"]
+           "fp8_dense_fwd", "fp8_block_sparse_fwd", "frame_group_stride", "check_block_idx", "check_csr", "version",
+           "H3AttnError", "load_library"]

@@ -50,6 +50,8 @@ SIGNATURES = {
                                                    _P]),
     "h3attn_block_sparse_csr_grouped_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32,
                                                            _I32, _I32, _P]),
+    "h3attn_check_block_idx": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P]),
+    "h3attn_check_csr": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _P, _P]),
     "h3attn_adaln_modulate": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I32, ctypes.c_float, _P]),
     "h3attn_swiglu": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I64, _I64, _P]),
     "h3attn_residual_workspace_bytes": (ctypes.c_size_t, [_I64]),
@@ -218,11 +220,47 @@ def subblock_select(q: torch.Tensor, k: torch.Tensor, sparsity: float, block_siz
     return idx
 
 
+def check_block_idx(block_idx: torch.Tensor) -> torch.Tensor:
+    """Per-row validity flags of a kept set [B, heads, nB, keep] (uint8 [B, heads, nB]: 0 valid, bit 0
+    an index outside [0, nB), bit 1 a repeated index), computed on the device."""
+    lib = load_library()
+    _need(block_idx, "block_idx", torch.int32, 4)
+    b, h, nb, keep = block_idx.shape
+    flags = torch.empty((b, h, nb), dtype=torch.uint8, device=block_idx.device)
+    _check(lib.h3attn_check_block_idx(block_idx.data_ptr(), b, h, nb, keep, flags.data_ptr(), _stream()))
+    return flags
+
+
+def check_csr(row_ptr: torch.Tensor, col_idx: torch.Tensor, batch: int, heads: int, n_blocks: int) -> torch.Tensor:
+    """Per-row validity flags of CSR kept sets (uint8 [B*heads*nB]: bits 0 and 1 as check_block_idx, bit 2
+    a row whose range is decreasing or runs past col_idx)."""
+    lib = load_library()
+    _need(row_ptr, "row_ptr", torch.int64, 1)
+    _need(col_idx, "col_idx", torch.int32, 1)
+    rows = batch * heads * n_blocks
+    if row_ptr.numel() != rows + 1:
+        raise ValueError(f"row_ptr must have B*heads*nB + 1 = {rows + 1} entries")
+    flags = torch.empty((rows,), dtype=torch.uint8, device=row_ptr.device)
+    _check(lib.h3attn_check_csr(row_ptr.data_ptr(), _ptr(col_idx if col_idx.numel() > 0 else None), col_idx.numel(),
+                                batch, heads, n_blocks, flags.data_ptr(), _stream()))
+    return flags
+
+
+def _raise_if_flagged(flags: torch.Tensor, what: str):
+    bad = torch.nonzero(flags.reshape(-1)).reshape(-1)
+    if bad.numel() > 0:
+        r = int(bad[0])
+        raise H3AttnError(1, f"{what}: {bad.numel()} invalid row(s), first row {r} (flags {int(flags.reshape(-1)[r])}: "
+                             "1 out of range, 2 repeated index, 4 bad row range)")
+
+
 def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: torch.Tensor,
                      block_size: int = 64, return_lse: bool = False, out: Optional[torch.Tensor] = None,
-                     group_stride: int = 1):
+                     group_stride: int = 1, validate: bool = False):
     """Attention of each 64-query block over its kept key blocks only. group_stride picks which
-    four query blocks share a workgroup (i, i+S, i+2S, i+3S); it changes speed, never the result."""
+    four query blocks share a workgroup (i, i+S, i+2S, i+3S); it changes speed, never the result.
+    validate=True first checks every kept-set row on the device (waits for the result) and raises
+    H3AttnError on an index outside [0, nB) or a repeated one."""
     lib = load_library()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16, 4)
@@ -234,6 +272,8 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_id
     if tuple(block_idx.shape[:3]) != (b, h, nb):
         raise ValueError(f"block_idx must be [B, heads, nB, keep] = [{b}, {h}, {nb}, keep]")
     keep = block_idx.shape[3]
+    if validate:
+        _raise_if_flagged(check_block_idx(block_idx), "block_idx")
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", torch.bfloat16, 4)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
@@ -279,8 +319,9 @@ def subblock_select_threshold(q: torch.Tensor, k: torch.Tensor, tau: float, bloc
 
 def block_sparse_csr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
                          col_idx: torch.Tensor, block_size: int = 64, return_lse: bool = False,
-                         out: Optional[torch.Tensor] = None, group_stride: int = 1):
-    """Block-sparse attention with a variable kept set per query block (CSR rows)."""
+                         out: Optional[torch.Tensor] = None, group_stride: int = 1, validate: bool = False):
+    """Block-sparse attention with a variable kept set per query block (CSR rows). validate=True
+    first checks every row on the device (as check_csr) and raises H3AttnError on a bad one."""
     lib = load_library()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16, 4)
@@ -292,6 +333,8 @@ def block_sparse_csr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_
     nb = -(-n // block_size)
     if row_ptr.numel() != b * h * nb + 1:
         raise ValueError(f"row_ptr must have B*heads*nB + 1 = {b * h * nb + 1} entries")
+    if validate:
+        _raise_if_flagged(check_csr(row_ptr, col_idx, b, h, nb), "CSR kept sets")
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", torch.bfloat16, 4)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
@@ -467,8 +510,9 @@ def fp8_dense_fwd(fq: Fp8QKV, return_lse: bool = False, out: Optional[torch.Tens
 
 
 def fp8_block_sparse_fwd(fq: Fp8QKV, block_idx: torch.Tensor, return_lse: bool = False,
-                         out: Optional[torch.Tensor] = None, group_stride: int = 1):
-    """Block-sparse attention on e4m3 tensors over the kept key blocks block_idx [B, heads, nB, keep]."""
+                         out: Optional[torch.Tensor] = None, group_stride: int = 1, validate: bool = False):
+    """Block-sparse attention on e4m3 tensors over the kept key blocks block_idx [B, heads, nB, keep]
+    (validate as in block_sparse_fwd)."""
     lib = load_library()
     b, n, h, d = _fp8_check(fq)
     _need(block_idx, "block_idx", torch.int32, 4)
@@ -476,6 +520,8 @@ def fp8_block_sparse_fwd(fq: Fp8QKV, block_idx: torch.Tensor, return_lse: bool =
     if tuple(block_idx.shape[:3]) != (b, h, nb):
         raise ValueError(f"block_idx must be [B, heads, nB, keep] = [{b}, {h}, {nb}, keep]")
     keep = block_idx.shape[3]
+    if validate:
+        _raise_if_flagged(check_block_idx(block_idx), "block_idx")
     o = torch.empty((b, n, h, d), dtype=torch.bfloat16, device=fq.q8.device) if out is None else out
     _need(o, "out", torch.bfloat16, 4)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=o.device) if return_lse else None

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libh3attn.so")
 SOURCES = ["qk_norm_rope.hip", "attention.hip", "attention_fp8.hip", "fp8_quant.hip", "subblock_select.hip",
-           "block_ops.hip", "cache_gate.hip", "api.cpp"]
+           "block_ops.hip", "cache_gate.hip", "index_check.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -376,6 +376,47 @@ h3attn_status h3attn_block_sparse_csr_grouped_fwd(const h3attn_bf16* q, const h3
                           heads, n_tokens, head_dim, block_size, group_stride, stream);
 }
 
+static h3attn_status check_rows_common(const uint8_t* row_flags, int32_t batch, int32_t heads, int32_t n_blocks) {
+  if (row_flags == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_flags is NULL");
+  if (batch <= 0 || heads <= 0 || n_blocks <= 0)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "batch, heads and n_blocks must be > 0");
+  if ((int64_t)n_blocks > h3attn::kIndexCheckLdsBytes * 8)
+    return fail(H3ATTN_ERR_UNSUPPORTED, "n_blocks must be at most %lld", (long long)(h3attn::kIndexCheckLdsBytes * 8));
+  if ((int64_t)batch * heads * n_blocks >= ((int64_t)1 << 31))
+    return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads*n_blocks must be below 2^31");
+  return H3ATTN_OK;
+}
+
+h3attn_status h3attn_check_block_idx(const int32_t* block_idx, int32_t batch, int32_t heads, int32_t n_blocks,
+                                     int32_t keep, uint8_t* row_flags, hipStream_t stream) {
+  if (block_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is NULL");
+  if (reinterpret_cast<uintptr_t>(block_idx) & 3u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is not 4-byte aligned");
+  h3attn_status st = check_rows_common(row_flags, batch, heads, n_blocks);
+  if (st != H3ATTN_OK) return st;
+  if (keep < 1 || keep > n_blocks) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep must be in [1, %d] (got %d)", n_blocks, keep);
+  h3attn::IndexCheckArgs a{};
+  a.block_idx = block_idx; a.row_flags = row_flags; a.rows = (int64_t)batch * heads * n_blocks;
+  a.n_blocks = n_blocks; a.keep = keep;
+  h3attn::launch_check_topk_rows(a, stream);
+  return check_launch("h3attn_check_block_idx");
+}
+
+h3attn_status h3attn_check_csr(const int64_t* row_ptr, const int32_t* col_idx, int64_t col_capacity, int32_t batch,
+                               int32_t heads, int32_t n_blocks, uint8_t* row_flags, hipStream_t stream) {
+  if (row_ptr == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_ptr is NULL");
+  if (reinterpret_cast<uintptr_t>(row_ptr) & 7u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "row_ptr is not 8-byte aligned");
+  if (col_capacity < 0) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "col_capacity must be >= 0");
+  if (col_capacity > 0 && col_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "col_idx is NULL");
+  if (reinterpret_cast<uintptr_t>(col_idx) & 3u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "col_idx is not 4-byte aligned");
+  h3attn_status st = check_rows_common(row_flags, batch, heads, n_blocks);
+  if (st != H3ATTN_OK) return st;
+  h3attn::IndexCheckArgs a{};
+  a.block_idx = col_idx; a.row_ptr = row_ptr; a.row_flags = row_flags;
+  a.rows = (int64_t)batch * heads * n_blocks; a.col_capacity = col_capacity; a.n_blocks = n_blocks;
+  h3attn::launch_check_csr_rows(a, stream);
+  return check_launch("h3attn_check_csr");
+}
+
 h3attn_status h3attn_adaln_modulate(const h3attn_bf16* x, const float* shift, const float* scale,
                                     h3attn_bf16* out, int32_t batch, int64_t n_tokens, int32_t hidden,
                                     float eps, hipStream_t stream) {

@@ -133,6 +133,20 @@ struct Fp8QuantArgs {
 
 constexpr int kFp8VChunk = 1024;  // tokens per V channel-maximum partial
 
+// Kept-set validation: one row per (b, head, query block); a bitmap of n_blocks bits in LDS.
+struct IndexCheckArgs {
+  const int32_t* block_idx;  // top-k rows [rows, keep], or the CSR col_idx
+  const int64_t* row_ptr;    // CSR only: [rows + 1]
+  uint8_t* row_flags;        // [rows]
+  int64_t rows;
+  int64_t col_capacity;      // CSR only: entries in col_idx
+  int32_t n_blocks, keep;
+};
+constexpr int64_t kIndexCheckLdsBytes = 128 * 1024;  // n_blocks <= 2^20
+
+void launch_check_topk_rows(const IndexCheckArgs& a, hipStream_t stream);
+void launch_check_csr_rows(const IndexCheckArgs& a, hipStream_t stream);
+
 void launch_fp8_quantize(const Fp8QuantArgs& a, hipStream_t stream);
 
 struct Fp8AttnArgs {
