@@ -113,7 +113,8 @@ void launch_residual_change(const ResidualArgs& a, hipStream_t stream);
 // ---- fp8 (OCP e4m3) attention ----
 // Quantised tensors: q8, k8 are [B, N, H, D] bytes (e4m3 codes of x / s, s the power-of-two
 // scale of the (b, head, 64-token block)); v8t is [B, H, D, nB*64] bytes: V transposed, each
-// 64-key block's keys stored in the order the P.V product consumes them (see fp8_key_slot), and
+// 64-key block's keys stored in the order the P.V product consumes them (key 32m + 8a + 4h + r at
+// slot 16 (2h + m) + 4a + r, r < 4, a < 4; the v8t layout comment in fp8_quant.hip derives it), and
 // keys past N zero; scales are float32 q_scale/k_scale [B, H, nB], v_scale [B, H, D].
 struct Fp8QuantArgs {
   const uint16_t* q;
