@@ -76,6 +76,23 @@ def measured_traffic(kernel_prefix: str):
     return None
 
 
+def provenance(cfg):
+    """What produced this line: library and runtime versions, the device, the first 16 hex digits
+    of each library source's sha256 (the tree is copied without version-control metadata) and the
+    input recipe."""
+    import hashlib
+    import video_diffusion_transformer_qk_amd as h3
+    from inputs import seed_for
+    csrc = os.path.join(ROOT, "video_diffusion_transformer_qk_amd", "csrc")
+    srcs = {}
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            srcs[f] = hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16]
+    return {"library": h3.version(), "torch": torch.__version__, "hip": torch.version.hip,
+            "device": torch.cuda.get_device_name(0), "sources_sha256": srcs,
+            "inputs": {"field": cfg.field, "seeds": {t: seed_for(cfg.id, t) for t in ("q", "k", "v", "wq", "wk")}}}
+
+
 def flush_caches(buf: torch.Tensor):
     buf.add_(1)  # rewrites 512 MB: evicts the 256 MB MALL and every L2
 
@@ -459,6 +476,7 @@ def main():
                    "group_stride": gs,
                    "step": "qk_norm_rope + dense_fwd + subblock_select + block_sparse_fwd"},
         "roofline": roofline, "cpu_baseline": cpu, "components": components,
+        "provenance": provenance(cfg),
     }
     print(json.dumps(line), flush=True)
 
