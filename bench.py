@@ -222,6 +222,9 @@ def main():
     value = (dense_flops + sparse_flops) / (ms_step * 1e-3) / 1e12
 
     components = {
+        "step_kernel_ms": {kname: {"median": float(np.median(vals)), "min": float(np.min(vals)),
+                                   "p90": float(np.percentile(vals, 90)), "mean": float(np.mean(vals))}
+                           for kname, vals in per.items()},
         "dense_ms": avg["dense"], "dense_tflops": dense_tf, "dense_frac_peak": dense_tf / PEAK_BF16_TFLOPS,
         "sparse_ms": avg["sparse"], "sparse_tflops_kept": sparse_tf, "sparse_frac_peak": sparse_tf / PEAK_BF16_TFLOPS,
         "select_ms": avg["select"], "norm_rope_ms": avg["norm_rope"], "norm_rope_gbs": nr_gbs,
