@@ -438,6 +438,47 @@ def test_kept_set_check_flags_exactly_the_bad_rows(h3):
     log("kept-set checks: valid sets pass, every planted bad row flagged with its reason")
 
 
+@pytest.mark.timeout(600)
+def test_select_threshold_and_sparse_at_the_row_limit(h3):
+    """nB = 19968 (1,277,952 tokens, one head): the longest row of float64 scores that the top-k and
+    threshold-fill kernels hold in one CU's LDS, the largest nB the selection accepts. The oracle's
+    scores for sampled query blocks: kept sets bit-exact (near ties excepted), threshold rows, and
+    block-sparse attention over the kept set."""
+    nb = 19968
+    n = nb * 64
+    c = random_case(1, n, 1, 64, seed=905, device=DEV)
+    q, k, v = c["q"], c["k"], c["v"]
+    keep = oracle.keep_count(nb, 0.75)
+    idx = h3.subblock_select(q, k, 0.75)
+    o = h3.block_sparse_fwd(q, k, v, idx)
+    _sync()
+    assert int(h3.check_block_idx(idx).count_nonzero()) == 0
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    rows = sample_query_blocks(nb, 24, seed=906, extra=(0, nb - 1))
+    scores = oracle.block_scores(f64(qh), f64(kh), 64)[:, :, rows]   # [1, 1, R, nB]
+    ih = idx.cpu().numpy()
+    check_block_sets(ih[:, :, rows], oracle.topk_blocks(scores, keep), scores, keep, "row-limit select s=0.75")
+    oh = o.cpu()
+    for i in rows[:6]:
+        rr = np.arange(i * 64, (i + 1) * 64)
+        keys = oracle.block_token_ids(ih[0, 0, i], 64, n)
+        ref, _ = oracle.attention_head(f64(qh[0, rr, 0]), f64(kh[0, keys, 0]), f64(vh[0, keys, 0]))
+        check_attention(f64(oh[0, rr, 0]), ref, f"row-limit sparse block {i}")
+    del o, idx
+    tau = _tau_for(scores, 0.05)
+    rp, ci = h3.subblock_select_threshold(q, k, tau)
+    _sync()
+    assert int(h3.check_csr(rp, ci, 1, 1, nb).count_nonzero()) == 0
+    rpn, cin = rp.cpu().numpy(), ci.cpu().numpy()
+    sub_rp, sub_ci = [0], []
+    for r in rows:
+        seg = cin[rpn[r]:rpn[r + 1]]
+        sub_ci.append(seg)
+        sub_rp.append(sub_rp[-1] + seg.size)
+    _check_threshold_sets(torch.tensor(sub_rp, dtype=torch.int64), torch.from_numpy(np.concatenate(sub_ci)), scores,
+                          tau, "row-limit threshold")
+
+
 def test_csr_keep_all_is_bitwise_dense_and_empty_rows(h3):
     c = random_case(1, 64 * 6, 2, 128, seed=21, device=DEV)
     rp, ci = h3.subblock_select_threshold(c["q"], c["k"], float("inf"))
