@@ -749,3 +749,68 @@ def test_fp8_video5s_sampled(h3):
                 bound = ATTN_MAX_ABS + 2.0 ** -8 * np.abs(ref) + 2.0 ** -3 * wm[:, None] * dv
                 log(f"fp8 {what} 5s head {h} block {i}: max-abs {err.max():.3g} mean-abs {err.mean():.3g}")
                 assert (err <= bound).all() and err.mean() <= ATTN_MEAN_ABS, f"fp8 {what} 5s head {h} block {i}"
+
+
+@pytest.mark.timeout(900)
+def test_offsets_past_two_to_the_31_elements(h3):
+    """q, k, v of 1 x 366,912 x 48 x 128 (2.25e9 elements, 4.5 GB each): element and byte offsets
+    past 2^31 in every kernel of the path and of the fp8 path. The last head holds the largest
+    offsets; its norm+RoPE rows, sampled dense and block-sparse rows, kept sets, e4m3 codes and
+    sampled fp8 dense and block-sparse rows are checked against the oracle."""
+    b, n, h, d = 1, 366912, 48, 128
+    grid, sections = (91, 84, 48), (32, 48, 48)
+    assert b * n * h * d > 2 ** 31
+    c = random_case(b, n, h, d, seed=907, device=DEV)
+    qo, ko = h3.qk_norm_rope(c["q"], c["k"], c["wq"], c["wk"], grid, sections, 1e4, 1e-6)
+    _sync()
+    last = slice(h - 1, h)
+    rq, rk = oracle.qk_norm_rope(f64(c["q"][:, :, last]), f64(c["k"][:, :, last]), f64(c["wq"]), f64(c["wk"]),
+                                 grid, sections, 1e4, float(np.float32(1e-6)))
+    for g, r, nm in ((qo[:, :, last], rq, "q"), (ko[:, :, last], rk, "k")):
+        worst, exact = check_norm_rope(f64(g), r)
+        log(f"2^31+ norm+rope {nm} last head: worst {worst:.3f} ulp, exact {exact:.5f}")
+        assert worst <= 1.0 and exact > 0.99
+    del c["q"], c["k"]
+    nb = n // 64
+    blocks = sample_query_blocks(nb, 3, seed=908, extra=(nb - 1,))
+    _sampled_dense(h3, qo, ko, c["v"], {h - 1: blocks}, "2^31+")
+    keep = oracle.keep_count(nb, 0.75)
+    idx = h3.subblock_select(qo, ko, 0.75)
+    o = h3.block_sparse_fwd(qo, ko, c["v"], idx, group_stride=h3.frame_group_stride(grid))
+    _sync()
+    qh, kh, vh = qo[:, :, last].cpu(), ko[:, :, last].cpu(), c["v"][:, :, last].cpu()
+    scores = oracle.block_scores(f64(qh), f64(kh), 64)
+    ih = idx[:, last].cpu().numpy()
+    check_block_sets(ih, oracle.topk_blocks(scores, keep), scores, keep, "2^31+ select last head")
+    oh = o[:, :, last].cpu()
+    for i in blocks:
+        rr = np.arange(i * 64, (i + 1) * 64)
+        keys = oracle.block_token_ids(ih[0, 0, i], 64, n)
+        ref, _ = oracle.attention_head(f64(qh[0, rr, 0]), f64(kh[0, keys, 0]), f64(vh[0, keys, 0]))
+        check_attention(f64(oh[0, rr, 0]), ref, f"2^31+ sparse last head block {i}")
+    del o
+    fq = h3.fp8_quantize(qo, ko, c["v"])
+    _sync()
+    for nm, src, t8, ts in (("q", qh, fq.q8, fq.q_scale), ("k", kh, fq.k8, fq.k_scale)):
+        ref8, refs = oracle.quantize_blocks(f64(src), 64)
+        np.testing.assert_array_equal(ts[:, last].cpu().numpy().astype(np.float64), refs, err_msg=f"{nm} scales")
+        np.testing.assert_array_equal(_e4m3(t8[:, :, last]), ref8, err_msg=f"{nm} codes")
+    v8, sv = oracle.quantize_channels(f64(vh))
+    np.testing.assert_array_equal(fq.v_scale[:, last].cpu().numpy().astype(np.float64), sv)
+    tok, pad = _v8t_to_tokens(_e4m3(fq.v8t[:, last]), n)
+    np.testing.assert_array_equal(tok, v8)
+    del qo, ko
+    o8 = h3.fp8_dense_fwd(fq)
+    os8 = h3.fp8_block_sparse_fwd(fq, idx, group_stride=h3.frame_group_stride(grid))
+    _sync()
+    qd, kd, vd = f64(qh), f64(kh), f64(vh)
+    o8h, os8h = o8[:, :, last].cpu(), os8[:, :, last].cpu()
+    for i in blocks:
+        rr = np.arange(i * 64, (i + 1) * 64)
+        for what, got, bidx in (("dense", o8h, None), ("sparse", os8h, ih[0, 0, i])):
+            ref, _, wm, dv = oracle.attention_fp8_rows(qd, kd, vd, 0, 0, i, block_idx=bidx, detail=True)
+            err = np.abs(f64(got[0, rr, 0]) - ref)
+            bound = ATTN_MAX_ABS + 2.0 ** -8 * np.abs(ref) + 2.0 ** -3 * wm[:, None] * dv
+            log(f"2^31+ fp8 {what} last head block {i}: max-abs {err.max():.3g} mean-abs {err.mean():.3g}")
+            assert (err <= bound).all() and err.mean() <= ATTN_MEAN_ABS, f"2^31+ fp8 {what} block {i}"
+    log("2^31+ offsets: norm+rope, dense, select, sparse, fp8 codes and fp8 attention of the last head match the oracle")
