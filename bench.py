@@ -93,6 +93,56 @@ def provenance(cfg):
             "inputs": {"field": cfg.field, "seeds": {t: seed_for(cfg.id, t) for t in ("q", "k", "v", "wq", "wk")}}}
 
 
+class ClockSampler:
+    """The GFX clock (MHz, mean over the XCDs) read with `amd-smi metric --clock --json` from a
+    thread while the timed steps run. Reading clocks changes nothing on the device; the result is
+    None when amd-smi is missing or its output cannot be read."""
+
+    def __init__(self, period_s: float = 0.25):
+        import shutil
+        import threading
+        self.exe = shutil.which("amd-smi")
+        self.period = period_s
+        self.samples = []
+        self.done = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True) if self.exe else None
+
+    def _read(self):
+        import subprocess
+        r = subprocess.run([self.exe, "metric", "--clock", "--json"], capture_output=True, text=True, timeout=10)
+        data = json.loads(r.stdout)
+        clk = data["gpu_data"][0]["clock"]
+        vals = [v["clk"]["value"] for key, v in clk.items() if key.startswith("gfx_") and isinstance(v, dict)]
+        vals = [float(x) for x in vals if isinstance(x, (int, float))]
+        return sum(vals) / len(vals) if vals else None
+
+    def _run(self):
+        while not self.done.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+            except Exception:  # noqa: BLE001 - a context figure only
+                return
+            self.done.wait(self.period)
+
+    def start(self):
+        if self.thread is not None:
+            self.thread.start()
+        return self
+
+    def stop(self):
+        if self.thread is None:
+            return None
+        self.done.set()
+        self.thread.join(timeout=15)
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
+                "source": "amd-smi metric --clock, mean of the gfx_* clocks, sampled during the timed steps"}
+
+
 def flush_caches(buf: torch.Tensor):
     buf.add_(1)  # rewrites 512 MB: evicts the 256 MB MALL and every L2
 
@@ -196,11 +246,13 @@ def main():
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    clocks = ClockSampler().start()
     start.record()
     for s in range(args.steps):
         step(events[s])
     end.record()
     torch.cuda.synchronize()
+    clock = clocks.stop()
     wall = time.perf_counter() - t0
     ms_step = elapsed_ms(start, end) / args.steps
     per = {"norm_rope": [], "dense": [], "select": [], "sparse": []}
@@ -222,6 +274,10 @@ def main():
     value = (dense_flops + sparse_flops) / (ms_step * 1e-3) / 1e12
 
     components = {
+        "gfx_clock_during_steps": clock,
+        # context only: the published peak assumes 2.4 GHz; the same MFMA rate at the clock read above
+        "dense_frac_peak_at_measured_clock": (dense_tf / (PEAK_BF16_TFLOPS * clock["median_mhz"] / 2400.0)
+                                              if clock else None),
         "step_kernel_ms": {kname: {"median": float(np.median(vals)), "min": float(np.min(vals)),
                                    "p90": float(np.percentile(vals, 90)), "mean": float(np.mean(vals))}
                            for kname, vals in per.items()},
