@@ -317,25 +317,53 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_count_kernel(SelectArg
   }
 }
 
-// exclusive scan of the per-row counts into row_ptr (one workgroup; rows split in contiguous runs)
+// Exclusive scan of the per-row counts into row_ptr, in one workgroup. Each step covers
+// kScanThreads * kScanPer rows: every thread loads kScanPer consecutive counts (all loads in
+// flight at once), the thread totals are scanned across the workgroup (wave shuffles, then the
+// wave totals through LDS), each thread writes its run, and a carry joins the steps.
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 16;
 __global__ __launch_bounds__(kScanThreads) void row_ptr_scan_kernel(SelectArgs a, int64_t rows) {
-  __shared__ int64_t part[kScanThreads];
-  const int tid = threadIdx.x;
-  const int64_t per = (rows + kScanThreads - 1) / kScanThreads;
-  const int64_t r0 = tid * per, r1 = r0 + per < rows ? r0 + per : rows;
-  int64_t s = 0;
-  for (int64_t r = r0; r < r1; ++r) s += a.row_cnt[r];
-  part[tid] = s;
+  __shared__ long long wave_tot[kScanThreads / 64];
+  __shared__ long long s_carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_carry = 0;
   __syncthreads();
-  if (tid == 0) {
-    int64_t acc = 0;
-    for (int i = 0; i < kScanThreads; ++i) { const int64_t v = part[i]; part[i] = acc; acc += v; }
-    a.row_ptr[rows] = acc;
+  for (int64_t base = 0; base < rows; base += (int64_t)kScanThreads * kScanPer) {
+    const int64_t r0 = base + (int64_t)tid * kScanPer;
+    long long v[kScanPer];
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) v[u] = r0 + u < rows ? a.row_cnt[r0 + u] : 0;
+    long long tot = 0;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) tot += v[u];
+    long long inc = tot;  // inclusive scan of the thread totals inside the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    if (lane == 63) wave_tot[wave] = inc;
+    __syncthreads();
+    long long before = s_carry, all = s_carry;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      const long long t = wave_tot[w];
+      if (w < wave) before += t;
+      all += t;
+    }
+    long long acc = before + inc - tot;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u)
+      if (r0 + u < rows) {
+        a.row_ptr[r0 + u] = acc;
+        acc += v[u];
+      }
+    __syncthreads();  // every thread has read wave_tot and s_carry
+    if (tid == 0) s_carry = all;
+    __syncthreads();
   }
-  __syncthreads();
-  int64_t acc = part[tid];
-  for (int64_t r = r0; r < r1; ++r) { a.row_ptr[r] = acc; acc += a.row_cnt[r]; }
+  if (tid == 0) a.row_ptr[rows] = s_carry;
 }
 
 // Threshold mode, pass 2: ordered compaction of {j : s_j >= thr} into col_idx[row_ptr[row] ..].
