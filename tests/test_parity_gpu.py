@@ -814,3 +814,63 @@ def test_offsets_past_two_to_the_31_elements(h3):
             log(f"2^31+ fp8 {what} last head block {i}: max-abs {err.max():.3g} mean-abs {err.mean():.3g}")
             assert (err <= bound).all() and err.mean() <= ATTN_MEAN_ABS, f"2^31+ fp8 {what} block {i}"
     log("2^31+ offsets: norm+rope, dense, select, sparse, fp8 codes and fp8 attention of the last head match the oracle")
+
+
+def test_c_program_drives_the_path_through_the_c_abi(h3, tmp_path):
+    """tests/c_abi_consumer.cpp (built by __graft_entry__.build()) is a host program with no Python
+    or torch: it allocates its own device buffers and stream and runs norm+RoPE -> dense -> select ->
+    block-sparse through the four entry points. Its outputs on a ragged two-batch case (N = 240,
+    a partial last block) are checked against the oracle."""
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_build", "c_abi_consumer")
+    assert os.path.exists(exe), "tests/_build/c_abi_consumer is missing: run __graft_entry__.build()"
+    b, grid, heads, d, sections, theta, eps, sparsity = 2, (3, 8, 10), 3, 128, (32, 48, 48), 1e4, 1e-6, 0.5
+    n = grid[0] * grid[1] * grid[2]
+    x = random_case(b, n, heads, d, seed=931)
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().astype("<i2").tobytes()
+    with open(tmp_path / "in.bin", "wb") as f:
+        f.write(np.array([b, *grid, heads, d, *sections], dtype="<i4").tobytes())
+        f.write(np.array([theta, eps], dtype="<f4").tobytes())
+        f.write(np.array([sparsity], dtype="<f8").tobytes())
+        for nm in ("q", "k", "v"):
+            f.write(bits(x[nm]))
+        f.write(x["wq"].numpy().astype("<f4").tobytes())
+        f.write(x["wk"].numpy().astype("<f4").tobytes())
+    r = subprocess.run([exe, str(tmp_path / "in.bin"), str(tmp_path / "out.bin")], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    log(r.stdout.strip())
+    raw = open(tmp_path / "out.bin", "rb").read()
+    elems = b * n * heads * d
+    nb = -(-n // 64)
+    off = 0
+
+    def take(dtype, count):
+        nonlocal off
+        a = np.frombuffer(raw, dtype=dtype, count=count, offset=off)
+        off += a.nbytes
+        return a
+
+    def bf16_array(a):
+        return torch.from_numpy(a.copy()).view(torch.bfloat16).reshape(b, n, heads, d)
+
+    qo, ko, od = (bf16_array(take("<i2", elems)) for _ in range(3))
+    lse = take("<f4", b * heads * n).reshape(b, heads, n)
+    keep = int(take("<i4", 1)[0])
+    idx = take("<i4", b * heads * nb * keep).reshape(b, heads, nb, keep)
+    osp = bf16_array(take("<i2", elems))
+    assert off == len(raw) and keep == oracle.keep_count(nb, sparsity)
+    rq, rk = oracle.qk_norm_rope(f64(x["q"]), f64(x["k"]), f64(x["wq"]), f64(x["wk"]), grid, sections, theta,
+                                 float(np.float32(eps)))
+    for got, ref, nm in ((qo, rq, "q"), (ko, rk, "k")):
+        worst, exact = check_norm_rope(f64(got), ref)
+        assert worst <= 1.0 and exact > 0.99, f"C consumer norm+rope {nm}: {worst} ulp"
+    qd, kd, vd = f64(qo), f64(ko), f64(x["v"])
+    ro, rl = oracle.attention(qd, kd, vd)
+    check_attention(f64(od), ro, "C consumer dense")
+    assert np.abs(lse.astype(np.float64) - rl).max() <= LSE_MAX_ABS
+    scores = oracle.block_scores(qd, kd, 64)
+    check_block_sets(idx, oracle.topk_blocks(scores, keep), scores, keep, "C consumer select")
+    rs, _ = oracle.sparse_attention(qd, kd, vd, idx, 64)
+    check_attention(f64(osp), rs, "C consumer block-sparse")
