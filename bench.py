@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-extra", action="store_true",
                    help="skip everything outside the step: flushed norm+RoPE, block ops, threshold mode, fp8, "
                         "the 10 s and 15 s workloads and the context rates")
+    p.add_argument("--no-clock", action="store_true",
+                   help="do not read the GFX clock with amd-smi during the timed steps (for profiled runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first copy 1 GiB once, so that memory counters of a known-size copy sit in the same trace")
     return p.parse_args()
@@ -98,10 +100,20 @@ class ClockSampler:
     thread while the timed steps run. Reading clocks changes nothing on the device; the result is
     None when amd-smi is missing or its output cannot be read."""
 
-    def __init__(self, period_s: float = 0.25):
+    def __init__(self, period_s: float = 0.25, enabled: bool = True):
         import shutil
         import threading
-        self.exe = shutil.which("amd-smi")
+        self.exe = shutil.which("amd-smi") if enabled else None
+        self.cmd = None
+        if self.exe:
+            # a Python tool is started with this interpreter directly: its launcher line would
+            # otherwise have a helper process exec the interpreter
+            try:
+                with open(self.exe, "rb") as f:
+                    first = f.readline()
+            except OSError:
+                first = b""
+            self.cmd = [sys.executable, self.exe] if first.startswith(b"#!") and b"python" in first else [self.exe]
         self.period = period_s
         self.samples = []
         self.done = threading.Event()
@@ -109,7 +121,7 @@ class ClockSampler:
 
     def _read(self):
         import subprocess
-        r = subprocess.run([self.exe, "metric", "--clock", "--json"], capture_output=True, text=True, timeout=10)
+        r = subprocess.run(self.cmd + ["metric", "--clock", "--json"], capture_output=True, text=True, timeout=10)
         data = json.loads(r.stdout)
         clk = data["gpu_data"][0]["clock"]
         vals = [v["clk"]["value"] for key, v in clk.items() if key.startswith("gfx_") and isinstance(v, dict)]
@@ -246,7 +258,7 @@ def main():
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    clocks = ClockSampler().start()
+    clocks = ClockSampler(enabled=not args.no_clock).start()
     start.record()
     for s in range(args.steps):
         step(events[s])
