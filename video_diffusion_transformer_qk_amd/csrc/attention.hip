@@ -27,6 +27,7 @@
 // of their kept key blocks (see attn_sparse_group_kernel).
 #include "device_util.h"
 #include "kernels.h"
+#include "launch_util.h"
 #include "sparse_union.h"
 
 namespace h3attn {
@@ -418,11 +419,7 @@ template <int D, int WAVES, int OCC>
 void launch_dense(const AttnArgs& a, hipStream_t stream) {
   const size_t lds = 2 * Tile<D, kBN>::BUF_BYTES;
   auto kern = attn_fwd_kernel<D, WAVES, OCC>;
-  static const bool lds_ok = [&] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
-  }();
-  (void)lds_ok;
+  allow_dynamic_lds(reinterpret_cast<const void*>(kern), (int)lds);
   const dim3 grid((unsigned)((a.n_tokens + WAVES * 32 - 1) / (WAVES * 32)), (unsigned)a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), lds, stream, a);
 }
@@ -431,11 +428,7 @@ template <int D, int G, int KW, bool CSR>
 void launch_group(const AttnArgs& a, hipStream_t stream) {
   const size_t lds = 2 * Tile<D, kBN>::BUF_BYTES + (size_t)KW * 4;
   auto kern = attn_sparse_group_kernel<D, G, KW, CSR>;
-  static const bool lds_ok = [&] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
-  }();
-  (void)lds_ok;
+  allow_dynamic_lds(reinterpret_cast<const void*>(kern), (int)lds);
   const dim3 grid((unsigned)n_groups<G>(a.n_blocks, a.group_stride), (unsigned)a.heads, (unsigned)a.batch);
   hipLaunchKernelGGL(kern, grid, dim3(G * 128), lds, stream, a);
 }

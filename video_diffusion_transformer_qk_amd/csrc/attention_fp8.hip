@@ -21,6 +21,7 @@
 // into registers one tile ahead and double-buffered in LDS, one barrier per tile.
 #include "device_util.h"
 #include "kernels.h"
+#include "launch_util.h"
 #include "sparse_union.h"
 
 namespace h3attn {
@@ -361,16 +362,10 @@ __global__ __launch_bounds__(512, 2) void attn_fp8_sparse_kernel(Fp8AttnArgs a) 
                  a.lse != nullptr ? a.lse + bh * N : nullptr, a.v_scale + bh * D, my_q, N, rs, hi);
 }
 
-template <typename K>
-void set_lds(K kern, size_t lds) {
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-}
-
 template <int D>
 void launch_dense(const Fp8AttnArgs& a, hipStream_t stream) {
   const size_t lds = 2 * Fp8Tile<D>::BUF_BYTES;
-  static const bool once = (set_lds(attn_fp8_dense_kernel<D>, lds), true);
-  (void)once;
+  allow_dynamic_lds(reinterpret_cast<const void*>(attn_fp8_dense_kernel<D>), (int)lds);
   hipLaunchKernelGGL(attn_fp8_dense_kernel<D>, dim3((unsigned)((a.n_tokens + 255) / 256), (unsigned)a.heads, (unsigned)a.batch),
                      dim3(512), lds, stream, a);
 }
@@ -380,8 +375,7 @@ void launch_sparse(const Fp8AttnArgs& a, hipStream_t stream) {
   constexpr int KW = 4096;
   const size_t lds = 2 * Fp8Tile<D>::BUF_BYTES + (size_t)KW * 4;
   auto kern = attn_fp8_sparse_kernel<D, KW>;
-  static const bool once = (set_lds(kern, lds), true);
-  (void)once;
+  allow_dynamic_lds(reinterpret_cast<const void*>(kern), (int)lds);
   hipLaunchKernelGGL(kern, dim3((unsigned)n_groups<4>(a.n_blocks, a.group_stride), (unsigned)a.heads, (unsigned)a.batch),
                      dim3(512), lds, stream, a);
 }

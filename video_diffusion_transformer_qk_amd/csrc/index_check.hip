@@ -12,6 +12,7 @@
 // is below its start or beyond the column capacity.
 #include "device_util.h"
 #include "kernels.h"
+#include "launch_util.h"
 
 namespace h3attn {
 namespace {
@@ -70,11 +71,7 @@ __global__ __launch_bounds__(kCheckThreads) void csr_rows_check_kernel(IndexChec
 template <typename K>
 void launch_check(K kern, const IndexCheckArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)((a.n_blocks + 31) / 32) * sizeof(uint32_t);
-  static const bool lds_ok = [&] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)kIndexCheckLdsBytes) == hipSuccess;
-  }();
-  (void)lds_ok;
+  allow_dynamic_lds(reinterpret_cast<const void*>(kern), (int)kIndexCheckLdsBytes);
   hipLaunchKernelGGL(kern, dim3((unsigned)a.rows), dim3(kCheckThreads), lds, stream, a);
 }
 

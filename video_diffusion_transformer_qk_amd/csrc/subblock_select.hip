@@ -22,6 +22,7 @@
 //                select of the keep-th largest key -> ordered compaction of the kept indices.
 #include "device_util.h"
 #include "kernels.h"
+#include "launch_util.h"
 
 namespace h3attn {
 namespace {
@@ -402,11 +403,7 @@ void launch_subblock_select(const SelectArgs& a, hipStream_t stream) {
   launch_pool_and_scores(a, stream);
   const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
   const size_t lds = (size_t)a.n_blocks * sizeof(uint64_t);
-  static const bool lds_ok = [] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSelectRowLdsBytes) == hipSuccess;
-  }();
-  (void)lds_ok;
+  allow_dynamic_lds(reinterpret_cast<const void*>(topk_kernel), (int)kSelectRowLdsBytes);
   hipLaunchKernelGGL(topk_kernel, g3, dim3(kTopkThreads), lds, stream, a);
 }
 
@@ -439,11 +436,7 @@ void launch_threshold_count(const SelectArgs& a, hipStream_t stream) {
 void launch_threshold_fill(const SelectArgs& a, hipStream_t stream) {
   const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
   const size_t lds = (size_t)a.n_blocks * sizeof(double);
-  static const bool lds_ok = [] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(threshold_fill_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSelectRowLdsBytes) == hipSuccess;
-  }();
-  (void)lds_ok;
+  allow_dynamic_lds(reinterpret_cast<const void*>(threshold_fill_kernel), (int)kSelectRowLdsBytes);
   hipLaunchKernelGGL(threshold_fill_kernel, g3, dim3(kTopkThreads), lds, stream, a);
 }
 
