@@ -419,6 +419,10 @@ def test_kept_set_check_flags_exactly_the_bad_rows(h3):
     with pytest.raises(h3.H3AttnError):
         h3.block_sparse_fwd(c["q"], c["k"], c["v"], bad, validate=True)
     h3.block_sparse_fwd(c["q"], c["k"], c["v"], idx, validate=True)  # valid: runs
+    fq = h3.fp8_quantize(c["q"], c["k"], c["v"])
+    with pytest.raises(h3.H3AttnError):
+        h3.fp8_block_sparse_fwd(fq, bad, validate=True)
+    h3.fp8_block_sparse_fwd(fq, idx, validate=True)
     # CSR: threshold-mode rows are valid
     rp, ci = h3.subblock_select_threshold(c["q"], c["k"], 0.3)
     assert int(h3.check_csr(rp, ci, b, h, nb).count_nonzero()) == 0
