@@ -56,7 +56,7 @@ struct WaveRows {
   bf16x8 qf[KSTEPS];
   f32x16 o[DT];
   float m_run;  // running max of s*sc (log2 units), shared by lanes l and l^32
-  float l_run;  // per-lane partial row sum
+  float l_part[4];  // per-lane partial row sums, four independent chains across all tiles
 };
 
 template <int D>
@@ -67,7 +67,8 @@ __device__ __forceinline__ void rows_begin(WaveRows<D>& w, const uint16_t* qp) {
 #pragma unroll
   for (int dt = 0; dt < WaveRows<D>::DT; ++dt) w.o[dt] = f32x16{};
   w.m_run = -INFINITY;
-  w.l_run = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w.l_part[j] = 0.f;
 }
 
 // The three parts of one 64-key tile for one wave. qk_tile: S^T = K . Q^T from the K tile at kb.
@@ -139,7 +140,8 @@ __device__ __forceinline__ void softmax_max(WaveRows<D>& w, const f32x16 (&s)[2]
     const float m_new = fmaxf(w.m_run, mx);
     const float alpha = fast_exp2(w.m_run - m_new);
     w.m_run = m_new;
-    w.l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w.l_part[j] *= alpha;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -148,9 +150,11 @@ __device__ __forceinline__ void softmax_max(WaveRows<D>& w, const f32x16 (&s)[2]
 }
 
 // softmax_exp: P^T = exp2(s*sc - m_run) as bf16 (pk, 8 values per 16-key step: step kk covers
-// s[kk/2] regs 8*(kk%2) .. +7), and the tile's row-sum partial of the bf16-rounded P.
-__device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], u32x4 (&pk)[4], float m_run, float sc) {
-  float psum[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial row sums
+// s[kk/2] regs 8*(kk%2) .. +7). The row sum of the bf16-rounded P that P.V uses is accumulated
+// with packed dot products against (1, 1) straight into the wave's four running per-lane
+// chains, which are added up only in the epilogue.
+__device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2], u32x4 (&pk)[4], float m_run, float sc,
+                                                float (&lp)[4]) {
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
 #pragma unroll
@@ -159,11 +163,9 @@ __device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], u32x4 (&pk)[4
       const float p1 = fast_exp2(fmaf(s[m][r + 1], sc, -m_run));
       const uint32_t pp = pack_bf16x2(p0, p1);
       pk[2 * m + r / 8][(r % 8) / 2] = pp;
-      // row sum of the bf16-rounded P that P.V uses: one packed dot product with (1, 1)
-      psum[(r / 2) % 4] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes2, psum[(r / 2) % 4], false);
+      lp[(r / 2) % 4] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes2, lp[(r / 2) % 4], false);
     }
   }
-  return (psum[0] + psum[1]) + (psum[2] + psum[3]);
 }
 
 // O^T += V^T . P^T with V^T read from the row-major V tile at vb through the LDS transpose read;
@@ -203,7 +205,7 @@ __device__ __forceinline__ void rows_tile(WaveRows<D>& w, const unsigned char* k
   if (key0 + BN > N) mask_tile(s, key0, N, lane);
   softmax_max(w, s, sc);
   u32x4 pk[4];
-  w.l_run += softmax_exp(s, pk, w.m_run, sc);
+  softmax_exp(s, pk, w.m_run, sc, w.l_part);
   pv_tile<D>(w.o, pk, vb, lane);
 }
 
@@ -215,7 +217,7 @@ template <int D>
 __device__ __forceinline__ void rows_end(const WaveRows<D>& w, uint16_t* out, float* lse_row, int64_t my_q,
                                          int64_t N, int64_t row_stride, bool empty, int hi) {
   constexpr int DT = D / 32;
-  const float l_tot = pair_sum(w.l_run);
+  const float l_tot = pair_sum((w.l_part[0] + w.l_part[1]) + (w.l_part[2] + w.l_part[3]));
   const float inv = empty ? 0.f : 1.0f / l_tot;
   if (my_q >= N) return;
   uint16_t* op = out + my_q * row_stride;
