@@ -519,6 +519,42 @@ def main():
                 del idx2
             components[c2.name] = rec
             del x2, q2, k2, v2, o2, ws2
+        # the two small workloads (tiny 4x8x8 and one 48x84 frame): each call of the path timed 50
+        # times (median, min, p90); launch-bound at these sizes, reported as context
+        for cid in (1, 2):
+            c2 = CONFIGS[cid]
+            x2 = make_inputs(c2, dev)
+            q2, k2, v2 = x2["q"], x2["k"], x2["v"]
+            b2, n2, h2, d2 = q2.shape
+            sp = c2.sparsities[0]
+            q2o, k2o, o2 = torch.empty_like(q2), torch.empty_like(k2), torch.empty_like(q2)
+            ws2 = torch.empty((h3.select_workspace_bytes(b2, h2, n2, d2),), dtype=torch.uint8, device=dev)
+            nb2 = (n2 + 63) // 64
+            idx2 = torch.empty((b2, h2, nb2, h3.keep_count(nb2, sp)), dtype=torch.int32, device=dev)
+            calls = {
+                "norm_rope": lambda: h3.qk_norm_rope(q2, k2, x2["wq"], x2["wk"], c2.grid, c2.sections, c2.theta, c2.eps,
+                                                     out=(q2o, k2o)),
+                "dense": lambda: h3.dense_fwd(q2o, k2o, v2, out=o2),
+                "select": lambda: h3.subblock_select(q2o, k2o, sp, workspace=ws2, out=idx2),
+                "sparse": lambda: h3.block_sparse_fwd(q2o, k2o, v2, idx2, out=o2),
+            }
+            rec = {"sparsity": sp, "runs": 50}
+            for nm, fn in calls.items():
+                fn()
+                torch.cuda.synchronize()
+                ts = []
+                for r in range(50):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(elapsed_ms(e0, e1) * 1e3)
+                rec[f"{nm}_us"] = {"median": float(np.median(ts)), "min": float(np.min(ts)),
+                                   "p90": float(np.percentile(ts, 90))}
+            components[c2.name] = rec
+            log(f"{c2.name}: " + ", ".join(f"{nm} {rec[nm + '_us']['median']:.1f} us" for nm in calls))
+            del x2, q2, k2, v2, q2o, k2o, o2, ws2, idx2
         # context rates on the same device: a bf16 GEMM through torch (hipBLASLt) and a device copy
         a_m = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
         b_m = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
