@@ -253,3 +253,14 @@ def test_kept_set_check_validation(lib):
     assert g(0x1000, 0x1000, -1, 1, 2, 10, 0x2000, None) == 1 and "col_capacity" in _err(lib)
     assert g(0x1000, 0x1000, 5, 1, 2, 10, None, None) == 1 and "row_flags" in _err(lib)
     assert g(0x1000, 0x1000, 5, 1, 2, (1 << 20) + 1, 0x2000, None) == 2
+
+
+def test_frame_group_stride_rule():
+    import video_diffusion_transformer_qk_amd as h3
+    assert h3.frame_group_stride((31, 48, 84)) == 63      # 5 s: 63 blocks per frame
+    assert h3.frame_group_stride((91, 84, 48)) == 63      # 15 s vertical
+    assert h3.frame_group_stride((4, 8, 8)) == 1          # frames of 64 tokens: one block each
+    assert h3.frame_group_stride((4, 16, 16)) == 4
+    assert h3.frame_group_stride((1, 48, 84)) == 1        # one frame
+    assert h3.frame_group_stride((3, 48, 84)) == 1        # fewer than four frames
+    assert h3.frame_group_stride((5, 10, 10)) == 1        # frames are not whole blocks

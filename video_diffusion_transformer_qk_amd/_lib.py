@@ -130,11 +130,13 @@ def version() -> str:
 
 
 def frame_group_stride(grid, block_size: int = 64) -> int:
-    """Query-block group stride for a T x H x W latent whose frames are whole blocks: H*W/64,
-    so a sparse workgroup takes one spatial position in four consecutive frames. 1 otherwise."""
+    """Query-block group stride for a T x H x W latent whose frames are whole blocks and that has
+    at least four frames: H*W/64, so a sparse workgroup takes one spatial position in four
+    consecutive frames. 1 otherwise (with fewer frames most of each four-block group would be
+    empty)."""
     t, h, w = (int(x) for x in grid)
     frame = h * w
-    if frame % block_size or frame // block_size >= -(-t * frame // block_size):
+    if frame % block_size or t < 4:
         return 1
     return frame // block_size
 
