@@ -293,9 +293,14 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_count_kernel(SelectArg
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = a.n_blocks;
   const int64_t row = ((int64_t)blockIdx.z * a.heads + blockIdx.y) * nb + blockIdx.x;
-  const double* sc = a.scores + row * nb;
+  // the row is read once, into LDS, and counted from there
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  double* sc = reinterpret_cast<double*>(smem);
   double m = -INFINITY;
-  for_row(sc, nb, [&](int, double x) { m = fmax(m, x); });
+  for_row(a.scores + row * nb, nb, [&](int j, double x) {
+    sc[j] = x;
+    m = fmax(m, x);
+  });
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
   if (lane == 0) red[wave] = m;
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(kTopkThreads) void threshold_count_kernel(SelectArg
   for (int w = 1; w < kTopkThreads / 64; ++w) m = fmax(m, red[w]);
   const double thr = m - a.tau_raw;
   int c = 0;
-  for_row(sc, nb, [&](int, double x) { c += x >= thr; });
+  for (int j = tid; j < nb; j += kTopkThreads) c += sc[j] >= thr;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
   if (lane == 0) cnt_red[wave] = c;
@@ -428,7 +433,8 @@ static void launch_pool_and_scores(const SelectArgs& a, hipStream_t stream) {
 void launch_threshold_count(const SelectArgs& a, hipStream_t stream) {
   launch_pool_and_scores(a, stream);
   const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
-  hipLaunchKernelGGL(threshold_count_kernel, g3, dim3(kTopkThreads), 0, stream, a);
+  allow_dynamic_lds(reinterpret_cast<const void*>(threshold_count_kernel), (int)kSelectRowLdsBytes);
+  hipLaunchKernelGGL(threshold_count_kernel, g3, dim3(kTopkThreads), (size_t)a.n_blocks * sizeof(double), stream, a);
   const int64_t rows = (int64_t)a.batch * a.heads * a.n_blocks;
   hipLaunchKernelGGL(row_ptr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a, rows);
 }
