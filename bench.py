@@ -41,7 +41,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--config", type=int, default=3, help="workload id (3 = 5 s video)")
+    p.add_argument("--config", type=int, default=3,
+                   help="workload id: 1 tiny, 2 one frame, 3 the 5 s video (default), 4 the 10 s video, 5 the 15 s video")
     p.add_argument("--sparsity", type=float, default=0.75)
     p.add_argument("--group-stride", type=int, default=0,
                    help="query-block group stride of the sparse kernels (0: one frame of blocks when frames "
@@ -210,7 +211,7 @@ def main():
               "the head-sharded layout it would use is described in the design notes.", file=sys.stderr)
         sys.exit(2)
     import video_diffusion_transformer_qk_amd as h3
-    from inputs import CONFIGS, make_inputs
+    from inputs import CONFIGS, FRAME, TINY, VIDEO10S, VIDEO15S, make_inputs
     h3.load_library()
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
@@ -303,8 +304,7 @@ def main():
     if not args.no_extra:
         # norm+RoPE alone with MALL/L2 flushed before every run, at the 10 s and frame workloads
         flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
-        for cid in (4, 2):
-            c2 = CONFIGS[cid]
+        for c2 in (VIDEO10S, FRAME):
             x2 = make_inputs(c2, dev)
             qq, kk2 = x2["q"], x2["k"]
             o1, o2 = torch.empty_like(qq), torch.empty_like(kk2)
@@ -323,7 +323,7 @@ def main():
             components[f"norm_rope_{c2.name}_us"] = med * 1e3
             components[f"norm_rope_{c2.name}_gbs"] = by / (med * 1e-3) / 1e9
             log(f"norm+rope {c2.name}: {med * 1e3:.1f} us median, {by / (med * 1e-3) / 1e9:.0f} GB/s (flushed)")
-            if cid == 2:
+            if c2 is FRAME:
                 # a single short launch between two events also times the events and the dispatch;
                 # 60 back-to-back launches rotating over 6 input/output sets (6 x 99 MB, more than
                 # the 256 MB MALL, so every launch reads from HBM) time the kernels themselves
@@ -466,14 +466,13 @@ def main():
         # the median of three runs each. The 10 s path starts with norm+RoPE; the 15 s path feeds
         # the synthetic q, k straight to attention and selection.
         del out_s, ws
-        for cid in (4, 5):
-            c2 = CONFIGS[cid]
+        for c2 in (VIDEO10S, VIDEO15S):
             x2 = make_inputs(c2, dev)
             q2, k2, v2 = x2["q"], x2["k"], x2["v"]
             b2, n2, h2, d2 = q2.shape
             nb2 = (n2 + 63) // 64
             gs2 = h3.frame_group_stride(c2.grid)
-            if cid == 4:
+            if c2 is VIDEO10S:
                 q2n, k2n = torch.empty_like(q2), torch.empty_like(k2)
                 h3.qk_norm_rope(q2, k2, x2["wq"], x2["wk"], c2.grid, c2.sections, c2.theta, c2.eps, out=(q2n, k2n))
                 q2, k2 = q2n, k2n
@@ -521,8 +520,7 @@ def main():
             del x2, q2, k2, v2, o2, ws2
         # the two small workloads (tiny 4x8x8 and one 48x84 frame): each call of the path timed 50
         # times (median, min, p90); launch-bound at these sizes, reported as context
-        for cid in (1, 2):
-            c2 = CONFIGS[cid]
+        for c2 in (TINY, FRAME):
             x2 = make_inputs(c2, dev)
             q2, k2, v2 = x2["q"], x2["k"], x2["v"]
             b2, n2, h2, d2 = q2.shape

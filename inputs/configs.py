@@ -55,15 +55,18 @@ CONFIGS = {
               ("dense", "select", "sparse")),
 }
 
+# the five workloads by name
+TINY, FRAME, VIDEO5S, VIDEO10S, VIDEO15S = (CONFIGS[i] for i in (1, 2, 3, 4, 5))
+
 # tensor ids used to derive per-tensor seeds
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "wq": 3, "wk": 4, "boxes": 5}
 BASE_SEED = 0
 
-# smooth-field recipe (configs 3-5): Gaussian sigma and truncation radius in tokens, added noise std
+# smooth-field recipe (the three video workloads): Gaussian sigma and truncation radius in tokens, added noise std
 FIELD_SIGMA = 2.0
 FIELD_RADIUS = 8
 FIELD_NOISE_STD = 0.5
-# planted subject boxes (config 5)
+# planted subject boxes (the 15 s workload)
 BOX_COUNT = 4
 BOX_EDGE = 8
 BOX_KEY_GAIN = 3.0

@@ -2,16 +2,17 @@
 import numpy as np
 import torch
 
-from inputs import CONFIGS, make_inputs, random_case, sample_query_blocks
+from inputs import FRAME, TINY, VIDEO5S, VIDEO10S, VIDEO15S, make_inputs, random_case, sample_query_blocks
 from inputs.generate import box_blocks, box_token_mask, gaussian_taps, plant_boxes, smooth_field
 
 
 def test_config_table_shapes():
-    expect = {1: (256, 4), 2: (4032, 63), 3: (124992, 1953), 4: (245952, 3843), 5: (366912, 5733)}
-    for cid, (n, nb) in expect.items():
-        assert CONFIGS[cid].n_tokens == n and CONFIGS[cid].n_blocks == nb
-        if CONFIGS[cid].sections is not None:
-            assert sum(CONFIGS[cid].sections) == CONFIGS[cid].head_dim
+    expect = [(TINY, 256, 4), (FRAME, 4032, 63), (VIDEO5S, 124992, 1953), (VIDEO10S, 245952, 3843),
+              (VIDEO15S, 366912, 5733)]
+    for cfg, n, nb in expect:
+        assert cfg.n_tokens == n and cfg.n_blocks == nb
+        if cfg.sections is not None:
+            assert sum(cfg.sections) == cfg.head_dim
 
 
 def test_make_inputs_deterministic_and_typed():
@@ -44,7 +45,7 @@ def test_smooth_field_statistics():
 
 
 def test_boxes_inside_grid_and_blocks():
-    grid = CONFIGS[5].grid
+    grid = VIDEO15S.grid
     boxes = plant_boxes(grid, torch.Generator().manual_seed(7))
     assert len(boxes) == 4
     for o in boxes:
@@ -53,7 +54,7 @@ def test_boxes_inside_grid_and_blocks():
     m = box_token_mask(grid, boxes, "cpu")
     assert m.sum().item() <= 4 * 512 and m.sum().item() >= 512
     bl = box_blocks(grid, boxes)
-    assert all(0 <= b < CONFIGS[5].n_blocks for b in bl)
+    assert all(0 <= b < VIDEO15S.n_blocks for b in bl)
 
 
 def test_sample_query_blocks():

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from inputs import CONFIGS, make_inputs, random_case, sample_query_blocks
+from inputs import FRAME, TINY, VIDEO5S, VIDEO10S, VIDEO15S, make_inputs, random_case, sample_query_blocks
 from inputs.generate import box_blocks
 from tests.parity_util import (ATTN_MAX_ABS, ATTN_MEAN_ABS, LSE_MAX_ABS, check_attention, check_block_sets,
                                check_norm_rope, f64, log)
@@ -72,7 +72,7 @@ def _full_select_sparse(h3, q, k, v, sparsity, what=""):
 
 
 def test_tiny_workload_all_stages(h3):
-    cfg = CONFIGS[1]
+    cfg = TINY
     x = make_inputs(cfg, DEV)
     qo, ko = _full_norm_rope(h3, x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps, "tiny")
     _full_dense(h3, qo, ko, x["v"], "tiny")
@@ -81,13 +81,13 @@ def test_tiny_workload_all_stages(h3):
 
 
 def test_frame_workload_norm_rope(h3):
-    cfg = CONFIGS[2]
+    cfg = FRAME
     x = make_inputs(cfg, DEV)
     _full_norm_rope(h3, x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps, "frame")
 
 
 def test_frame_workload_dense_select_sparse(h3):
-    cfg = CONFIGS[2]
+    cfg = FRAME
     x = make_inputs(cfg, DEV)
     qo, ko = h3.qk_norm_rope(x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps)
     _full_dense(h3, qo, ko, x["v"], "frame")
@@ -288,14 +288,14 @@ def _samples(cfg, per_head, extra=()):
 
 @pytest.mark.timeout(900)
 def test_video5s_dense_sampled(h3):
-    cfg = CONFIGS[3]
+    cfg = VIDEO5S
     x = make_inputs(cfg, DEV)
     _sampled_dense(h3, x["q"], x["k"], x["v"], _samples(cfg, 3), "5s")
 
 
 @pytest.mark.timeout(900)
 def test_video5s_select_and_sparse(h3):
-    cfg = CONFIGS[3]
+    cfg = VIDEO5S
     x = make_inputs(cfg, DEV)
     _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, _samples(cfg, 3), "5s", head_chunk=8,
                                 group_stride=h3.frame_group_stride(cfg.grid))
@@ -303,7 +303,7 @@ def test_video5s_select_and_sparse(h3):
 
 @pytest.mark.timeout(900)
 def test_video10s_norm_rope_full(h3):
-    cfg = CONFIGS[4]
+    cfg = VIDEO10S
     x = make_inputs(cfg, DEV)
     qo, ko = h3.qk_norm_rope(x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps)
     _sync()
@@ -321,7 +321,7 @@ def test_video10s_norm_rope_full(h3):
 
 @pytest.mark.timeout(900)
 def test_video10s_dense_select_sparse(h3):
-    cfg = CONFIGS[4]
+    cfg = VIDEO10S
     x = make_inputs(cfg, DEV)
     qo, ko = h3.qk_norm_rope(x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps)
     _sampled_dense(h3, qo, ko, x["v"], _samples(cfg, 3), "10s")
@@ -332,7 +332,7 @@ def test_video10s_dense_select_sparse(h3):
 
 @pytest.mark.timeout(900)
 def test_video15s_boxes_select_sparse_dense(h3):
-    cfg = CONFIGS[5]
+    cfg = VIDEO15S
     x = make_inputs(cfg, DEV)
     bb = box_blocks(cfg.grid, x["boxes"])
     extra = [bb[0], bb[len(bb) // 2], bb[-1]]
@@ -503,7 +503,7 @@ def test_csr_keep_all_is_bitwise_dense_and_empty_rows(h3):
 
 @pytest.mark.timeout(900)
 def test_video5s_threshold_select_and_csr_sparse(h3):
-    cfg = CONFIGS[3]
+    cfg = VIDEO5S
     x = make_inputs(cfg, DEV)
     q, k, v = x["q"], x["k"], x["v"]
     qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
@@ -717,7 +717,7 @@ def test_fp8_dense_and_sparse_full(h3, b, n, d):
 
 
 def test_fp8_frame_workload(h3):
-    x = make_inputs(CONFIGS[2], DEV)
+    x = make_inputs(FRAME, DEV)
     qd, kd, vd = f64(x["q"]), f64(x["k"]), f64(x["v"])
     fq = h3.fp8_quantize(x["q"], x["k"], x["v"])
     o, lse = h3.fp8_dense_fwd(fq, return_lse=True)
@@ -732,7 +732,7 @@ def test_fp8_frame_workload(h3):
 
 @pytest.mark.timeout(900)
 def test_fp8_video5s_sampled(h3):
-    cfg = CONFIGS[3]
+    cfg = VIDEO5S
     x = make_inputs(cfg, DEV)
     fq = h3.fp8_quantize(x["q"], x["k"], x["v"])
     o = h3.fp8_dense_fwd(fq)
