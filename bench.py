@@ -9,8 +9,9 @@ Printed JSON line: value = attention TFLOP/s of the step (dense 4*B*H*N^2*D plus
 4*B*H*nB*keep*64^2*D flops, divided by the whole step's time, norm+RoPE and selection included).
 Per-kernel times come from HIP events recorded on the launch stream between the calls of every
 timed step; `roofline` describes the dense kernel (the dominant one) against the bf16 MFMA peak.
-`cpu_baseline` times the float64 oracle's dense attention on a bounded sample of query rows of
-the same workload on the host cores.
+`cpu_baseline` times every stage of the float64 oracle (norm+RoPE, selection, dense and sparse
+attention) on bounded samples of the same workload on the host cores, each extrapolated to the
+whole step and labelled so.
 """
 from __future__ import annotations
 
@@ -48,7 +49,7 @@ def parse():
                    help="query-block group stride of the sparse kernels (0: one frame of blocks when frames "
                         "are whole blocks, else 1)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=16.0, help="target CPU time of the oracle samples")
     p.add_argument("--no-extra", action="store_true",
                    help="skip everything outside the step: flushed norm+RoPE, block ops, threshold mode, fp8, "
                         "the 10 s and 15 s workloads and the context rates")
@@ -164,44 +165,112 @@ def elapsed_ms(a, b):
     return a.elapsed_time(b)
 
 
-def cpu_baseline(q, k, v, cfg, target_s):
-    """Float64 oracle dense attention on a sample of query blocks of head 0 (and more heads if
-    time allows), timed on the host; returns TFLOP/s and what the sample was."""
-    import oracle
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
-    n = q.shape[1]
-    d = q.shape[3]
+        return int(os.cpu_count() or 1)
+
+
+def cpu_baseline(q_in, k_in, wq, wk, q, k, v, cfg, sparsity, target_s):
+    """The float64 oracle timed stage by stage on the host, on bounded samples of the step's own
+    workload, each extrapolated to the whole workload (labelled as extrapolated):
+      norm+RoPE   the first frames of the grid, every head (numpy ufuncs: one core);
+      select      block means, block scores and top-k of a few whole heads (scores by BLAS);
+      dense       sampled query blocks of several heads against all keys (BLAS);
+      sparse      sampled query blocks over their oracle kept sets (BLAS).
+    value = the step's attention flops (dense + kept sparse) / the extrapolated oracle step time,
+    the same unit as the GPU line. Inputs: the raw q, k and weights (norm+RoPE) and the normed q, k
+    and v that the other stages consume."""
+    import oracle
+    f64 = lambda t: t.detach().cpu().to(torch.float64).numpy()
+    b, n, hd, d = q.shape
     nb = (n + 63) // 64
-    done_rows = 0
-    spent = 0.0
-    samples = []
+    keep = oracle.keep_count(nb, sparsity)
     rng = np.random.default_rng(0)
-    head = 0
-    kh = vh = None
-    while spent < target_s and head < q.shape[2]:
-        if kh is None:
-            kh = k[0, :, head].cpu().to(torch.float64).numpy()
-            vh = v[0, :, head].cpu().to(torch.float64).numpy()
-        blk = int(rng.integers(0, nb))
-        rows = np.arange(blk * 64, min(n, blk * 64 + 64))
-        qh = q[0, rows, head].cpu().to(torch.float64).numpy()
+    stages = {}
+    share = {"norm_rope": 0.15, "select": 0.25, "dense": 0.4, "sparse": 0.2}
+
+    # norm+RoPE: whole frames from the start of the grid (their positions are those of the full grid)
+    if cfg.sections is not None:
+        t_len, h_len, w_len = cfg.grid
+        frame = h_len * w_len
+        frames, spent, elems = 1, 0.0, 0
+        while True:
+            tok = frames * frame
+            qs, ks = f64(q_in[:, :tok]), f64(k_in[:, :tok])
+            t0 = time.perf_counter()
+            oracle.qk_norm_rope(qs, ks, f64(wq), f64(wk), (frames, h_len, w_len), cfg.sections, cfg.theta,
+                                float(np.float32(cfg.eps)))
+            spent = time.perf_counter() - t0
+            elems = 2 * qs.size
+            if spent > share["norm_rope"] * target_s / 4 or frames >= t_len:
+                break
+            frames = min(t_len, frames * 2)
+        full = spent * (2 * b * n * hd * d) / elems
+        stages["norm_rope"] = {"threads": 1, "seconds": spent, "sample": f"{frames} of {t_len} frames, all heads",
+                               "gb_per_s": 8.0 * elems / 2 / spent / 1e9, "extrapolated_full_s": full}
+
+    # selection: whole heads (pooling, scores, top-k), extrapolated over the heads
+    spent, heads_done, sel = 0.0, 0, {}
+    while heads_done < hd and (heads_done == 0 or spent < share["select"] * target_s):
+        h = heads_done
+        qs, ks = f64(q[:, :, h:h + 1]), f64(k[:, :, h:h + 1])
         t0 = time.perf_counter()
-        oracle.attention_head(qh, kh, vh)
+        sel[h] = oracle.subblock_select(qs, ks, 64, sparsity)
         spent += time.perf_counter() - t0
-        done_rows += len(rows)
-        samples.append((head, blk))
-        if len(samples) % 16 == 0:
-            head += 1
-            kh = None
-    flops = 4.0 * done_rows * n * d
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 dense attention of {done_rows} query rows ({len(samples)} query blocks of "
-                      f"heads 0..{samples[-1][0]}) against all {n} keys, {spent:.1f} s",
-            "seconds": spent, "cpu_count": os.cpu_count()}
+        heads_done += 1
+    stages["select"] = {"threads": _blas_threads(), "seconds": spent, "sample": f"{heads_done} of {hd} heads, whole",
+                        "extrapolated_full_s": spent * hd / heads_done}
+
+    # dense and sparse attention: sampled query blocks of the heads selected above
+    for name in ("dense", "sparse"):
+        spent, rows_done, blocks, keys_done = 0.0, 0, 0, 0
+        h = 0
+        kh = vh = None
+        while spent < share[name] * target_s and blocks < 64 * len(sel):
+            if kh is None:
+                kh, vh = f64(k[0, :, h]), f64(v[0, :, h])
+            i = int(rng.integers(0, nb))
+            rows = np.arange(i * 64, min(n, i * 64 + 64))
+            qh = f64(q[0, rows, h])
+            keys = slice(None) if name == "dense" else oracle.block_token_ids(sel[h][0, 0, i], 64, n)
+            kk, vv = kh[keys], vh[keys]
+            t0 = time.perf_counter()
+            oracle.attention_head(qh, kk, vv)
+            spent += time.perf_counter() - t0
+            rows_done += len(rows)
+            keys_done += len(rows) * kk.shape[0]
+            blocks += 1
+            if blocks % 16 == 0:
+                h = (h + 1) % len(sel)
+                kh = None
+        flops = 4.0 * keys_done * d
+        total = 4.0 * b * hd * n * n * d if name == "dense" else 4.0 * b * hd * nb * keep * 64 * 64 * d
+        stages[name] = {"threads": _blas_threads(), "seconds": spent,
+                        "sample": f"{blocks} query blocks ({rows_done} rows) of heads 0..{min(len(sel), hd) - 1}",
+                        "tflops": flops / spent / 1e12, "extrapolated_full_s": spent * total / flops}
+
+    step_flops = 4.0 * b * hd * n * n * d + 4.0 * b * hd * nb * keep * 64 * 64 * d
+    step_s = sum(st["extrapolated_full_s"] for st in stages.values())
+    measured = sum(st["seconds"] for st in stages.values())
+    return {"value": step_flops / step_s / 1e12, "unit": "TFLOP/s",
+            "cores": max(st["threads"] for st in stages.values()), "kind": "oracle",
+            "sample": f"{cfg.name}: every oracle stage on a bounded sample ({measured:.1f} s measured), "
+                      f"extrapolated to one whole step ({step_s:.0f} s extrapolated)",
+            "seconds": measured, "extrapolated_step_s": step_s, "stages": stages,
+            "cpu_model": _cpu_model(), "cpu_count": os.cpu_count(), "blas_threads": _blas_threads()}
 
 
 def main():
@@ -594,8 +663,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample (host cores)")
-        cpu = cpu_baseline(qo, ko, v, cfg, args.cpu_seconds)
-        log(f"cpu baseline {cpu['value']:.4g} TFLOP/s ({cpu['sample']})")
+        cpu = cpu_baseline(q, k, wq, wk, qo, ko, v, cfg, args.sparsity, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']:.4g} TFLOP/s ({cpu['sample']}); stages "
+            + ", ".join(f"{k_}: {st['seconds']:.1f} s -> {st['extrapolated_full_s']:.3g} s" for k_, st in cpu["stages"].items()))
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

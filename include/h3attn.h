@@ -270,6 +270,12 @@ h3attn_status h3attn_cache_gate_init(h3attn_cache_gate* gate, double threshold, 
  * run of reused steps. */
 int32_t h3attn_cache_gate_decide(h3attn_cache_gate* gate, double rel_change);
 
+/* Decide one step from the two sums h3attn_residual_change wrote (read back by the caller into a
+ * HOST array): the relative change is sums[0] / sums[1], or +infinity (compute) when sums[1] is
+ * not positive or sums is NULL (the first step, with nothing to compare with). Returns as
+ * h3attn_cache_gate_decide. */
+int32_t h3attn_cache_gate_decide_sums(h3attn_cache_gate* gate, const double* sums);
+
 /* ---- FP8 (OCP e4m3) attention ----
  * "智東西…H3 Lightning" (hao.cnyes.com), section "02. 從50步壓到9步三層最佳化實現12倍提速":
  * SageAttention2 speeds up the attention computation; "VDN-MiniMax-H3：基于MiniMax H3的视频生成

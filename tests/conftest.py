@@ -26,3 +26,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """One line per (workload, check) with the parity figures the GPU tests measured: worst and
+    mean absolute errors, LSE error, ulps, exact-rounding fraction, mismatched and near-tie rows."""
+    from tests.parity_util import RECORDS, format_record
+    if not RECORDS:
+        return
+    terminalreporter.write_sep("-", "parity summary (GPU vs float64 oracle)")
+    for r in RECORDS:
+        terminalreporter.write_line(format_record(r))

@@ -194,6 +194,14 @@ void check_block_ops() {
   EXPECT(h3attn_cache_gate_decide(&gate, 0.01) == 1);  // small change: reuse
   EXPECT(h3attn_cache_gate_decide(&gate, 0.01) == 0);  // at most one reuse in a row
   EXPECT(h3attn_cache_gate_decide(&gate, 0.2) == 0);
+  {
+    const double small[2] = {0.5, 100.0}, zero_prev[2] = {0.0, 0.0};
+    EXPECT(h3attn_cache_gate_init(&gate, 0.05, 3) == H3ATTN_OK);
+    EXPECT(h3attn_cache_gate_decide_sums(&gate, nullptr) == 0);    // first step: nothing to compare with
+    EXPECT(h3attn_cache_gate_decide_sums(&gate, small) == 1);      // 0.005 < 0.05
+    EXPECT(h3attn_cache_gate_decide_sums(&gate, zero_prev) == 0);  // no positive denominator: compute
+    EXPECT(h3attn_cache_gate_decide_sums(nullptr, small) == -1);
+  }
   EXPECT(h3attn_cache_gate_init(&gate, -1.0, 1) == H3ATTN_ERR_INVALID_ARGUMENT);
   EXPECT(h3attn_cache_gate_init(nullptr, 0.05, 1) == H3ATTN_ERR_INVALID_ARGUMENT);
 }

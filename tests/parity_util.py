@@ -12,10 +12,55 @@ ATTN_MAX_ABS = 2e-2
 ATTN_MEAN_ABS = 2e-3
 LSE_MAX_ABS = 2e-3
 NEAR_TIE_REL = 1e-5
+# fp8 (e4m3) attention against exact float64 attention: q, k, v and the probabilities each carry
+# 3 significant bits, so the bar is looser than the bf16 one. For the workloads' inputs
+# (v ~ N(0,1)): absolute; measured worst 0.033 / 2.2e-3 on the frame workload (sparse) and
+# 0.072 / 3.2e-3 on sampled 5 s blocks (sparse, block 0), about half these limits.
+FP8_EXACT_MAX_ABS = 0.15
+FP8_EXACT_MEAN_ABS = 1e-2
+# For inputs whose token and channel magnitudes differ by powers of two (scores up to ~16), the
+# error is taken relative to the RMS of each value channel over the keys; measured worst 0.74 /
+# 0.016 on the ragged cases.
+FP8_EXACT_MAX_REL_RMS = 1.5
+FP8_EXACT_MEAN_REL_RMS = 3e-2
 
 
 def log(msg: str):
     print(f"[parity {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+# One summary record per (workload, check), printed at the end of the pytest session by
+# tests/conftest.py, so that the figures behind every pass are in the run's own output.
+RECORDS = []
+
+
+def record(workload: str, check: str, **fields):
+    """Add or merge a summary record: numeric fields keep their worst value (max, except fields
+    ending in _min which keep the min), counters (ints) add up."""
+    for r in RECORDS:
+        if r["workload"] == workload and r["check"] == check:
+            for k, v in fields.items():
+                if k not in r:
+                    r[k] = v
+                elif isinstance(v, bool) or isinstance(v, str):
+                    r[k] = v
+                elif isinstance(v, int):
+                    r[k] += v
+                elif k.endswith("_min"):
+                    r[k] = min(r[k], v)
+                else:
+                    r[k] = max(r[k], v)
+            return
+    RECORDS.append({"workload": workload, "check": check, **fields})
+
+
+def format_record(r) -> str:
+    parts = []
+    for k, v in r.items():
+        if k in ("workload", "check"):
+            continue
+        parts.append(f"{k}={v:.3g}" if isinstance(v, float) else f"{k}={v}")
+    return f"{r['workload']:>18s} {r['check']:<22s} " + " ".join(parts)
 
 
 def host_bf16(t: torch.Tensor) -> torch.Tensor:
@@ -51,7 +96,7 @@ def check_norm_rope(gpu: np.ndarray, ref: np.ndarray):
 
 def check_attention(gpu: np.ndarray, ref: np.ndarray, what: str):
     d = np.abs(gpu - ref)
-    mx, mean = float(d.max()), float(d.mean())
+    mx, mean = float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
     log(f"{what}: max-abs {mx:.3e} mean-abs {mean:.3e}")
     assert np.isfinite(gpu).all(), f"{what}: non-finite output"
     assert mx <= ATTN_MAX_ABS, f"{what}: max-abs {mx} > {ATTN_MAX_ABS}"
@@ -77,4 +122,12 @@ def check_block_sets(gpu_idx: np.ndarray, ref_idx: np.ndarray, scores: np.ndarra
     log(f"{what}: rows {g.shape[0]}, mismatched {int(mism.sum())} (near-tie {int((mism & near).sum())}), "
         f"near-tie rows {int(near.sum())}")
     assert not bad.any(), f"{what}: {int(bad.sum())} non-near-tie rows differ, first row {int(np.argmax(bad))}"
+    # in an excused row, only blocks whose scores tie with the keep-th score (within the same
+    # relative band) may be swapped
+    flat = scores.reshape(-1, nb)
+    for row in np.nonzero(mism)[0]:
+        kth = np.sort(flat[row])[::-1][keep - 1]
+        for j in set(g[row].tolist()) ^ set(r[row].tolist()):
+            assert abs(flat[row, j] - kth) <= NEAR_TIE_REL * max(abs(kth), abs(flat[row, j])), \
+                f"{what}: row {row} swaps block {j} (score {flat[row, j]!r}) far from the keep-th score {kth!r}"
     return int(mism.sum()), int(near.sum())

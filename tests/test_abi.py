@@ -200,6 +200,17 @@ def test_cache_gate_policy_matches_oracle_rule(lib):
         for r in rng.choice([0.0, 0.01, 0.05, 0.099, 0.1, 0.3, 1.0], size=40):
             assert bool(lib.h3attn_cache_gate_decide(ctypes.byref(st), float(r))) == ref.decide(float(r))
         assert st.steps == 40
+    # the ratio of the two device sums is formed inside the library
+    for mc in (1, 3):
+        st = CacheGateState()
+        assert lib.h3attn_cache_gate_init(ctypes.byref(st), 0.1, mc) == 0
+        ref = oracle.CacheGate(0.1, mc)
+        seq = [None, (0.5, 10.0), (0.5, 10.0), (0.5, 10.0), (3.0, 10.0), (0.0, 0.0), (0.2, 10.0), (0.99, 10.0)]
+        for sums in seq:
+            arg = None if sums is None else ctypes.cast((ctypes.c_double * 2)(*sums), ctypes.c_void_p)
+            want = ref.decide(float("inf") if sums is None or sums[1] <= 0 else sums[0] / sums[1])
+            assert bool(lib.h3attn_cache_gate_decide_sums(ctypes.byref(st), arg)) == want
+    assert lib.h3attn_cache_gate_decide_sums(None, None) == -1
     st = CacheGateState()
     assert lib.h3attn_cache_gate_init(ctypes.byref(st), -1.0, 1) == 1
     assert lib.h3attn_cache_gate_init(ctypes.byref(st), 0.1, -1) == 1

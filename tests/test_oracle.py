@@ -346,6 +346,36 @@ def test_near_tie_rows():
     assert not O.near_tie_rows(s, 4).any()
 
 
+def test_near_threshold_entries_hand_built_rows():
+    """Entries at, just inside and just outside the threshold max - tau, for a window of 1e-9 times
+    the row's largest magnitude. Each row is built so that one plausible slip flips an entry:
+    comparing with the maximum instead of max - tau (row a, first entry), a wider or narrower
+    window (row a, entries 3 and 7), and scaling
+    by the row maximum instead of the largest magnitude (rows b and c)."""
+    # row a: threshold 0.5, largest magnitude 1.0 -> window 1e-9
+    a = np.array([[1.0, 0.5, 0.5 + 4e-10, 0.5 + 2e-9, 0.5 - 9e-10, 0.5 - 1.1e-9, 0.5 + 1e-6, -1.0]])
+    np.testing.assert_array_equal(O.near_threshold_entries(a, 0.5),
+                                  [[False, True, True, False, True, False, False, False]])
+    # row b: the threshold -0.3 is negative while the maximum 0.2 is positive; largest magnitude
+    # 0.3 -> window 3e-10 (a window from the maximum, 2e-10, would miss entries 4 and 8)
+    b = np.array([[0.2, -0.3, 0.1, -0.3 + 2.5e-10, -0.3 + 4e-10, 0.15, 0.0, -0.3 - 2.5e-10]])
+    np.testing.assert_array_equal(O.near_threshold_entries(b, 0.5),
+                                  [[False, True, False, True, False, False, False, True]])
+    # row c: a large negative entry sets the scale (5.0 -> window 5e-9), far wider than the
+    # maximum 0.01 would give
+    c = np.array([[0.01, -5.0, -0.01 + 4e-9, -0.01 + 6e-9, -0.01, 0.0, 0.005, -0.01 - 4.9e-9]])
+    np.testing.assert_array_equal(O.near_threshold_entries(c, 0.02),
+                                  [[False, False, True, False, True, False, False, True]])
+    # the rows are independent: stacked, each keeps its own maximum and scale
+    both = np.concatenate([a, a * 4.0], axis=0)
+    np.testing.assert_array_equal(O.near_threshold_entries(both, 0.5)[0], O.near_threshold_entries(a, 0.5)[0])
+    np.testing.assert_array_equal(O.near_threshold_entries(both, 0.5)[1],
+                                  [False, False, False, False, False, False, False, False])
+    # tau = 0: the window sits on the maximum itself
+    np.testing.assert_array_equal(O.near_threshold_entries(np.array([[2.0, 2.0 - 1e-9, 1.0]]), 0.0),
+                                  [[True, True, False]])
+
+
 # ----------------------------------------------------------------------------------- sparse attention
 
 def test_sparse_keep_all_equals_dense():

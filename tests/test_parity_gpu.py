@@ -12,8 +12,9 @@ import torch
 import oracle
 from inputs import FRAME, TINY, VIDEO5S, VIDEO10S, VIDEO15S, make_inputs, random_case, sample_query_blocks
 from inputs.generate import box_blocks
-from tests.parity_util import (ATTN_MAX_ABS, ATTN_MEAN_ABS, LSE_MAX_ABS, check_attention, check_block_sets,
-                               check_norm_rope, f64, log)
+from tests.parity_util import (ATTN_MAX_ABS, ATTN_MEAN_ABS, FP8_EXACT_MAX_ABS, FP8_EXACT_MAX_REL_RMS,
+                               FP8_EXACT_MEAN_ABS, FP8_EXACT_MEAN_REL_RMS, LSE_MAX_ABS, check_attention,
+                               check_block_sets, check_norm_rope, f64, log, record)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -32,7 +33,7 @@ def _sync():
 
 # ------------------------------------------------------------------ full comparisons (small)
 
-def _full_norm_rope(h3, q, k, wq, wk, grid, sections, theta=1e4, eps=1e-6, what=""):
+def _full_norm_rope(h3, q, k, wq, wk, grid, sections, theta=1e4, eps=1e-6, what="", wl=None):
     qo, ko = h3.qk_norm_rope(q, k, wq, wk, grid, sections, theta, eps)
     _sync()
     rq, rk = oracle.qk_norm_rope(f64(q), f64(k), f64(wq), f64(wk), tuple(grid), tuple(sections), theta,
@@ -40,21 +41,24 @@ def _full_norm_rope(h3, q, k, wq, wk, grid, sections, theta=1e4, eps=1e-6, what=
     for g, r, nm in ((qo, rq, "q"), (ko, rk, "k")):
         worst, exact = check_norm_rope(f64(g), r)
         log(f"{what} norm+rope {nm}: worst {worst:.3f} ulp, exact-RNE fraction {exact:.5f}")
+        record(wl or what, "norm+rope", worst_ulp=worst, exact_rne_min=exact)
         assert worst <= 1.0, f"{what} {nm}: {worst} ulp"
         assert exact > 0.99
     return qo, ko
 
 
-def _full_dense(h3, q, k, v, what=""):
+def _full_dense(h3, q, k, v, what="", wl=None):
     o, lse = h3.dense_fwd(q, k, v, return_lse=True)
     _sync()
     ro, rl = oracle.attention(f64(q), f64(k), f64(v))
-    check_attention(f64(o), ro, f"{what} dense")
-    assert np.abs(f64(lse) - rl).max() <= LSE_MAX_ABS
+    mx, mean = check_attention(f64(o), ro, f"{what} dense")
+    lerr = float(np.abs(f64(lse) - rl).max())
+    record(wl or what, "dense (full)", max_abs=mx, mean_abs=mean, lse_max_abs=lerr)
+    assert lerr <= LSE_MAX_ABS
     return o
 
 
-def _full_select_sparse(h3, q, k, v, sparsity, what=""):
+def _full_select_sparse(h3, q, k, v, sparsity, what="", wl=None):
     idx = h3.subblock_select(q, k, sparsity)
     _sync()
     qd, kd = f64(q), f64(k)
@@ -62,12 +66,15 @@ def _full_select_sparse(h3, q, k, v, sparsity, what=""):
     keep = oracle.keep_count(scores.shape[-1], sparsity)
     ref_idx = oracle.topk_blocks(scores, keep)
     assert tuple(idx.shape) == ref_idx.shape
-    check_block_sets(idx.cpu().numpy(), ref_idx, scores, keep, f"{what} select s={sparsity}")
+    mism, near = check_block_sets(idx.cpu().numpy(), ref_idx, scores, keep, f"{what} select s={sparsity}")
+    record(wl or what, f"select s={sparsity}", rows=int(np.prod(scores.shape[:-1])), mismatched=mism, near_tie_rows=near)
     o, lse = h3.block_sparse_fwd(q, k, v, idx, return_lse=True)
     _sync()
     ro, rl = oracle.sparse_attention(qd, kd, f64(v), idx.cpu().numpy(), 64)
-    check_attention(f64(o), ro, f"{what} sparse s={sparsity}")
-    assert np.abs(f64(lse) - rl).max() <= LSE_MAX_ABS
+    mx, mean = check_attention(f64(o), ro, f"{what} sparse s={sparsity}")
+    lerr = float(np.abs(f64(lse) - rl).max())
+    record(wl or what, f"sparse s={sparsity} (full)", max_abs=mx, mean_abs=mean, lse_max_abs=lerr)
+    assert lerr <= LSE_MAX_ABS
     return idx, o
 
 
@@ -99,9 +106,9 @@ def test_frame_workload_dense_select_sparse(h3):
 @pytest.mark.parametrize("n", [1, 63, 200, 333])
 def test_ragged_shapes_full(h3, n, d):
     c = random_case(2, n, 3, d, seed=100 + n + d, device=DEV)
-    _full_dense(h3, c["q"], c["k"], c["v"], f"ragged n={n} d={d}")
+    _full_dense(h3, c["q"], c["k"], c["v"], f"ragged n={n} d={d}", wl="ragged")
     for s in (0.0, 0.5, 0.9):
-        _full_select_sparse(h3, c["q"], c["k"], c["v"], s, f"ragged n={n} d={d}")
+        _full_select_sparse(h3, c["q"], c["k"], c["v"], s, f"ragged n={n} d={d}", wl="ragged")
 
 
 def test_ragged_norm_rope_grids(h3):
@@ -109,7 +116,7 @@ def test_ragged_norm_rope_grids(h3):
                          ((1, 1, 9), 128, (0, 64, 64)), ((5, 2, 3), 64, (64, 0, 0))):
         n = grid[0] * grid[1] * grid[2]
         c = random_case(2, n, 5, d, seed=7 + n, device=DEV, scale=3.0)
-        _full_norm_rope(h3, c["q"], c["k"], c["wq"], c["wk"], grid, sec, 1e4, 1e-6, f"grid {grid}")
+        _full_norm_rope(h3, c["q"], c["k"], c["wq"], c["wk"], grid, sec, 1e4, 1e-6, f"grid {grid}", wl="ragged grids")
 
 
 def test_norm_rope_inplace_matches_out_of_place(h3):
@@ -237,33 +244,70 @@ def test_python_layer_rejects_bad_inputs(h3):
         h3.dense_fwd(c2["q"], c2["k"], c2["v"])
     with pytest.raises(ValueError):
         h3.qk_norm_rope(c["q"], c["k"], c["wq"], c["wk"], (2, 2, 2), (16, 24, 24))
+    # outputs and weights of the wrong size or on the host are refused before any launch (the
+    # kernels would write or read past them)
+    grid, sec = (1, 8, 8), (16, 24, 24)
+    with pytest.raises(ValueError):
+        h3.qk_norm_rope(c["q"], c["k"], c["wq"][:32].contiguous(), c["wk"], grid, sec)
+    with pytest.raises(ValueError):
+        h3.qk_norm_rope(c["q"], c["k"], c["wq"], c["wk"], grid, sec, out=(torch.empty_like(c["q"][:, :32]),
+                                                                           torch.empty_like(c["k"])))
+    with pytest.raises(ValueError):
+        h3.dense_fwd(c["q"], c["k"], c["v"], out=torch.empty_like(c["q"][:, :32]))
+    with pytest.raises(ValueError):
+        h3.dense_fwd(c["q"], c["k"], c["v"], out=torch.empty(tuple(c["q"].shape), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        h3.subblock_select(c["q"], c["k"], 0.5, out=torch.empty((1, 2, 1, 2), dtype=torch.int32, device=DEV))
+    idx = h3.subblock_select(c["q"], c["k"], 0.0)
+    with pytest.raises(ValueError):
+        h3.block_sparse_fwd(c["q"], c["k"], c["v"], idx, out=torch.empty_like(c["q"][:, :, :1]))
+    with pytest.raises((ValueError, TypeError)):
+        h3.block_sparse_fwd(c["q"], c["k"], c["v"], idx.cpu())
+    x = torch.randn((1, 4, 64), device=DEV).to(torch.bfloat16)
+    sh = torch.zeros((1, 64), device=DEV)
+    with pytest.raises(ValueError):
+        h3.adaln_modulate(x, sh, sh, out=torch.empty_like(x[:, :2]))
+    with pytest.raises(ValueError):
+        h3.swiglu(x, x, out=torch.empty_like(x[:, :2]))
+    with pytest.raises(ValueError):
+        h3.residual_change(x, x, out=torch.empty((3,), dtype=torch.float64, device=DEV))
+    _sync()
 
 
 # ------------------------------------------------------------------ long-video workloads (sampled)
 
 def _sampled_dense(h3, q, k, v, qblocks_per_head, what):
-    o = h3.dense_fwd(q, k, v)
+    """Dense output and LSE of every sampled query block against the oracle (each sampled row is
+    exact: it depends on all keys and on no other row)."""
+    o, lse = h3.dense_fwd(q, k, v, return_lse=True)
     _sync()
-    qh, kh, vh, oh = q.cpu(), k.cpu(), v.cpu(), o.cpu()
-    worst = 0.0
+    qh, kh, vh, oh, lh = q.cpu(), k.cpu(), v.cpu(), o.cpu(), lse.cpu()
+    worst, lworst, means = 0.0, 0.0, []
     for h, blocks in qblocks_per_head.items():
-        rows = np.concatenate([np.arange(i * 64, (i + 1) * 64) for i in blocks])
-        ref, _ = oracle.attention_head(f64(qh[0, rows, h]), f64(kh[0, :, h]), f64(vh[0, :, h]))
-        mx, _ = check_attention(f64(oh[0, rows, h]), ref, f"{what} dense head {h} blocks {blocks}")
-        worst = max(worst, mx)
+        rows = np.concatenate([np.arange(i * 64, min((i + 1) * 64, q.shape[1])) for i in blocks])
+        ref, rl = oracle.attention_head(f64(qh[0, rows, h]), f64(kh[0, :, h]), f64(vh[0, :, h]))
+        mx, mean = check_attention(f64(oh[0, rows, h]), ref, f"{what} dense head {h} ({len(blocks)} blocks)")
+        lerr = float(np.abs(f64(lh[0, h, rows]) - rl).max())
+        assert lerr <= LSE_MAX_ABS, f"{what} dense head {h}: lse error {lerr}"
+        worst, lworst = max(worst, mx), max(lworst, lerr)
+        means.append(mean)
+    nblk = sum(len(b) for b in qblocks_per_head.values())
+    record(what, "dense (sampled)", blocks=nblk, max_abs=worst, mean_abs=float(np.mean(means)), lse_max_abs=lworst)
     return worst
 
 
 def _full_select_sampled_sparse(h3, q, k, v, sparsity, qblocks_per_head, what, head_chunk=4, group_stride=1):
+    """Kept sets of every row against the oracle, then block-sparse output and LSE of the sampled
+    query blocks over their kept key blocks."""
     idx = h3.subblock_select(q, k, sparsity)
-    o = h3.block_sparse_fwd(q, k, v, idx, group_stride=group_stride)
+    o, lse = h3.block_sparse_fwd(q, k, v, idx, group_stride=group_stride, return_lse=True)
     if group_stride != 1:
         o1 = h3.block_sparse_fwd(q, k, v, idx)
         _sync()
         assert torch.equal(o, o1), f"{what}: group stride {group_stride} changed the result"
         del o1
     _sync()
-    qh, kh, vh, oh, ih = q.cpu(), k.cpu(), v.cpu(), o.cpu(), idx.cpu().numpy()
+    qh, kh, vh, oh, lh, ih = q.cpu(), k.cpu(), v.cpu(), o.cpu(), lse.cpu(), idx.cpu().numpy()
     heads = q.shape[2]
     nb = idx.shape[2]
     keep = idx.shape[3]
@@ -272,13 +316,23 @@ def _full_select_sampled_sparse(h3, q, k, v, sparsity, qblocks_per_head, what, h
         sl = slice(h0, min(heads, h0 + head_chunk))
         scores = oracle.block_scores(f64(qh[:, :, sl]), f64(kh[:, :, sl]), 64)
         ref_idx = oracle.topk_blocks(scores, keep)
-        check_block_sets(ih[:, sl], ref_idx, scores, keep, f"{what} select s={sparsity} heads {h0}..")
+        mism, near = check_block_sets(ih[:, sl], ref_idx, scores, keep, f"{what} select s={sparsity} heads {h0}..")
+        record(what, f"select s={sparsity}", rows=int(np.prod(scores.shape[:-1])), mismatched=mism,
+               near_tie_rows=near)
+    worst, lworst, means, nblk = 0.0, 0.0, [], 0
     for h, blocks in qblocks_per_head.items():
         for i in blocks:
-            rows = np.arange(i * 64, (i + 1) * 64)
+            rows = np.arange(i * 64, min((i + 1) * 64, q.shape[1]))
             keys = oracle.block_token_ids(ih[0, h, i], 64, q.shape[1])
-            ref, _ = oracle.attention_head(f64(qh[0, rows, h]), f64(kh[0, keys, h]), f64(vh[0, keys, h]))
-            check_attention(f64(oh[0, rows, h]), ref, f"{what} sparse s={sparsity} head {h} block {i}")
+            ref, rl = oracle.attention_head(f64(qh[0, rows, h]), f64(kh[0, keys, h]), f64(vh[0, keys, h]))
+            mx, mean = check_attention(f64(oh[0, rows, h]), ref, f"{what} sparse s={sparsity} head {h} block {i}")
+            lerr = float(np.abs(f64(lh[0, h, rows]) - rl).max())
+            assert lerr <= LSE_MAX_ABS, f"{what} sparse head {h} block {i}: lse error {lerr}"
+            worst, lworst = max(worst, mx), max(lworst, lerr)
+            means.append(mean)
+            nblk += 1
+    record(what, f"sparse s={sparsity} (sampled)", blocks=nblk, max_abs=worst, mean_abs=float(np.mean(means)),
+           lse_max_abs=lworst)
 
 
 def _samples(cfg, per_head, extra=()):
@@ -290,14 +344,14 @@ def _samples(cfg, per_head, extra=()):
 def test_video5s_dense_sampled(h3):
     cfg = VIDEO5S
     x = make_inputs(cfg, DEV)
-    _sampled_dense(h3, x["q"], x["k"], x["v"], _samples(cfg, 3), "5s")
+    _sampled_dense(h3, x["q"], x["k"], x["v"], _samples(cfg, 32), "5s")
 
 
 @pytest.mark.timeout(900)
 def test_video5s_select_and_sparse(h3):
     cfg = VIDEO5S
     x = make_inputs(cfg, DEV)
-    _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, _samples(cfg, 3), "5s", head_chunk=8,
+    _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, _samples(cfg, 32), "5s", head_chunk=8,
                                 group_stride=h3.frame_group_stride(cfg.grid))
 
 
@@ -316,6 +370,7 @@ def test_video10s_norm_rope_full(h3):
         for g, r, nm in ((qoh[:, :, sl], rq, "q"), (koh[:, :, sl], rk, "k")):
             worst, exact = check_norm_rope(f64(g), r)
             log(f"10s norm+rope {nm} heads {h0}..{h0 + 1}: worst {worst:.3f} ulp, exact {exact:.5f}")
+            record("10s", "norm+rope", worst_ulp=worst, exact_rne_min=exact)
             assert worst <= 1.0 and exact > 0.99
 
 
@@ -324,9 +379,9 @@ def test_video10s_dense_select_sparse(h3):
     cfg = VIDEO10S
     x = make_inputs(cfg, DEV)
     qo, ko = h3.qk_norm_rope(x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, cfg.theta, cfg.eps)
-    _sampled_dense(h3, qo, ko, x["v"], _samples(cfg, 3), "10s")
+    _sampled_dense(h3, qo, ko, x["v"], _samples(cfg, 32), "10s")
     for s in cfg.sparsities:
-        _full_select_sampled_sparse(h3, qo, ko, x["v"], s, _samples(cfg, 3), "10s",
+        _full_select_sampled_sparse(h3, qo, ko, x["v"], s, _samples(cfg, 32), "10s",
                                     group_stride=h3.frame_group_stride(cfg.grid))
 
 
@@ -336,10 +391,10 @@ def test_video15s_boxes_select_sparse_dense(h3):
     x = make_inputs(cfg, DEV)
     bb = box_blocks(cfg.grid, x["boxes"])
     extra = [bb[0], bb[len(bb) // 2], bb[-1]]
-    smp = _samples(cfg, 4, extra=extra)
+    smp = _samples(cfg, 32, extra=extra)
     _full_select_sampled_sparse(h3, x["q"], x["k"], x["v"], 0.75, smp, "15s",
                                 group_stride=h3.frame_group_stride(cfg.grid))
-    _sampled_dense(h3, x["q"], x["k"], x["v"], _samples(cfg, 2), "15s")
+    _sampled_dense(h3, x["q"], x["k"], x["v"], smp, "15s")
 
 
 # ------------------------------------------------------------------ threshold mode (CSR)
@@ -373,6 +428,8 @@ def _check_threshold_sets(rp, ci, scores, tau, what):
     near = oracle.near_threshold_entries(flat, tau)
     log(f"{what}: tau {tau:.4g}, kept {g.sum()} of {g.size} ({g.mean():.3f}), differing {int(diff.sum())} "
         f"(near-threshold {int((diff & near).sum())})")
+    record(what.split()[0], "threshold select", entries=int(g.size), kept=int(g.sum()), differing=int(diff.sum()),
+           near_threshold_entries=int(near.sum()))
     assert not (diff & ~near).any(), f"{what}: {int((diff & ~near).sum())} entries differ away from the threshold"
 
 
@@ -670,13 +727,32 @@ def test_fp8_quantize_bit_exact(h3, b, n, h, d):
     log(f"fp8 quantize {b}x{n}x{h}x{d}: codes and scales bit-exact")
 
 
-def _fp8_compare(o, lse, ref, rl, wmax, dev, what, exact=None):
+def _fp8_vs_exact(g, exact, what, wl, v=None):
+    """fp8 output against exact float64 attention: absolute for the workloads' N(0,1) values, or,
+    with v given, relative to the RMS of each value channel over the keys of its (batch, head)."""
+    err = np.abs(g - exact)
+    if v is None:
+        mx, mean = float(err.max()), float(err.mean())
+        lim = (FP8_EXACT_MAX_ABS, FP8_EXACT_MEAN_ABS)
+    else:
+        rms = np.sqrt(np.mean(v * v, axis=1, keepdims=True))          # [B, 1, Hd, D]
+        rel = err / np.maximum(rms, 1e-30)
+        mx, mean = float(rel.max()), float(rel.mean())
+        lim = (FP8_EXACT_MAX_REL_RMS, FP8_EXACT_MEAN_REL_RMS)
+    log(f"{what}: fp8 path vs exact attention max {mx:.3g} mean {mean:.3g} (limits {lim[0]}, {lim[1]}"
+        f"{', per value-channel RMS' if v is not None else ''})")
+    record(wl, "fp8 vs exact" + (" (rel rms)" if v is not None else ""), max_abs=mx, mean_abs=mean)
+    assert mx <= lim[0] and mean <= lim[1], f"{what}: fp8 vs exact attention max {mx} mean {mean}"
+
+
+def _fp8_compare(o, lse, ref, rl, wmax, dev, what, exact=None, wl="fp8", v=None):
     """fp8 path vs its oracle. Where the fp32 score decides an e4m3 probability code next to a
     rounding boundary, the GPU and the float64 oracle may pick neighbouring codes; one such
     choice moves a row by at most 2^-3 * wmax * dev (oracle quantities of that row). The bound
     per element is therefore ATTN_MAX_ABS + 2^-8 |ref| (bf16 output rounding of larger values)
     + 2^-3 * wmax * dev; the mean error must stay within the bf16 path's bound and at most 2% of
-    the rows may exceed ATTN_MAX_ABS + 2^-8 |ref|."""
+    the rows may exceed ATTN_MAX_ABS + 2^-8 |ref|. With `exact` given, the output is also held to
+    the fp8 bar against exact attention (_fp8_vs_exact)."""
     g = f64(o)
     err = np.abs(g - ref)
     w = np.transpose(wmax, (0, 2, 1))[..., None]                       # [B, N, Hd, 1]
@@ -687,13 +763,14 @@ def _fp8_compare(o, lse, ref, rl, wmax, dev, what, exact=None):
     lbound = LSE_MAX_ABS + math.log(2.0) * np.log2(1.0 + 2.0 ** -3 * wmax)
     log(f"{what}: max-abs {err.max():.3g} mean-abs {err.mean():.3g}, rows over base: {int(over.sum())} "
         f"of {over.size}, worst err/bound {(err / bound).max():.3f}, lse max-abs {lerr.max():.3g}")
-    if exact is not None:
-        log(f"{what}: fp8 path vs exact attention max-abs {np.abs(g - exact).max():.3g}, "
-            f"mean-abs {np.abs(g - exact).mean():.3g} (diagnostic)")
+    record(wl, "fp8 vs fp8 oracle", max_abs=float(err.max()), mean_abs=float(err.mean()),
+           err_over_bound=float((err / bound).max()), rows_over_base=int(over.sum()), rows=int(over.size))
     assert err.mean() <= ATTN_MEAN_ABS + 2.0 ** -9 * np.abs(ref).mean(), what
     assert (err <= bound).all(), what
     assert over.mean() <= 0.02, what
     assert (lerr <= lbound).all(), what
+    if exact is not None:
+        _fp8_vs_exact(g, exact, what, wl, v)
 
 
 @pytest.mark.parametrize("b,n,d", [(1, 1, 64), (1, 63, 128), (2, 200, 64), (1, 333, 128), (1, 64 * 20, 128),
@@ -705,13 +782,16 @@ def test_fp8_dense_and_sparse_full(h3, b, n, d):
     o, lse = h3.fp8_dense_fwd(fq, return_lse=True)
     _sync()
     ref, rl, wm, dv = oracle.attention_fp8_detail(qd, kd, vd)
-    _fp8_compare(o, lse, ref, rl, wm, dv, f"fp8 dense n={n} d={d}", exact=oracle.attention(qd, kd, vd)[0])
+    _fp8_compare(o, lse, ref, rl, wm, dv, f"fp8 dense n={n} d={d}", exact=oracle.attention(qd, kd, vd)[0],
+                 wl="fp8 ragged", v=vd)
     for s in (0.0, 0.5, 0.9):
         idx = h3.subblock_select(c["q"], c["k"], s)
         os_, ls = h3.fp8_block_sparse_fwd(fq, idx, return_lse=True)
         _sync()
-        rs, rls, wms, dvs = oracle.attention_fp8_detail(qd, kd, vd, idx.cpu().numpy())
-        _fp8_compare(os_, ls, rs, rls, wms, dvs, f"fp8 sparse n={n} d={d} s={s}")
+        ih = idx.cpu().numpy()
+        rs, rls, wms, dvs = oracle.attention_fp8_detail(qd, kd, vd, ih)
+        _fp8_compare(os_, ls, rs, rls, wms, dvs, f"fp8 sparse n={n} d={d} s={s}",
+                     exact=oracle.sparse_attention(qd, kd, vd, ih, 64)[0], wl="fp8 ragged", v=vd)
         if s == 0.0:
             assert torch.equal(os_, o), "keep-all fp8 sparse must equal fp8 dense bit for bit"
 
@@ -725,9 +805,11 @@ def test_fp8_frame_workload(h3):
     os_, ls = h3.fp8_block_sparse_fwd(fq, idx, return_lse=True)
     _sync()
     ref, rl, wm, dv = oracle.attention_fp8_detail(qd, kd, vd)
-    _fp8_compare(o, lse, ref, rl, wm, dv, "fp8 dense frame", exact=oracle.attention(qd, kd, vd)[0])
-    rs, rls, wms, dvs = oracle.attention_fp8_detail(qd, kd, vd, idx.cpu().numpy())
-    _fp8_compare(os_, ls, rs, rls, wms, dvs, "fp8 sparse frame s=0.75")
+    _fp8_compare(o, lse, ref, rl, wm, dv, "fp8 dense frame", exact=oracle.attention(qd, kd, vd)[0], wl="frame")
+    ih = idx.cpu().numpy()
+    rs, rls, wms, dvs = oracle.attention_fp8_detail(qd, kd, vd, ih)
+    _fp8_compare(os_, ls, rs, rls, wms, dvs, "fp8 sparse frame s=0.75",
+                 exact=oracle.sparse_attention(qd, kd, vd, ih, 64)[0], wl="frame")
 
 
 @pytest.mark.timeout(900)
@@ -745,14 +827,20 @@ def test_fp8_video5s_sampled(h3):
     qh, kh, vh, oh, osh, ih = x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), o.cpu(), os_.cpu(), idx.cpu().numpy()
     for h in (0, 17, 47):
         qd, kd, vd = f64(qh[:, :, h:h + 1]), f64(kh[:, :, h:h + 1]), f64(vh[:, :, h:h + 1])
-        for i in sample_query_blocks(cfg.n_blocks, 3, seed=3000 + h):
+        for i in sample_query_blocks(cfg.n_blocks, 4, seed=3000 + h):
             rows = np.arange(i * 64, (i + 1) * 64)
             for what, got, bidx in (("dense", oh, None), ("sparse", osh, ih[0, h, i])):
                 ref, rl, wm, dv = oracle.attention_fp8_rows(qd, kd, vd, 0, 0, i, block_idx=bidx, detail=True)
-                err = np.abs(f64(got[0, rows, h]) - ref)
+                g = f64(got[0, rows, h])
+                err = np.abs(g - ref)
                 bound = ATTN_MAX_ABS + 2.0 ** -8 * np.abs(ref) + 2.0 ** -3 * wm[:, None] * dv
                 log(f"fp8 {what} 5s head {h} block {i}: max-abs {err.max():.3g} mean-abs {err.mean():.3g}")
+                record("5s", f"fp8 {what} vs fp8 oracle", blocks=1, max_abs=float(err.max()),
+                       mean_abs=float(err.mean()))
                 assert (err <= bound).all() and err.mean() <= ATTN_MEAN_ABS, f"fp8 {what} 5s head {h} block {i}"
+                keys = slice(None) if bidx is None else oracle.block_token_ids(bidx, 64, cfg.n_tokens)
+                exact, _ = oracle.attention_head(qd[0, rows, 0], kd[0, keys, 0], vd[0, keys, 0])
+                _fp8_vs_exact(g, exact, f"fp8 {what} 5s head {h} block {i}", "5s")
 
 
 @pytest.mark.timeout(900)

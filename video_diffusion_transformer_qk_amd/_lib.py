@@ -58,6 +58,7 @@ SIGNATURES = {
     "h3attn_residual_change": (ctypes.c_int, [_P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "h3attn_cache_gate_init": (ctypes.c_int, [_P, ctypes.c_double, _I32]),
     "h3attn_cache_gate_decide": (_I32, [_P, ctypes.c_double]),
+    "h3attn_cache_gate_decide_sums": (_I32, [_P, _P]),
     "h3attn_fp8_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I64, _I32, _I32]),
     "h3attn_fp8_quantize": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _I32,
                                            _P, ctypes.c_size_t, _P]),
@@ -121,6 +122,21 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
 
 
+def _need_shape(t: torch.Tensor, name: str, shape, like: torch.Tensor):
+    """t has exactly `shape` and lives on the same device as `like` (the kernels write and read
+    exactly that many elements on that device)."""
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+    if t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, expected {like.device}")
+
+
+def _same_device(like: torch.Tensor, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != like.device:
+            raise ValueError(f"{name} is on {t.device}, expected {like.device}")
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -165,12 +181,17 @@ def qk_norm_rope(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch
     if q.shape != k.shape:
         raise ValueError("q and k must have the same shape")
     b, n, h, d = q.shape
+    _need_shape(w_q, "w_q", (d,), q)
+    _need_shape(w_k, "w_k", (d,), q)
+    _same_device(q, k=k)
     if inplace:
         qo, ko = q, k
     elif out is not None:
         qo, ko = out
         _need(qo, "q_out", torch.bfloat16, 4)
         _need(ko, "k_out", torch.bfloat16, 4)
+        _need_shape(qo, "q_out", q.shape, q)
+        _need_shape(ko, "k_out", q.shape, q)
     else:
         qo, ko = torch.empty_like(q), torch.empty_like(k)
     g = Grid(*[int(x) for x in grid])
@@ -192,8 +213,10 @@ def dense_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, return_lse: boo
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k, v must have the same shape")
     b, n, h, d = q.shape
+    _same_device(q, k=k, v=v)
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", torch.bfloat16, 4)
+    _need_shape(o, "out", q.shape, q)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
     _check(lib.h3attn_dense_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
                                 b, h, n, d, _stream()))
@@ -215,8 +238,10 @@ def subblock_select(q: torch.Tensor, k: torch.Tensor, sparsity: float, block_siz
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8, 1)
+    _same_device(q, k=k, workspace=workspace)
     idx = torch.empty((b, h, nb, keep), dtype=torch.int32, device=q.device) if out is None else out
     _need(idx, "block_idx", torch.int32, 4)
+    _need_shape(idx, "block_idx", (b, h, nb, keep), q)
     _check(lib.h3attn_subblock_select(q.data_ptr(), k.data_ptr(), b, h, n, d, block_size, float(sparsity),
                                       keep, idx.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()))
     return idx
@@ -274,10 +299,12 @@ def block_sparse_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_id
     if tuple(block_idx.shape[:3]) != (b, h, nb):
         raise ValueError(f"block_idx must be [B, heads, nB, keep] = [{b}, {h}, {nb}, keep]")
     keep = block_idx.shape[3]
+    _same_device(q, k=k, v=v, block_idx=block_idx)
     if validate:
         _raise_if_flagged(check_block_idx(block_idx), "block_idx")
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", torch.bfloat16, 4)
+    _need_shape(o, "out", q.shape, q)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), block_idx.data_ptr(), keep, o.data_ptr(), _ptr(lse), b, h, n, d,
             block_size)
@@ -308,6 +335,7 @@ def subblock_select_threshold(q: torch.Tensor, k: torch.Tensor, tau: float, bloc
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8, 1)
+    _same_device(q, k=k, workspace=workspace)
     row_ptr = torch.empty((b * h * nb + 1,), dtype=torch.int64, device=q.device)
     st = _stream()
     _check(lib.h3attn_subblock_threshold_count(q.data_ptr(), k.data_ptr(), b, h, n, d, block_size, float(tau),
@@ -335,10 +363,12 @@ def block_sparse_csr_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_
     nb = -(-n // block_size)
     if row_ptr.numel() != b * h * nb + 1:
         raise ValueError(f"row_ptr must have B*heads*nB + 1 = {b * h * nb + 1} entries")
+    _same_device(q, k=k, v=v, row_ptr=row_ptr, col_idx=col_idx)
     if validate:
         _raise_if_flagged(check_csr(row_ptr, col_idx, b, h, nb), "CSR kept sets")
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", torch.bfloat16, 4)
+    _need_shape(o, "out", q.shape, q)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device) if return_lse else None
     ci = col_idx if col_idx.numel() > 0 else torch.zeros((1,), dtype=torch.int32, device=q.device)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), row_ptr.data_ptr(), ci.data_ptr(), o.data_ptr(), _ptr(lse), b, h,
@@ -360,8 +390,10 @@ def adaln_modulate(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor, ep
     b, n, c = x.shape
     if tuple(shift.shape) != (b, c) or tuple(scale.shape) != (b, c):
         raise ValueError("shift and scale must be [B, C]")
+    _same_device(x, shift=shift, scale=scale)
     o = torch.empty_like(x) if out is None else out
     _need(o, "out", torch.bfloat16, 3)
+    _need_shape(o, "out", x.shape, x)
     _check(lib.h3attn_adaln_modulate(x.data_ptr(), shift.data_ptr(), scale.data_ptr(), o.data_ptr(), b, n, c,
                                      float(eps), _stream()))
     return o
@@ -385,8 +417,10 @@ def swiglu(gate: torch.Tensor, up: torch.Tensor, out: Optional[torch.Tensor] = N
             return f
         t2 = t.reshape(-1, f) if t.is_contiguous() else t.view(-1, f)
         return t2.stride(0)
+    _same_device(gate, up=up)
     o = torch.empty(gate.shape, dtype=torch.bfloat16, device=gate.device) if out is None else out
     _need(o, "out", torch.bfloat16)
+    _need_shape(o, "out", gate.shape, gate)
     _check(lib.h3attn_swiglu(gate.data_ptr(), up.data_ptr(), o.data_ptr(), rows, f, row_stride(gate), row_stride(up),
                              _stream()))
     return o
@@ -404,8 +438,11 @@ def residual_change(cur: torch.Tensor, prev: torch.Tensor, workspace: Optional[t
     need = int(lib.h3attn_residual_workspace_bytes(n))
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=cur.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _same_device(cur, prev=prev, workspace=workspace)
     res = torch.empty((2,), dtype=torch.float64, device=cur.device) if out is None else out
     _need(res, "out", torch.float64, 1)
+    _need_shape(res, "out", (2,), cur)
     _check(lib.h3attn_residual_change(cur.data_ptr(), prev.data_ptr(), n, res.data_ptr(), workspace.data_ptr(),
                                       workspace.numel(), _stream()))
     return res
@@ -429,11 +466,16 @@ class CacheGate:
         return bool(r)
 
     def step(self, cur: torch.Tensor, prev: Optional[torch.Tensor]) -> bool:
-        """Measure the change of cur against prev on the GPU (one host read) and decide."""
-        if prev is None:
-            return self.decide(float("inf"))
-        d, p = residual_change(cur, prev).tolist()
-        return self.decide(d / p if p > 0 else float("inf"))
+        """Measure the change of cur against prev on the GPU, read the two sums back and let the
+        library form the ratio and decide (h3attn_cache_gate_decide_sums)."""
+        sums = None
+        if prev is not None:
+            host = (ctypes.c_double * 2)(*residual_change(cur, prev).cpu().tolist())
+            sums = ctypes.cast(host, ctypes.c_void_p)
+        r = self._lib.h3attn_cache_gate_decide_sums(ctypes.byref(self._state), sums)
+        if r < 0:
+            raise RuntimeError("invalid gate state")
+        return bool(r)
 
 
 class Fp8QKV(NamedTuple):
@@ -463,6 +505,7 @@ def fp8_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: 
     b, n, h, d = q.shape
     nb = -(-n // block_size)
     dev = q.device
+    _same_device(q, k=k, v=v)
     if out is None:
         fq = Fp8QKV(torch.empty((b, n, h, d), dtype=torch.uint8, device=dev),
                     torch.empty((b, n, h, d), dtype=torch.uint8, device=dev),
@@ -474,9 +517,11 @@ def fp8_quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: 
         fq = out
         if _fp8_check(fq) != (b, n, h, d):
             raise ValueError("out tensors do not match q's shape")
+        _same_device(q, q8=fq.q8, k8=fq.k8, v8t=fq.v8t, q_scale=fq.q_scale, k_scale=fq.k_scale, v_scale=fq.v_scale)
     need = fp8_workspace_bytes(b, h, n, d, block_size)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _same_device(q, workspace=workspace)
     _check(lib.h3attn_fp8_quantize(q.data_ptr(), k.data_ptr(), v.data_ptr(), fq.q8.data_ptr(), fq.k8.data_ptr(),
                                    fq.v8t.data_ptr(), fq.q_scale.data_ptr(), fq.k_scale.data_ptr(),
                                    fq.v_scale.data_ptr(), b, h, n, d, block_size, workspace.data_ptr(),
@@ -495,6 +540,7 @@ def _fp8_check(fq: Fp8QKV):
             tuple(fq.q_scale.shape) != (b, h, nb) or tuple(fq.k_scale.shape) != (b, h, nb) or \
             tuple(fq.v_scale.shape) != (b, h, d):
         raise ValueError("inconsistent fp8 tensors")
+    _same_device(fq.q8, k8=fq.k8, v8t=fq.v8t, q_scale=fq.q_scale, k_scale=fq.k_scale, v_scale=fq.v_scale)
     return b, n, h, d
 
 
@@ -504,6 +550,7 @@ def fp8_dense_fwd(fq: Fp8QKV, return_lse: bool = False, out: Optional[torch.Tens
     b, n, h, d = _fp8_check(fq)
     o = torch.empty((b, n, h, d), dtype=torch.bfloat16, device=fq.q8.device) if out is None else out
     _need(o, "out", torch.bfloat16, 4)
+    _need_shape(o, "out", (b, n, h, d), fq.q8)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=o.device) if return_lse else None
     _check(lib.h3attn_fp8_dense_fwd(fq.q8.data_ptr(), fq.k8.data_ptr(), fq.v8t.data_ptr(), fq.q_scale.data_ptr(),
                                     fq.k_scale.data_ptr(), fq.v_scale.data_ptr(), o.data_ptr(), _ptr(lse), b, h, n, d,
@@ -522,10 +569,12 @@ def fp8_block_sparse_fwd(fq: Fp8QKV, block_idx: torch.Tensor, return_lse: bool =
     if tuple(block_idx.shape[:3]) != (b, h, nb):
         raise ValueError(f"block_idx must be [B, heads, nB, keep] = [{b}, {h}, {nb}, keep]")
     keep = block_idx.shape[3]
+    _same_device(fq.q8, block_idx=block_idx)
     if validate:
         _raise_if_flagged(check_block_idx(block_idx), "block_idx")
     o = torch.empty((b, n, h, d), dtype=torch.bfloat16, device=fq.q8.device) if out is None else out
     _need(o, "out", torch.bfloat16, 4)
+    _need_shape(o, "out", (b, n, h, d), fq.q8)
     lse = torch.empty((b, h, n), dtype=torch.float32, device=o.device) if return_lse else None
     _check(lib.h3attn_fp8_block_sparse_fwd(fq.q8.data_ptr(), fq.k8.data_ptr(), fq.v8t.data_ptr(),
                                            fq.q_scale.data_ptr(), fq.k_scale.data_ptr(), fq.v_scale.data_ptr(),

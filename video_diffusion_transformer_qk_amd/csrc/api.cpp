@@ -598,4 +598,9 @@ int32_t h3attn_cache_gate_decide(h3attn_cache_gate* gate, double rel_change) {
   return reuse ? 1 : 0;
 }
 
+int32_t h3attn_cache_gate_decide_sums(h3attn_cache_gate* gate, const double* sums) {
+  const double rel = (sums != nullptr && sums[1] > 0.0) ? sums[0] / sums[1] : INFINITY;
+  return h3attn_cache_gate_decide(gate, rel);
+}
+
 }  // extern "C"
