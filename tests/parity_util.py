@@ -10,7 +10,11 @@ import torch
 # spec tolerances for bf16 attention outputs against the float64 oracle (N(0,1) inputs)
 ATTN_MAX_ABS = 2e-2
 ATTN_MEAN_ABS = 2e-3
-LSE_MAX_ABS = 2e-3
+# LSE (natural log). The kernels add up the bf16-rounded probabilities that P.V uses (each within
+# 2^-9 relative), so ln(sum) may move by up to ln(1 + 2^-9) = 1.95e-3; the float32 logits (128
+# exact products summed in float32) add up to D 2^-24 sum|q||k| / sqrt(D), about 1e-3 on the rows
+# of the 15 s workload's planted high-norm keys. 4e-3 covers both.
+LSE_MAX_ABS = 4e-3
 NEAR_TIE_REL = 1e-5
 # fp8 (e4m3) attention against exact float64 attention: q, k, v and the probabilities each carry
 # 3 significant bits, so the bar is looser than the bf16 one. For the workloads' inputs
