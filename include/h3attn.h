@@ -62,9 +62,12 @@ const char* h3attn_last_error(void);
  * Returns -1 if n_kblocks <= 0 or sparsity is outside [0, 1). */
 int32_t h3attn_keep_count(int32_t n_kblocks, double sparsity);
 
-/* Device workspace bytes that h3attn_subblock_select needs: pooled block means of q and k in
- * float64 ([batch, heads, nB, head_dim] each) plus the float64 block-score matrix
- * ([batch, heads, nB, nB]), each region 256-byte aligned. Returns 0 on invalid sizes. */
+/* Device workspace bytes that h3attn_subblock_select needs, O(batch * heads * nB * head_dim):
+ * the pooled block means of q and k in float64 ([batch, heads, nB, head_dim] each), their
+ * base-256 integer digits (3 bytes per mean), a power-of-two exponent and two norms per block,
+ * per-head key maxima and a list of rows for the exact fallback, each region 256-byte aligned
+ * (22 * head_dim + 36 bytes per (batch, head, block), plus padding). No score matrix is stored:
+ * block scores live on chip. Returns 0 on invalid sizes. */
 size_t h3attn_select_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tokens,
                                      int32_t head_dim, int32_t block_size);
 
@@ -100,13 +103,16 @@ h3attn_status h3attn_dense_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const
  * (the last one may be partial). Block importance is estimated, since the pages leave it open,
  * as the dot product of the mean query of block i and the mean key of block j (over sqrt(D));
  * per query block i the `keep` highest-scoring key blocks are kept, equal scores ranking the
- * lower key index first. Means and scores are computed in float64.
+ * lower key index first. The kept sets are those of the float64 scores of the float64 block
+ * means: every score is bounded on the int8 matrix cores (exact integer products of the means'
+ * base-256 digits, with a rigorous error bound) and only the entries whose bound straddles the
+ * keep-th score are decided on their float64 value; no score matrix is written to memory.
  * block_idx: int32 [batch, heads, nB, keep], each row ascending. keep must equal
  * h3attn_keep_count(nB, sparsity). workspace: device buffer of at least
  * h3attn_select_workspace_bytes(...) bytes, 256-byte aligned; its contents are scratch.
  * Errors: bad pointers/sizes, sparsity outside [0,1), keep mismatch, workspace too small ->
  * INVALID_ARGUMENT; head_dim not 64/128, block_size != 64 or nB > 19968 (a row of float64
- * scores must fit in one CU's LDS) -> UNSUPPORTED. */
+ * scores must fit in one CU's LDS for the exact fallback) -> UNSUPPORTED. */
 h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
                                      int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
                                      int32_t block_size, double sparsity, int32_t keep,
@@ -167,7 +173,8 @@ h3attn_status h3attn_check_block_idx(const int32_t* block_idx, int32_t batch, in
 size_t h3attn_threshold_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tokens,
                                         int32_t head_dim, int32_t block_size);
 
-/* Pass 1: pools, scores, per-row thresholds and counts; writes row_ptr (int64, B*heads*nB + 1
+/* Pass 1: pools, per-row exact maxima, thresholds and counts (scores recomputed on chip, the
+ * entries near the threshold decided on their float64 score); writes row_ptr (int64, B*heads*nB + 1
  * entries, row_ptr[0] = 0, last entry = total kept count). Errors: as h3attn_subblock_select
  * (nB > 19968 -> UNSUPPORTED included), plus tau < 0 or NaN -> INVALID_ARGUMENT. */
 h3attn_status h3attn_subblock_threshold_count(const h3attn_bf16* q, const h3attn_bf16* k,
@@ -176,7 +183,8 @@ h3attn_status h3attn_subblock_threshold_count(const h3attn_bf16* q, const h3attn
                                               int64_t* row_ptr, void* workspace, size_t workspace_bytes,
                                               hipStream_t stream);
 
-/* Pass 2: fills col_idx (int32) from the workspace left by pass 1 (same sizes, same workspace,
+/* Pass 2: recomputes the scores and fills col_idx (int32), deciding every entry as pass 1 did,
+ * from the workspace left by pass 1 (same sizes, same workspace,
  * same stream, nothing in between that writes the workspace). Entries at positions >=
  * col_capacity are not written: size col_idx from row_ptr's last entry. */
 h3attn_status h3attn_subblock_threshold_fill(int32_t batch, int32_t heads, int64_t n_tokens,

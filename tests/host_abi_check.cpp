@@ -126,18 +126,31 @@ void check_attention() {
 
 void check_select() {
   const size_t ws = h3attn_select_workspace_bytes(1, 2, 640, 64, 64);
-  EXPECT(ws >= 2 * 1 * 2 * 10 * 64 * sizeof(double) + 1 * 2 * 10 * 10 * sizeof(double));
+  EXPECT(ws >= 2 * 1 * 2 * 10 * 64 * sizeof(double) + 2 * 1 * 2 * 32 * 64 * 3);
   int32_t* idx = P<int32_t>(0xA0000);
   const int32_t keep = h3attn_keep_count(10, 0.75);
   EXPECT(keep == 3);
   int n0 = g_launches;
   EXPECT(launched(h3attn_subblock_select(Q, K, 1, 2, 640, 64, 64, 0.75, keep, idx, WS, ws, nullptr), n0));
   EXPECT(g_sel.n_blocks == 10 && g_sel.keep == 3 && g_sel.block_idx == idx);
-  // the three workspace regions are 256-byte aligned and disjoint inside the workspace
-  const uintptr_t w0 = (uintptr_t)WS;
-  const uintptr_t m = (uintptr_t)g_sel.q_mean, km = (uintptr_t)g_sel.k_mean, sc = (uintptr_t)g_sel.scores;
-  EXPECT(m == w0 && km >= m + 2 * 10 * 64 * 8 && sc >= km + 2 * 10 * 64 * 8 && sc + 2 * 10 * 10 * 8 <= w0 + ws);
-  EXPECT((km & 255) == 0 && (sc & 255) == 0);
+  // the workspace regions are 256-byte aligned, in order, disjoint and inside the workspace
+  // (B*H = 2, nB = 10 padded to 32, D = 64)
+  {
+    const uintptr_t w0 = (uintptr_t)WS;
+    const uintptr_t reg[] = {(uintptr_t)g_sel.q_mean, (uintptr_t)g_sel.k_mean, (uintptr_t)g_sel.q_digits,
+                             (uintptr_t)g_sel.k_digits, (uintptr_t)g_sel.q_exp, (uintptr_t)g_sel.k_exp,
+                             (uintptr_t)g_sel.q_norm, (uintptr_t)g_sel.k_norm, (uintptr_t)g_sel.key_stat,
+                             (uintptr_t)g_sel.fb_count};
+    const size_t len[] = {2 * 10 * 64 * 8, 2 * 10 * 64 * 8, 2 * 32 * 64 * 3, 2 * 32 * 64 * 3, 2 * 32 * 4, 2 * 32 * 4,
+                          2 * 32 * 8, 2 * 32 * 8, 2 * 16, (1 + 2 * 10) * 4};
+    EXPECT(reg[0] == w0);
+    for (int i = 0; i < 10; ++i) {
+      EXPECT((reg[i] & 255) == 0);
+      if (i > 0) EXPECT(reg[i] >= reg[i - 1] + len[i - 1]);
+    }
+    EXPECT(reg[9] + len[9] <= w0 + ws);
+    EXPECT((uintptr_t)g_sel.fb_rows == reg[9] + 4);
+  }
   EXPECT(h3attn_subblock_select(Q, K, 1, 2, 640, 64, 64, 0.75, keep, idx, WS, ws - 1, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
   EXPECT(h3attn_subblock_select(Q, K, 1, 2, 640, 64, 64, 1.0, keep, idx, WS, ws, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
   EXPECT(h3attn_subblock_select(Q, K, 1, 2, 19969LL * 64, 64, 64, 0.75, keep, idx, WS, ws, nullptr) == H3ATTN_ERR_UNSUPPORTED);

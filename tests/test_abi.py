@@ -59,11 +59,18 @@ def test_keep_count_matches_oracle_and_golden(lib):
 
 
 def test_workspace_bytes(lib):
-    nb = 1953
-    means = 48 * nb * 128 * 8
-    scores = 48 * nb * nb * 8
+    """The select workspace is O(B * heads * nB * D): float64 means, 3 digit bytes per mean, an
+    exponent and two norms per block (blocks padded to 32), per-head key maxima, the fallback list.
+    No nB x nB score matrix."""
     r = lambda x: (x + 255) // 256 * 256
-    assert lib.h3attn_select_workspace_bytes(1, 48, 124992, 128, 64) == 2 * r(means) + r(scores)
+    for (bh, nb, d) in ((48, 1953, 128), (12, 5733, 128), (2, 10, 64)):
+        nbp = (nb + 31) // 32 * 32
+        want = 2 * (r(bh * nb * d * 8) + r(bh * nbp * d * 3) + r(bh * nbp * 4) + r(bh * nbp * 8)) \
+            + r(bh * 16) + r((1 + bh * nb) * 4)
+        assert lib.h3attn_select_workspace_bytes(1, bh, nb * 64, d, 64) == want
+        assert want < bh * nbp * (22 * d + 36) + 10 * 256          # linear in nB, far below nB^2
+    # 5 s workload: 0.27 GB (the float64 score matrix alone would have been 1.46 GB)
+    assert lib.h3attn_select_workspace_bytes(1, 48, 124992, 128, 64) < 0.28e9
     assert lib.h3attn_select_workspace_bytes(0, 48, 124992, 128, 64) == 0
 
 

@@ -233,6 +233,50 @@ def test_select_ties_resolve_to_lower_index(h3):
             assert 2 in row
 
 
+@pytest.mark.parametrize("nb", [100, 300])
+def test_select_rows_of_equal_scores(h3, nb):
+    """Every key block equal: every score of a row ties, so the kept set is the lowest `keep`
+    indices. With 100 blocks the row's entries all fall in one bracket and are decided on their
+    float64 scores; with 300 the bracket cannot be narrowed and the row goes to the exact radix
+    fallback. Both must give the same answer as the oracle's stable sort."""
+    c = random_case(1, 64 * nb, 3, 128, seed=31 + nb, device=DEV)
+    k = c["k"][:, :64].repeat(1, nb, 1, 1).contiguous()
+    idx = h3.subblock_select(c["q"], k, 0.5)
+    _sync()
+    keep = oracle.keep_count(nb, 0.5)
+    got = idx.cpu().numpy().reshape(-1, keep)
+    assert (got == np.arange(keep)).all(), f"{nb} equal blocks: first bad row {np.nonzero((got != np.arange(keep)).any(1))[0][:3]}"
+    scores = oracle.block_scores(f64(c["q"]), f64(k), 64)
+    np.testing.assert_array_equal(got, oracle.topk_blocks(scores, keep).reshape(-1, keep))
+    record("equal scores", f"select nB={nb}", rows=got.shape[0], mismatched=0)
+
+
+def test_select_scores_apart_by_far_less_than_the_bound(h3):
+    """Key blocks that differ only in one channel of one token, by (j + 1) 2^-20: the block scores
+    of a row differ by about 1e-8 of their size, far inside the error bound of the integer-digit
+    scores and far above float64 rounding, so every entry is decided on its float64 score. The
+    kept sets must equal the oracle's bit for bit (no near-tie allowance is used here)."""
+    nb, d = 40, 128
+    c = random_case(1, 64 * nb, 4, d, seed=77, device=DEV)
+    k = c["k"][:, :64].repeat(1, nb, 1, 1).float()
+    for j in range(nb):
+        k[:, 64 * j, :, 0] = (j + 1) * 2.0 ** -20
+    k = k.to(torch.bfloat16).contiguous()
+    for s in (0.5, 0.8):
+        idx = h3.subblock_select(c["q"], k, s)
+        _sync()
+        keep = oracle.keep_count(nb, s)
+        scores = oracle.block_scores(f64(c["q"]), f64(k), 64)
+        ref = oracle.topk_blocks(scores, keep)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+        # the construction really is ordered by j: the kept blocks are the highest or the lowest
+        q0 = oracle.block_means(f64(c["q"]), 64)[..., 0].reshape(-1)
+        rows = ref.reshape(-1, keep)
+        assert all((r == np.arange(nb - keep, nb)).all() if q > 0 else (r == np.arange(keep)).all()
+                   for r, q in zip(rows, q0) if q != 0)
+        record("near-equal scores", f"select s={s}", rows=rows.shape[0], mismatched=0)
+
+
 def test_python_layer_rejects_bad_inputs(h3):
     c = random_case(1, 64, 2, 64, seed=1, device=DEV)
     with pytest.raises(TypeError):

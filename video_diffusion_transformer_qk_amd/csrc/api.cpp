@@ -81,14 +81,48 @@ int32_t h3attn_keep_count(int32_t n_kblocks, double sparsity) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Regions of the selection workspace, each 256-byte aligned: float64 means of q and k
+// [B*H, nB, D]; their base-256 digits [B*H, nBp, D, 3] int8 (nBp = nB rounded up to 32); the
+// per-block exponents [B*H, nBp] int32 and norms [B*H, nBp, 2] float32 of q and k; per-head key
+// maxima [B*H, 4] int32; the fallback row count and list [1 + B*H*nB] int32.
+struct SelectLayout {
+  size_t mean, digits, exps, norms, key_stat, fb, total;
+};
+
+static SelectLayout select_layout(int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim, int32_t block_size) {
+  SelectLayout L{};
+  const size_t nb = (size_t)((n_tokens + block_size - 1) / block_size);
+  const size_t nbp = (nb + 31) / 32 * 32;
+  const size_t bh = (size_t)batch * (size_t)heads;
+  L.mean = align256(bh * nb * (size_t)head_dim * sizeof(double));
+  L.digits = align256(bh * nbp * (size_t)head_dim * 3);
+  L.exps = align256(bh * nbp * sizeof(int32_t));
+  L.norms = align256(bh * nbp * 2 * sizeof(float));
+  L.key_stat = align256(bh * 4 * sizeof(int32_t));
+  L.fb = align256((1 + bh * nb) * sizeof(int32_t));
+  L.total = 2 * (L.mean + L.digits + L.exps + L.norms) + L.key_stat + L.fb;
+  return L;
+}
+
+static void select_pointers(h3attn::SelectArgs& a, void* workspace, const SelectLayout& L) {
+  unsigned char* p = static_cast<unsigned char*>(workspace);
+  a.q_mean = reinterpret_cast<double*>(p); p += L.mean;
+  a.k_mean = reinterpret_cast<double*>(p); p += L.mean;
+  a.q_digits = reinterpret_cast<int8_t*>(p); p += L.digits;
+  a.k_digits = reinterpret_cast<int8_t*>(p); p += L.digits;
+  a.q_exp = reinterpret_cast<int32_t*>(p); p += L.exps;
+  a.k_exp = reinterpret_cast<int32_t*>(p); p += L.exps;
+  a.q_norm = reinterpret_cast<float*>(p); p += L.norms;
+  a.k_norm = reinterpret_cast<float*>(p); p += L.norms;
+  a.key_stat = reinterpret_cast<int32_t*>(p); p += L.key_stat;
+  a.fb_count = reinterpret_cast<int32_t*>(p);
+  a.fb_rows = reinterpret_cast<int32_t*>(p) + 1;
+}
+
 size_t h3attn_select_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tokens,
                                      int32_t head_dim, int32_t block_size) {
   if (batch <= 0 || heads <= 0 || n_tokens <= 0 || head_dim <= 0 || block_size <= 0) return 0;
-  const size_t nb = (size_t)((n_tokens + block_size - 1) / block_size);
-  const size_t bh = (size_t)batch * (size_t)heads;
-  const size_t means = align256(bh * nb * (size_t)head_dim * sizeof(double));
-  const size_t scores = align256(bh * nb * nb * sizeof(double));
-  return 2 * means + scores;
+  return select_layout(batch, heads, n_tokens, head_dim, block_size).total;
 }
 
 h3attn_status h3attn_qk_norm_rope(const h3attn_bf16* q_in, const h3attn_bf16* k_in,
@@ -179,7 +213,7 @@ h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
   if ((int64_t)batch * heads > 65535) return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads must be <= 65535");
   const int64_t nb = (n_tokens + block_size - 1) / block_size;
   if (nb * 8 > h3attn::kSelectRowLdsBytes)
-    return fail(H3ATTN_ERR_UNSUPPORTED, "%lld blocks exceed the per-row LDS budget of the top-k kernel", (long long)nb);
+    return fail(H3ATTN_ERR_UNSUPPORTED, "%lld blocks exceed the per-row LDS budget of the selection kernels", (long long)nb);
   const int32_t want = h3attn_keep_count((int32_t)nb, sparsity);
   if (keep != want) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep %d does not match keep_count(%lld, %g) = %d", keep, (long long)nb, sparsity, want);
   const size_t need = h3attn_select_workspace_bytes(batch, heads, n_tokens, head_dim, block_size);
@@ -191,11 +225,7 @@ h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
   h3attn::SelectArgs a{};
   a.q = q; a.k = k; a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
   a.block_size = block_size; a.n_blocks = (int32_t)nb; a.keep = keep; a.block_idx = block_idx;
-  const size_t means = align256((size_t)batch * heads * (size_t)nb * head_dim * sizeof(double));
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  a.q_mean = reinterpret_cast<double*>(ws);
-  a.k_mean = reinterpret_cast<double*>(ws + means);
-  a.scores = reinterpret_cast<double*>(ws + 2 * means);
+  select_pointers(a, workspace, select_layout(batch, heads, n_tokens, head_dim, block_size));
   h3attn::launch_subblock_select(a, stream);
   return check_launch("h3attn_subblock_select");
 }
@@ -269,15 +299,12 @@ size_t h3attn_threshold_workspace_bytes(int32_t batch, int32_t heads, int64_t n_
 
 static void threshold_layout(h3attn::SelectArgs& a, void* workspace, int32_t batch, int32_t heads,
                              int64_t nb, int32_t head_dim) {
-  const size_t means = align256((size_t)batch * heads * (size_t)nb * head_dim * sizeof(double));
-  const size_t scores = align256((size_t)batch * heads * (size_t)nb * (size_t)nb * sizeof(double));
+  const SelectLayout L = select_layout(batch, heads, nb * 64, head_dim, 64);
+  select_pointers(a, workspace, L);
   const size_t rows = align256((size_t)batch * heads * (size_t)nb * 8);
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  a.q_mean = reinterpret_cast<double*>(ws);
-  a.k_mean = reinterpret_cast<double*>(ws + means);
-  a.scores = reinterpret_cast<double*>(ws + 2 * means);
-  a.row_thr = reinterpret_cast<double*>(ws + 2 * means + scores);
-  a.row_cnt = reinterpret_cast<int64_t*>(ws + 2 * means + scores + rows);
+  unsigned char* ws = static_cast<unsigned char*>(workspace) + L.total;
+  a.row_thr = reinterpret_cast<double*>(ws);
+  a.row_cnt = reinterpret_cast<int64_t*>(ws + rows);
 }
 
 h3attn_status h3attn_subblock_threshold_count(const h3attn_bf16* q, const h3attn_bf16* k,

@@ -48,8 +48,9 @@ void launch_dense_fwd(const AttnArgs& a, hipStream_t stream);
 void launch_block_sparse_fwd(const AttnArgs& a, hipStream_t stream);
 void launch_block_sparse_csr_fwd(const AttnArgs& a, hipStream_t stream);
 
-// Dynamic LDS for one row of nB float64 scores (the top-k keys, the threshold fill's staged row):
-// what a CU's 160 KB leaves after the kernels' static LDS; rows longer than this are refused.
+// Dynamic LDS for one row of nB float64 scores (the selection fallback's row) and for the
+// selection kernels' per-row bitmaps: what a CU's 160 KB leaves after the kernels' static LDS;
+// longer rows are refused.
 constexpr int64_t kSelectRowLdsBytes = 160 * 1024 - 4096;
 
 struct SelectArgs {
@@ -58,9 +59,18 @@ struct SelectArgs {
   int64_t n_tokens;
   int32_t batch, heads, head_dim, block_size, n_blocks, keep;
   int32_t* block_idx;
-  double* q_mean;   // workspace: [B, H, nB, D]
-  double* k_mean;   // workspace: [B, H, nB, D]
-  double* scores;   // workspace: [B, H, nB, nB]
+  // workspace (layout in api.cpp); nBp = nB rounded up to 32
+  double* q_mean;      // [B*H, nB, D] float64 block means
+  double* k_mean;
+  int8_t* q_digits;    // [B*H, nBp/32, D/32, 3, 64 lanes, 16 bytes]: base-256 digits of the means
+  int8_t* k_digits;    //   in the int8 MFMA operand order
+  int32_t* q_exp;      // [B*H, nBp] power-of-two exponent of each block's digits
+  int32_t* k_exp;
+  float* q_norm;       // [B*H, nBp, 2] L1 and L2 norm of each block's mean (rounded up)
+  float* k_norm;
+  int32_t* key_stat;   // [B*H, 4]: largest key exponent, largest key L1 and L2 norm (float bits)
+  int32_t* fb_count;   // rows routed to the exact fallback
+  int32_t* fb_rows;    // [B*H*nB] their row indices
   // threshold mode only
   double tau_raw;           // tau * sqrt(D): threshold offset on the unscaled dot products
   double* row_thr;          // workspace: [B*H*nB] per-row threshold

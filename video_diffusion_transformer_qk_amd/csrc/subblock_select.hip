@@ -1,25 +1,41 @@
-// SubBlock key-block selection for gfx950: block pooling, block scores, per-row top-k.
+// SubBlock key-block selection for gfx950: block pooling, block scores and the per-row selection,
+// with the scores kept on chip.
 //
 // Source: "MiniMax-H3 的 6.24 倍，不能直接算成六倍产能" (xiaodao.ai), section
 // "6.24 倍里，真正有损的部分大约是三倍": queries and keys are cut into 64-token blocks, the key
 // blocks that would contribute little are estimated and dropped, and the fraction dropped is
 // the sparsity. The pages leave the estimator open; this library scores key block j for query
-// block i by mean(q over block i) . mean(k over block j) and keeps the keep highest per row,
-// equal scores ranking the lower key index first, indices written in ascending order.
+// block i by s_ij = mean(q over block i) . mean(k over block j) and keeps the keep highest per
+// row, equal scores ranking the lower key index first, indices written in ascending order. The
+// 1/sqrt(D) of the definition is a positive factor and does not change the order.
 //
-// Exactness: block sums of bf16 values are exact in float64, and the 1/sqrt(D) scale is
-// dropped (a positive factor does not change the order), so the GPU ranks by a float64 dot
-// product of the same means the float64 definition uses; the top-k itself is an exact radix
-// select over order-preserving 64-bit keys.
+// Exactness. Block sums of bf16 values are exact in float64, so the float64 block means are the
+// definition's means. Ranking by a float64 dot product of them would need the float64 matrix
+// cores for every score (4.7e10 flop at the 5 s workload); instead every score is first bounded:
+//   * each mean vector x is written as integers X = round(x * 2^-e) with |X| <= 2^22 (one power of
+//     two e per block), each X split into three signed base-256 digits d2 d1 d0;
+//   * the int8 matrix cores form, exactly in int32, the digit products of weight 2^32, 2^24 and
+//     2^16 (six of the nine digit pairs); the rest, and the rounding of x to X, is bounded
+//     rigorously per row (row_bound below);
+//   * so every approximate score v_ij carries |v_ij - s_ij * scale_i| <= E_i.
+// A row's keep-th largest v is bracketed by a histogram of its v values (one more pass of the
+// same products when a bin holds too many); every entry above the bracket by more than 2 E_i is
+// kept, every entry below it by more than 2 E_i dropped, and only the entries in between are
+// decided on their float64 scores (a handful per row). The kept sets are therefore those of the
+// float64 scores, the same as the float64 definition except where two float64 scores differ in
+// their last bits. Rows that do not resolve this way (ties of many equal scores) go to a
+// fallback kernel that computes the whole row's float64 scores and selects with an exact radix
+// select.
 //
-// Kernels:
-//  pool_kernel   grid (heads * nB, 1, batch): 256 threads, 16-byte coalesced row reads (all
-//                issued before the sums), fp64 sums reduced through LDS in a fixed order ->
-//                means [B, H, nB, D] for q and k.
-//  score_kernel  grid (ceil(nB/T), ceil(nB/T), B*H), T = 64 or 128: a T x T tile of Qm . Km^T on
-//                the fp64 MFMA (v_mfma_f64_16x16x4f64), D staged through LDS in chunks of 32.
-//  topk_kernel   grid (nB, heads, batch): one row of nB scores -> LDS keys -> 8-pass MSB radix
-//                select of the keep-th largest key -> ordered compaction of the kept indices.
+// Kernels (top-k mode):
+//  pool_kernel          one workgroup per (batch, head, block): fp64 means, their integer digits in
+//                       the int8 MFMA operand order, exponent and norms.
+//  key_stats_kernel     per (batch, head): largest key exponent and norms (for the bounds).
+//  topk_select_kernel   per (batch, head, 32 query blocks): histogram pass(es), classification
+//                       pass, resolution on float64 scores, ordered write of the kept indices.
+//  fallback_kernel      rows routed there: float64 row in LDS, radix select.
+// Threshold mode (keep j iff s_ij >= max_j s_ij - tau): threshold_count_kernel (exact row maximum
+// and kept counts), row_ptr_scan_kernel, threshold_fill_kernel (the same decisions, written as CSR).
 #include "device_util.h"
 #include "kernels.h"
 #include "launch_util.h"
@@ -27,13 +43,36 @@
 namespace h3attn {
 namespace {
 
-constexpr int kPoolThreads = 256;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(16))) int i32x16;
 
+constexpr int kPoolThreads = 256;
+constexpr int kRows = 32;                   // query blocks per selection workgroup (the MFMA's columns)
+constexpr int kSelThreads = 256;            // 4 waves
+constexpr int kWaves = kSelThreads / 64;
+constexpr int kBins = 1024;                 // histogram bins per row and level
+constexpr int kHistStride = kBins / 2 + 1;  // 32-bit words per row (two 16-bit counts each, +1 pad)
+constexpr int kCap = 160;                   // candidate slots per row
+constexpr int kAmbCap = 64;                 // entries decided on float64 scores per row
+constexpr int kDigitShift = 21;             // |x| * 2^-e in [2^21, 2^22): |X| <= 2^22
+constexpr int kZeroExp = -1000;             // exponent recorded for an all-zero mean vector
+// |P1 * 2^8 + P0| per channel for the dropped digit pairs (d1 d0', d0 d1' and d0 d0', digits in
+// [-128, 127]) plus the 1/4 of the rounding product term: 128*128*(2*256 + 1) + 1/4
+constexpr double kDropPerChannel = 8404992.25;
+
+__device__ __forceinline__ int64_t n_pad(int32_t nb) { return ((int64_t)nb + kRows - 1) / kRows * kRows; }
+
+// ------------------------------------------------------------------------------------ pooling
+
+// One workgroup per (b, head, block j), head fastest. Threads hold 16-byte row chunks of q and k
+// and sum in fp64 (exact); lanes of the first wave finish the sums in a fixed order, write the
+// means, reduce max|x|, sum|x| and sum x^2 across the row's chunks, and write the digits.
 template <int D>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int PAIRS = 2 * CH;        // (tensor, chunk) pairs
   constexpr int TL = kPoolThreads / PAIRS;  // token lanes
+  constexpr int KS = D / 32;           // MFMA k steps
   __shared__ double red[TL][PAIRS][8];
 
   const int tid = threadIdx.x;
@@ -69,84 +108,263 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[tl][pair][e] = acc[e];
   __syncthreads();
-  // tl == 0 lanes finish the sum in a fixed order and write the mean
+  if (tid >= 64) return;
+  // lanes 0 .. PAIRS-1 of the first wave: (tensor, chunk) = (lane / CH, lane % CH)
+  const int64_t bh = (int64_t)b * a.heads + head;
+  const double cnt = (double)(t1 - t0);
+  double m[8];
+  double amax = 0.0, l1 = 0.0, l2 = 0.0;
   if (tl == 0) {
-    const double cnt = (double)(t1 - t0);
-    double* dst = (tensor == 0 ? a.q_mean : a.k_mean) + (((int64_t)b * a.heads + head) * a.n_blocks + j) * D + chunk * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       double s = 0.0;
       for (int u = 0; u < TL; ++u) s += red[u][pair][e];
-      dst[e] = s / cnt;
+      m[e] = s / cnt;
+      amax = fmax(amax, fabs(m[e]));
+      l1 += fabs(m[e]);
+      l2 += m[e] * m[e];
+    }
+    double* dst = (tensor == 0 ? a.q_mean : a.k_mean) + (bh * a.n_blocks + j) * D + chunk * 8;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) *reinterpret_cast<double2*>(dst + e) = double2{m[e], m[e + 1]};
+  }
+  // reduce over the CH lanes of the same tensor (xor offsets below CH stay inside the group)
+#pragma unroll
+  for (int off = 1; off < CH; off <<= 1) {
+    amax = fmax(amax, __shfl_xor(amax, off));
+    l1 += __shfl_xor(l1, off);
+    l2 += __shfl_xor(l2, off);
+  }
+  if (tl != 0) return;
+  const int ex = amax > 0.0 ? ilogb(amax) - kDigitShift : 0;
+  // digits: X = d0 + 256 d1 + 65536 d2, each digit in [-128, 127]; |X| <= 2^22 so |d2| <= 64
+  uint32_t dig[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int x = (int)rint(ldexp(m[e], -ex));
+    const int d0 = ((x & 255) ^ 128) - 128;
+    const int x1 = (x - d0) >> 8;
+    const int d1 = ((x1 & 255) ^ 128) - 128;
+    const int d2 = (x1 - d1) >> 8;
+    dig[0][e / 4] |= (uint32_t)(d0 & 255) << (8 * (e % 4));
+    dig[1][e / 4] |= (uint32_t)(d1 & 255) << (8 * (e % 4));
+    dig[2][e / 4] |= (uint32_t)(d2 & 255) << (8 * (e % 4));
+  }
+  // operand slot of this 8-channel chunk: k step t = chunk / 4, lane group g = (chunk % 4) / 2,
+  // bytes 8 * (chunk % 2) of lane (j % 32) + 32 g in the 1 KB fragment of (chunk-of-32 j / 32, t, digit)
+  const int t = chunk / 4, g = (chunk % 4) / 2, half = chunk % 2;
+  const int64_t nchunks = n_pad(a.n_blocks) / kRows;
+  int8_t* base = (tensor == 0 ? a.q_digits : a.k_digits);
+#pragma unroll
+  for (int L = 0; L < 3; ++L) {
+    int8_t* p = base + (((bh * nchunks + j / kRows) * KS + t) * 3 + L) * 1024 + ((j % kRows) + 32 * g) * 16 + 8 * half;
+    *reinterpret_cast<u32x2*>(p) = u32x2{dig[L][0], dig[L][1]};
+  }
+  if (chunk == 0) {
+    const int64_t r = bh * n_pad(a.n_blocks) + j;
+    (tensor == 0 ? a.q_exp : a.k_exp)[r] = amax > 0.0 ? ex : kZeroExp;
+    // norms rounded up (with a margin for the float64 sums' own rounding): they only bound errors
+    const float n1 = __double2float_ru(l1 * (1.0 + 0x1p-40));
+    const float n2 = __double2float_ru(sqrt(l2) * (1.0 + 0x1p-40));
+    *reinterpret_cast<float2*>((tensor == 0 ? a.q_norm : a.k_norm) + 2 * r) = float2{n1, n2};
+  }
+}
+
+// Per (batch, head): the largest key exponent and key norms over the blocks; also clears the
+// count of fallback rows (this kernel runs after pooling and before any selection kernel).
+__global__ __launch_bounds__(256) void key_stats_kernel(SelectArgs a) {
+  __shared__ int s_e[4];
+  __shared__ float s_1[4], s_2[4];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int e = kZeroExp;
+  float n1 = 0.f, n2 = 0.f;
+  const int64_t r0 = bh * n_pad(a.n_blocks);
+  for (int j = tid; j < a.n_blocks; j += 256) {
+    e = max(e, a.k_exp[r0 + j]);
+    const float2 nn = *reinterpret_cast<const float2*>(a.k_norm + 2 * (r0 + j));
+    n1 = fmaxf(n1, nn.x);
+    n2 = fmaxf(n2, nn.y);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    e = max(e, __shfl_xor(e, off));
+    n1 = fmaxf(n1, __shfl_xor(n1, off));
+    n2 = fmaxf(n2, __shfl_xor(n2, off));
+  }
+  if (lane == 0) { s_e[wave] = e; s_1[wave] = n1; s_2[wave] = n2; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) { e = max(e, s_e[w]); n1 = fmaxf(n1, s_1[w]); n2 = fmaxf(n2, s_2[w]); }
+    a.key_stat[4 * bh + 0] = e;
+    a.key_stat[4 * bh + 1] = __float_as_int(n1);
+    a.key_stat[4 * bh + 2] = __float_as_int(n2);
+    a.key_stat[4 * bh + 3] = 0;
+    if (bh == 0) *a.fb_count = 0;
+  }
+}
+
+// ------------------------------------------------------------------------------- the bounds
+
+// Row i's approximate scores are v_ij = I_ij * 2^(f_j - F) (I_ij the kept digit products over
+// 2^16, f_j key block j's exponent, F the largest over the head's key blocks), in float32. They
+// stand for s_ij * 2^-(e_i + 16 + F). With X = x 2^-e + dx, |dx| <= 1/2 per channel (likewise Y):
+//   |X.Y - 2^-(e+f) s| <= |x|_1 2^-e / 2 + |y|_1 2^-f / 2 + D/4,   dropped pairs <= D * 8404992,
+// hence in v units |v - s 2^-(e+16+F)| <= D 8404992.25 2^-16 + |x|_1 2^-(e+17) + max|y|_1 2^-(F+17),
+// plus 2^-22 |v| for the float32 evaluation of v and 2^-126 for float32 underflow. The range
+// bound |v| <= |x|_2 max|y|_2 2^-(e+16+F) + E gives the histogram's span.
+struct RowBound {
+  double e_v;      // error bound E (v units)
+  double b_v;      // |v| <= b_v
+  double to_v;     // v units per unit of s: 2^-(e+16+F)
+};
+
+template <int D>
+__device__ __forceinline__ RowBound row_bound(const SelectArgs& a, int64_t bh, int i) {
+  const int64_t r = bh * n_pad(a.n_blocks) + i;
+  const int e = a.q_exp[r];
+  const float2 qn = *reinterpret_cast<const float2*>(a.q_norm + 2 * r);
+  const int F = a.key_stat[4 * bh + 0];
+  const double y1 = (double)__int_as_float(a.key_stat[4 * bh + 1]);
+  const double y2 = (double)__int_as_float(a.key_stat[4 * bh + 2]);
+  RowBound rb;
+  const double to_v = ldexp(1.0, -(e + 16 + F));
+  double ev = (double)D * kDropPerChannel * 0x1p-16;
+  if (qn.x > 0.f) ev += (double)qn.x * ldexp(1.0, -(e + 17));
+  if (y1 > 0.0) ev += y1 * ldexp(1.0, -(F + 17));
+  double bv = (double)qn.y * y2 * to_v + ev;
+  bv *= 1.0 + 0x1p-10;
+  rb.e_v = (ev + 0x1p-22 * bv) * (1.0 + 0x1p-10) + 0x1p-126;
+  rb.b_v = bv;
+  rb.to_v = to_v;
+  return rb;
+}
+
+// The float64 score q_mean_i . k_mean_j, summed in channel order (the one float64 evaluation used
+// by every kernel here, so that all of them decide an entry the same way).
+template <int D>
+__device__ __forceinline__ double exact_score(const double* qm, const double* km) {
+  double s = 0.0;
+#pragma unroll 8
+  for (int d = 0; d < D; d += 2) {
+    const double2 x = *reinterpret_cast<const double2*>(qm + d);
+    const double2 y = *reinterpret_cast<const double2*>(km + d);
+    s = fma(x.x, y.x, s);
+    s = fma(x.y, y.y, s);
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------- the score pass
+
+// Query operand of a workgroup's 32 rows: for each k step and digit, lane l holds the 16 bytes
+// of row (i0 + l % 32) for channels 32 t + 16 (l / 32) ..; the key operand is laid out alike.
+template <int D>
+struct QueryOperand {
+  i32x4 f[D / 32][3];
+  __device__ __forceinline__ void load(const SelectArgs& a, int64_t bh, int chunk, int lane) {
+    const int64_t nchunks = n_pad(a.n_blocks) / kRows;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int L = 0; L < 3; ++L)
+        f[t][L] = *reinterpret_cast<const i32x4*>(a.q_digits + (((bh * nchunks + chunk) * (D / 32) + t) * 3 + L) * 1024 + lane * 16);
+  }
+};
+
+// Every (row, key) score of the workgroup's rows, key chunks of 32 spread over the waves. For each
+// valid entry calls f(r, j, v): r the row inside the workgroup, j the key block, v the
+// approximate score. The MFMA's output holds key 8 (k / 4) + 4 (l / 32) + k % 4 of query l % 32 in
+// accumulator k of lane l.
+template <int D, typename Fn>
+__device__ __forceinline__ void score_pass(const SelectArgs& a, const QueryOperand<D>& qo, int64_t bh, int F,
+                                           int wave, int lane, Fn&& fn) {
+  const int nb = a.n_blocks;
+  const int64_t nchunks = n_pad(nb) / kRows;
+  const int8_t* kd = a.k_digits + bh * nchunks * (D / 32) * 3 * 1024 + lane * 16;
+  const int* ke = a.k_exp + bh * n_pad(nb) + 4 * (lane >> 5);
+  const int r = lane & 31;
+  for (int c = wave; c < nchunks; c += kWaves) {
+    i32x4 kf[D / 32][3];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int L = 0; L < 3; ++L)
+        kf[t][L] = *reinterpret_cast<const i32x4*>(kd + ((c * (D / 32) + t) * 3 + L) * 1024);
+    i32x4 fe[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) fe[g] = *reinterpret_cast<const i32x4*>(ke + 32 * c + 8 * g);
+    i32x16 p4 = {}, p3 = {}, p2 = {};
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      p4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][2], qo.f[t][2], p4, 0, 0, 0);
+      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][2], qo.f[t][1], p3, 0, 0, 0);
+      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][1], qo.f[t][2], p3, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][2], qo.f[t][0], p2, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][1], qo.f[t][1], p2, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][0], qo.f[t][2], p2, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int j = 32 * c + 8 * (k / 4) + 4 * (lane >> 5) + (k % 4);
+      if (j < nb) {
+        const float hi = fmaf((float)p4[k], 65536.f, (float)p3[k] * 256.f);
+        const float v = ldexpf(hi + (float)p2[k], fe[k / 4][k % 4] - F);
+        fn(r, j, v);
+      }
     }
   }
 }
 
-typedef double f64x4 __attribute__((ext_vector_type(4)));
+// ---------------------------------------------------------------------- histogram bracketing
 
-// Qm . Km^T on the fp64 matrix cores. v_mfma_f64_16x16x4f64 takes A[i][k] from lane i + 16k and
-// B[k][j] from lane j + 16k, and returns D[4r + l/16][l%16] in register r of lane l. A workgroup
-// of 4 waves computes a TILE x TILE block of scores, each wave a (TILE/2)^2 quarter as
-// (TILE/32)^2 16x16 tiles. Both operands are staged through LDS as [row][d] with a row stride of
-// DC + 4 doubles, so the 16 rows x 4 k of an operand read fall in 2 passes over the 64 banks.
-template <int D, int TILE, int DC>
-__global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
-  constexpr int LD = DC + 4;
-  constexpr int RT = TILE / 32;  // 16x16 tiles per wave per dimension
-  __shared__ __attribute__((aligned(16))) double qs[TILE * LD];
-  __shared__ __attribute__((aligned(16))) double ks[TILE * LD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, kq = lane >> 4;
-  const int64_t bh = blockIdx.z;
-  const int nb = a.n_blocks;
-  const int i0 = blockIdx.y * TILE, j0 = blockIdx.x * TILE;
-  const int rb = (wave >> 1) * (TILE / 2), cb = (wave & 1) * (TILE / 2);
-  const double* qm = a.q_mean + bh * (int64_t)nb * D;
-  const double* km = a.k_mean + bh * (int64_t)nb * D;
-  f64x4 acc[RT][RT];
+// Bin of v in a row's first-level histogram over [-B, B] (t = (v + B) * NBINS / 2B, clamped),
+// and the sub-bin inside a chosen bin b (exact: t - b is in [0, 1) for entries of bin b, except in
+// the clamped end bins, whose sub-bins are clamped too).
+__device__ __forceinline__ float bin_pos(float v, float bsum, float scale) { return (v + bsum) * scale; }
+__device__ __forceinline__ int bin_of(float t) { return (int)fminf(fmaxf(t, 0.f), (float)(kBins - 1)); }
+__device__ __forceinline__ int sub_of(float t, int b) { return (int)fminf(fmaxf((t - (float)b) * (float)kBins, 0.f), (float)(kBins - 1)); }
+
+__device__ __forceinline__ void hist_add(uint32_t* hist, int r, int bin) {
+  atomicAdd(&hist[r * kHistStride + (bin >> 1)], 1u << (16 * (bin & 1)));
+}
+__device__ __forceinline__ int hist_get(const uint32_t* hist, int r, int bin) {
+  return (int)((hist[r * kHistStride + (bin >> 1)] >> (16 * (bin & 1))) & 0xffffu);
+}
+
+// One wave finds, in row r's histogram, the bin holding the want-th largest entry: returns the bin
+// and, through above/count, the entries in higher bins and in the bin. Lane l owns bins
+// [kBins - 16 (l + 1), kBins - 16 l), highest first.
+__device__ int find_bin(const uint32_t* hist, int r, int want, int lane, int* above, int* count) {
+  int c[16];
+  int s = 0;
 #pragma unroll
-  for (int u = 0; u < RT; ++u)
-#pragma unroll
-    for (int w = 0; w < RT; ++w) acc[u][w] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int dc = 0; dc < D; dc += DC) {
-    // stage TILE x DC of Qm and Km, 16 bytes per thread and step (rows past nb repeat the last)
-#pragma unroll
-    for (int e = tid; e < TILE * DC / 2; e += 256) {
-      const int r = e / (DC / 2), c2 = e % (DC / 2);
-      const int qi = i0 + r < nb ? i0 + r : nb - 1;
-      const int kj = j0 + r < nb ? j0 + r : nb - 1;
-      *reinterpret_cast<double2*>(&qs[r * LD + 2 * c2]) = *reinterpret_cast<const double2*>(qm + (int64_t)qi * D + dc + 2 * c2);
-      *reinterpret_cast<double2*>(&ks[r * LD + 2 * c2]) = *reinterpret_cast<const double2*>(km + (int64_t)kj * D + dc + 2 * c2);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < DC / 4; ++kk) {
-      double av[RT], bv[RT];
-#pragma unroll
-      for (int u = 0; u < RT; ++u) {
-        av[u] = qs[(rb + 16 * u + l16) * LD + 4 * kk + kq];
-        bv[u] = ks[(cb + 16 * u + l16) * LD + 4 * kk + kq];
-      }
-#pragma unroll
-      for (int u = 0; u < RT; ++u)
-#pragma unroll
-        for (int w = 0; w < RT; ++w) acc[u][w] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[w], acc[u][w], 0, 0, 0);
-    }
-    __syncthreads();
+  for (int u = 0; u < 16; ++u) {
+    c[u] = hist_get(hist, r, kBins - 1 - (16 * lane + u));
+    s += c[u];
   }
-  double* out = a.scores + bh * (int64_t)nb * nb;
+  int inc = s;
 #pragma unroll
-  for (int u = 0; u < RT; ++u)
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  const int before = inc - s;
+  const unsigned long long hit = __ballot(before < want && want <= inc);
+  const int owner = hit ? (int)__builtin_ctzll(hit) : 63;
+  int bin = 0, ab = 0, cn = 0;
+  if (lane == owner) {
+    int acc = before;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + rb + 16 * u + 4 * r + kq;
-      if (i >= nb) continue;
-#pragma unroll
-      for (int w = 0; w < RT; ++w) {
-        const int j = j0 + cb + 16 * w + l16;
-        if (j < nb) __builtin_nontemporal_store(acc[u][w][r], out + (int64_t)i * nb + j);
-      }
+    for (int u = 0; u < 16; ++u) {
+      if (acc < want && want <= acc + c[u]) { bin = kBins - 1 - (16 * lane + u); ab = acc; cn = c[u]; }
+      acc += c[u];
     }
+  }
+  bin = __shfl(bin, owner);
+  *above = __shfl(ab, owner);
+  *count = __shfl(cn, owner);
+  return bin;
 }
 
 // order-preserving map of a double to uint64 (larger double -> larger key); -0 is folded to +0
@@ -156,27 +374,269 @@ __device__ __forceinline__ uint64_t order_key(double x) {
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
 
-constexpr int kTopkThreads = 256;
-static_assert(kTopkThreads == 256, "one histogram bin per thread");
+// wave-wide sums and exclusive scans of one int per lane
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+__device__ __forceinline__ int wave_excl_scan(int x, int lane) {
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  return inc - x;
+}
 
-// Calls f(j, row[j]) for this thread's j = tid, tid + 256, ... < n, issuing 8 loads at a time so
-// that a thread has several in flight (a plain loop waits for each load before the next).
-template <typename F>
-__device__ __forceinline__ void for_row(const double* row, int n, F f) {
-  for (int j0 = threadIdx.x; j0 < n; j0 += 8 * kTopkThreads) {
-    double v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = j0 + u * kTopkThreads;
-      v[u] = j < n ? __builtin_nontemporal_load(row + j) : 0.0;
+// Writes the set bits of a row's bitmap (words [0, words)) in ascending order to dst, one wave;
+// returns the number written (positions at or past cap are not written).
+__device__ int64_t write_bits(const uint32_t* bits, int words, int32_t* dst, int64_t cap, int lane) {
+  int64_t carry = 0;
+  for (int w0 = 0; w0 < words; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t m = w < words ? bits[w] : 0u;
+    const int cnt = __popc(m);
+    int64_t pos = carry + wave_excl_scan(cnt, lane);
+    while (m) {
+      const int bt = __builtin_ctz(m);
+      if (pos < cap) dst[pos] = 32 * w + bt;
+      ++pos;
+      m &= m - 1;
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = j0 + u * kTopkThreads;
-      if (j < n) f(j, v[u]);
+    carry += wave_sum(cnt);
+  }
+  return carry;
+}
+
+// ----------------------------------------------------------------------------- top-k select
+
+// Per-row state of a selection workgroup, in LDS.
+struct RowState {
+  float bsum[kRows], scale[kRows];   // histogram span and bins per unit of v
+  double e_v[kRows], to_v[kRows], b_v[kRows];
+  int bin1[kRows], bin2[kRows];      // chosen first-level bin, chosen sub-bin (-1: none)
+  int above[kRows], count[kRows];    // entries above the chosen (sub)bin and inside it
+  int status[kRows];                 // 0 resolving, 1 invalid row, 2 routed to the fallback
+  float in_thr[kRows], cand_thr[kRows];  // classification thresholds (v units, rounded outward)
+  int ncand[kRows];
+  double t_sel[kWaves];
+  int amb_j[kWaves][kAmbCap];
+  double amb_s[kWaves][kAmbCap];
+  int amb_n[kWaves];
+  int refine;
+};
+
+template <int D>
+__global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  __shared__ RowState st;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = a.n_blocks, keep = a.keep;
+  const int64_t bh = blockIdx.y;
+  const int i0 = blockIdx.x * kRows;
+  const int words = (nb + 31) / 32;
+  uint32_t* hist = dyn;                                        // [kRows][kHistStride]
+  uint32_t* bits = dyn;                                        // [kRows][words]   (after the histograms)
+  float* cand_v = reinterpret_cast<float*>(dyn + kRows * words);            // [kRows][kCap]
+  uint16_t* cand_j = reinterpret_cast<uint16_t*>(cand_v + kRows * kCap);   // [kRows][kCap]
+
+  int32_t* out_base = a.block_idx + (bh * nb + i0) * (int64_t)keep;
+  if (keep == nb) {  // every block kept
+    for (int r = wave; r < kRows; r += kWaves)
+      if (i0 + r < nb)
+        for (int j = lane; j < nb; j += 64) out_base[(int64_t)r * keep + j] = j;
+    return;
+  }
+  const int F = a.key_stat[4 * bh];
+  if (tid < kRows) {
+    const int i = i0 + tid;
+    st.status[tid] = i < nb ? 0 : 1;
+    st.bin2[tid] = -1;
+    st.ncand[tid] = 0;
+    if (i < nb) {
+      const RowBound rb = row_bound<D>(a, bh, i);
+      st.e_v[tid] = rb.e_v;
+      st.to_v[tid] = rb.to_v;
+      st.b_v[tid] = rb.b_v;
+      const float bs = __double2float_ru(rb.b_v);
+      st.bsum[tid] = bs;
+      st.scale[tid] = (float)kBins / (2.f * bs);
+    } else {
+      st.bsum[tid] = 1.f;
+      st.scale[tid] = 1.f;
     }
   }
+  if (tid == 0) st.refine = 0;
+  QueryOperand<D> qo;
+  qo.load(a, bh, blockIdx.x, lane);
+  for (int w = tid; w < kRows * kHistStride; w += kSelThreads) hist[w] = 0u;
+  __syncthreads();
+
+  // level 1: histogram of every valid row
+  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
+    if (st.status[r] == 0) hist_add(hist, r, bin_of(bin_pos(v, st.bsum[r], st.scale[r])));
+  });
+  __syncthreads();
+  for (int r = wave; r < kRows; r += kWaves) {
+    if (st.status[r] != 0) continue;
+    int ab, cn;
+    const int b = find_bin(hist, r, keep, lane, &ab, &cn);
+    if (lane == 0) {
+      st.bin1[r] = b;
+      st.above[r] = ab;
+      st.count[r] = cn;
+      if (cn > kCap) st.refine = 1;
+    }
+  }
+  __syncthreads();
+  // level 2, only when some row's bin holds more entries than the candidate slots
+  if (st.refine) {
+    for (int w = tid; w < kRows * kHistStride; w += kSelThreads) hist[w] = 0u;
+    __syncthreads();
+    score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
+      if (st.status[r] != 0 || st.count[r] <= kCap) return;
+      const float t = bin_pos(v, st.bsum[r], st.scale[r]);
+      const int b = bin_of(t);
+      if (b == st.bin1[r]) hist_add(hist, r, sub_of(t, b));
+    });
+    __syncthreads();
+    for (int r = wave; r < kRows; r += kWaves) {
+      if (st.status[r] != 0 || st.count[r] <= kCap) continue;
+      int ab, cn;
+      const int b2 = find_bin(hist, r, keep - st.above[r], lane, &ab, &cn);
+      if (lane == 0) {
+        st.bin2[r] = b2;
+        st.above[r] += ab;
+        st.count[r] = cn;
+        if (cn > kCap) st.status[r] = 2;
+      }
+    }
+    __syncthreads();
+  }
+  // classification thresholds: the chosen (sub)bin spans t in [tlo, thi); back in v units with a
+  // slack of 2^-20 B for the float32 bin arithmetic, then widened by 2 E and rounded outward
+  if (tid < kRows && st.status[tid] == 0) {
+    const int r = tid;
+    const double b1 = st.bin1[r];
+    const double tlo = st.bin2[r] < 0 ? b1 : b1 + st.bin2[r] / (double)kBins;
+    const double thi = st.bin2[r] < 0 ? b1 + 1.0 : b1 + (st.bin2[r] + 1) / (double)kBins;
+    const double bs = st.bsum[r], sc = st.scale[r];
+    const double slack = 0x1p-20 * bs;
+    const double e2 = 2.0 * st.e_v[r];
+    st.cand_thr[r] = tlo <= 0.0 ? -INFINITY : __double2float_rd(tlo / sc - bs - slack - e2);
+    st.in_thr[r] = thi >= (double)kBins ? INFINITY : __double2float_ru(thi / sc - bs + slack + e2);
+  }
+  __syncthreads();
+  for (int w = tid; w < kRows * words; w += kSelThreads) bits[w] = 0u;
+  __syncthreads();
+  // classification: above the bracket by more than 2E -> kept; within it -> candidate
+  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
+    if (st.status[r] != 0) return;
+    if (v > st.in_thr[r]) {
+      atomicOr(&bits[r * words + (j >> 5)], 1u << (j & 31));
+    } else if (v >= st.cand_thr[r]) {
+      const int slot = atomicAdd(&st.ncand[r], 1);
+      if (slot < kCap) {
+        cand_v[r * kCap + slot] = v;
+        cand_j[r * kCap + slot] = (uint16_t)j;
+      }
+    }
+  });
+  __syncthreads();
+
+  // resolution, one wave per row
+  const double* qm_base = a.q_mean + (bh * nb + i0) * D;
+  const double* km_base = a.k_mean + bh * nb * (int64_t)D;
+  for (int r = wave; r < kRows; r += kWaves) {
+    if (st.status[r] == 1) continue;
+    const int n = st.ncand[r];
+    bool fb = st.status[r] == 2 || n > kCap;
+    int nsure = 0;
+    for (int w = lane; w < words; w += 64) nsure += __popc(bits[r * words + w]);
+    nsure = wave_sum(nsure);
+    const int need = keep - nsure;
+    if (!fb && (need < 1 || need > n)) fb = true;
+    if (!fb) {
+      const float* cv = cand_v + r * kCap;
+      const uint16_t* cj = cand_j + r * kCap;
+      // rank of each candidate by (v descending, j ascending): a permutation of 0 .. n-1
+      int rank[3] = {0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int c = lane + 64 * u;
+        if (c >= n) continue;
+        const float v = cv[c];
+        const int j = cj[c];
+        int rk = 0;
+        for (int c2 = 0; c2 < n; ++c2) {
+          const float v2 = cv[c2];
+          rk += (v2 > v) || (v2 == v && (int)cj[c2] < j);
+        }
+        rank[u] = rk;
+        if (rk == need - 1) st.t_sel[wave] = (double)v;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const double tsel = st.t_sel[wave];
+      const double e2 = 2.0 * st.e_v[r];
+      // kept outright, decided on float64 scores, or dropped
+      int nin = 0;
+      if (lane == 0) st.amb_n[wave] = 0;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int c = lane + 64 * u;
+        if (c >= n) continue;
+        const double v = cv[c];
+        if (v - e2 > tsel) {
+          ++nin;
+          atomicOr(&bits[r * words + (cj[c] >> 5)], 1u << (cj[c] & 31));
+        } else if (v + e2 >= tsel) {
+          const int slot = atomicAdd(&st.amb_n[wave], 1);
+          if (slot < kAmbCap) {
+            const int j = cj[c];
+            st.amb_j[wave][slot] = j;
+            st.amb_s[wave][slot] = exact_score<D>(qm_base + (int64_t)r * D, km_base + (int64_t)j * D);
+          }
+        }
+      }
+      nin = wave_sum(nin);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const int na = st.amb_n[wave];
+      const int need_a = need - nin;
+      if (na > kAmbCap || need_a < 1 || need_a > na) {
+        fb = true;
+      } else if (lane < na) {
+        const double s = st.amb_s[wave][lane];
+        const int j = st.amb_j[wave][lane];
+        int rk = 0;
+        for (int c2 = 0; c2 < na; ++c2) {
+          const double s2 = st.amb_s[wave][c2];
+          rk += (s2 > s) || (s2 == s && st.amb_j[wave][c2] < j);
+        }
+        if (rk < need_a) atomicOr(&bits[r * words + (j >> 5)], 1u << (j & 31));
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+    if (fb) {
+      if (lane == 0) {
+        const int slot = atomicAdd(a.fb_count, 1);
+        a.fb_rows[slot] = (int32_t)(bh * nb + i0 + r);
+      }
+      continue;
+    }
+    write_bits(bits + r * words, words, out_base + (int64_t)r * keep, keep, lane);
+  }
 }
+
+// --------------------------------------------------------------------------------- fallback
+
+constexpr int kFbThreads = 256;
 
 // block-wide exclusive prefix sum of one int per thread; returns the block total in *total
 __device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= 4 ints */) {
@@ -191,7 +651,7 @@ __device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= 4 ints
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w) {
+  for (int w = 0; w < kFbThreads / 64; ++w) {
     const int s = scratch[w];
     if (w < wave) before += s;
     all += s;
@@ -207,7 +667,7 @@ __device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= 4 ints
 __device__ void ordered_compact(const uint64_t* keys, int nb, uint64_t thr, uint64_t mask, int k_rem, int32_t* dst,
                                 int keep, int* scan_scratch) {
   const int tid = threadIdx.x;
-  const int per = (nb + kTopkThreads - 1) / kTopkThreads;
+  const int per = (nb + kFbThreads - 1) / kFbThreads;
   const int j0 = tid * per;
   const int j1 = j0 + per < nb ? j0 + per : nb;
   int n_eq = 0;
@@ -234,92 +694,184 @@ __device__ void ordered_compact(const uint64_t* keys, int nb, uint64_t thr, uint
   }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
+// Rows the bracketing could not resolve (many exactly equal scores at the keep-th place): the
+// row's float64 scores in LDS as order-preserving keys, then an MSB radix select of the keep-th
+// largest key, 8 bits per pass (thread t owns bin 255 - t; a block prefix sum finds the digit;
+// the select stops once the chosen bin holds exactly the keys still wanted), then the ordered
+// compaction. A fixed grid walks the list of routed rows.
+template <int D>
+__global__ __launch_bounds__(kFbThreads) void fallback_kernel(SelectArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
   __shared__ uint32_t hist[256];
   __shared__ int scan_scratch[4];
   __shared__ uint64_t sh_prefix;
   __shared__ int sh_krem, sh_done;
-
   const int tid = threadIdx.x;
   const int nb = a.n_blocks;
-  const int i = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
-  const int64_t row = ((int64_t)b * a.heads + head) * nb + i;
-  const double* sc = a.scores + row * nb;
-  for_row(sc, nb, [&](int j, double x) { keys[j] = order_key(x); });
-
-  // Digit by digit from the top: the 8-bit digit of the keep-th largest key is the bin where the
-  // count of keys in higher bins first reaches k_rem (thread t owns bin 255 - t, so a block
-  // prefix sum gives every bin the count above it and exactly one thread finds the digit). The
-  // select stops early once the chosen bin holds exactly the k_rem keys still wanted: all of
-  // them are kept, so the remaining digits cannot change the kept set.
-  uint64_t prefix = 0, mask = 0;
-  int k_rem = a.keep;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    hist[tid] = 0;
+  const int total = *a.fb_count;
+  for (int e = blockIdx.x; e < total; e += gridDim.x) {
+    const int64_t row = a.fb_rows[e];
+    const int64_t bh = row / nb;
+    const double* qm = a.q_mean + row * D;
+    const double* km = a.k_mean + bh * nb * (int64_t)D;
+    for (int j = tid; j < nb; j += kFbThreads) keys[j] = order_key(exact_score<D>(qm, km + (int64_t)j * D));
     __syncthreads();
-    for (int j = tid; j < nb; j += kTopkThreads) {
-      const uint64_t key = keys[j];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    uint64_t prefix = 0, mask = 0;
+    int k_rem = a.keep;
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      hist[tid] = 0;
+      __syncthreads();
+      for (int j = tid; j < nb; j += kFbThreads) {
+        const uint64_t key = keys[j];
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      const int d = 255 - tid;
+      const int h = (int)hist[d];
+      int tot;
+      const int above = block_exclusive_scan(h, &tot, scan_scratch);
+      if (above < k_rem && k_rem <= above + h) {
+        sh_prefix = prefix | ((uint64_t)d << shift);
+        sh_krem = k_rem - above;
+        sh_done = h == k_rem - above;
+      }
+      __syncthreads();
+      prefix = sh_prefix;
+      k_rem = sh_krem;
+      mask |= (uint64_t)0xff << shift;
+      if (sh_done) break;  // block-uniform
     }
+    ordered_compact(keys, nb, prefix, mask, k_rem, a.block_idx + row * a.keep, a.keep, scan_scratch);
     __syncthreads();
-    const int d = 255 - tid;
-    const int h = (int)hist[d];
-    int tot;
-    const int above = block_exclusive_scan(h, &tot, scan_scratch);  // keys in the bins above d
-    if (above < k_rem && k_rem <= above + h) {
-      sh_prefix = prefix | ((uint64_t)d << shift);
-      sh_krem = k_rem - above;
-      sh_done = h == k_rem - above;
-    }
-    __syncthreads();
-    prefix = sh_prefix;
-    k_rem = sh_krem;
-    mask |= (uint64_t)0xff << shift;
-    if (sh_done) break;  // block-uniform
   }
-
-  // keys whose top digits exceed the prefix are kept, plus k_rem of those equal to it
-  ordered_compact(keys, nb, prefix, mask, k_rem, a.block_idx + row * a.keep, a.keep, scan_scratch);
 }
 
-// Threshold mode, pass 1: per row, the largest unscaled score m and the kept count
-// #{j : s_j >= m - tau*sqrt(D)}; the threshold is stored so that pass 2 uses the same value.
-__global__ __launch_bounds__(kTopkThreads) void threshold_count_kernel(SelectArgs a) {
-  __shared__ double red[kTopkThreads / 64];
-  __shared__ int cnt_red[kTopkThreads / 64];
+// ---------------------------------------------------------------------------- threshold mode
+
+// Threshold mode keeps j iff s_ij >= m_i - tau sqrt(D), m_i = max_j s_ij (unscaled float64
+// scores). Entries further than E from the threshold are decided on v, the others on their
+// float64 score, so the count and fill kernels decide every entry identically.
+struct ThrState {
+  double e_v[kRows], to_v[kRows], thr_s[kRows], thr_v[kRows];
+  int vmax[kRows];                // order-preserving int of the largest v
+  unsigned long long smax[kRows]; // order key of the largest float64 score near the top
+  int cnt[kRows];
+  int valid[kRows];
+};
+
+__device__ __forceinline__ int order_int(float v) {
+  const int u = __float_as_int(v + 0.f);
+  return u >= 0 ? u : (u ^ 0x7fffffff);
+}
+__device__ __forceinline__ float from_order_int(int o) { return __int_as_float(o >= 0 ? o : (o ^ 0x7fffffff)); }
+__device__ __forceinline__ double from_order_key(uint64_t k) {
+  return __longlong_as_double((k & 0x8000000000000000ull) ? (long long)(k & 0x7fffffffffffffffull) : (long long)~k);
+}
+
+// 1 keep, 0 drop; decided on v when it is clear of the threshold by more than E
+template <int D>
+__device__ __forceinline__ int thr_keep(const ThrState& ts, int r, float v, const double* qm, const double* km) {
+  const double dv = v;
+  if (dv - ts.e_v[r] > ts.thr_v[r]) return 1;
+  if (dv + ts.e_v[r] < ts.thr_v[r]) return 0;
+  return exact_score<D>(qm, km) >= ts.thr_s[r] ? 1 : 0;
+}
+
+template <int D>
+__device__ void thr_setup(const SelectArgs& a, ThrState& ts, int64_t bh, int i0, int tid) {
+  if (tid < kRows) {
+    const int i = i0 + tid;
+    ts.valid[tid] = i < a.n_blocks;
+    ts.vmax[tid] = order_int(-INFINITY);
+    ts.smax[tid] = 0ull;
+    ts.cnt[tid] = 0;
+    if (i < a.n_blocks) {
+      const RowBound rb = row_bound<D>(a, bh, i);
+      ts.e_v[tid] = rb.e_v;
+      ts.to_v[tid] = rb.to_v;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kSelThreads, 2) void threshold_count_kernel(SelectArgs a) {
+  __shared__ ThrState ts;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = a.n_blocks;
-  const int64_t row = ((int64_t)blockIdx.z * a.heads + blockIdx.y) * nb + blockIdx.x;
-  // the row is read once, into LDS, and counted from there
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  double* sc = reinterpret_cast<double*>(smem);
-  double m = -INFINITY;
-  for_row(a.scores + row * nb, nb, [&](int j, double x) {
-    sc[j] = x;
-    m = fmax(m, x);
+  const int64_t bh = blockIdx.y;
+  const int i0 = blockIdx.x * kRows;
+  const int F = a.key_stat[4 * bh];
+  thr_setup<D>(a, ts, bh, i0, tid);
+  QueryOperand<D> qo;
+  qo.load(a, bh, blockIdx.x, lane);
+  __syncthreads();
+  const double* qm_base = a.q_mean + (bh * nb + i0) * D;
+  const double* km_base = a.k_mean + bh * nb * (int64_t)D;
+  // the largest v of each row
+  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
+    if (ts.valid[r]) atomicMax(&ts.vmax[r], order_int(v));
   });
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
-  if (lane == 0) red[wave] = m;
   __syncthreads();
-  m = red[0];
-#pragma unroll
-  for (int w = 1; w < kTopkThreads / 64; ++w) m = fmax(m, red[w]);
-  const double thr = m - a.tau_raw;
-  int c = 0;
-  for (int j = tid; j < nb; j += kTopkThreads) c += sc[j] >= thr;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-  if (lane == 0) cnt_red[wave] = c;
+  // the exact maximum is among the entries within 2E of the largest v
+  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
+    if (!ts.valid[r]) return;
+    if ((double)v + 2.0 * ts.e_v[r] >= (double)from_order_int(ts.vmax[r]))
+      atomicMax(&ts.smax[r], (unsigned long long)order_key(exact_score<D>(qm_base + (int64_t)r * D, km_base + (int64_t)j * D)));
+  });
   __syncthreads();
-  if (tid == 0) {
-    int tot = 0;
-    for (int w = 0; w < kTopkThreads / 64; ++w) tot += cnt_red[w];
-    a.row_cnt[row] = tot;
-    a.row_thr[row] = thr;
+  if (tid < kRows && ts.valid[tid]) {
+    const double m = from_order_key(ts.smax[tid]);
+    const double thr = m - a.tau_raw;
+    ts.thr_s[tid] = thr;
+    ts.thr_v[tid] = thr * ts.to_v[tid];
+  }
+  __syncthreads();
+  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
+    if (ts.valid[r] && thr_keep<D>(ts, r, v, qm_base + (int64_t)r * D, km_base + (int64_t)j * D))
+      atomicAdd(&ts.cnt[r], 1);
+  });
+  __syncthreads();
+  if (tid < kRows && ts.valid[tid]) {
+    const int64_t row = bh * nb + i0 + tid;
+    a.row_cnt[row] = ts.cnt[tid];
+    a.row_thr[row] = ts.thr_s[tid];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kSelThreads, 2) void threshold_fill_kernel(SelectArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t bits[];  // [kRows][words]
+  __shared__ ThrState ts;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = a.n_blocks;
+  const int words = (nb + 31) / 32;
+  const int64_t bh = blockIdx.y;
+  const int i0 = blockIdx.x * kRows;
+  const int F = a.key_stat[4 * bh];
+  thr_setup<D>(a, ts, bh, i0, tid);
+  if (tid < kRows && ts.valid[tid]) {
+    ts.thr_s[tid] = a.row_thr[bh * nb + i0 + tid];
+    ts.thr_v[tid] = ts.thr_s[tid] * ts.to_v[tid];
+  }
+  QueryOperand<D> qo;
+  qo.load(a, bh, blockIdx.x, lane);
+  for (int w = tid; w < kRows * words; w += kSelThreads) bits[w] = 0u;
+  __syncthreads();
+  const double* qm_base = a.q_mean + (bh * nb + i0) * D;
+  const double* km_base = a.k_mean + bh * nb * (int64_t)D;
+  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
+    if (ts.valid[r] && thr_keep<D>(ts, r, v, qm_base + (int64_t)r * D, km_base + (int64_t)j * D))
+      atomicOr(&bits[r * words + (j >> 5)], 1u << (j & 31));
+  });
+  __syncthreads();
+  for (int r = wave; r < kRows; r += kWaves) {
+    if (!ts.valid[r]) continue;
+    const int64_t row = bh * nb + i0 + r;
+    const int64_t start = a.row_ptr[row];
+    const int64_t room = a.col_capacity - start;
+    write_bits(bits + r * words, words, a.col_idx + start, room > 0 ? room : 0, lane);
   }
 }
 
@@ -372,78 +924,63 @@ __global__ __launch_bounds__(kScanThreads) void row_ptr_scan_kernel(SelectArgs a
   if (tid == 0) a.row_ptr[rows] = s_carry;
 }
 
-// Threshold mode, pass 2: ordered compaction of {j : s_j >= thr} into col_idx[row_ptr[row] ..].
-// Writes past col_capacity are dropped (the caller sizes col_idx from row_ptr's last entry).
-__global__ __launch_bounds__(kTopkThreads) void threshold_fill_kernel(SelectArgs a) {
-  __shared__ int scan_scratch[4];
-  const int tid = threadIdx.x;
-  const int nb = a.n_blocks;
-  const int64_t row = ((int64_t)blockIdx.z * a.heads + blockIdx.y) * nb + blockIdx.x;
-  // the row is staged in LDS with coalesced loads; the ordered scans below walk contiguous runs
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  double* sc = reinterpret_cast<double*>(smem);
-  for_row(a.scores + row * nb, nb, [&](int j, double x) { sc[j] = x; });
-  __syncthreads();
-  const double thr = a.row_thr[row];
-  const int64_t start = a.row_ptr[row];
-  const int per = (nb + kTopkThreads - 1) / kTopkThreads;
-  const int j0 = tid * per;
-  const int j1 = j0 + per < nb ? j0 + per : nb;
-  int n_sel = 0;
-  for (int j = j0; j < j1; ++j) n_sel += sc[j] >= thr;
-  int tot;
-  int64_t p = start + block_exclusive_scan(n_sel, &tot, scan_scratch);
-  for (int j = j0; j < j1; ++j)
-    if (sc[j] >= thr) {
-      if (p < a.col_capacity) a.col_idx[p] = j;
-      ++p;
-    }
-}
-
-}  // namespace
-
-static void launch_pool_and_scores(const SelectArgs& a, hipStream_t stream);
-
-void launch_subblock_select(const SelectArgs& a, hipStream_t stream) {
-  launch_pool_and_scores(a, stream);
-  const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
-  const size_t lds = (size_t)a.n_blocks * sizeof(uint64_t);
-  allow_dynamic_lds(reinterpret_cast<const void*>(topk_kernel), (int)kSelectRowLdsBytes);
-  hipLaunchKernelGGL(topk_kernel, g3, dim3(kTopkThreads), lds, stream, a);
-}
-
-template <int TILE>
-void launch_scores(const SelectArgs& a, hipStream_t stream) {
-  const unsigned tiles = (unsigned)((a.n_blocks + TILE - 1) / TILE);
-  const dim3 gs(tiles, tiles, (unsigned)(a.batch * a.heads));
-  if (a.head_dim == 128) hipLaunchKernelGGL((score_kernel<128, TILE, 32>), gs, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((score_kernel<64, TILE, 32>), gs, dim3(256), 0, stream, a);
-}
-
-static void launch_pool_and_scores(const SelectArgs& a, hipStream_t stream) {
+template <int D>
+void launch_pool(const SelectArgs& a, hipStream_t stream) {
   const dim3 g3((unsigned)a.n_blocks * (unsigned)a.heads, 1, (unsigned)a.batch);
-  if (a.head_dim == 128) hipLaunchKernelGGL(pool_kernel<128>, g3, dim3(kPoolThreads), 0, stream, a);
-  else hipLaunchKernelGGL(pool_kernel<64>, g3, dim3(kPoolThreads), 0, stream, a);
-  // 128 x 128 score tiles once there are enough of them (half the operand staging per score);
-  // 64 x 64 for short rows, where 128-wide tiles leave most of the chip idle
-  if (a.n_blocks >= 1024) launch_scores<128>(a, stream);
-  else launch_scores<64>(a, stream);
+  hipLaunchKernelGGL(pool_kernel<D>, g3, dim3(kPoolThreads), 0, stream, a);
+  hipLaunchKernelGGL(key_stats_kernel, dim3((unsigned)(a.batch * a.heads)), dim3(256), 0, stream, a);
 }
 
-void launch_threshold_count(const SelectArgs& a, hipStream_t stream) {
-  launch_pool_and_scores(a, stream);
-  const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
-  allow_dynamic_lds(reinterpret_cast<const void*>(threshold_count_kernel), (int)kSelectRowLdsBytes);
-  hipLaunchKernelGGL(threshold_count_kernel, g3, dim3(kTopkThreads), (size_t)a.n_blocks * sizeof(double), stream, a);
+size_t topk_dyn_lds(int32_t nb) {
+  const size_t words = ((size_t)nb + 31) / 32;
+  const size_t hist = (size_t)kRows * kHistStride * 4;
+  const size_t classify = (size_t)kRows * words * 4 + (size_t)kRows * kCap * 6;
+  return hist > classify ? hist : classify;
+}
+
+template <int D>
+void launch_topk(const SelectArgs& a, hipStream_t stream) {
+  launch_pool<D>(a, stream);
+  const dim3 grid((unsigned)((a.n_blocks + kRows - 1) / kRows), (unsigned)(a.batch * a.heads));
+  const size_t lds = topk_dyn_lds(a.n_blocks);
+  allow_dynamic_lds(reinterpret_cast<const void*>(topk_select_kernel<D>), (int)kSelectRowLdsBytes);
+  hipLaunchKernelGGL(topk_select_kernel<D>, grid, dim3(kSelThreads), lds, stream, a);
+  allow_dynamic_lds(reinterpret_cast<const void*>(fallback_kernel<D>), (int)kSelectRowLdsBytes);
+  hipLaunchKernelGGL(fallback_kernel<D>, dim3(256), dim3(kFbThreads), (size_t)a.n_blocks * 8, stream, a);
+}
+
+template <int D>
+void launch_thr_count(const SelectArgs& a, hipStream_t stream) {
+  launch_pool<D>(a, stream);
+  const dim3 grid((unsigned)((a.n_blocks + kRows - 1) / kRows), (unsigned)(a.batch * a.heads));
+  hipLaunchKernelGGL(threshold_count_kernel<D>, grid, dim3(kSelThreads), 0, stream, a);
   const int64_t rows = (int64_t)a.batch * a.heads * a.n_blocks;
   hipLaunchKernelGGL(row_ptr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a, rows);
 }
 
+template <int D>
+void launch_thr_fill(const SelectArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.n_blocks + kRows - 1) / kRows), (unsigned)(a.batch * a.heads));
+  const size_t lds = (size_t)kRows * (((size_t)a.n_blocks + 31) / 32) * 4;
+  allow_dynamic_lds(reinterpret_cast<const void*>(threshold_fill_kernel<D>), (int)kSelectRowLdsBytes);
+  hipLaunchKernelGGL(threshold_fill_kernel<D>, grid, dim3(kSelThreads), lds, stream, a);
+}
+
+}  // namespace
+
+void launch_subblock_select(const SelectArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) launch_topk<128>(a, stream);
+  else launch_topk<64>(a, stream);
+}
+
+void launch_threshold_count(const SelectArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) launch_thr_count<128>(a, stream);
+  else launch_thr_count<64>(a, stream);
+}
+
 void launch_threshold_fill(const SelectArgs& a, hipStream_t stream) {
-  const dim3 g3((unsigned)a.n_blocks, (unsigned)a.heads, (unsigned)a.batch);
-  const size_t lds = (size_t)a.n_blocks * sizeof(double);
-  allow_dynamic_lds(reinterpret_cast<const void*>(threshold_fill_kernel), (int)kSelectRowLdsBytes);
-  hipLaunchKernelGGL(threshold_fill_kernel, g3, dim3(kTopkThreads), lds, stream, a);
+  if (a.head_dim == 128) launch_thr_fill<128>(a, stream);
+  else launch_thr_fill<64>(a, stream);
 }
 
 }  // namespace h3attn
