@@ -273,47 +273,88 @@ struct QueryOperand {
 };
 
 // Every (row, key) score of the workgroup's rows, key chunks of 32 spread over the waves. For each
-// valid entry calls f(r, j, v): r the row inside the workgroup, j the key block, v the
-// approximate score. The MFMA's output holds key 8 (k / 4) + 4 (l / 32) + k % 4 of query l % 32 in
-// accumulator k of lane l.
-template <int D, typename Fn>
+// valid entry calls f(j, v): j the key block, v the approximate score of row r = lane % 32 (every
+// entry a lane sees belongs to that row). The MFMA's output holds key 8 (k / 4) + 4 (l / 32) + k % 4
+// of query l % 32 in accumulator k of lane l. The next chunk's operands are loaded while the
+// current one is multiplied.
+template <int D>
+struct KeyOperand {
+  i32x4 f[D / 32][3];
+};
+
+// PREFETCH: load the wave's next chunk of key digits while the current one is multiplied (more
+// registers: the kernels that also evaluate float64 scores inside the pass do without).
+template <int D, bool PREFETCH, typename Fn>
 __device__ __forceinline__ void score_pass(const SelectArgs& a, const QueryOperand<D>& qo, int64_t bh, int F,
                                            int wave, int lane, Fn&& fn) {
   const int nb = a.n_blocks;
-  const int64_t nchunks = n_pad(nb) / kRows;
+  const int nchunks = (int)(n_pad(nb) / kRows);
   const int8_t* kd = a.k_digits + bh * nchunks * (D / 32) * 3 * 1024 + lane * 16;
   const int* ke = a.k_exp + bh * n_pad(nb) + 4 * (lane >> 5);
-  const int r = lane & 31;
-  for (int c = wave; c < nchunks; c += kWaves) {
-    i32x4 kf[D / 32][3];
+  auto load = [&](int c, KeyOperand<D>& k) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int L = 0; L < 3; ++L)
-        kf[t][L] = *reinterpret_cast<const i32x4*>(kd + ((c * (D / 32) + t) * 3 + L) * 1024);
-    i32x4 fe[4];
+        k.f[t][L] = *reinterpret_cast<const i32x4*>(kd + ((int64_t)(c * (D / 32) + t) * 3 + L) * 1024);
+  };
+  auto compute = [&](int c, const KeyOperand<D>& k) {
+    // the exponents of the lane's 16 keys, loaded under the products
+    i32x4 e[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) fe[g] = *reinterpret_cast<const i32x4*>(ke + 32 * c + 8 * g);
+    for (int g = 0; g < 4; ++g) e[g] = *reinterpret_cast<const i32x4*>(ke + 32 * c + 8 * g);
     i32x16 p4 = {}, p3 = {}, p2 = {};
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
-      p4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][2], qo.f[t][2], p4, 0, 0, 0);
-      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][2], qo.f[t][1], p3, 0, 0, 0);
-      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][1], qo.f[t][2], p3, 0, 0, 0);
-      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][2], qo.f[t][0], p2, 0, 0, 0);
-      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][1], qo.f[t][1], p2, 0, 0, 0);
-      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[t][0], qo.f[t][2], p2, 0, 0, 0);
+      p4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][2], qo.f[t][2], p4, 0, 0, 0);
+      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][2], qo.f[t][1], p3, 0, 0, 0);
+      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][1], qo.f[t][2], p3, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][2], qo.f[t][0], p2, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][1], qo.f[t][1], p2, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][0], qo.f[t][2], p2, 0, 0, 0);
     }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int j = 32 * c + 8 * (k / 4) + 4 * (lane >> 5) + (k % 4);
+    for (int q = 0; q < 16; ++q) {
+      const int j = 32 * c + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
       if (j < nb) {
-        const float hi = fmaf((float)p4[k], 65536.f, (float)p3[k] * 256.f);
-        const float v = ldexpf(hi + (float)p2[k], fe[k / 4][k % 4] - F);
-        fn(r, j, v);
+        const float hi = fmaf((float)p4[q], 65536.f, (float)p3[q] * 256.f);
+        const float v = ldexpf(hi + (float)p2[q], e[q / 4][q % 4] - F);
+        fn(j, v);
       }
     }
+  };
+  if constexpr (PREFETCH) {
+    KeyOperand<D> ka, kb;
+    int c = wave;
+    if (c < nchunks) load(c, ka);
+    while (c < nchunks) {
+      if (c + kWaves < nchunks) load(c + kWaves, kb);
+      compute(c, ka);
+      c += kWaves;
+      if (c >= nchunks) break;
+      if (c + kWaves < nchunks) load(c + kWaves, ka);
+      compute(c, kb);
+      c += kWaves;
+    }
+  } else {
+    for (int c = wave; c < nchunks; c += kWaves) {
+      KeyOperand<D> k;
+      load(c, k);
+      compute(c, k);
+    }
   }
+}
+
+// The float64 score of row qm against the key rows of the wave's list, all 64 lanes on one score:
+// lane l multiplies channels 2l and 2l+1, a fixed shuffle tree adds the 64 products (the same order
+// for every entry). Used where a whole wave decides a row.
+template <int D>
+__device__ __forceinline__ double wave_exact_score(const double2 qv, const double* km, int lane) {
+  const double2 kv = 2 * lane < D ? *reinterpret_cast<const double2*>(km + 2 * lane) : double2{0.0, 0.0};
+  double p = fma(qv.y, kv.y, qv.x * kv.x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) p += __shfl_down(p, off);
+  return __shfl(p, 0);
 }
 
 // ---------------------------------------------------------------------- histogram bracketing
@@ -474,9 +515,19 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
   for (int w = tid; w < kRows * kHistStride; w += kSelThreads) hist[w] = 0u;
   __syncthreads();
 
-  // level 1: histogram of every valid row
-  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
-    if (st.status[r] == 0) hist_add(hist, r, bin_of(bin_pos(v, st.bsum[r], st.scale[r])));
+  // every entry a lane sees belongs to row r = lane % 32: its parameters stay in registers
+  const int my_r = lane & 31;
+  const bool my_live = st.status[my_r] == 0;
+  const float my_bsum = st.bsum[my_r], my_scale = st.scale[my_r];
+  uint32_t* my_hist = hist + my_r * kHistStride;
+
+  // level 1: histogram of every valid row. (The passes run with every lane active: the MFMA
+  // operands of a lane feed the outputs of other lanes, so liveness is tested inside.)
+  score_pass<D, true>(a, qo, bh, F, wave, lane, [&](int j, float v) {
+    if (my_live) {
+      const int b = bin_of(bin_pos(v, my_bsum, my_scale));
+      atomicAdd(&my_hist[b >> 1], 1u << (16 * (b & 1)));
+    }
   });
   __syncthreads();
   for (int r = wave; r < kRows; r += kWaves) {
@@ -493,13 +544,17 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
   __syncthreads();
   // level 2, only when some row's bin holds more entries than the candidate slots
   if (st.refine) {
+    const bool my_refine = my_live && st.count[my_r] > kCap;
+    const int my_bin1 = st.bin1[my_r];
+    __syncthreads();
     for (int w = tid; w < kRows * kHistStride; w += kSelThreads) hist[w] = 0u;
     __syncthreads();
-    score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
-      if (st.status[r] != 0 || st.count[r] <= kCap) return;
-      const float t = bin_pos(v, st.bsum[r], st.scale[r]);
-      const int b = bin_of(t);
-      if (b == st.bin1[r]) hist_add(hist, r, sub_of(t, b));
+    score_pass<D, true>(a, qo, bh, F, wave, lane, [&](int j, float v) {
+      const float t = bin_pos(v, my_bsum, my_scale);
+      if (my_refine && bin_of(t) == my_bin1) {
+        const int b = sub_of(t, my_bin1);
+        atomicAdd(&my_hist[b >> 1], 1u << (16 * (b & 1)));
+      }
     });
     __syncthreads();
     for (int r = wave; r < kRows; r += kWaves) {
@@ -528,26 +583,32 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
     st.cand_thr[r] = tlo <= 0.0 ? -INFINITY : __double2float_rd(tlo / sc - bs - slack - e2);
     st.in_thr[r] = thi >= (double)kBins ? INFINITY : __double2float_ru(thi / sc - bs + slack + e2);
   }
-  __syncthreads();
   for (int w = tid; w < kRows * words; w += kSelThreads) bits[w] = 0u;
   __syncthreads();
   // classification: above the bracket by more than 2E -> kept; within it -> candidate
-  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
-    if (st.status[r] != 0) return;
-    if (v > st.in_thr[r]) {
-      atomicOr(&bits[r * words + (j >> 5)], 1u << (j & 31));
-    } else if (v >= st.cand_thr[r]) {
-      const int slot = atomicAdd(&st.ncand[r], 1);
-      if (slot < kCap) {
-        cand_v[r * kCap + slot] = v;
-        cand_j[r * kCap + slot] = (uint16_t)j;
+  {
+    const bool live = st.status[my_r] == 0;
+    const float in_thr = st.in_thr[my_r], cand_thr = st.cand_thr[my_r];
+    uint32_t* my_bits = bits + my_r * words;
+    float* my_cv = cand_v + my_r * kCap;
+    uint16_t* my_cj = cand_j + my_r * kCap;
+    int* my_n = &st.ncand[my_r];
+    score_pass<D, true>(a, qo, bh, F, wave, lane, [&](int j, float v) {
+      if (!live) return;
+      if (v > in_thr) {
+        atomicOr(&my_bits[j >> 5], 1u << (j & 31));
+      } else if (v >= cand_thr) {
+        const int slot = atomicAdd(my_n, 1);
+        if (slot < kCap) {
+          my_cv[slot] = v;
+          my_cj[slot] = (uint16_t)j;
+        }
       }
-    }
-  });
+    });
+  }
   __syncthreads();
 
   // resolution, one wave per row
-  const double* qm_base = a.q_mean + (bh * nb + i0) * D;
   const double* km_base = a.k_mean + bh * nb * (int64_t)D;
   for (int r = wave; r < kRows; r += kWaves) {
     if (st.status[r] == 1) continue;
@@ -561,10 +622,11 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
     if (!fb) {
       const float* cv = cand_v + r * kCap;
       const uint16_t* cj = cand_j + r * kCap;
-      // rank of each candidate by (v descending, j ascending): a permutation of 0 .. n-1
-      int rank[3] = {0, 0, 0};
+      // the need-th candidate by (v descending, j ascending): ranks are a permutation of 0 .. n-1
+      float tsel = 0.f;
+      int found = 0;
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
+      for (int u = 0; u < (kCap + 63) / 64; ++u) {
         const int c = lane + 64 * u;
         if (c >= n) continue;
         const float v = cv[c];
@@ -574,33 +636,27 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
           const float v2 = cv[c2];
           rk += (v2 > v) || (v2 == v && (int)cj[c2] < j);
         }
-        rank[u] = rk;
-        if (rk == need - 1) st.t_sel[wave] = (double)v;
+        if (rk == need - 1) { tsel = v; found = 1; }
       }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      const double tsel = st.t_sel[wave];
-      const double e2 = 2.0 * st.e_v[r];
-      // kept outright, decided on float64 scores, or dropped
+      const unsigned long long who = __ballot(found);
+      tsel = __shfl(tsel, who ? (int)__builtin_ctzll(who) : 0);
+      const double t = tsel, e2 = 2.0 * st.e_v[r];
+      // kept outright, dropped, or listed for a float64 decision
       int nin = 0;
       if (lane == 0) st.amb_n[wave] = 0;
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
+      for (int u = 0; u < (kCap + 63) / 64; ++u) {
         const int c = lane + 64 * u;
         if (c >= n) continue;
         const double v = cv[c];
-        if (v - e2 > tsel) {
+        if (v - e2 > t) {
           ++nin;
           atomicOr(&bits[r * words + (cj[c] >> 5)], 1u << (cj[c] & 31));
-        } else if (v + e2 >= tsel) {
+        } else if (v + e2 >= t) {
           const int slot = atomicAdd(&st.amb_n[wave], 1);
-          if (slot < kAmbCap) {
-            const int j = cj[c];
-            st.amb_j[wave][slot] = j;
-            st.amb_s[wave][slot] = exact_score<D>(qm_base + (int64_t)r * D, km_base + (int64_t)j * D);
-          }
+          if (slot < kAmbCap) st.amb_j[wave][slot] = cj[c];
         }
       }
       nin = wave_sum(nin);
@@ -610,15 +666,27 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
       const int need_a = need - nin;
       if (na > kAmbCap || need_a < 1 || need_a > na) {
         fb = true;
-      } else if (lane < na) {
-        const double s = st.amb_s[wave][lane];
-        const int j = st.amb_j[wave][lane];
-        int rk = 0;
-        for (int c2 = 0; c2 < na; ++c2) {
-          const double s2 = st.amb_s[wave][c2];
-          rk += (s2 > s) || (s2 == s && st.amb_j[wave][c2] < j);
+      } else {
+        // the listed entries' float64 scores, a whole wave per score
+        const double* qm = a.q_mean + (bh * nb + i0 + r) * D;
+        const double2 qv = 2 * lane < D ? *reinterpret_cast<const double2*>(qm + 2 * lane) : double2{0.0, 0.0};
+        double my_s = 0.0;
+        for (int e = 0; e < na; ++e) {
+          const double sc = wave_exact_score<D>(qv, km_base + (int64_t)st.amb_j[wave][e] * D, lane);
+          if (lane == e) my_s = sc;
         }
-        if (rk < need_a) atomicOr(&bits[r * words + (j >> 5)], 1u << (j & 31));
+        if (lane < na) st.amb_s[wave][lane] = my_s;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        if (lane < na) {
+          const int j = st.amb_j[wave][lane];
+          int rk = 0;
+          for (int c2 = 0; c2 < na; ++c2) {
+            const double s2 = st.amb_s[wave][c2];
+            rk += (s2 > my_s) || (s2 == my_s && st.amb_j[wave][c2] < j);
+          }
+          if (rk < need_a) atomicOr(&bits[r * words + (j >> 5)], 1u << (j & 31));
+        }
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -770,13 +838,15 @@ __device__ __forceinline__ double from_order_key(uint64_t k) {
   return __longlong_as_double((k & 0x8000000000000000ull) ? (long long)(k & 0x7fffffffffffffffull) : (long long)~k);
 }
 
-// 1 keep, 0 drop; decided on v when it is clear of the threshold by more than E
+// 1 keep, 0 drop; decided on v when it is clear of the threshold by more than E (thr_v, e_v in v
+// units), otherwise on the float64 score against thr_s
 template <int D>
-__device__ __forceinline__ int thr_keep(const ThrState& ts, int r, float v, const double* qm, const double* km) {
+__device__ __forceinline__ int thr_keep(double thr_v, double e_v, double thr_s, float v, const double* qm,
+                                        const double* km) {
   const double dv = v;
-  if (dv - ts.e_v[r] > ts.thr_v[r]) return 1;
-  if (dv + ts.e_v[r] < ts.thr_v[r]) return 0;
-  return exact_score<D>(qm, km) >= ts.thr_s[r] ? 1 : 0;
+  if (dv - e_v > thr_v) return 1;
+  if (dv + e_v < thr_v) return 0;
+  return exact_score<D>(qm, km) >= thr_s ? 1 : 0;
 }
 
 template <int D>
@@ -809,17 +879,27 @@ __global__ __launch_bounds__(kSelThreads, 2) void threshold_count_kernel(SelectA
   __syncthreads();
   const double* qm_base = a.q_mean + (bh * nb + i0) * D;
   const double* km_base = a.k_mean + bh * nb * (int64_t)D;
-  // the largest v of each row
-  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
-    if (ts.valid[r]) atomicMax(&ts.vmax[r], order_int(v));
-  });
+  const int r = lane & 31;
+  const bool live = ts.valid[r];
+  // the largest v of each row (a per-lane maximum first)
+  {
+    float vm = -INFINITY;
+    score_pass<D, false>(a, qo, bh, F, wave, lane, [&](int, float v) { vm = fmaxf(vm, v); });
+    if (live) atomicMax(&ts.vmax[r], order_int(vm));
+  }
   __syncthreads();
   // the exact maximum is among the entries within 2E of the largest v
-  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
-    if (!ts.valid[r]) return;
-    if ((double)v + 2.0 * ts.e_v[r] >= (double)from_order_int(ts.vmax[r]))
-      atomicMax(&ts.smax[r], (unsigned long long)order_key(exact_score<D>(qm_base + (int64_t)r * D, km_base + (int64_t)j * D)));
-  });
+  {
+    const double lim = (double)from_order_int(ts.vmax[r]) - 2.0 * ts.e_v[r];
+    unsigned long long sm = 0ull;
+    score_pass<D, false>(a, qo, bh, F, wave, lane, [&](int j, float v) {
+      if (live && (double)v >= lim) {
+        const uint64_t key = order_key(exact_score<D>(qm_base + (int64_t)r * D, km_base + (int64_t)j * D));
+        sm = key > sm ? key : sm;
+      }
+    });
+    if (live) atomicMax(&ts.smax[r], sm);
+  }
   __syncthreads();
   if (tid < kRows && ts.valid[tid]) {
     const double m = from_order_key(ts.smax[tid]);
@@ -828,10 +908,15 @@ __global__ __launch_bounds__(kSelThreads, 2) void threshold_count_kernel(SelectA
     ts.thr_v[tid] = thr * ts.to_v[tid];
   }
   __syncthreads();
-  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
-    if (ts.valid[r] && thr_keep<D>(ts, r, v, qm_base + (int64_t)r * D, km_base + (int64_t)j * D))
-      atomicAdd(&ts.cnt[r], 1);
-  });
+  {
+    int cnt = 0;
+    const double thr_v = ts.thr_v[r], e_v = ts.e_v[r], thr_s = ts.thr_s[r];
+    const double* qm = qm_base + (int64_t)r * D;
+    score_pass<D, false>(a, qo, bh, F, wave, lane, [&](int j, float v) {
+      if (live) cnt += thr_keep<D>(thr_v, e_v, thr_s, v, qm, km_base + (int64_t)j * D);
+    });
+    if (live) atomicAdd(&ts.cnt[r], cnt);
+  }
   __syncthreads();
   if (tid < kRows && ts.valid[tid]) {
     const int64_t row = bh * nb + i0 + tid;
@@ -861,10 +946,17 @@ __global__ __launch_bounds__(kSelThreads, 2) void threshold_fill_kernel(SelectAr
   __syncthreads();
   const double* qm_base = a.q_mean + (bh * nb + i0) * D;
   const double* km_base = a.k_mean + bh * nb * (int64_t)D;
-  score_pass<D>(a, qo, bh, F, wave, lane, [&](int r, int j, float v) {
-    if (ts.valid[r] && thr_keep<D>(ts, r, v, qm_base + (int64_t)r * D, km_base + (int64_t)j * D))
-      atomicOr(&bits[r * words + (j >> 5)], 1u << (j & 31));
-  });
+  {
+    const int r = lane & 31;
+    const double thr_v = ts.thr_v[r], e_v = ts.e_v[r], thr_s = ts.thr_s[r];
+    const double* qm = qm_base + (int64_t)r * D;
+    uint32_t* my_bits = bits + r * words;
+    const bool live = ts.valid[r];
+    score_pass<D, false>(a, qo, bh, F, wave, lane, [&](int j, float v) {
+      if (live && thr_keep<D>(thr_v, e_v, thr_s, v, qm, km_base + (int64_t)j * D))
+        atomicOr(&my_bits[j >> 5], 1u << (j & 31));
+    });
+  }
   __syncthreads();
   for (int r = wave; r < kRows; r += kWaves) {
     if (!ts.valid[r]) continue;
@@ -943,7 +1035,9 @@ void launch_topk(const SelectArgs& a, hipStream_t stream) {
   launch_pool<D>(a, stream);
   const dim3 grid((unsigned)((a.n_blocks + kRows - 1) / kRows), (unsigned)(a.batch * a.heads));
   const size_t lds = topk_dyn_lds(a.n_blocks);
-  allow_dynamic_lds(reinterpret_cast<const void*>(topk_select_kernel<D>), (int)kSelectRowLdsBytes);
+  // the dynamic-LDS limit plus the kernel's static LDS (RowState) must stay within a CU's 160 KB
+  static_assert(sizeof(RowState) <= 8192, "per-row state outgrew its LDS share");
+  allow_dynamic_lds(reinterpret_cast<const void*>(topk_select_kernel<D>), 160 * 1024 - 8192);
   hipLaunchKernelGGL(topk_select_kernel<D>, grid, dim3(kSelThreads), lds, stream, a);
   allow_dynamic_lds(reinterpret_cast<const void*>(fallback_kernel<D>), (int)kSelectRowLdsBytes);
   hipLaunchKernelGGL(fallback_kernel<D>, dim3(256), dim3(kFbThreads), (size_t)a.n_blocks * 8, stream, a);
