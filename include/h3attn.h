@@ -262,6 +262,17 @@ h3attn_status h3attn_residual_change(const h3attn_bf16* cur, const h3attn_bf16* 
                                      double* result, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
+/* h3attn_residual_change without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the partial sums live in a file-scope device array of 2^17 pairs (2 MB, held by every GPU the
+ * library runs on until the process ends), so n is limited to 2^33 elements; larger n ->
+ * INVALID_ARGUMENT. Nothing is allocated and nothing needs clearing (every partial is written
+ * before it is read). Calls on one GPU share the array: calls that overlap on one GPU (two
+ * streams, two host threads) race. Same results as h3attn_residual_change, bit for bit.
+ * Errors: as h3attn_residual_change; a failed lookup of the array -> LAUNCH. */
+h3attn_status h3attn_residual_change_noalloc(const h3attn_bf16* cur, const h3attn_bf16* prev, int64_t n,
+                                             double* result, hipStream_t stream);
+
 /* Host-side reuse policy (plain C state; no GPU work). */
 typedef struct {
   double threshold;        /* reuse only when the relative change is strictly below this */

@@ -46,6 +46,7 @@ void launch_fp8_block_sparse_fwd(const Fp8AttnArgs& a, hipStream_t) { g_fa = a; 
 void launch_adaln(const AdaLNArgs& a, hipStream_t) { g_ad = a; ++g_launches; }
 void launch_swiglu(const SwiGLUArgs& a, hipStream_t) { g_sw = a; ++g_launches; }
 void launch_residual_change(const ResidualArgs& a, hipStream_t) { g_res = a; ++g_launches; }
+double* residual_noalloc_scratch() { return reinterpret_cast<double*>(0xD00000); }
 int residual_parts(int64_t n) {
   const int64_t chunks = (n + 7) / 8;
   return (int)((chunks + kResidualChunksPerBlock - 1) / kResidualChunksPerBlock);
@@ -200,6 +201,18 @@ void check_block_ops() {
   EXPECT(launched(h3attn_residual_change(Q, K, 655371, res, WS, rws, nullptr), n0));
   EXPECT(g_res.n == 655371 && g_res.result == res);
   EXPECT(h3attn_residual_change(Q, K, 655371, res, WS, rws - 1, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+  // the allocation-free variant: the partial sums go to the library's device array; sizes past
+  // its 2^17 pairs are refused before any launch
+  n0 = g_launches;
+  EXPECT(launched(h3attn_residual_change_noalloc(Q, K, 655371, res, nullptr), n0));
+  EXPECT(g_res.n == 655371 && g_res.result == res && g_res.partial == reinterpret_cast<double*>(0xD00000));
+  const int64_t max_n = h3attn::kResidualNoAllocParts * h3attn::kResidualChunksPerBlock * 8;
+  n0 = g_launches;
+  EXPECT(launched(h3attn_residual_change_noalloc(Q, K, max_n, res, nullptr), n0));
+  EXPECT(h3attn_residual_change_noalloc(Q, K, max_n + 1, res, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+  EXPECT(h3attn_residual_change_noalloc(Q, K, 0, res, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+  EXPECT(h3attn_residual_change_noalloc(Q, K, 100, nullptr, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+  EXPECT(g_launches == n0 + 1);
   // the reuse policy is host code on a caller-owned struct
   h3attn_cache_gate gate;
   EXPECT(h3attn_cache_gate_init(&gate, 0.05, 1) == H3ATTN_OK);

@@ -56,6 +56,7 @@ SIGNATURES = {
     "h3attn_swiglu": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I64, _I64, _P]),
     "h3attn_residual_workspace_bytes": (ctypes.c_size_t, [_I64]),
     "h3attn_residual_change": (ctypes.c_int, [_P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "h3attn_residual_change_noalloc": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
     "h3attn_cache_gate_init": (ctypes.c_int, [_P, ctypes.c_double, _I32]),
     "h3attn_cache_gate_decide": (_I32, [_P, ctypes.c_double]),
     "h3attn_cache_gate_decide_sums": (_I32, [_P, _P]),

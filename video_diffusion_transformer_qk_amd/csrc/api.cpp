@@ -504,6 +504,25 @@ h3attn_status h3attn_residual_change(const h3attn_bf16* cur, const h3attn_bf16* 
   return check_launch("h3attn_residual_change");
 }
 
+h3attn_status h3attn_residual_change_noalloc(const h3attn_bf16* cur, const h3attn_bf16* prev, int64_t n,
+                                             double* result, hipStream_t stream) {
+  CHECK_PTR(cur); CHECK_PTR(prev);
+  if (result == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "result is NULL");
+  if (reinterpret_cast<uintptr_t>(result) & 7u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "result is not 8-byte aligned");
+  if (n <= 0) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "n must be > 0");
+  if (h3attn::residual_parts(n) > h3attn::kResidualNoAllocParts)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT,
+                "n = %lld needs %d partial sums, more than the %lld of the allocation-free scratch (n <= %lld)",
+                (long long)n, h3attn::residual_parts(n), (long long)h3attn::kResidualNoAllocParts,
+                (long long)(h3attn::kResidualNoAllocParts * h3attn::kResidualChunksPerBlock * 8));
+  double* partial = h3attn::residual_noalloc_scratch();
+  if (partial == nullptr) return fail(H3ATTN_ERR_LAUNCH, "h3attn_residual_change_noalloc: device scratch lookup failed");
+  h3attn::ResidualArgs a{};
+  a.cur = cur; a.prev = prev; a.n = n; a.partial = partial; a.result = result;
+  h3attn::launch_residual_change(a, stream);
+  return check_launch("h3attn_residual_change_noalloc");
+}
+
 h3attn_status h3attn_cache_gate_init(h3attn_cache_gate* gate, double threshold, int32_t max_consecutive) {
   if (gate == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "gate is NULL");
   if (!(threshold >= 0.0)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "threshold must be >= 0");

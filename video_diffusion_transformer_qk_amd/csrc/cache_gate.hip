@@ -12,6 +12,8 @@
 //   read once with nontemporal loads.
 // residual_final_kernel: one workgroup adds the per-workgroup pairs in a fixed order, so the
 //   result is deterministic run to run.
+#include <mutex>
+
 #include "device_util.h"
 #include "kernels.h"
 
@@ -76,7 +78,28 @@ __global__ __launch_bounds__(kRedThreads) void residual_final_kernel(ResidualArg
   }
 }
 
+// Partial sums of h3attn_residual_change_noalloc. Every GPU the library runs on holds its own copy
+// until the process ends; calls on one GPU share it, so calls that overlap on one GPU race.
+static __device__ __align__(256) double scratch[2 * kResidualNoAllocParts];
+
 }  // namespace
+
+double* residual_noalloc_scratch() {
+  // one lookup per device, with that device current; the array's host-side name is not a device
+  // address, so only the looked-up pointer is ever handed to kernels
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static double* ptr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = static_cast<double*>(p);
+  }
+  return ptr[dev];
+}
 
 int residual_parts(int64_t n) {
   const int64_t chunks = (n + 7) / 8;

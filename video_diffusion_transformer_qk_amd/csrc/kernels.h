@@ -120,6 +120,13 @@ struct ResidualArgs {
 int residual_parts(int64_t n);
 void launch_residual_change(const ResidualArgs& a, hipStream_t stream);
 
+// The allocation-free residual change keeps its per-workgroup partial sums in a file-scope device
+// array of this many (sum |cur - prev|, sum |prev|) pairs (2 MB; n up to 2^33 elements).
+constexpr int64_t kResidualNoAllocParts = (int64_t)1 << 17;
+// Device address of that array on the current device (looked up once per device with
+// hipGetSymbolAddress); null if the lookup failed.
+double* residual_noalloc_scratch();
+
 // ---- fp8 (OCP e4m3) attention ----
 // Quantised tensors: q8, k8 are [B, N, H, D] bytes (e4m3 codes of x / s, s the power-of-two
 // scale of the (b, head, 64-token block)); v8t is [B, H, D, nB*64] bytes: V transposed, each
