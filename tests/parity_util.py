@@ -18,8 +18,8 @@ LSE_MAX_ABS = 4e-3
 NEAR_TIE_REL = 1e-5
 # fp8 (e4m3) attention against exact float64 attention: q, k, v and the probabilities each carry
 # 3 significant bits, so the bar is looser than the bf16 one. For the workloads' inputs
-# (v ~ N(0,1)): absolute; measured worst 0.033 / 2.2e-3 on the frame workload (sparse) and
-# 0.072 / 3.2e-3 on sampled 5 s blocks (sparse, block 0), about half these limits.
+# (v ~ N(0,1)): absolute; measured worst 0.041 / 2.2e-3 on the frame workload and 0.125 / 3.2e-3
+# on sampled 5 s blocks (the oracle's own fp8 rule against exact attention: 0.072 / 3.2e-3).
 FP8_EXACT_MAX_ABS = 0.15
 FP8_EXACT_MEAN_ABS = 1e-2
 # For inputs whose token and channel magnitudes differ by powers of two (scores up to ~16), the
