@@ -36,6 +36,8 @@
 //  fallback_kernel      rows routed there: float64 row in LDS, radix select.
 // Threshold mode (keep j iff s_ij >= max_j s_ij - tau): threshold_count_kernel (exact row maximum
 // and kept counts), row_ptr_scan_kernel, threshold_fill_kernel (the same decisions, written as CSR).
+#include <type_traits>
+
 #include "device_util.h"
 #include "kernels.h"
 #include "launch_util.h"
@@ -51,9 +53,9 @@ constexpr int kRows = 32;                   // query blocks per selection workgr
 constexpr int kSelThreads = 256;            // 4 waves
 constexpr int kWaves = kSelThreads / 64;
 constexpr int kBins = 1024;                 // histogram bins per row and level
-constexpr int kHistStride = kBins / 2 + 1;  // 32-bit words per row (two 16-bit counts each, +1 pad)
+constexpr int kHistStride = kBins / 2 + 4;  // 32-bit words per row (two 16-bit counts each; word 512 is the
+                                            // pad, 16-byte aligned rows)
 constexpr int kCap = 160;                   // candidate slots per row
-constexpr int kAmbCap = 64;                 // entries decided on float64 scores per row
 constexpr int kDigitShift = 21;             // |x| * 2^-e in [2^21, 2^22): |X| <= 2^22
 constexpr int kZeroExp = -1000;             // exponent recorded for an all-zero mean vector
 // |P1 * 2^8 + P0| per channel for the dropped digit pairs (d1 d0', d0 d1' and d0 d0', digits in
@@ -64,78 +66,73 @@ __device__ __forceinline__ int64_t n_pad(int32_t nb) { return ((int64_t)nb + kRo
 
 // ------------------------------------------------------------------------------------ pooling
 
-// One workgroup per (b, head, block j), head fastest. Threads hold 16-byte row chunks of q and k
-// and sum in fp64 (exact); lanes of the first wave finish the sums in a fixed order, write the
-// means, reduce max|x|, sum|x| and sum x^2 across the row's chunks, and write the digits.
+// One workgroup per (batch, tensor, block j, group of heads): thread t owns the 16-byte chunk t of
+// the group's slice of every token row (kPoolThreads * 16 bytes of consecutive heads), so each
+// wave reads 1 KB contiguous per row and the 64 rows stream in with 16 loads in flight per
+// thread. Each thread sums its 8 channels over the block in float64 (exact whenever a channel's
+// nonzero values in the block lie within a factor 2^39 of each other: 8-bit significands, 64
+// terms, 53 bits; always so for data of these workloads' ranges), then the
+// D / 8 threads of a head finish the block: means, max |x|, sum |x| and sum x^2 over the head's
+// channels (a fixed xor-shuffle tree), the digits, exponent and norms. No LDS, no barriers.
 template <int D>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
-  constexpr int CH = D / 8;            // 16-byte chunks per row
-  constexpr int PAIRS = 2 * CH;        // (tensor, chunk) pairs
-  constexpr int TL = kPoolThreads / PAIRS;  // token lanes
-  constexpr int KS = D / 32;           // MFMA k steps
-  __shared__ double red[TL][PAIRS][8];
-
+  constexpr int CH = D / 8;                 // 16-byte chunks per head row
+  constexpr int HPW = kPoolThreads / CH;    // heads per workgroup
+  constexpr int KS = D / 32;                // MFMA k steps
+  constexpr int UNROLL = 16;                // rows in flight per thread
   const int tid = threadIdx.x;
-  const int pair = tid % PAIRS;
-  const int tl = tid / PAIRS;
-  const int tensor = pair / CH;
-  const int chunk = pair % CH;
-  const int head = (int)(blockIdx.x % (unsigned)a.heads), j = (int)(blockIdx.x / (unsigned)a.heads), b = blockIdx.z;
+  const int groups = (a.heads + HPW - 1) / HPW;
+  const int hg = (int)(blockIdx.x % (unsigned)groups), j = (int)(blockIdx.x / (unsigned)groups);
+  const int tensor = (int)(blockIdx.z & 1u), b = (int)(blockIdx.z >> 1);
+  const int head = hg * HPW + tid / CH, chunk = tid % CH;
+  if (head >= a.heads) return;  // whole heads drop out together (CH divides 64)
   const int64_t N = a.n_tokens;
   const int64_t row_stride = (int64_t)a.heads * D;
   const int64_t t0 = (int64_t)j * a.block_size;
-  const int64_t t1 = t0 + a.block_size < N ? t0 + a.block_size : N;
-  const uint16_t* src = (tensor == 0 ? a.q : a.k) + ((int64_t)b * N) * row_stride + (int64_t)head * D + chunk * 8;
+  const int rows = (int)(t0 + a.block_size < N ? a.block_size : N - t0);
+  const uint16_t* src = (tensor == 0 ? a.q : a.k) + ((int64_t)b * N + t0) * row_stride + (int64_t)head * D + chunk * 8;
 
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  constexpr int R = 64 / TL;  // rows per thread: blocks are 64 tokens (the entry points accept no other size)
-  u32x4 w[R];
+  // blocks are 64 tokens (the entry points accept no other size)
+#pragma unroll 1
+  for (int g = 0; g < 64; g += UNROLL) {
+    u32x4 w[UNROLL];
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int64_t t = t0 + tl + (int64_t)i * TL;
-    w[i] = u32x4{0u, 0u, 0u, 0u};
-    if (t < t1) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + t * row_stride));
-  }
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    if (t0 + tl + (int64_t)i * TL >= t1) break;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += (double)bf16_lo(w[i][e]);
-      acc[2 * e + 1] += (double)bf16_hi(w[i][e]);
+    for (int i = 0; i < UNROLL; ++i) {
+      w[i] = u32x4{0u, 0u, 0u, 0u};
+      if (g + i < rows) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(g + i) * row_stride));
     }
-  }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red[tl][pair][e] = acc[e];
-  __syncthreads();
-  if (tid >= 64) return;
-  // lanes 0 .. PAIRS-1 of the first wave: (tensor, chunk) = (lane / CH, lane % CH)
+    for (int i = 0; i < UNROLL; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)bf16_lo(w[i][e]);
+        acc[2 * e + 1] += (double)bf16_hi(w[i][e]);
+      }
+  }
   const int64_t bh = (int64_t)b * a.heads + head;
-  const double cnt = (double)(t1 - t0);
+  const double cnt = (double)rows;
   double m[8];
   double amax = 0.0, l1 = 0.0, l2 = 0.0;
-  if (tl == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      double s = 0.0;
-      for (int u = 0; u < TL; ++u) s += red[u][pair][e];
-      m[e] = s / cnt;
-      amax = fmax(amax, fabs(m[e]));
-      l1 += fabs(m[e]);
-      l2 += m[e] * m[e];
-    }
+  for (int e = 0; e < 8; ++e) {
+    m[e] = acc[e] / cnt;
+    amax = fmax(amax, fabs(m[e]));
+    l1 += fabs(m[e]);
+    l2 += m[e] * m[e];
+  }
+  {
     double* dst = (tensor == 0 ? a.q_mean : a.k_mean) + (bh * a.n_blocks + j) * D + chunk * 8;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) *reinterpret_cast<double2*>(dst + e) = double2{m[e], m[e + 1]};
   }
-  // reduce over the CH lanes of the same tensor (xor offsets below CH stay inside the group)
+  // reduce over the CH lanes of the head (xor offsets below CH stay inside the group)
 #pragma unroll
   for (int off = 1; off < CH; off <<= 1) {
     amax = fmax(amax, __shfl_xor(amax, off));
     l1 += __shfl_xor(l1, off);
     l2 += __shfl_xor(l2, off);
   }
-  if (tl != 0) return;
   const int ex = amax > 0.0 ? ilogb(amax) - kDigitShift : 0;
   // digits: X = d0 + 256 d1 + 65536 d2, each digit in [-128, 127]; |X| <= 2^22 so |d2| <= 64
   uint32_t dig[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
@@ -170,11 +167,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
   }
 }
 
-// Per (batch, head): the largest key exponent and key norms over the blocks; also clears the
-// count of fallback rows (this kernel runs after pooling and before any selection kernel).
+// Per (batch, head): the largest key exponent F and the largest key norms (for the bounds); then
+// every key block's exponent is rewritten in place as its shift e_j - F, the power of two the
+// score passes scale its products by. Also clears the count of fallback rows (this kernel runs
+// after pooling and before any selection kernel).
 __global__ __launch_bounds__(256) void key_stats_kernel(SelectArgs a) {
   __shared__ int s_e[4];
   __shared__ float s_1[4], s_2[4];
+  __shared__ int s_f;
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int e = kZeroExp;
@@ -200,8 +200,12 @@ __global__ __launch_bounds__(256) void key_stats_kernel(SelectArgs a) {
     a.key_stat[4 * bh + 1] = __float_as_int(n1);
     a.key_stat[4 * bh + 2] = __float_as_int(n2);
     a.key_stat[4 * bh + 3] = 0;
+    s_f = e;
     if (bh == 0) *a.fb_count = 0;
   }
+  __syncthreads();
+  const int F = s_f;
+  for (int j = tid; j < a.n_blocks; j += 256) a.k_exp[r0 + j] -= F;
 }
 
 // ------------------------------------------------------------------------------- the bounds
@@ -210,9 +214,10 @@ __global__ __launch_bounds__(256) void key_stats_kernel(SelectArgs a) {
 // 2^16, f_j key block j's exponent, F the largest over the head's key blocks), in float32. They
 // stand for s_ij * 2^-(e_i + 16 + F). With X = x 2^-e + dx, |dx| <= 1/2 per channel (likewise Y):
 //   |X.Y - 2^-(e+f) s| <= |x|_1 2^-e / 2 + |y|_1 2^-f / 2 + D/4,   dropped pairs <= D * 8404992,
-// hence in v units |v - s 2^-(e+16+F)| <= D 8404992.25 2^-16 + |x|_1 2^-(e+17) + max|y|_1 2^-(F+17),
-// plus 2^-22 |v| for the float32 evaluation of v and 2^-126 for float32 underflow. The range
-// bound |v| <= |x|_2 max|y|_2 2^-(e+16+F) + E gives the histogram's span.
+// hence in v units |v - s 2^-(e+16+F)| <= D 8404992.25 2^-16 + |x|_1 2^-(e+17) + max|y|_1 2^-(F+17).
+// The float32 evaluation of v (two roundings, of the 2^8-weight products and of the sum with the
+// 2^0-weight ones, |p2| <= D 2^15) adds at most 2^-23 |v| + D 2^-9, float32 underflow 2^-126.
+// The range bound |v| <= |x|_2 max|y|_2 2^-(e+16+F) + E gives the histogram's span.
 struct RowBound {
   double e_v;      // error bound E (v units)
   double b_v;      // |v| <= b_v
@@ -234,14 +239,14 @@ __device__ __forceinline__ RowBound row_bound(const SelectArgs& a, int64_t bh, i
   if (y1 > 0.0) ev += y1 * ldexp(1.0, -(F + 17));
   double bv = (double)qn.y * y2 * to_v + ev;
   bv *= 1.0 + 0x1p-10;
-  rb.e_v = (ev + 0x1p-22 * bv) * (1.0 + 0x1p-10) + 0x1p-126;
+  rb.e_v = (ev + 0x1p-22 * bv + (double)D * 0x1p-9) * (1.0 + 0x1p-10) + 0x1p-126;
   rb.b_v = bv;
   rb.to_v = to_v;
   return rb;
 }
 
-// The float64 score q_mean_i . k_mean_j, summed in channel order (the one float64 evaluation used
-// by every kernel here, so that all of them decide an entry the same way).
+// The float64 score q_mean_i . k_mean_j, summed in channel order (the evaluation of the kernels
+// that decide single entries: the threshold passes and the fallback).
 template <int D>
 __device__ __forceinline__ double exact_score(const double* qm, const double* km) {
   double s = 0.0;
@@ -272,126 +277,125 @@ struct QueryOperand {
   }
 };
 
-// Every (row, key) score of the workgroup's rows, key chunks of 32 spread over the waves. For each
-// valid entry calls f(j, v): j the key block, v the approximate score of row r = lane % 32 (every
-// entry a lane sees belongs to that row). The MFMA's output holds key 8 (k / 4) + 4 (l / 32) + k % 4
-// of query l % 32 in accumulator k of lane l. The next chunk's operands are loaded while the
-// current one is multiplied.
-template <int D>
-struct KeyOperand {
-  i32x4 f[D / 32][3];
-};
-
-// PREFETCH: load the wave's next chunk of key digits while the current one is multiplied (more
-// registers: the kernels that also evaluate float64 scores inside the pass do without).
-template <int D, bool PREFETCH, typename Fn>
-__device__ __forceinline__ void score_pass(const SelectArgs& a, const QueryOperand<D>& qo, int64_t bh, int F,
-                                           int wave, int lane, Fn&& fn) {
+// Every (row, key) score of the workgroup's rows, key chunks of 32 spread over the waves. For
+// each entry calls fn(q, j, v, valid): the lane's q-th product (0..15), key block j, the
+// approximate score v of row r = lane % 32 (every entry a lane sees belongs to that row) and
+// whether j is a real key block (the last chunk is padded); then done(c) once the 16 entries of
+// chunk c are through. The MFMA's output holds key 8 (q / 4) + 4 (l / 32) + q % 4 of query
+// l % 32 in accumulator q of lane l, so lanes r and r + 32 together see all 32 keys of a chunk.
+// The next chunk's operands are loaded once the products are issued and arrive under the
+// per-entry work. Every lane runs every pass (the MFMA operands of a lane feed the outputs of
+// the other lanes), so callers fold row liveness and validity into their arithmetic, and the
+// loop bounds are uniform over the wave. PIPE = false loads each chunk just before its products
+// (fewer registers, for the passes that also evaluate float64 scores).
+template <int D, bool PIPE = true, typename Fn, typename Done>
+__device__ __forceinline__ void score_pass(const SelectArgs& a, const QueryOperand<D>& qo, int64_t bh, int wave,
+                                           int lane, Fn&& fn, Done&& done) {
   const int nb = a.n_blocks;
   const int nchunks = (int)(n_pad(nb) / kRows);
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  if (w >= nchunks) return;
+  const int last = nchunks - 1;
   const int8_t* kd = a.k_digits + bh * nchunks * (D / 32) * 3 * 1024 + lane * 16;
-  const int* ke = a.k_exp + bh * n_pad(nb) + 4 * (lane >> 5);
-  auto load = [&](int c, KeyOperand<D>& k) {
+  const int* ks = a.k_exp + bh * n_pad(nb) + 4 * (lane >> 5);
+  typedef i32x4 Digits[D / 32][3];
+  auto load = [&](int c, Digits& f) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int L = 0; L < 3; ++L)
-        k.f[t][L] = *reinterpret_cast<const i32x4*>(kd + ((int64_t)(c * (D / 32) + t) * 3 + L) * 1024);
+        f[t][L] = *reinterpret_cast<const i32x4*>(kd + ((int64_t)(c * (D / 32) + t) * 3 + L) * 1024);
   };
-  auto compute = [&](int c, const KeyOperand<D>& k) {
-    // the exponents of the lane's 16 keys, loaded under the products
-    i32x4 e[4];
+  Digits f;
+  if (PIPE) load(w, f);
+  // TAIL: the last chunk, where key blocks past nb are padding
+  auto chunk = [&](int c, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
+    if (!PIPE) load(c, f);
+    i32x4 sh[4];  // needed after the products: loaded under them
 #pragma unroll
-    for (int g = 0; g < 4; ++g) e[g] = *reinterpret_cast<const i32x4*>(ke + 32 * c + 8 * g);
+    for (int g = 0; g < 4; ++g) sh[g] = *reinterpret_cast<const i32x4*>(ks + 32 * c + 8 * g);
     i32x16 p4 = {}, p3 = {}, p2 = {};
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
-      p4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][2], qo.f[t][2], p4, 0, 0, 0);
-      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][2], qo.f[t][1], p3, 0, 0, 0);
-      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][1], qo.f[t][2], p3, 0, 0, 0);
-      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][2], qo.f[t][0], p2, 0, 0, 0);
-      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][1], qo.f[t][1], p2, 0, 0, 0);
-      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k.f[t][0], qo.f[t][2], p2, 0, 0, 0);
+      p4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[t][2], qo.f[t][2], p4, 0, 0, 0);
+      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[t][2], qo.f[t][1], p3, 0, 0, 0);
+      p3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[t][1], qo.f[t][2], p3, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[t][2], qo.f[t][0], p2, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[t][1], qo.f[t][1], p2, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[t][0], qo.f[t][2], p2, 0, 0, 0);
     }
+    if (PIPE && !TAIL) load(c + kWaves <= last ? c + kWaves : last, f);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int j = 32 * c + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
-      if (j < nb) {
-        const float hi = fmaf((float)p4[q], 65536.f, (float)p3[q] * 256.f);
-        const float v = ldexpf(hi + (float)p2[q], e[q / 4][q % 4] - F);
-        fn(j, v);
-      }
+      // 2^8 p4 + p3 is exact in int32: |p4| <= D 2^12 (|d2| <= 64), |p3| <= D 2^14
+      const int m = (p4[q] << 8) + p3[q];
+      const float v = ldexpf(fmaf((float)m, 256.f, (float)p2[q]), sh[q / 4][q % 4]);
+      fn(q, j, v, TAIL ? j < nb : true);
     }
+    done(c);
   };
-  if constexpr (PREFETCH) {
-    KeyOperand<D> ka, kb;
-    int c = wave;
-    if (c < nchunks) load(c, ka);
-    while (c < nchunks) {
-      if (c + kWaves < nchunks) load(c + kWaves, kb);
-      compute(c, ka);
-      c += kWaves;
-      if (c >= nchunks) break;
-      if (c + kWaves < nchunks) load(c + kWaves, ka);
-      compute(c, kb);
-      c += kWaves;
-    }
-  } else {
-    for (int c = wave; c < nchunks; c += kWaves) {
-      KeyOperand<D> k;
-      load(c, k);
-      compute(c, k);
-    }
-  }
-}
-
-// The float64 score of row qm against the key rows of the wave's list, all 64 lanes on one score:
-// lane l multiplies channels 2l and 2l+1, a fixed shuffle tree adds the 64 products (the same order
-// for every entry). Used where a whole wave decides a row.
-template <int D>
-__device__ __forceinline__ double wave_exact_score(const double2 qv, const double* km, int lane) {
-  const double2 kv = 2 * lane < D ? *reinterpret_cast<const double2*>(km + 2 * lane) : double2{0.0, 0.0};
-  double p = fma(qv.y, kv.y, qv.x * kv.x);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) p += __shfl_down(p, off);
-  return __shfl(p, 0);
+  int c = w;
+  for (; c < last; c += kWaves) chunk(c, std::false_type{});
+  if (c == last) chunk(c, std::true_type{});
 }
 
 // ---------------------------------------------------------------------- histogram bracketing
 
-// Bin of v in a row's first-level histogram over [-B, B] (t = (v + B) * NBINS / 2B, clamped),
-// and the sub-bin inside a chosen bin b (exact: t - b is in [0, 1) for entries of bin b, except in
-// the clamped end bins, whose sub-bins are clamped too).
-__device__ __forceinline__ float bin_pos(float v, float bsum, float scale) { return (v + bsum) * scale; }
-__device__ __forceinline__ int bin_of(float t) { return (int)fminf(fmaxf(t, 0.f), (float)(kBins - 1)); }
-__device__ __forceinline__ int sub_of(float t, int b) { return (int)fminf(fmaxf((t - (float)b) * (float)kBins, 0.f), (float)(kBins - 1)); }
-
-__device__ __forceinline__ void hist_add(uint32_t* hist, int r, int bin) {
-  atomicAdd(&hist[r * kHistStride + (bin >> 1)], 1u << (16 * (bin & 1)));
+// Bin position of v in a row's first-level histogram over [-B, B]: t = v * scale + off with
+// scale = NBINS / 2B and off = B * scale (rounded once, by the fma); the bin is t clamped to
+// [0, NBINS - 1] and truncated, the sub-bin inside a chosen bin b likewise from (t - b) NBINS
+// (exact: t - b is in [0, 1) for entries of bin b, except in the clamped end bins, whose
+// sub-bins are clamped too). The value kBins stands for "no bin": it lands in the pad word.
+__device__ __forceinline__ float bin_pos(float v, float scale, float off) { return fmaf(v, scale, off); }
+__device__ __forceinline__ int bin_of(float t) { return (int)__builtin_amdgcn_fmed3f(t, 0.f, (float)(kBins - 1)); }
+__device__ __forceinline__ int sub_of(float t, int b) {
+  return (int)__builtin_amdgcn_fmed3f((t - (float)b) * (float)kBins, 0.f, (float)(kBins - 1));
 }
-__device__ __forceinline__ int hist_get(const uint32_t* hist, int r, int bin) {
-  return (int)((hist[r * kHistStride + (bin >> 1)] >> (16 * (bin & 1))) & 0xffffu);
+
+// 16-bit counts, two per word; bin kBins is the row's pad word
+__device__ __forceinline__ void hist_inc(uint32_t* row_hist, int bin) {
+  atomicAdd(&row_hist[bin >> 1], 1u << ((bin & 1) << 4));
+}
+
+// Wave-wide sum and exclusive scan of a non-negative value below 2^B per lane, bit-sliced through
+// ballots (no data moves between lanes).
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+template <int B>
+__device__ __forceinline__ int wave_sum_b(uint32_t x) {
+  int s = 0;
+#pragma unroll
+  for (int b = 0; b < B; ++b) s += __popcll(__ballot((x >> b) & 1u)) << b;
+  return s;
+}
+template <int B>
+__device__ __forceinline__ int wave_excl_scan_b(uint32_t x) {
+  int s = 0;
+#pragma unroll
+  for (int b = 0; b < B; ++b) s += lanes_below(__ballot((x >> b) & 1u)) << b;
+  return s;
 }
 
 // One wave finds, in row r's histogram, the bin holding the want-th largest entry: returns the bin
-// and, through above/count, the entries in higher bins and in the bin. Lane l owns bins
-// [kBins - 16 (l + 1), kBins - 16 l), highest first.
+// and, through above/count, the entries in higher bins and in the bin. Lane l owns the 8 words
+// [512 - 8 (l + 1), 512 - 8 l), i.e. bins [kBins - 16 (l + 1), kBins - 16 l), highest first.
+// (Counts are at most nB <= 19968 < 2^15.)
 __device__ int find_bin(const uint32_t* hist, int r, int want, int lane, int* above, int* count) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(hist + r * kHistStride + kBins / 2 - 8 * (lane + 1));
+  const u32x4 lo = p[0], hi = p[1];
+  const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   int c[16];
   int s = 0;
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
-    c[u] = hist_get(hist, r, kBins - 1 - (16 * lane + u));
+    c[u] = (int)((wd[7 - u / 2] >> (16 * (1 - (u & 1)))) & 0xffffu);  // bin kBins - 1 - (16 lane + u)
     s += c[u];
   }
-  int inc = s;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off);
-    if (lane >= off) inc += y;
-  }
-  const int before = inc - s;
-  const unsigned long long hit = __ballot(before < want && want <= inc);
+  const int before = wave_excl_scan_b<15>((uint32_t)s);
+  const unsigned long long hit = __ballot(before < want && want <= before + s);
   const int owner = hit ? (int)__builtin_ctzll(hit) : 63;
   int bin = 0, ab = 0, cn = 0;
   if (lane == owner) {
@@ -414,21 +418,19 @@ __device__ __forceinline__ uint64_t order_key(double x) {
   const uint64_t u = __double_as_longlong(x);
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
-
-// wave-wide sums and exclusive scans of one int per lane
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+// the same for float32: every finite float maps above 0
+__device__ __forceinline__ uint32_t order_u32(float x) {
+  const uint32_t u = __float_as_uint(x + 0.f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ int wave_excl_scan(int x, int lane) {
-  int inc = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off);
-    if (lane >= off) inc += y;
-  }
-  return inc - x;
+__device__ __forceinline__ float from_order_u32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// OR of the values of lanes l and l ^ 32, in both
+__device__ __forceinline__ uint32_t pair_or(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return r[0] | r[1];
 }
 
 // Writes the set bits of a row's bitmap (words [0, words)) in ascending order to dst, one wave;
@@ -439,49 +441,107 @@ __device__ int64_t write_bits(const uint32_t* bits, int words, int32_t* dst, int
     const int w = w0 + lane;
     uint32_t m = w < words ? bits[w] : 0u;
     const int cnt = __popc(m);
-    int64_t pos = carry + wave_excl_scan(cnt, lane);
+    int64_t pos = carry + wave_excl_scan_b<6>((uint32_t)cnt);
     while (m) {
       const int bt = __builtin_ctz(m);
       if (pos < cap) dst[pos] = 32 * w + bt;
       ++pos;
       m &= m - 1;
     }
-    carry += wave_sum(cnt);
+    carry += wave_sum_b<6>((uint32_t)cnt);
+  }
+  return carry;
+}
+
+// write_bits through an LDS staging area of 2048 ints (one wave's): 64 words at a time, each lane
+// expands its word's set bits into the staging area at the word's offset, then the wave copies
+// the run out with consecutive lanes on consecutive indices.
+__device__ int64_t write_bits_staged(const uint32_t* bits, int words, int32_t* dst, int64_t cap, int lane,
+                                     int32_t* stage) {
+  int64_t carry = 0;
+  for (int w0 = 0; w0 < words; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t m = w < words ? bits[w] : 0u;
+    const int cnt = __popc(m);
+    int pos = wave_excl_scan_b<6>((uint32_t)cnt);
+    const int tot = wave_sum_b<6>((uint32_t)cnt);
+    while (m) {
+      stage[pos++] = 32 * w + __builtin_ctz(m);
+      m &= m - 1;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    for (int p = lane; p < tot; p += 64)
+      if (carry + p < cap) dst[carry + p] = stage[p];
+    carry += tot;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
   return carry;
 }
 
 // ----------------------------------------------------------------------------- top-k select
 
+// The (batch-head, row chunk) of a selection workgroup. Consecutive workgroup ids are dealt to
+// the 8 XCDs in turn; renumbered so that each XCD takes one contiguous range of (head, chunk)
+// pairs, the workgroups of a head share one XCD's L2 and read its key operands from there.
+struct WgTile {
+  int64_t bh;
+  int chunk;
+};
+__device__ __forceinline__ WgTile xcd_tile() {
+  const int nrc = (int)gridDim.x;
+  const int total = nrc * (int)gridDim.y;
+  const int id = (int)blockIdx.x + nrc * (int)blockIdx.y;
+  const int per = total / 8, rem = total % 8, x = id % 8, s = id / 8;
+  const int lin = x < rem ? x * (per + 1) + s : rem * (per + 1) + (x - rem) * per + s;
+  return WgTile{lin / nrc, lin % nrc};
+}
+
+constexpr int kAmbList = 256;  // entries of a workgroup decided on float64 scores
+constexpr int kStage = 2048;   // ints of a wave's output staging area (64 bitmap words)
+static_assert(kWaves * kStage * 4 <= kRows * (kCap + 1) * 8, "staging must fit in the candidate lists");
+
 // Per-row state of a selection workgroup, in LDS.
 struct RowState {
-  float bsum[kRows], scale[kRows];   // histogram span and bins per unit of v
-  double e_v[kRows], to_v[kRows], b_v[kRows];
+  float scale[kRows], off[kRows], bsum[kRows];  // bin position t = v * scale + off over [-bsum, bsum]
+  double e_v[kRows];                 // error bound E (v units)
   int bin1[kRows], bin2[kRows];      // chosen first-level bin, chosen sub-bin (-1: none)
   int above[kRows], count[kRows];    // entries above the chosen (sub)bin and inside it
   int status[kRows];                 // 0 resolving, 1 invalid row, 2 routed to the fallback
   float in_thr[kRows], cand_thr[kRows];  // classification thresholds (v units, rounded outward)
   int ncand[kRows];
-  double t_sel[kWaves];
-  int amb_j[kWaves][kAmbCap];
-  double amb_s[kWaves][kAmbCap];
-  int amb_n[kWaves];
+  int need_a[kRows], amb0[kRows], namb[kRows];  // float64 decisions: the row's slice of the list
+  int amb_total;
   int refine;
+  uint32_t amb_e[kAmbList];          // (row << 16) | key block
+  double amb_s[kAmbList];            // their float64 scores
 };
 
+// Per workgroup: 32 query blocks of one (batch, head).
+//  1. histogram of every row's approximate scores (a second, finer pass over the chosen bin when
+//     it holds more than kCap entries) -> the bin holding the keep-th largest;
+//  2. classification pass: above the bin by more than 2E (plus the bin arithmetic's slack) ->
+//     kept, written as bitmap words; within -> candidate (v, j) in the row's LDS list;
+//  3. per row (one wave): the keep-th largest v among the candidates (t), candidates above t by
+//     more than 2E kept, the ones within 2E of t listed for a float64 decision;
+//  4. the listed entries' float64 scores, the whole workgroup at once; per row the best of them
+//     by (score descending, index ascending) fill the remaining places;
+//  5. the row's kept set written in ascending order. Rows that do not resolve (a bin that cannot
+//     be split, overfull lists) are routed to the fallback kernel.
 template <int D>
 __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   __shared__ RowState st;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = a.n_blocks, keep = a.keep;
-  const int64_t bh = blockIdx.y;
-  const int i0 = blockIdx.x * kRows;
+  const WgTile tile = xcd_tile();
+  const int64_t bh = tile.bh;
+  const int i0 = tile.chunk * kRows;
   const int words = (nb + 31) / 32;
   uint32_t* hist = dyn;                                        // [kRows][kHistStride]
   uint32_t* bits = dyn;                                        // [kRows][words]   (after the histograms)
-  float* cand_v = reinterpret_cast<float*>(dyn + kRows * words);            // [kRows][kCap]
-  uint16_t* cand_j = reinterpret_cast<uint16_t*>(cand_v + kRows * kCap);   // [kRows][kCap]
+  uint2* cand = reinterpret_cast<uint2*>(dyn + kRows * words);  // [kRows][kCap + 1]: (v bits, j), last slot discards
 
   int32_t* out_base = a.block_idx + (bh * nb + i0) * (int64_t)keep;
   if (keep == nb) {  // every block kept
@@ -490,45 +550,45 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
         for (int j = lane; j < nb; j += 64) out_base[(int64_t)r * keep + j] = j;
     return;
   }
-  const int F = a.key_stat[4 * bh];
   if (tid < kRows) {
     const int i = i0 + tid;
     st.status[tid] = i < nb ? 0 : 1;
     st.bin2[tid] = -1;
     st.ncand[tid] = 0;
+    st.namb[tid] = 0;
+    float bs = 1.f;
     if (i < nb) {
       const RowBound rb = row_bound<D>(a, bh, i);
       st.e_v[tid] = rb.e_v;
-      st.to_v[tid] = rb.to_v;
-      st.b_v[tid] = rb.b_v;
-      const float bs = __double2float_ru(rb.b_v);
-      st.bsum[tid] = bs;
-      st.scale[tid] = (float)kBins / (2.f * bs);
-    } else {
-      st.bsum[tid] = 1.f;
-      st.scale[tid] = 1.f;
+      bs = __double2float_ru(rb.b_v);
     }
+    const float sc = (float)kBins / (2.f * bs);
+    st.bsum[tid] = bs;
+    st.scale[tid] = sc;
+    st.off[tid] = bs * sc;
   }
-  if (tid == 0) st.refine = 0;
+  if (tid == 0) {
+    st.refine = 0;
+    st.amb_total = 0;
+  }
+  for (int e = tid; e < kAmbList; e += kSelThreads) st.amb_e[e] = 0u;  // a harmless (row 0, key 0)
   QueryOperand<D> qo;
-  qo.load(a, bh, blockIdx.x, lane);
+  qo.load(a, bh, tile.chunk, lane);
   for (int w = tid; w < kRows * kHistStride; w += kSelThreads) hist[w] = 0u;
   __syncthreads();
 
   // every entry a lane sees belongs to row r = lane % 32: its parameters stay in registers
   const int my_r = lane & 31;
   const bool my_live = st.status[my_r] == 0;
-  const float my_bsum = st.bsum[my_r], my_scale = st.scale[my_r];
+  const float my_scale = st.scale[my_r], my_off = st.off[my_r];
   uint32_t* my_hist = hist + my_r * kHistStride;
+  auto no_done = [](int) {};
 
-  // level 1: histogram of every valid row. (The passes run with every lane active: the MFMA
-  // operands of a lane feed the outputs of other lanes, so liveness is tested inside.)
-  score_pass<D, true>(a, qo, bh, F, wave, lane, [&](int j, float v) {
-    if (my_live) {
-      const int b = bin_of(bin_pos(v, my_bsum, my_scale));
-      atomicAdd(&my_hist[b >> 1], 1u << (16 * (b & 1)));
-    }
-  });
+  // 1. level 1: histogram of every valid row
+  // (rows past the end count garbage into their own, unread histograms)
+  score_pass<D>(a, qo, bh, wave, lane, [&](int, int, float v, bool valid) {
+    hist_inc(my_hist, valid ? bin_of(bin_pos(v, my_scale, my_off)) : kBins);
+  }, no_done);
   __syncthreads();
   for (int r = wave; r < kRows; r += kWaves) {
     if (st.status[r] != 0) continue;
@@ -549,13 +609,10 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
     __syncthreads();
     for (int w = tid; w < kRows * kHistStride; w += kSelThreads) hist[w] = 0u;
     __syncthreads();
-    score_pass<D, true>(a, qo, bh, F, wave, lane, [&](int j, float v) {
-      const float t = bin_pos(v, my_bsum, my_scale);
-      if (my_refine && bin_of(t) == my_bin1) {
-        const int b = sub_of(t, my_bin1);
-        atomicAdd(&my_hist[b >> 1], 1u << (16 * (b & 1)));
-      }
-    });
+    score_pass<D>(a, qo, bh, wave, lane, [&](int, int, float v, bool valid) {
+      const float t = bin_pos(v, my_scale, my_off);
+      hist_inc(my_hist, valid && my_refine && bin_of(t) == my_bin1 ? sub_of(t, my_bin1) : kBins);
+    }, no_done);
     __syncthreads();
     for (int r = wave; r < kRows; r += kWaves) {
       if (st.status[r] != 0 || st.count[r] <= kCap) continue;
@@ -577,128 +634,184 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
     const double b1 = st.bin1[r];
     const double tlo = st.bin2[r] < 0 ? b1 : b1 + st.bin2[r] / (double)kBins;
     const double thi = st.bin2[r] < 0 ? b1 + 1.0 : b1 + (st.bin2[r] + 1) / (double)kBins;
-    const double bs = st.bsum[r], sc = st.scale[r];
-    const double slack = 0x1p-20 * bs;
+    const double sc = st.scale[r], off = st.off[r];
+    const double slack = 0x1p-20 * (double)st.bsum[r];
     const double e2 = 2.0 * st.e_v[r];
-    st.cand_thr[r] = tlo <= 0.0 ? -INFINITY : __double2float_rd(tlo / sc - bs - slack - e2);
-    st.in_thr[r] = thi >= (double)kBins ? INFINITY : __double2float_ru(thi / sc - bs + slack + e2);
+    st.cand_thr[r] = tlo <= 0.0 ? -INFINITY : __double2float_rd((tlo - off) / sc - slack - e2);
+    st.in_thr[r] = thi >= (double)kBins ? INFINITY : __double2float_ru((thi - off) / sc + slack + e2);
   }
-  for (int w = tid; w < kRows * words; w += kSelThreads) bits[w] = 0u;
   __syncthreads();
-  // classification: above the bracket by more than 2E -> kept; within it -> candidate
+  // 2. classification: every bitmap word is written by the wave that scores its chunk (rows not
+  // resolving here write their own, unread regions)
   {
-    const bool live = st.status[my_r] == 0;
     const float in_thr = st.in_thr[my_r], cand_thr = st.cand_thr[my_r];
     uint32_t* my_bits = bits + my_r * words;
-    float* my_cv = cand_v + my_r * kCap;
-    uint16_t* my_cj = cand_j + my_r * kCap;
+    uint2* my_cand = cand + my_r * (kCap + 1);
     int* my_n = &st.ncand[my_r];
-    score_pass<D, true>(a, qo, bh, F, wave, lane, [&](int j, float v) {
-      if (!live) return;
-      if (v > in_thr) {
-        atomicOr(&my_bits[j >> 5], 1u << (j & 31));
-      } else if (v >= cand_thr) {
-        const int slot = atomicAdd(my_n, 1);
-        if (slot < kCap) {
-          my_cv[slot] = v;
-          my_cj[slot] = (uint16_t)j;
-        }
+    uint32_t inm = 0u, cm = 0u;
+    float cv[16];
+    score_pass<D>(a, qo, bh, wave, lane, [&](int q, int j, float v, bool valid) {
+      const bool in = valid && v > in_thr;
+      const bool cd = valid && !(v > in_thr) && v >= cand_thr;
+      inm |= (uint32_t)in << (j & 31);
+      cm |= (uint32_t)cd << q;
+      cv[q] = v;
+    }, [&](int c) {
+      my_bits[c] = pair_or(inm);
+      const int base = atomicAdd(my_n, __popc(cm));
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int slot = base + __popc(cm & ((1u << q) - 1u));
+        const bool put = ((cm >> q) & 1u) && slot < kCap;
+        const int j = 32 * c + 8 * (q / 4) + 4 * (lane >> 5) + (q % 4);
+        my_cand[put ? slot : kCap] = uint2{__float_as_uint(cv[q]), (uint32_t)j};
       }
+      inm = 0u;
+      cm = 0u;
     });
   }
   __syncthreads();
 
-  // resolution, one wave per row
-  const double* km_base = a.k_mean + bh * nb * (int64_t)D;
+  // 3. per row: the pivot, the sure entries and the list for float64 decisions
   for (int r = wave; r < kRows; r += kWaves) {
     if (st.status[r] == 1) continue;
     const int n = st.ncand[r];
     bool fb = st.status[r] == 2 || n > kCap;
     int nsure = 0;
     for (int w = lane; w < words; w += 64) nsure += __popc(bits[r * words + w]);
-    nsure = wave_sum(nsure);
+    nsure = wave_sum_b<15>((uint32_t)nsure);
     const int need = keep - nsure;
     if (!fb && (need < 1 || need > n)) fb = true;
     if (!fb) {
-      const float* cv = cand_v + r * kCap;
-      const uint16_t* cj = cand_j + r * kCap;
-      // the need-th candidate by (v descending, j ascending): ranks are a permutation of 0 .. n-1
-      float tsel = 0.f;
-      int found = 0;
+      const uint2* cr = cand + r * (kCap + 1);
+      constexpr int U = (kCap + 63) / 64;
+      uint32_t key[U];
+      float cvv[U];
+      int cjj[U];
 #pragma unroll
-      for (int u = 0; u < (kCap + 63) / 64; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int c = lane + 64 * u;
-        if (c >= n) continue;
-        const float v = cv[c];
-        const int j = cj[c];
-        int rk = 0;
-        for (int c2 = 0; c2 < n; ++c2) {
-          const float v2 = cv[c2];
-          rk += (v2 > v) || (v2 == v && (int)cj[c2] < j);
-        }
-        if (rk == need - 1) { tsel = v; found = 1; }
+        const uint2 e = c < n ? cr[c] : uint2{0u, 0u};
+        cvv[u] = __uint_as_float(e.x);
+        cjj[u] = (int)e.y;
+        key[u] = c < n ? order_u32(cvv[u]) : 0u;
       }
-      const unsigned long long who = __ballot(found);
-      tsel = __shfl(tsel, who ? (int)__builtin_ctzll(who) : 0);
-      const double t = tsel, e2 = 2.0 * st.e_v[r];
-      // kept outright, dropped, or listed for a float64 decision
+      // t: the need-th largest v, bit by bit from the top (absent slots hold key 0)
+      uint32_t T = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t T2 = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) cnt += __popcll(__ballot(key[u] >= T2));
+        if (cnt >= need) T = T2;
+      }
+      const double t = from_order_u32(T), e2 = 2.0 * st.e_v[r];
       int nin = 0;
-      if (lane == 0) st.amb_n[wave] = 0;
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      bool am[U];
 #pragma unroll
-      for (int u = 0; u < (kCap + 63) / 64; ++u) {
-        const int c = lane + 64 * u;
-        if (c >= n) continue;
-        const double v = cv[c];
-        if (v - e2 > t) {
-          ++nin;
-          atomicOr(&bits[r * words + (cj[c] >> 5)], 1u << (cj[c] & 31));
-        } else if (v + e2 >= t) {
-          const int slot = atomicAdd(&st.amb_n[wave], 1);
-          if (slot < kAmbCap) st.amb_j[wave][slot] = cj[c];
-        }
+      for (int u = 0; u < U; ++u) {
+        const bool present = lane + 64 * u < n;
+        const double v = cvv[u];
+        const bool in = present && v - e2 > t;
+        am[u] = present && !in && v + e2 >= t;
+        if (in) atomicOr(&bits[r * words + (cjj[u] >> 5)], 1u << (cjj[u] & 31));
+        nin += in;
       }
-      nin = wave_sum(nin);
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      const int na = st.amb_n[wave];
+      nin = wave_sum_b<2>((uint32_t)nin);
+      unsigned long long bm[U];
+      int na = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        bm[u] = __ballot(am[u]);
+        na += __popcll(bm[u]);
+      }
       const int need_a = need - nin;
-      if (na > kAmbCap || need_a < 1 || need_a > na) {
+      if (need_a < 1 || need_a > na) {
         fb = true;
+      } else if (need_a == na) {  // every listed entry is kept: no float64 decision needed
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (am[u]) atomicOr(&bits[r * words + (cjj[u] >> 5)], 1u << (cjj[u] & 31));
       } else {
-        // the listed entries' float64 scores, a whole wave per score
-        const double* qm = a.q_mean + (bh * nb + i0 + r) * D;
-        const double2 qv = 2 * lane < D ? *reinterpret_cast<const double2*>(qm + 2 * lane) : double2{0.0, 0.0};
-        double my_s = 0.0;
-        for (int e = 0; e < na; ++e) {
-          const double sc = wave_exact_score<D>(qv, km_base + (int64_t)st.amb_j[wave][e] * D, lane);
-          if (lane == e) my_s = sc;
-        }
-        if (lane < na) st.amb_s[wave][lane] = my_s;
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        if (lane < na) {
-          const int j = st.amb_j[wave][lane];
-          int rk = 0;
-          for (int c2 = 0; c2 < na; ++c2) {
-            const double s2 = st.amb_s[wave][c2];
-            rk += (s2 > my_s) || (s2 == my_s && st.amb_j[wave][c2] < j);
+        int start = 0;
+        if (lane == 0) start = atomicAdd(&st.amb_total, na);
+        start = __shfl(start, 0);
+        if (start + na > kAmbList) {
+          fb = true;
+        } else {
+          int pos = start;
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (am[u]) st.amb_e[pos + lanes_below(bm[u])] = ((uint32_t)r << 16) | (uint32_t)cjj[u];
+            pos += __popcll(bm[u]);
           }
-          if (rk < need_a) atomicOr(&bits[r * words + (j >> 5)], 1u << (j & 31));
+          if (lane == 0) {
+            st.need_a[r] = need_a;
+            st.amb0[r] = start;
+            st.namb[r] = na;
+          }
         }
       }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     }
-    if (fb) {
-      if (lane == 0) {
-        const int slot = atomicAdd(a.fb_count, 1);
-        a.fb_rows[slot] = (int32_t)(bh * nb + i0 + r);
+    if (fb && lane == 0) {
+      st.status[r] = 2;
+      const int slot = atomicAdd(a.fb_count, 1);
+      a.fb_rows[slot] = (int32_t)(bh * nb + i0 + r);
+    }
+  }
+  __syncthreads();
+
+  // 4. the listed entries' float64 scores, four per wave at a time: lane l multiplies channels
+  // 2l and 2l+1, a fixed shuffle tree adds the 64 products
+  {
+    const int total = st.amb_total < kAmbList ? st.amb_total : kAmbList;
+    const double* qm_base = a.q_mean + (bh * nb + i0) * (int64_t)D;
+    const double* km_base = a.k_mean + bh * nb * (int64_t)D;
+    for (int e0 = 4 * wave; e0 < total; e0 += 4 * kWaves) {
+      double p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        p[u] = 0.0;
+        const int e = e0 + u;
+        if (e < total && 2 * lane < D) {
+          const uint32_t ent = st.amb_e[e];
+          const double2 x = *reinterpret_cast<const double2*>(qm_base + (int64_t)(ent >> 16) * D + 2 * lane);
+          const double2 y = *reinterpret_cast<const double2*>(km_base + (int64_t)(ent & 0xffffu) * D + 2 * lane);
+          p[u] = fma(x.y, y.y, x.x * y.x);
+        }
       }
-      continue;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p[u] += __shfl_down(p[u], off);
+      if (lane == 0)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (e0 + u < total) st.amb_s[e0 + u] = p[u];
     }
-    write_bits(bits + r * words, words, out_base + (int64_t)r * keep, keep, lane);
+  }
+  __syncthreads();
+
+  // 5. per row: the best need_a listed entries by (score descending, index ascending), then the
+  // ordered write (staged in the candidate lists' LDS, no longer needed)
+  int32_t* stage = reinterpret_cast<int32_t*>(cand) + wave * kStage;
+  for (int r = wave; r < kRows; r += kWaves) {
+    if (st.status[r] != 0) continue;
+    const int na = st.namb[r], s0 = st.amb0[r], need_a = st.need_a[r];
+    for (int c = lane; c < na; c += 64) {
+      const double s = st.amb_s[s0 + c];
+      const int j = (int)(st.amb_e[s0 + c] & 0xffffu);
+      int rk = 0;
+      for (int c2 = 0; c2 < na; ++c2) {
+        const double s2 = st.amb_s[s0 + c2];
+        const int j2 = (int)(st.amb_e[s0 + c2] & 0xffffu);
+        rk += (s2 > s) || (s2 == s && j2 < j);
+      }
+      if (rk < need_a) atomicOr(&bits[r * words + (j >> 5)], 1u << (j & 31));
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    write_bits_staged(bits + r * words, words, out_base + (int64_t)r * keep, keep, lane, stage);
   }
 }
 
@@ -870,12 +983,12 @@ __global__ __launch_bounds__(kSelThreads, 2) void threshold_count_kernel(SelectA
   __shared__ ThrState ts;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = a.n_blocks;
-  const int64_t bh = blockIdx.y;
-  const int i0 = blockIdx.x * kRows;
-  const int F = a.key_stat[4 * bh];
+  const WgTile tile = xcd_tile();
+  const int64_t bh = tile.bh;
+  const int i0 = tile.chunk * kRows;
   thr_setup<D>(a, ts, bh, i0, tid);
   QueryOperand<D> qo;
-  qo.load(a, bh, blockIdx.x, lane);
+  qo.load(a, bh, tile.chunk, lane);
   __syncthreads();
   const double* qm_base = a.q_mean + (bh * nb + i0) * D;
   const double* km_base = a.k_mean + bh * nb * (int64_t)D;
@@ -884,7 +997,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void threshold_count_kernel(SelectA
   // the largest v of each row (a per-lane maximum first)
   {
     float vm = -INFINITY;
-    score_pass<D, false>(a, qo, bh, F, wave, lane, [&](int, float v) { vm = fmaxf(vm, v); });
+    score_pass<D, false>(a, qo, bh, wave, lane, [&](int, int, float v, bool valid) { vm = fmaxf(vm, valid ? v : -INFINITY); },
+                  [](int) {});
     if (live) atomicMax(&ts.vmax[r], order_int(vm));
   }
   __syncthreads();
@@ -892,12 +1006,12 @@ __global__ __launch_bounds__(kSelThreads, 2) void threshold_count_kernel(SelectA
   {
     const double lim = (double)from_order_int(ts.vmax[r]) - 2.0 * ts.e_v[r];
     unsigned long long sm = 0ull;
-    score_pass<D, false>(a, qo, bh, F, wave, lane, [&](int j, float v) {
-      if (live && (double)v >= lim) {
+    score_pass<D, false>(a, qo, bh, wave, lane, [&](int, int j, float v, bool valid) {
+      if (live && valid && (double)v >= lim) {
         const uint64_t key = order_key(exact_score<D>(qm_base + (int64_t)r * D, km_base + (int64_t)j * D));
         sm = key > sm ? key : sm;
       }
-    });
+    }, [](int) {});
     if (live) atomicMax(&ts.smax[r], sm);
   }
   __syncthreads();
@@ -912,9 +1026,9 @@ __global__ __launch_bounds__(kSelThreads, 2) void threshold_count_kernel(SelectA
     int cnt = 0;
     const double thr_v = ts.thr_v[r], e_v = ts.e_v[r], thr_s = ts.thr_s[r];
     const double* qm = qm_base + (int64_t)r * D;
-    score_pass<D, false>(a, qo, bh, F, wave, lane, [&](int j, float v) {
-      if (live) cnt += thr_keep<D>(thr_v, e_v, thr_s, v, qm, km_base + (int64_t)j * D);
-    });
+    score_pass<D, false>(a, qo, bh, wave, lane, [&](int, int j, float v, bool valid) {
+      if (live && valid) cnt += thr_keep<D>(thr_v, e_v, thr_s, v, qm, km_base + (int64_t)j * D);
+    }, [](int) {});
     if (live) atomicAdd(&ts.cnt[r], cnt);
   }
   __syncthreads();
@@ -932,16 +1046,16 @@ __global__ __launch_bounds__(kSelThreads, 2) void threshold_fill_kernel(SelectAr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = a.n_blocks;
   const int words = (nb + 31) / 32;
-  const int64_t bh = blockIdx.y;
-  const int i0 = blockIdx.x * kRows;
-  const int F = a.key_stat[4 * bh];
+  const WgTile tile = xcd_tile();
+  const int64_t bh = tile.bh;
+  const int i0 = tile.chunk * kRows;
   thr_setup<D>(a, ts, bh, i0, tid);
   if (tid < kRows && ts.valid[tid]) {
     ts.thr_s[tid] = a.row_thr[bh * nb + i0 + tid];
     ts.thr_v[tid] = ts.thr_s[tid] * ts.to_v[tid];
   }
   QueryOperand<D> qo;
-  qo.load(a, bh, blockIdx.x, lane);
+  qo.load(a, bh, tile.chunk, lane);
   for (int w = tid; w < kRows * words; w += kSelThreads) bits[w] = 0u;
   __syncthreads();
   const double* qm_base = a.q_mean + (bh * nb + i0) * D;
@@ -952,10 +1066,10 @@ __global__ __launch_bounds__(kSelThreads, 2) void threshold_fill_kernel(SelectAr
     const double* qm = qm_base + (int64_t)r * D;
     uint32_t* my_bits = bits + r * words;
     const bool live = ts.valid[r];
-    score_pass<D, false>(a, qo, bh, F, wave, lane, [&](int j, float v) {
-      if (live && thr_keep<D>(thr_v, e_v, thr_s, v, qm, km_base + (int64_t)j * D))
+    score_pass<D, false>(a, qo, bh, wave, lane, [&](int, int j, float v, bool valid) {
+      if (live && valid && thr_keep<D>(thr_v, e_v, thr_s, v, qm, km_base + (int64_t)j * D))
         atomicOr(&my_bits[j >> 5], 1u << (j & 31));
-    });
+    }, [](int) {});
   }
   __syncthreads();
   for (int r = wave; r < kRows; r += kWaves) {
@@ -1018,7 +1132,8 @@ __global__ __launch_bounds__(kScanThreads) void row_ptr_scan_kernel(SelectArgs a
 
 template <int D>
 void launch_pool(const SelectArgs& a, hipStream_t stream) {
-  const dim3 g3((unsigned)a.n_blocks * (unsigned)a.heads, 1, (unsigned)a.batch);
+  const unsigned groups = (unsigned)((a.heads + kPoolThreads / (D / 8) - 1) / (kPoolThreads / (D / 8)));
+  const dim3 g3((unsigned)a.n_blocks * groups, 1, 2u * (unsigned)a.batch);
   hipLaunchKernelGGL(pool_kernel<D>, g3, dim3(kPoolThreads), 0, stream, a);
   hipLaunchKernelGGL(key_stats_kernel, dim3((unsigned)(a.batch * a.heads)), dim3(256), 0, stream, a);
 }
@@ -1026,7 +1141,7 @@ void launch_pool(const SelectArgs& a, hipStream_t stream) {
 size_t topk_dyn_lds(int32_t nb) {
   const size_t words = ((size_t)nb + 31) / 32;
   const size_t hist = (size_t)kRows * kHistStride * 4;
-  const size_t classify = (size_t)kRows * words * 4 + (size_t)kRows * kCap * 6;
+  const size_t classify = (size_t)kRows * words * 4 + (size_t)kRows * (kCap + 1) * sizeof(uint2);
   return hist > classify ? hist : classify;
 }
 
