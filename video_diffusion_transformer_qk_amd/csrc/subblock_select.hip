@@ -379,37 +379,65 @@ __device__ __forceinline__ int wave_excl_scan_b(uint32_t x) {
   return s;
 }
 
-// One wave finds, in row r's histogram, the bin holding the want-th largest entry: returns the bin
-// and, through above/count, the entries in higher bins and in the bin. Lane l owns the 8 words
-// [512 - 8 (l + 1), 512 - 8 l), i.e. bins [kBins - 16 (l + 1), kBins - 16 l), highest first.
-// (Counts are at most nB <= 19968 < 2^15.)
-__device__ int find_bin(const uint32_t* hist, int r, int want, int lane, int* above, int* count) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(hist + r * kHistStride + kBins / 2 - 8 * (lane + 1));
-  const u32x4 lo = p[0], hi = p[1];
-  const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  int c[16];
+// Per-row work runs on 16-lane segments (a DPP row), four rows per wave at once; sums and scans
+// over a segment use DPP row rotations and shifts.
+constexpr int kSeg = 16;                 // lanes per row
+constexpr int kSegRows = 64 / kSeg;      // rows per wave at once
+__device__ __forceinline__ int seg_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false);  // row_ror:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x124, 0xf, 0xf, false);  // row_ror:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x122, 0xf, 0xf, false);  // row_ror:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x121, 0xf, 0xf, false);  // row_ror:1
+  return x;
+}
+__device__ __forceinline__ int seg_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1, zeros shifted in
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  return x;
+}
+// the value of the segment's lane src (a lane of the same segment)
+__device__ __forceinline__ int seg_get(int x, int src) { return __shfl(x, src); }
+
+// Each segment finds, in its row's histogram, the bin holding the want-th largest entry: returns
+// the bin and, through above/count, the entries in higher bins and in the bin. Level a: lane s of
+// the segment owns bins [kBins - 64 (s + 1), kBins - 64 s) (32 words, highest first); level b:
+// the 64 bins of the lane holding the entry, 4 per lane. (Counts are at most nB <= 19968.)
+__device__ int find_bin_seg(const uint32_t* row_hist, int want, int lane, int* above, int* count) {
+  const int sl = lane & (kSeg - 1), seg0 = lane & ~(kSeg - 1);
+  const unsigned long long segmask = 0xffffull << seg0;
   int s = 0;
+  {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row_hist + kBins / 2 - 32 * (sl + 1));
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    c[u] = (int)((wd[7 - u / 2] >> (16 * (1 - (u & 1)))) & 0xffffu);  // bin kBins - 1 - (16 lane + u)
-    s += c[u];
-  }
-  const int before = wave_excl_scan_b<15>((uint32_t)s);
-  const unsigned long long hit = __ballot(before < want && want <= before + s);
-  const int owner = hit ? (int)__builtin_ctzll(hit) : 63;
-  int bin = 0, ab = 0, cn = 0;
-  if (lane == owner) {
-    int acc = before;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      if (acc < want && want <= acc + c[u]) { bin = kBins - 1 - (16 * lane + u); ab = acc; cn = c[u]; }
-      acc += c[u];
+    for (int k = 0; k < 8; ++k) {
+      const u32x4 w = p[k];
+      s += (int)((w.x & 0xffffu) + (w.x >> 16) + (w.y & 0xffffu) + (w.y >> 16) + (w.z & 0xffffu) + (w.z >> 16) +
+                 (w.w & 0xffffu) + (w.w >> 16));
     }
   }
-  bin = __shfl(bin, owner);
-  *above = __shfl(ab, owner);
-  *count = __shfl(cn, owner);
-  return bin;
+  int inc = seg_incl_scan(s);
+  unsigned long long hit = __ballot(inc - s < want && want <= inc) & segmask;
+  const int o = hit ? (int)__builtin_ctzll(hit) : seg0;        // lane holding the entry
+  const int before_o = seg_get(inc - s, o);
+  // level b: bins kBins - 1 - 64 (o - seg0) - (4 sl + u), u = 0..3, in two words
+  const int top = kBins - 1 - 64 * (o - seg0) - 4 * sl;
+  const uint32_t w1 = row_hist[top >> 1], w0 = row_hist[(top >> 1) - 1];
+  const int c[4] = {(int)(w1 >> 16), (int)(w1 & 0xffffu), (int)(w0 >> 16), (int)(w0 & 0xffffu)};
+  const int s2 = c[0] + c[1] + c[2] + c[3];
+  const int inc2 = seg_incl_scan(s2) + before_o;
+  hit = __ballot(inc2 - s2 < want && want <= inc2) & segmask;
+  const int o2 = hit ? (int)__builtin_ctzll(hit) : seg0;
+  int bin = 0, ab = 0, cn = 0, acc = inc2 - s2;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (acc < want && want <= acc + c[u]) { bin = top - u; ab = acc; cn = c[u]; }
+    acc += c[u];
+  }
+  *above = seg_get(ab, o2);
+  *count = seg_get(cn, o2);
+  return seg_get(bin, o2);
 }
 
 // order-preserving map of a double to uint64 (larger double -> larger key); -0 is folded to +0
@@ -453,33 +481,6 @@ __device__ int64_t write_bits(const uint32_t* bits, int words, int32_t* dst, int
   return carry;
 }
 
-// write_bits through an LDS staging area of 2048 ints (one wave's): 64 words at a time, each lane
-// expands its word's set bits into the staging area at the word's offset, then the wave copies
-// the run out with consecutive lanes on consecutive indices.
-__device__ int64_t write_bits_staged(const uint32_t* bits, int words, int32_t* dst, int64_t cap, int lane,
-                                     int32_t* stage) {
-  int64_t carry = 0;
-  for (int w0 = 0; w0 < words; w0 += 64) {
-    const int w = w0 + lane;
-    uint32_t m = w < words ? bits[w] : 0u;
-    const int cnt = __popc(m);
-    int pos = wave_excl_scan_b<6>((uint32_t)cnt);
-    const int tot = wave_sum_b<6>((uint32_t)cnt);
-    while (m) {
-      stage[pos++] = 32 * w + __builtin_ctz(m);
-      m &= m - 1;
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    for (int p = lane; p < tot; p += 64)
-      if (carry + p < cap) dst[carry + p] = stage[p];
-    carry += tot;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  }
-  return carry;
-}
-
 // ----------------------------------------------------------------------------- top-k select
 
 // The (batch-head, row chunk) of a selection workgroup. Consecutive workgroup ids are dealt to
@@ -499,8 +500,7 @@ __device__ __forceinline__ WgTile xcd_tile() {
 }
 
 constexpr int kAmbList = 256;  // entries of a workgroup decided on float64 scores
-constexpr int kStage = 2048;   // ints of a wave's output staging area (64 bitmap words)
-static_assert(kWaves * kStage * 4 <= kRows * (kCap + 1) * 8, "staging must fit in the candidate lists");
+static_assert(kWaves * kSegRows * kSeg * 32 * 4 <= kRows * (kCap + 1) * 8, "staging must fit in the candidate lists");
 
 // Per-row state of a selection workgroup, in LDS.
 struct RowState {
@@ -590,11 +590,12 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
     hist_inc(my_hist, valid ? bin_of(bin_pos(v, my_scale, my_off)) : kBins);
   }, no_done);
   __syncthreads();
-  for (int r = wave; r < kRows; r += kWaves) {
-    if (st.status[r] != 0) continue;
+  const int seg = lane / kSeg, sl = lane % kSeg;
+  for (int r0 = wave * kSegRows; r0 < kRows; r0 += kWaves * kSegRows) {
+    const int r = r0 + seg;
     int ab, cn;
-    const int b = find_bin(hist, r, keep, lane, &ab, &cn);
-    if (lane == 0) {
+    const int b = find_bin_seg(hist + r * kHistStride, keep, lane, &ab, &cn);
+    if (sl == 0 && st.status[r] == 0) {
       st.bin1[r] = b;
       st.above[r] = ab;
       st.count[r] = cn;
@@ -614,11 +615,12 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
       hist_inc(my_hist, valid && my_refine && bin_of(t) == my_bin1 ? sub_of(t, my_bin1) : kBins);
     }, no_done);
     __syncthreads();
-    for (int r = wave; r < kRows; r += kWaves) {
-      if (st.status[r] != 0 || st.count[r] <= kCap) continue;
+    for (int r0 = wave * kSegRows; r0 < kRows; r0 += kWaves * kSegRows) {
+      const int r = r0 + seg;
+      const bool act = st.status[r] == 0 && st.count[r] > kCap;
       int ab, cn;
-      const int b2 = find_bin(hist, r, keep - st.above[r], lane, &ab, &cn);
-      if (lane == 0) {
+      const int b2 = find_bin_seg(hist + r * kHistStride, keep - st.above[r], lane, &ab, &cn);
+      if (sl == 0 && act) {
         st.bin2[r] = b2;
         st.above[r] += ab;
         st.count[r] = cn;
@@ -672,60 +674,65 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
   }
   __syncthreads();
 
-  // 3. per row: the pivot, the sure entries and the list for float64 decisions
-  for (int r = wave; r < kRows; r += kWaves) {
-    if (st.status[r] == 1) continue;
+  // 3. per row (a segment): the pivot, the sure entries and the list for float64 decisions
+  for (int r0 = wave * kSegRows; r0 < kRows; r0 += kWaves * kSegRows) {
+    const int r = r0 + seg;
+    const int status = st.status[r];
     const int n = st.ncand[r];
-    bool fb = st.status[r] == 2 || n > kCap;
+    bool fb = status == 2 || n > kCap;
     int nsure = 0;
-    for (int w = lane; w < words; w += 64) nsure += __popc(bits[r * words + w]);
-    nsure = wave_sum_b<15>((uint32_t)nsure);
+    for (int w = sl; w < words; w += kSeg) nsure += __popc(bits[r * words + w]);
+    nsure = seg_sum(nsure);
     const int need = keep - nsure;
-    if (!fb && (need < 1 || need > n)) fb = true;
-    if (!fb) {
-      const uint2* cr = cand + r * (kCap + 1);
-      constexpr int U = (kCap + 63) / 64;
-      uint32_t key[U];
-      float cvv[U];
-      int cjj[U];
+    fb = fb || need < 1 || need > n;
+    const bool go = status != 1 && !fb;
+    const uint2* cr = cand + r * (kCap + 1);
+    constexpr int U = (kCap + kSeg - 1) / kSeg;
+    uint32_t key[U];
+    float cvv[U];
+    int cjj[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = lane + 64 * u;
-        const uint2 e = c < n ? cr[c] : uint2{0u, 0u};
-        cvv[u] = __uint_as_float(e.x);
-        cjj[u] = (int)e.y;
-        key[u] = c < n ? order_u32(cvv[u]) : 0u;
-      }
-      // t: the need-th largest v, bit by bit from the top (absent slots hold key 0)
-      uint32_t T = 0u;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t T2 = T | (1u << bit);
-        int cnt = 0;
+    for (int u = 0; u < U; ++u) {
+      const int c = sl + kSeg * u;
+      const bool present = go && c < n;
+      const uint2 e = present ? cr[c] : uint2{0u, 0u};
+      cvv[u] = __uint_as_float(e.x);
+      cjj[u] = (int)e.y;
+      key[u] = present ? order_u32(cvv[u]) : 0u;
+    }
+    // t: the need-th largest v, bit by bit. Every candidate lies in [cand_thr, in_thr], so the bits
+    // above the highest one where the bracket's keys differ are the bracket's; the search runs over
+    // the rest (the wave's widest), absent slots holding key 0.
+    const uint32_t lo = order_u32(st.cand_thr[r]), hi = order_u32(st.in_thr[r]);
+    const uint32_t diff = go ? lo ^ hi : 0u;
+    const uint32_t dw = (uint32_t)__builtin_amdgcn_readlane((int)diff, 0) | (uint32_t)__builtin_amdgcn_readlane((int)diff, 16) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)diff, 32) | (uint32_t)__builtin_amdgcn_readlane((int)diff, 48);
+    const int top = dw ? 31 - __builtin_clz(dw) : -1;
+    uint32_t T = top < 0 ? lo : (top >= 31 ? 0u : (lo & ~((2u << top) - 1u)));
+    for (int bit = top; bit >= 0; --bit) {
+      const uint32_t T2 = T | (1u << bit);
+      int cnt = 0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) cnt += __popcll(__ballot(key[u] >= T2));
-        if (cnt >= need) T = T2;
-      }
-      const double t = from_order_u32(T), e2 = 2.0 * st.e_v[r];
-      int nin = 0;
-      bool am[U];
+      for (int u = 0; u < U; ++u) cnt += key[u] >= T2;
+      if (seg_sum(cnt) >= need) T = T2;
+    }
+    const double t = from_order_u32(T), e2 = 2.0 * st.e_v[r];
+    int nin = 0, nam = 0;
+    bool am[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool present = lane + 64 * u < n;
-        const double v = cvv[u];
-        const bool in = present && v - e2 > t;
-        am[u] = present && !in && v + e2 >= t;
-        if (in) atomicOr(&bits[r * words + (cjj[u] >> 5)], 1u << (cjj[u] & 31));
-        nin += in;
-      }
-      nin = wave_sum_b<2>((uint32_t)nin);
-      unsigned long long bm[U];
-      int na = 0;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        bm[u] = __ballot(am[u]);
-        na += __popcll(bm[u]);
-      }
-      const int need_a = need - nin;
+    for (int u = 0; u < U; ++u) {
+      const bool present = go && sl + kSeg * u < n;
+      const double v = cvv[u];
+      const bool in = present && v - e2 > t;
+      am[u] = present && !in && v + e2 >= t;
+      if (in) atomicOr(&bits[r * words + (cjj[u] >> 5)], 1u << (cjj[u] & 31));
+      nin += in;
+      nam += am[u];
+    }
+    nin = seg_sum(nin);
+    const int na = seg_sum(nam);
+    const int need_a = need - nin;
+    if (go) {
       if (need_a < 1 || need_a > na) {
         fb = true;
       } else if (need_a == na) {  // every listed entry is kept: no float64 decision needed
@@ -734,18 +741,16 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
           if (am[u]) atomicOr(&bits[r * words + (cjj[u] >> 5)], 1u << (cjj[u] & 31));
       } else {
         int start = 0;
-        if (lane == 0) start = atomicAdd(&st.amb_total, na);
-        start = __shfl(start, 0);
+        if (sl == 0) start = atomicAdd(&st.amb_total, na);
+        start = seg_get(start, lane & ~(kSeg - 1));
         if (start + na > kAmbList) {
           fb = true;
         } else {
-          int pos = start;
+          int pos = start + seg_incl_scan(nam) - nam;
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            if (am[u]) st.amb_e[pos + lanes_below(bm[u])] = ((uint32_t)r << 16) | (uint32_t)cjj[u];
-            pos += __popcll(bm[u]);
-          }
-          if (lane == 0) {
+          for (int u = 0; u < U; ++u)
+            if (am[u]) st.amb_e[pos++] = ((uint32_t)r << 16) | (uint32_t)cjj[u];
+          if (sl == 0) {
             st.need_a[r] = need_a;
             st.amb0[r] = start;
             st.namb[r] = na;
@@ -753,7 +758,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
         }
       }
     }
-    if (fb && lane == 0) {
+    if (fb && status != 1 && sl == 0) {
       st.status[r] = 2;
       const int slot = atomicAdd(a.fb_count, 1);
       a.fb_rows[slot] = (int32_t)(bh * nb + i0 + r);
@@ -792,26 +797,48 @@ __global__ __launch_bounds__(kSelThreads, 2) void topk_select_kernel(SelectArgs 
   }
   __syncthreads();
 
-  // 5. per row: the best need_a listed entries by (score descending, index ascending), then the
-  // ordered write (staged in the candidate lists' LDS, no longer needed)
-  int32_t* stage = reinterpret_cast<int32_t*>(cand) + wave * kStage;
-  for (int r = wave; r < kRows; r += kWaves) {
-    if (st.status[r] != 0) continue;
-    const int na = st.namb[r], s0 = st.amb0[r], need_a = st.need_a[r];
-    for (int c = lane; c < na; c += 64) {
-      const double s = st.amb_s[s0 + c];
+  // 5. per row (a segment): the best need_a listed entries by (score descending, index ascending),
+  // then the ordered write, 16 bitmap words (at most 512 indices) at a time through a staging
+  // area in the candidate lists' LDS (no longer needed), copied out with consecutive lanes on
+  // consecutive indices
+  int32_t* stage = reinterpret_cast<int32_t*>(cand) + (wave * kSegRows + seg) * (kSeg * 32);
+  for (int r0 = wave * kSegRows; r0 < kRows; r0 += kWaves * kSegRows) {
+    const int r = r0 + seg;
+    const bool go = st.status[r] == 0;
+    const int na = go ? st.namb[r] : 0, s0 = st.amb0[r], need_a = st.need_a[r];
+    for (int c = sl; c < na; c += kSeg) {
+      const double sc = st.amb_s[s0 + c];
       const int j = (int)(st.amb_e[s0 + c] & 0xffffu);
       int rk = 0;
       for (int c2 = 0; c2 < na; ++c2) {
         const double s2 = st.amb_s[s0 + c2];
         const int j2 = (int)(st.amb_e[s0 + c2] & 0xffffu);
-        rk += (s2 > s) || (s2 == s && j2 < j);
+        rk += (s2 > sc) || (s2 == sc && j2 < j);
       }
       if (rk < need_a) atomicOr(&bits[r * words + (j >> 5)], 1u << (j & 31));
     }
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    write_bits_staged(bits + r * words, words, out_base + (int64_t)r * keep, keep, lane, stage);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    int32_t* dst = out_base + (int64_t)r * keep;
+    int carry = 0;
+    for (int w0 = 0; w0 < words; w0 += kSeg) {
+      const int w = w0 + sl;
+      uint32_t m = go && w < words ? bits[r * words + w] : 0u;
+      const int cnt = __popc(m);
+      int pos = seg_incl_scan(cnt) - cnt;
+      const int tot = seg_sum(cnt);
+      while (m) {
+        stage[pos++] = 32 * w + __builtin_ctz(m);
+        m &= m - 1;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+      for (int p = sl; p < tot; p += kSeg)
+        if (carry + p < keep) dst[carry + p] = stage[p];
+      carry += tot;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    }
   }
 }
 
