@@ -353,6 +353,9 @@ def main():
     dense_tf = dense_flops / (avg["dense"] * 1e-3) / 1e12
     sparse_tf = sparse_flops / (avg["sparse"] * 1e-3) / 1e12
     nr_gbs = nr_bytes / (avg["norm_rope"] * 1e-3) / 1e9
+    # selection's algorithmic bytes: q' and k' read once (pooling), the kept indices written once
+    sel_bytes = 4.0 * b * n * hd * d + 4.0 * b * hd * nb * keep
+    sel_gbs = sel_bytes / (avg["select"] * 1e-3) / 1e9
     value = (dense_flops + sparse_flops) / (ms_step * 1e-3) / 1e12
 
     components = {
@@ -365,7 +368,9 @@ def main():
                            for kname, vals in per.items()},
         "dense_ms": avg["dense"], "dense_tflops": dense_tf, "dense_frac_peak": dense_tf / PEAK_BF16_TFLOPS,
         "sparse_ms": avg["sparse"], "sparse_tflops_kept": sparse_tf, "sparse_frac_peak": sparse_tf / PEAK_BF16_TFLOPS,
-        "select_ms": avg["select"], "norm_rope_ms": avg["norm_rope"], "norm_rope_gbs": nr_gbs,
+        "select_ms": avg["select"], "select_bytes": sel_bytes, "select_gbs": sel_gbs,
+        "select_frac_peak": sel_gbs / PEAK_HBM_GBS,
+        "norm_rope_ms": avg["norm_rope"], "norm_rope_gbs": nr_gbs,
         "norm_rope_frac_peak": nr_gbs / PEAK_HBM_GBS, "keep": keep, "n_blocks": nb,
         "dense_flops": dense_flops, "sparse_flops": sparse_flops, "norm_rope_bytes": nr_bytes,
     }

@@ -111,12 +111,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
       }
   }
   const int64_t bh = (int64_t)b * a.heads + head;
+  // a full block divides by 64 = 2^6: the product by 2^-6 is the same correctly rounded quotient
+  const bool full = rows == 64;
   const double cnt = (double)rows;
   double m[8];
   double amax = 0.0, l1 = 0.0, l2 = 0.0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    m[e] = acc[e] / cnt;
+    m[e] = full ? acc[e] * 0x1p-6 : acc[e] / cnt;
     amax = fmax(amax, fabs(m[e]));
     l1 += fabs(m[e]);
     l2 += m[e] * m[e];
