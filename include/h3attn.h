@@ -64,9 +64,10 @@ int32_t h3attn_keep_count(int32_t n_kblocks, double sparsity);
 
 /* Device workspace bytes that h3attn_subblock_select needs, O(batch * heads * nB * head_dim):
  * the pooled block means of q and k in float64 ([batch, heads, nB, head_dim] each), their
- * base-256 integer digits (3 bytes per mean), a power-of-two exponent and two norms per block,
- * per-head key maxima and a list of rows for the exact fallback, each region 256-byte aligned
- * (22 * head_dim + 36 bytes per (batch, head, block), plus padding). No score matrix is stored:
+ * base-256 integer digits (3 bytes per channel), a power-of-two exponent and two norms per
+ * block, per-head key maxima and a list of rows for the exact fallback, each region 256-byte
+ * aligned (22 * head_dim + 28 bytes per (batch, head, block), plus 16 bytes per (batch, head);
+ * the digit, exponent and norm regions padded to a multiple of 32 blocks). No score matrix is stored:
  * block scores live on chip. Returns 0 on invalid sizes. */
 size_t h3attn_select_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tokens,
                                      int32_t head_dim, int32_t block_size);

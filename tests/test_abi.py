@@ -68,7 +68,7 @@ def test_workspace_bytes(lib):
         want = 2 * (r(bh * nb * d * 8) + r(bh * nbp * d * 3) + r(bh * nbp * 4) + r(bh * nbp * 8)) \
             + r(bh * 16) + r((1 + bh * nb) * 4)
         assert lib.h3attn_select_workspace_bytes(1, bh, nb * 64, d, 64) == want
-        assert want < bh * nbp * (22 * d + 36) + 10 * 256          # linear in nB, far below nB^2
+        assert want <= bh * nbp * (22 * d + 28) + bh * 16 + 4 + 10 * 256   # linear in nB, far below nB^2
     # 5 s workload: 0.27 GB (the float64 score matrix alone would have been 1.46 GB)
     assert lib.h3attn_select_workspace_bytes(1, 48, 124992, 128, 64) < 0.28e9
     assert lib.h3attn_select_workspace_bytes(0, 48, 124992, 128, 64) == 0
