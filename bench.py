@@ -80,6 +80,24 @@ def measured_traffic(kernel_prefix: str):
     return None
 
 
+def measured_traffic_range():
+    """The dense kernel's scaled traffic over every PMC pass recorded in the summary's header (its
+    L2 hit rate, and so its FETCH_SIZE, varies between passes), or None."""
+    summary = os.path.join(ROOT, "profiles", "pmc_traffic_video5s.txt")
+    try:
+        text = open(summary).read()
+    except OSError:
+        return None
+    import re
+    m = re.search(r"passes so far read ([0-9, and\n#]+?) KiB", text)
+    w = [l for l in text.splitlines() if l.startswith("attn_fwd_kernel<")]
+    if not m or not w:
+        return None
+    fetch = [float(x) for x in re.findall(r"[0-9]+", m.group(1))]
+    write_kib = float(w[0].split("|")[2])
+    return [(min(fetch) * 2.0 + write_kib) * 1024, (max(fetch) * 2.0 + write_kib) * 1024]
+
+
 def provenance(cfg):
     """What produced this line: library and runtime versions, the device, the first 16 hex digits
     of each library source's sha256 (the tree is copied without version-control metadata) and the
@@ -663,6 +681,8 @@ def main():
                 "frac": dense_tf / PEAK_BF16_TFLOPS,
                 "traffic": traffic,
                 "traffic_unit": "bytes per launch (FETCH_SIZE x2.000 + WRITE_SIZE x1.000, copy-calibrated)",
+                # one pass's figure above; the range over every recorded pass (the L2 hit rate varies)
+                "traffic_observed_range": measured_traffic_range() if traffic is not None else None,
                 "per_launch_flops": dense_flops, "avg_launch_ms": avg["dense"]}
 
     cpu = None
