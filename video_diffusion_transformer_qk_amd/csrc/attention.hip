@@ -71,23 +71,88 @@ __device__ __forceinline__ void rows_begin(WaveRows<D>& w, const uint16_t* qp) {
   for (int j = 0; j < 4; ++j) w.l_part[j] = 0.f;
 }
 
+// Where a lane's operands sit in a K/V tile in LDS, for the MFMA fragment reads.
+//
+// qk_tile's fragment i (k step i/2, 32-key half i%2): this lane's key row 32 (i%2) + lane%32 and
+// its 16-byte chunk 2 (i/2) + lane/32 of the K row. pv_tile's read (16-key step kk, 32-channel
+// step dt): within each group of 16 lanes, 4 rows x 4 8-byte pieces of V, the lane's row
+// 16 kk + 4 (lane/32) + (lane%16)/4 and channels 32 dt + 16 ((lane/16)%2) + 4 (lane%4); the second
+// read of the pair is 8 rows further.
+//
+// PadLayout: rows padded (K: 16 bytes, V: 64 bytes per row), filled through registers. With a
+// row stride of 17 (K) or 20 (V) chunks, the chunks one wave instruction reads fall on distinct
+// bank positions.
+template <int D>
+struct PadLayout {
+  using T = Tile<D, kBN>;
+  static constexpr int V8 = 8 * T::VS;  // byte distance of 8 V rows
+  int l32, hi, ig, g16;
+  __device__ __forceinline__ explicit PadLayout(int lane)
+      : l32(lane & 31), hi(lane >> 5), ig(lane & 15), g16((lane >> 4) & 1) {}
+  __device__ __forceinline__ int kfrag(int i) const { return (32 * (i & 1) + l32) * T::KS + (16 * (i >> 1) + 8 * hi) * 2; }
+  __device__ __forceinline__ int vfrag(int kk, int dt) const {
+    const int k0 = 16 * kk + 4 * hi;
+    const int d0 = 32 * dt + 16 * g16;
+    return (k0 + (ig >> 2)) * T::VS + (d0 + 4 * (ig & 3)) * 2;
+  }
+};
+
+// SwzLayout: unpadded rows of 2D bytes (CPR = D/8 chunks), filled by direct global -> LDS loads,
+// which write each wave instruction's 64 x 16 bytes to consecutive LDS addresses. The chunks of
+// a row are rotated instead of padded, so that the bank positions match the padded layout's:
+//   K: chunk c of row r at column (c + r) mod 16 (D = 128) or (c + r/2) mod 8 (D = 64);
+//   V: chunk c of row r at column (c + 4r) mod 16 (D = 128) or (c + 4 (r/2)) mod 8 (D = 64).
+// A lane's columns depend only on the lane and the k (channel) step, never on the 32-key half or
+// the 16-key step, so the offsets are computed once per kernel (D/16 for K, D/32 for V) and the
+// steps add constants.
+template <int D>
+struct SwzLayout {
+  static constexpr int ROW = 2 * D;
+  static constexpr int CPR = D / 8;
+  static constexpr int K_BYTES = kBN * ROW;
+  static constexpr int BUF_BYTES = 2 * K_BYTES;
+  static constexpr int V8 = 8 * ROW;
+  __device__ static __forceinline__ int kcol(int r, int c) {
+    return D == 128 ? (c + r) & 15 : (c + (r >> 1)) & 7;
+  }
+  __device__ static __forceinline__ int vcol(int r, int c) {
+    return D == 128 ? (c + 4 * r) & 15 : (c + 4 * (r >> 1)) & 7;
+  }
+  // logical chunk stored at column col of row r (the inverses)
+  __device__ static __forceinline__ int kchunk(int r, int col) {
+    return D == 128 ? (col - r) & 15 : (col - (r >> 1)) & 7;
+  }
+  __device__ static __forceinline__ int vchunk(int r, int col) {
+    return D == 128 ? (col - 4 * r) & 15 : (col - 4 * (r >> 1)) & 7;
+  }
+  int koff[D / 16], voff[D / 32];
+  __device__ __forceinline__ explicit SwzLayout(int lane) {
+    const int l32 = lane & 31, hi = lane >> 5, ig = lane & 15, g16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) koff[k] = l32 * ROW + kcol(l32, 2 * k + hi) * 16;
+    const int r = 4 * hi + (ig >> 2);  // the row inside the 16-key step; 16 kk adds whole rotations
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int byte = (32 * dt + 16 * g16 + 4 * (ig & 3)) * 2;
+      voff[dt] = r * ROW + vcol(r, byte / 16) * 16 + byte % 16;
+    }
+  }
+  __device__ __forceinline__ int kfrag(int i) const { return koff[i >> 1] + (i & 1) * 32 * ROW; }
+  __device__ __forceinline__ int vfrag(int kk, int dt) const { return 16 * kk * ROW + voff[dt]; }
+};
+
 // The three parts of one 64-key tile for one wave. qk_tile: S^T = K . Q^T from the K tile at kb.
 // The K fragments (k step ks, 32-key half m) are read in MFMA order through a ring of kQkInFlight
 // registers, and the schedule is pinned (kQkInFlight reads, then one MFMA per read, then the
 // last MFMAs): left alone, the compiler reuses one register quad and every MFMA waits for its
 // own LDS read (3 % slower at 4 reads in flight).
 constexpr int kQkInFlight = 4;
-template <int D>
+template <int D, typename L>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const bf16x8 (&qf)[D / 16], const unsigned char* kb,
-                                        int lane) {
-  using T = Tile<D, kBN>;
+                                        const L& lay) {
   constexpr int NF = 2 * (D / 16);  // fragments i = 2 ks + m
   constexpr int PF = kQkInFlight;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  auto frag = [&](int i) {
-    return *reinterpret_cast<const bf16x8*>(kb + (32 * (i & 1) + l32) * T::KS + (16 * (i >> 1) + 8 * hi) * 2);
-  };
+  auto frag = [&](int i) { return *reinterpret_cast<const bf16x8*>(kb + lay.kfrag(i)); };
   s[0] = f32x16{};
   s[1] = f32x16{};
   bf16x8 kf[PF];
@@ -170,23 +235,17 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2], u32x4 (&pk)[4]
 
 // O^T += V^T . P^T with V^T read from the row-major V tile at vb through the LDS transpose read;
 // the key order inside each 16-key step matches the registers that hold P^T.
-template <int D>
+template <int D, typename L>
 __device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const u32x4 (&pk)[4], const unsigned char* vb,
-                                        int lane) {
-  using T = Tile<D, kBN>;
-  const int hi = lane >> 5;
-  const int ig = lane & 15;  // index inside the 16-lane group
+                                        const L& lay) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const int m = kk >> 1, half = kk & 1;
-    const int k0 = 32 * m + 16 * half + 4 * hi;
     const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[kk]);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const int d0 = 32 * dt + 16 * ((lane >> 4) & 1);
-      const unsigned char* p1 = vb + (k0 + (ig >> 2)) * T::VS + (d0 + 4 * (ig & 3)) * 2;
+      const unsigned char* p1 = vb + lay.vfrag(kk, dt);
       const i16x4 lo = lds_read_tr16(p1);
-      const i16x4 hi4 = lds_read_tr16(p1 + 8 * T::VS);
+      const i16x4 hi4 = lds_read_tr16(p1 + L::V8);
       typedef __attribute__((ext_vector_type(8))) short i16x8;
       const i16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, vv), pb, o[dt]);
@@ -197,17 +256,17 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const u32x4 (&pk)[4
 // One K/V tile of 64 keys (K rows at kb, V rows at vb in LDS; first key key0) applied to the
 // wave's rows: S^T = K . Q^T, online softmax, O^T += V^T . P^T. `partial` (wave-uniform) marks
 // the tile that holds the last token when N is not a multiple of 64.
-template <int D, int BN>
+template <int D, int BN, typename L>
 __device__ __forceinline__ void rows_tile(WaveRows<D>& w, const unsigned char* kb, const unsigned char* vb,
-                                          int64_t key0, int64_t N, bool partial, int lane, float sc) {
+                                          int64_t key0, int64_t N, bool partial, int lane, float sc, const L& lay) {
   static_assert(BN == kBN, "64-key tiles");
   f32x16 s[2];
-  qk_tile<D>(s, w.qf, kb, lane);
+  qk_tile<D>(s, w.qf, kb, lay);
   if (partial) mask_tile(s, key0, N, lane);
   softmax_max(w, s, sc);
   u32x4 pk[4];
   softmax_exp(s, pk, w.m_run, sc, w.l_part);
-  pv_tile<D>(w.o, pk, vb, lane);
+  pv_tile<D>(w.o, pk, vb, lay);
 }
 
 // Epilogue: combine the two lane-partial sums, normalise and store query row my_q if it is
@@ -290,12 +349,85 @@ struct TileStage {
   }
 };
 
+// Direct global -> LDS staging of one K/V tile into the SwzLayout (gfx950 global_load_lds_dwordx4:
+// no staging registers, no LDS write instructions). A wave instruction writes 64 lanes x 16 bytes
+// to consecutive LDS addresses, so LDS slot p = 64 (J w + j) + lane of wave w's instruction j is
+// row p / CPR, column p % CPR of the tile, and the lane fetches the logical chunk that the
+// rotation puts at that column. Rows past the end of the sequence are clamped to the last token,
+// only in the tile that holds it. The loads are counted by vmcnt: a wave waits for its own
+// (wait_dma) before the barrier that hands the tile to the other waves.
+//
+// The load is issued from an asm block: through the compiler builtin, every LDS read issued while
+// a load is in flight (the current tile's V reads, while the next tile arrives in the other
+// buffer) got a vmcnt(0) wait in front of it. The block has no output register that the load
+// writes; it saves and restores M0 (which the load takes its LDS address from), with the one
+// wait state the hardware needs between writing M0 and the load.
+template <int D, int NT>
+struct TileDma {
+  using L = SwzLayout<D>;
+  static constexpr int WAVES = NT / 64;
+  static constexpr int J = L::CPR / WAVES;  // instructions per wave and tensor
+  static_assert(L::CPR % WAVES == 0, "the tile's 1 KB slices must split evenly over the waves");
+  int krow[J], koff[J], voff[J];
+  int lds0;  // byte offset of the wave's first slice (wave-uniform)
+
+  __device__ __forceinline__ void init(int tid, int64_t row_stride) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    lds0 = wave * J * 1024;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int p = 64 * (J * wave + j) + lane;
+      const int r = p / L::CPR, col = p % L::CPR;
+      krow[j] = r;
+      koff[j] = r * (int)row_stride + 8 * L::kchunk(r, col);
+      voff[j] = r * (int)row_stride + 8 * L::vchunk(r, col);
+    }
+  }
+  // 16 bytes per lane from g to the LDS byte address lds + 16 * lane (lds wave-uniform)
+  __device__ static __forceinline__ void dma16(const uint16_t* g, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(lds));
+  }
+  // buf: LDS byte address of the tile buffer (wave-uniform)
+  __device__ __forceinline__ void fetch(const uint16_t* k, const uint16_t* v, int64_t base, int64_t key0,
+                                        int64_t N, int64_t row_stride, uint32_t buf) const {
+    const int64_t tile = base + key0 * row_stride;
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(buf + lds0);
+    if (key0 + kBN <= N) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        dma16(k + tile + koff[j], l0 + 1024 * j);
+        dma16(v + tile + voff[j], l0 + L::K_BYTES + 1024 * j);
+      }
+    } else {
+      const int last = (int)(N - 1 - key0);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int64_t adj = krow[j] < last ? 0 : (int64_t)(last - krow[j]) * row_stride;
+        dma16(k + tile + koff[j] + adj, l0 + 1024 * j);
+        dma16(v + tile + voff[j] + adj, l0 + L::K_BYTES + 1024 * j);
+      }
+    }
+  }
+};
+
+// vmcnt(0): this wave's direct loads have landed in LDS (expcnt and lgkmcnt left alone)
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Dense attention. WAVES waves per workgroup (32 queries each); OCC minimum waves per SIMD (2
 // caps the kernel at 256 registers so that two waves share each SIMD and overlap each other's
 // MFMA and softmax work).
 template <int D, int WAVES, int OCC>
 __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
-  using T = Tile<D, kBN>;
+  using L = SwzLayout<D>;
   constexpr int NT = WAVES * 64;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -318,19 +450,23 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
 
   const int n_tiles = (int)((N + kBN - 1) / kBN);
   const int last_partial = N % kBN ? n_tiles - 1 : -1;  // the tile to mask, if any
-  TileStage<D, kBN, NT> st;
-  st.init(tid, row_stride);
+  TileDma<D, NT> dma;
+  dma.init(tid, row_stride);
+  const L lay(lane);
   const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
 
-  st.fetch(a.k, a.v, base, 0, N, row_stride);
-  st.stash(smem, tid);
+  // LDS byte address of the tile buffers
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  dma.fetch(a.k, a.v, base, 0, N, row_stride, smem_lds);
+  wait_dma();
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) st.fetch(a.k, a.v, base, (int64_t)(t + 1) * kBN, N, row_stride);
-    const unsigned char* kb = smem + buf * T::BUF_BYTES;
-    rows_tile<D, kBN>(w, kb, kb + T::K_BYTES, (int64_t)t * kBN, N, t == last_partial, lane, sc);
-    if (t + 1 < n_tiles) st.stash(smem + (buf ^ 1) * T::BUF_BYTES, tid);
+    if (t + 1 < n_tiles)
+      dma.fetch(a.k, a.v, base, (int64_t)(t + 1) * kBN, N, row_stride, smem_lds + (buf ^ 1) * L::BUF_BYTES);
+    const unsigned char* kb = smem + buf * L::BUF_BYTES;
+    rows_tile<D, kBN>(w, kb, kb + L::K_BYTES, (int64_t)t * kBN, N, t == last_partial, lane, sc, lay);
+    wait_dma();
     __syncthreads();
   }
   rows_end(w, a.out + base, a.lse != nullptr ? a.lse + ((int64_t)b * a.heads + head) * N : nullptr, my_q, N,
@@ -390,6 +526,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
   rows_begin(w, a.q + base + my_q_c * row_stride + 8 * hi);
   TileStage<D, kBN, NT> st;
   st.init(tid, row_stride);
+  const PadLayout<D> lay(lane);
   const float sc = 1.4426950408889634f / sqrtf((float)D);
   const uint32_t my_bit = 1u << gblk;
 
@@ -411,7 +548,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
         // a 64-bit compare here: the 32-bit block-index compare of the dense kernel measured 8 %
         // slower in this kernel
         const int64_t key0 = (j0 + (int64_t)(e >> 8)) * kBN;
-        rows_tile<D, kBN>(w, kb, kb + T::K_BYTES, key0, N, key0 + kBN > N, lane, sc);
+        rows_tile<D, kBN>(w, kb, kb + T::K_BYTES, key0, N, key0 + kBN > N, lane, sc, lay);
       }
       if (t + 1 < nu) st.stash(smem + (buf ^ 1) * T::BUF_BYTES, tid);
       __syncthreads();
@@ -424,7 +561,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
 
 template <int D, int WAVES, int OCC>
 void launch_dense(const AttnArgs& a, hipStream_t stream) {
-  const size_t lds = 2 * Tile<D, kBN>::BUF_BYTES;
+  const size_t lds = 2 * SwzLayout<D>::BUF_BYTES;
   auto kern = attn_fwd_kernel<D, WAVES, OCC>;
   allow_dynamic_lds(reinterpret_cast<const void*>(kern), (int)lds);
   const dim3 grid((unsigned)((a.n_tokens + WAVES * 32 - 1) / (WAVES * 32)), (unsigned)a.heads, (unsigned)a.batch);
