@@ -19,8 +19,8 @@
 // with log2(e)/sqrt(D) folded into one FMA, and the running max only moves (with a wave-uniform
 // O rescale) when a tile exceeds it by more than 2^8.
 //
-// Pipeline: tile t+1 is fetched from global memory into registers while tile t is computed,
-// then stored to the other half of a double-buffered LDS tile (one barrier per tile). Dense:
+// Pipeline: tile t+1 is loaded from global memory straight into the other half of a
+// double-buffered LDS tile while tile t is computed (one barrier per tile). Dense:
 // 8 waves (256 queries) share each 64-key K/V tile, two waves per SIMD (256-register budget) so
 // one wave's MFMAs overlap the other's softmax. Block-sparse: a workgroup takes 4 query blocks
 // (consecutive, or one per frame at the same position with a group stride) and walks the union
@@ -36,16 +36,6 @@ namespace {
 constexpr int kBN = 64;  // keys per tile (= SubBlock block size)
 
 #define kOnes2 (__builtin_bit_cast(bf16x2, 0x3f803f80u))  // bf16 pair (1.0, 1.0)
-
-template <int D, int BN>
-struct Tile {
-  static constexpr int KS = 2 * D + 16;   // K row stride in LDS (bytes): conflict-free b128 reads
-  static constexpr int VS = 2 * D + 64;   // V row stride in LDS (bytes) for the transpose reads
-  static constexpr int K_BYTES = BN * KS;
-  static constexpr int V_BYTES = BN * VS;
-  static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
-  static constexpr int CHUNKS = BN * D / 8;  // 16-byte chunks per tensor tile
-};
 
 // One wave's share of the forward pass: 32 query rows, their Q^T fragments (B operand, one
 // bf16x8 per 16-wide k step), the O^T accumulator and the running softmax statistics.
@@ -79,27 +69,10 @@ __device__ __forceinline__ void rows_begin(WaveRows<D>& w, const uint16_t* qp) {
 // 16 kk + 4 (lane/32) + (lane%16)/4 and channels 32 dt + 16 ((lane/16)%2) + 4 (lane%4); the second
 // read of the pair is 8 rows further.
 //
-// PadLayout: rows padded (K: 16 bytes, V: 64 bytes per row), filled through registers. With a
-// row stride of 17 (K) or 20 (V) chunks, the chunks one wave instruction reads fall on distinct
-// bank positions.
-template <int D>
-struct PadLayout {
-  using T = Tile<D, kBN>;
-  static constexpr int V8 = 8 * T::VS;  // byte distance of 8 V rows
-  int l32, hi, ig, g16;
-  __device__ __forceinline__ explicit PadLayout(int lane)
-      : l32(lane & 31), hi(lane >> 5), ig(lane & 15), g16((lane >> 4) & 1) {}
-  __device__ __forceinline__ int kfrag(int i) const { return (32 * (i & 1) + l32) * T::KS + (16 * (i >> 1) + 8 * hi) * 2; }
-  __device__ __forceinline__ int vfrag(int kk, int dt) const {
-    const int k0 = 16 * kk + 4 * hi;
-    const int d0 = 32 * dt + 16 * g16;
-    return (k0 + (ig >> 2)) * T::VS + (d0 + 4 * (ig & 3)) * 2;
-  }
-};
-
 // SwzLayout: unpadded rows of 2D bytes (CPR = D/8 chunks), filled by direct global -> LDS loads,
-// which write each wave instruction's 64 x 16 bytes to consecutive LDS addresses. The chunks of
-// a row are rotated instead of padded, so that the bank positions match the padded layout's:
+// which write each wave instruction's 64 x 16 bytes to consecutive LDS addresses, so rows cannot
+// be padded. The chunks of a row are rotated instead, so that the chunks one read instruction
+// touches fall on distinct banks (the bank positions of rows padded to 17 (K) or 20 (V) chunks):
 //   K: chunk c of row r at column (c + r) mod 16 (D = 128) or (c + r/2) mod 8 (D = 64);
 //   V: chunk c of row r at column (c + 4r) mod 16 (D = 128) or (c + 4 (r/2)) mod 8 (D = 64).
 // A lane's columns depend only on the lane and the k (channel) step, never on the 32-key half or
@@ -296,59 +269,6 @@ __device__ __forceinline__ void rows_end(const WaveRows<D>& w, uint16_t* out, fl
     *lse_p = empty ? -INFINITY : (w.m_run + __log2f(l_tot)) * 0.6931471805599453f;
 }
 
-// Global -> register staging of one K/V tile by NT threads, and register -> LDS store. Each
-// thread's 16-byte chunks sit at fixed offsets from the tile's first row (32-bit: < BN rows x
-// row_stride); rows past the end of the sequence are clamped to the last token, only in the
-// tile that holds it.
-template <int D, int BN, int NT>
-struct TileStage {
-  using T = Tile<D, BN>;
-  static constexpr int LOADS = T::CHUNKS / NT;  // 16-byte loads per thread per tensor
-  static_assert(T::CHUNKS % NT == 0, "tile must split evenly");
-  int toff[LOADS], trow[LOADS];
-  u32x4 kst[LOADS], vst[LOADS];
-
-  __device__ __forceinline__ void init(int tid, int64_t row_stride) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int ci = tid + i * NT;
-      trow[i] = ci / (D / 8);
-      toff[i] = trow[i] * (int)row_stride + (ci % (D / 8)) * 8;
-    }
-  }
-  __device__ __forceinline__ void fetch(const uint16_t* k, const uint16_t* v, int64_t base, int64_t key0,
-                                        int64_t N, int64_t row_stride) {
-    const int64_t tile = base + key0 * row_stride;
-    if (key0 + BN <= N) {
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        kst[i] = *reinterpret_cast<const u32x4*>(k + tile + toff[i]);
-        vst[i] = *reinterpret_cast<const u32x4*>(v + tile + toff[i]);
-      }
-    } else {
-      const int last = (int)(N - 1 - key0);
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int r = trow[i] < last ? trow[i] : last;
-        const int64_t off = tile + toff[i] + (int64_t)(r - trow[i]) * row_stride;
-        kst[i] = *reinterpret_cast<const u32x4*>(k + off);
-        vst[i] = *reinterpret_cast<const u32x4*>(v + off);
-      }
-    }
-  }
-  __device__ __forceinline__ void stash(unsigned char* kb, int tid) const { stash2(kb, kb + T::K_BYTES, tid); }
-  __device__ __forceinline__ void stash2(unsigned char* kb, unsigned char* vb, int tid) const {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int ci = tid + i * NT;
-      const int row = ci / (D / 8);
-      const int col = ci % (D / 8);
-      *reinterpret_cast<u32x4*>(kb + row * T::KS + col * 16) = kst[i];
-      *reinterpret_cast<u32x4*>(vb + row * T::VS + col * 16) = vst[i];
-    }
-  }
-};
-
 // Direct global -> LDS staging of one K/V tile into the SwzLayout (gfx950 global_load_lds_dwordx4:
 // no staging registers, no LDS write instructions). A wave instruction writes 64 lanes x 16 bytes
 // to consecutive LDS addresses, so LDS slot p = 64 (J w + j) + lane of wave w's instruction j is
@@ -486,13 +406,13 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
 // so that the two waves of a SIMD (w and w+4) belong to different blocks.
 template <int D, int G, int KW, bool CSR>
 __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs a) {
-  using T = Tile<D, kBN>;
+  using L = SwzLayout<D>;
   static_assert(G == 2 || G == 4, "2 or 4 query blocks per workgroup");
   constexpr int WAVES = 2 * G;
   constexpr int NT = WAVES * 64;
   static_assert(KW <= (1 << 24), "window slots must fit in 24 bits");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint32_t* ulist = reinterpret_cast<uint32_t*>(smem + 2 * T::BUF_BYTES);  // KW words
+  uint32_t* ulist = reinterpret_cast<uint32_t*>(smem + 2 * L::BUF_BYTES);  // KW words
   __shared__ int s_wave_tot[WAVES];
   __shared__ int s_nu;
 
@@ -524,9 +444,10 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
 
   WaveRows<D> w;
   rows_begin(w, a.q + base + my_q_c * row_stride + 8 * hi);
-  TileStage<D, kBN, NT> st;
-  st.init(tid, row_stride);
-  const PadLayout<D> lay(lane);
+  TileDma<D, NT> dma;
+  dma.init(tid, row_stride);
+  const L lay(lane);
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
   const float sc = 1.4426950408889634f / sqrtf((float)D);
   const uint32_t my_bit = 1u << gblk;
 
@@ -536,21 +457,21 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
     if (nu == 0) continue;
 
     auto key0_of = [&](int t) -> int64_t { return (j0 + (int64_t)(ulist[t] >> 8)) * kBN; };
-    st.fetch(a.k, a.v, base, key0_of(0), N, row_stride);
-    st.stash(smem, tid);
+    dma.fetch(a.k, a.v, base, key0_of(0), N, row_stride, smem_lds);
+    wait_dma();
     __syncthreads();
     for (int t = 0; t < nu; ++t) {
       const int buf = t & 1;
       const uint32_t e = __builtin_amdgcn_readfirstlane(ulist[t]);  // uniform: scalar tests and loads
-      if (t + 1 < nu) st.fetch(a.k, a.v, base, key0_of(t + 1), N, row_stride);
+      if (t + 1 < nu) dma.fetch(a.k, a.v, base, key0_of(t + 1), N, row_stride, smem_lds + (buf ^ 1) * L::BUF_BYTES);
       if (e & my_bit) {
-        const unsigned char* kb = smem + buf * T::BUF_BYTES;
+        const unsigned char* kb = smem + buf * L::BUF_BYTES;
         // a 64-bit compare here: the 32-bit block-index compare of the dense kernel measured 8 %
         // slower in this kernel
         const int64_t key0 = (j0 + (int64_t)(e >> 8)) * kBN;
-        rows_tile<D, kBN>(w, kb, kb + T::K_BYTES, key0, N, key0 + kBN > N, lane, sc, lay);
+        rows_tile<D, kBN>(w, kb, kb + L::K_BYTES, key0, N, key0 + kBN > N, lane, sc, lay);
       }
-      if (t + 1 < nu) st.stash(smem + (buf ^ 1) * T::BUF_BYTES, tid);
+      wait_dma();
       __syncthreads();
     }
   }
@@ -570,7 +491,7 @@ void launch_dense(const AttnArgs& a, hipStream_t stream) {
 
 template <int D, int G, int KW, bool CSR>
 void launch_group(const AttnArgs& a, hipStream_t stream) {
-  const size_t lds = 2 * Tile<D, kBN>::BUF_BYTES + (size_t)KW * 4;
+  const size_t lds = 2 * SwzLayout<D>::BUF_BYTES + (size_t)KW * 4;
   auto kern = attn_sparse_group_kernel<D, G, KW, CSR>;
   allow_dynamic_lds(reinterpret_cast<const void*>(kern), (int)lds);
   const dim3 grid((unsigned)n_groups<G>(a.n_blocks, a.group_stride), (unsigned)a.heads, (unsigned)a.batch);
