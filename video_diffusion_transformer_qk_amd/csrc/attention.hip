@@ -276,12 +276,6 @@ __device__ __forceinline__ void rows_end(const WaveRows<D>& w, uint16_t* out, fl
 // rotation puts at that column. Rows past the end of the sequence are clamped to the last token,
 // only in the tile that holds it. The loads are counted by vmcnt: a wave waits for its own
 // (wait_dma) before the barrier that hands the tile to the other waves.
-//
-// The load is issued from an asm block: through the compiler builtin, every LDS read issued while
-// a load is in flight (the current tile's V reads, while the next tile arrives in the other
-// buffer) got a vmcnt(0) wait in front of it. The block has no output register that the load
-// writes; it saves and restores M0 (which the load takes its LDS address from), with the one
-// wait state the hardware needs between writing M0 and the load.
 template <int D, int NT>
 struct TileDma {
   using L = SwzLayout<D>;
@@ -304,18 +298,6 @@ struct TileDma {
       voff[j] = r * (int)row_stride + 8 * L::vchunk(r, col);
     }
   }
-  // 16 bytes per lane from g to the LDS byte address lds + 16 * lane (lds wave-uniform)
-  __device__ static __forceinline__ void dma16(const uint16_t* g, uint32_t lds) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(g), "s"(lds));
-  }
   // buf: LDS byte address of the tile buffer (wave-uniform)
   __device__ __forceinline__ void fetch(const uint16_t* k, const uint16_t* v, int64_t base, int64_t key0,
                                         int64_t N, int64_t row_stride, uint32_t buf) const {
@@ -324,23 +306,20 @@ struct TileDma {
     if (key0 + kBN <= N) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        dma16(k + tile + koff[j], l0 + 1024 * j);
-        dma16(v + tile + voff[j], l0 + L::K_BYTES + 1024 * j);
+        lds_dma16(k + tile + koff[j], l0 + 1024 * j);
+        lds_dma16(v + tile + voff[j], l0 + L::K_BYTES + 1024 * j);
       }
     } else {
       const int last = (int)(N - 1 - key0);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int64_t adj = krow[j] < last ? 0 : (int64_t)(last - krow[j]) * row_stride;
-        dma16(k + tile + koff[j] + adj, l0 + 1024 * j);
-        dma16(v + tile + voff[j] + adj, l0 + L::K_BYTES + 1024 * j);
+        lds_dma16(k + tile + koff[j] + adj, l0 + 1024 * j);
+        lds_dma16(v + tile + voff[j] + adj, l0 + L::K_BYTES + 1024 * j);
       }
     }
   }
 };
-
-// vmcnt(0): this wave's direct loads have landed in LDS (expcnt and lgkmcnt left alone)
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Dense attention. WAVES waves per workgroup (32 queries each); OCC minimum waves per SIMD (2
 // caps the kernel at 256 registers so that two waves share each SIMD and overlap each other's
@@ -376,7 +355,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
   const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
 
   // LDS byte address of the tile buffers
-  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  const uint32_t smem_lds = lds_address(smem);
   dma.fetch(a.k, a.v, base, 0, N, row_stride, smem_lds);
   wait_dma();
   __syncthreads();
@@ -447,7 +426,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
   TileDma<D, NT> dma;
   dma.init(tid, row_stride);
   const L lay(lane);
-  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  const uint32_t smem_lds = lds_address(smem);
   const float sc = 1.4426950408889634f / sqrtf((float)D);
   const uint32_t my_bit = 1u << gblk;
 

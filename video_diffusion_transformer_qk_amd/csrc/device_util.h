@@ -24,6 +24,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
+// Direct global -> LDS load (gfx950 global_load_lds_dwordx4): 16 bytes per lane from g to the
+// LDS byte address lds + 16 * lane, lds wave-uniform; no register receives the data. The load is
+// counted by vmcnt like any global load: wait_dma before the LDS is read.
+//
+// It is issued from an asm block: through the compiler builtin, the compiler put a vmcnt(0) wait in
+// front of LDS reads issued while such a load is in flight, also where they read another buffer
+// (a tile is computed while the next one arrives). The block has no output that the load writes;
+// it saves and restores M0 (which the load takes its LDS address from), with the one wait state
+// the hardware needs between writing M0 and the load.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds));
+}
+
+// vmcnt(0): this wave's direct loads have landed in LDS (expcnt and lgkmcnt left alone)
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// LDS byte address of a pointer into shared memory
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
 // D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
 // Lane l holds A[l%32][8*(l/32) .. +7], B[8*(l/32) .. +7][l%32];
 // accumulator register r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
