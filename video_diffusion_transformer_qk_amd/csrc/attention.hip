@@ -356,6 +356,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
 
   // LDS byte address of the tile buffers
   const uint32_t smem_lds = lds_address(smem);
+  wait_own_loads();  // the Q fragments
   dma.fetch(a.k, a.v, base, 0, N, row_stride, smem_lds);
   wait_dma();
   __syncthreads();
@@ -436,6 +437,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
     if (nu == 0) continue;
 
     auto key0_of = [&](int t) -> int64_t { return (j0 + (int64_t)(ulist[t] >> 8)) * kBN; };
+    wait_own_loads();  // Q fragments, kept ranges and block lists
     dma.fetch(a.k, a.v, base, key0_of(0), N, row_stride, smem_lds);
     wait_dma();
     __syncthreads();

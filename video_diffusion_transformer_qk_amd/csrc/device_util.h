@@ -45,8 +45,19 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
       : "v"(g), "s"(lds));
 }
 
-// vmcnt(0): this wave's direct loads have landed in LDS (expcnt and lgkmcnt left alone)
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Waits for this wave's direct loads: all of them (wait_dma) or all but the last N (wait_dma_keep).
+// They are asm, not the s_waitcnt builtin: the compiler's wait pass does not know of the loads
+// issued by lds_dma16 and dropped a builtin wait it took for redundant. For the same reason the
+// compiler's own waits (for loads it issued itself) must not be left open across a direct load:
+// a kernel waits for its ordinary loads with the builtin before its first lds_dma16
+// (wait_own_loads), so that no compiler wait inside the tile loop counts the direct loads.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_dma_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_own_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // LDS byte address of a pointer into shared memory
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
