@@ -2,8 +2,11 @@
 
 One step = the whole path on one batch of the 5 s 1344x768 video workload (latent grid
 31 x 48 x 84 = 124,992 tokens, 48 heads, head_dim 128, smooth-field q/k, N(0,1) v, bf16):
-  qk_norm_rope -> dense_fwd -> subblock_select (sparsity 0.75) -> block_sparse_fwd.
+  qk_norm_rope_pool (norm+RoPE, pooling q' and k' for the selection in the same pass) -> dense_fwd
+  -> subblock_select_pooled (sparsity 0.75) -> block_sparse_fwd.
 Inputs are resident in HBM before the timed region; outputs and workspaces are preallocated.
+After the timed steps, norm+RoPE alone and the selection with its own pooling pass (the
+stand-alone calls) are timed on the same inputs, and their kept sets compared with the step's.
 
 Printed JSON line: value = attention TFLOP/s of the step (dense 4*B*H*N^2*D plus block-sparse
 4*B*H*nB*keep*64^2*D flops, divided by the whole step's time, norm+RoPE and selection included).
@@ -325,13 +328,18 @@ def main():
     ws = torch.empty((h3.select_workspace_bytes(b, hd, n, d),), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    # one pass of the hot path: norm+RoPE (pooling q', k' for the selection in the same pass),
+    # dense attention, the selection on the pooled blocks, block-sparse attention
+    pooled = {}
+
     def step(ev=None):
         if ev is not None: ev[0].record()
-        h3.qk_norm_rope(q, k, wq, wk, cfg.grid, sections, cfg.theta, cfg.eps, out=(qo, ko))
+        pooled["p"] = h3.qk_norm_rope_pool(q, k, wq, wk, cfg.grid, sections, cfg.theta, cfg.eps, workspace=ws,
+                                           out=(qo, ko))[2]
         if ev is not None: ev[1].record()
         h3.dense_fwd(qo, ko, v, out=out_d)
         if ev is not None: ev[2].record()
-        h3.subblock_select(qo, ko, args.sparsity, workspace=ws, out=idx)
+        h3.subblock_select_pooled(pooled["p"], args.sparsity, out=idx)
         if ev is not None: ev[3].record()
         h3.block_sparse_fwd(qo, ko, v, idx, out=out_s, group_stride=gs)
         if ev is not None: ev[4].record()
@@ -355,9 +363,9 @@ def main():
     clock = clocks.stop()
     wall = time.perf_counter() - t0
     ms_step = elapsed_ms(start, end) / args.steps
-    per = {"norm_rope": [], "dense": [], "select": [], "sparse": []}
+    per = {"norm_rope_pool": [], "dense": [], "select": [], "sparse": []}
     for ev in events:
-        per["norm_rope"].append(elapsed_ms(ev[0], ev[1]))
+        per["norm_rope_pool"].append(elapsed_ms(ev[0], ev[1]))
         per["dense"].append(elapsed_ms(ev[1], ev[2]))
         per["select"].append(elapsed_ms(ev[2], ev[3]))
         per["sparse"].append(elapsed_ms(ev[3], ev[4]))
@@ -368,13 +376,41 @@ def main():
     dense_flops = 4.0 * b * hd * n * n * d
     sparse_flops = 4.0 * b * hd * nb * keep * 64 * 64 * d
     nr_bytes = 8.0 * b * n * hd * d
+    # the pooled block statistics the fused pass also writes: per (tensor, batch, head, block) the
+    # float64 means (8 D), their digits (3 D), exponent (4) and norms (8)
+    pool_bytes = 2.0 * b * hd * nb * (11 * d + 12)
     dense_tf = dense_flops / (avg["dense"] * 1e-3) / 1e12
     sparse_tf = sparse_flops / (avg["sparse"] * 1e-3) / 1e12
-    nr_gbs = nr_bytes / (avg["norm_rope"] * 1e-3) / 1e9
-    # selection's algorithmic bytes: q' and k' read once (pooling), the kept indices written once
-    sel_bytes = 4.0 * b * n * hd * d + 4.0 * b * hd * nb * keep
-    sel_gbs = sel_bytes / (avg["select"] * 1e-3) / 1e9
+    nrp_gbs = (nr_bytes + pool_bytes) / (avg["norm_rope_pool"] * 1e-3) / 1e9
     value = (dense_flops + sparse_flops) / (ms_step * 1e-3) / 1e12
+
+    # the stand-alone calls on the same inputs: norm+RoPE alone, and the selection with its own
+    # pooling pass (which also checks that the pooled path kept the same blocks)
+    def median_ms(fn, reps=10, warm=2):
+        ts = []
+        for r in range(warm + reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= warm:
+                ts.append(elapsed_ms(e0, e1))
+        return float(np.median(ts))
+    idx_pooled = idx.clone()
+    nr_ms = median_ms(lambda: h3.qk_norm_rope(q, k, wq, wk, cfg.grid, sections, cfg.theta, cfg.eps, out=(qo, ko)))
+    sel_alone_ms = median_ms(lambda: h3.subblock_select(qo, ko, args.sparsity, workspace=ws, out=idx))
+    same_sets = bool(torch.equal(idx, idx_pooled))
+    nr_gbs = nr_bytes / (nr_ms * 1e-3) / 1e9
+    # selection's algorithmic bytes: q' and k' read once (pooling), the kept indices written once. On
+    # the pooled path its time is the pooled selection plus what pooling adds to the norm+RoPE pass
+    sel_bytes = 4.0 * b * n * hd * d + 4.0 * b * hd * nb * keep
+    sel_extra_ms = max(0.0, avg["norm_rope_pool"] - nr_ms)
+    sel_total_ms = avg["select"] + sel_extra_ms
+    sel_gbs = sel_bytes / (sel_total_ms * 1e-3) / 1e9
+    log(f"norm+rope alone {nr_ms:.3f} ms ({nr_gbs:.0f} GB/s); norm+rope with pooling {avg['norm_rope_pool']:.3f} ms; "
+        f"selection {avg['select']:.3f} ms after pooling ({sel_total_ms:.3f} ms with the pooling's share), "
+        f"{sel_alone_ms:.3f} ms with its own pooling pass; same kept sets: {same_sets}")
 
     components = {
         "gfx_clock_during_steps": clock,
@@ -386,10 +422,15 @@ def main():
                            for kname, vals in per.items()},
         "dense_ms": avg["dense"], "dense_tflops": dense_tf, "dense_frac_peak": dense_tf / PEAK_BF16_TFLOPS,
         "sparse_ms": avg["sparse"], "sparse_tflops_kept": sparse_tf, "sparse_frac_peak": sparse_tf / PEAK_BF16_TFLOPS,
-        "select_ms": avg["select"], "select_bytes": sel_bytes, "select_gbs": sel_gbs,
-        "select_frac_peak": sel_gbs / PEAK_HBM_GBS,
-        "norm_rope_ms": avg["norm_rope"], "norm_rope_gbs": nr_gbs,
-        "norm_rope_frac_peak": nr_gbs / PEAK_HBM_GBS, "keep": keep, "n_blocks": nb,
+        # selection after the pooling in the norm+RoPE pass, and with the pooling's share of that pass
+        "select_ms": avg["select"], "select_pool_share_ms": sel_extra_ms, "select_total_ms": sel_total_ms,
+        "select_bytes": sel_bytes, "select_gbs": sel_gbs, "select_frac_peak": sel_gbs / PEAK_HBM_GBS,
+        "select_standalone_ms": sel_alone_ms, "pooled_select_equals_standalone": same_sets,
+        # norm+RoPE alone (same inputs, after the timed steps) and the step's pass that also pools
+        "norm_rope_ms": nr_ms, "norm_rope_gbs": nr_gbs, "norm_rope_frac_peak": nr_gbs / PEAK_HBM_GBS,
+        "norm_rope_pool_ms": avg["norm_rope_pool"], "norm_rope_pool_bytes": nr_bytes + pool_bytes,
+        "norm_rope_pool_gbs": nrp_gbs, "norm_rope_pool_frac_peak": nrp_gbs / PEAK_HBM_GBS,
+        "keep": keep, "n_blocks": nb,
         "dense_flops": dense_flops, "sparse_flops": sparse_flops, "norm_rope_bytes": nr_bytes,
     }
 

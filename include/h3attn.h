@@ -120,6 +120,32 @@ h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
                                      int32_t* block_idx, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
+/* h3attn_qk_norm_rope and the pooling step of h3attn_subblock_select in one pass [P3 "先把近两倍的
+ * 免费收益拿走": a fused pass saves an intermediate tensor's memory traffic; here it also saves the
+ * selection's re-read of q' and k']. Writes q_out, k_out exactly as h3attn_qk_norm_rope does (the same bits) and
+ * the block means of q_out and k_out (with their digits, exponents and norms) into workspace, which
+ * must then be passed, untouched and with the same batch, heads, n_tokens (grid.t * grid.h * grid.w),
+ * head_dim and block_size, to h3attn_subblock_select_pooled. workspace: as h3attn_subblock_select
+ * (at least h3attn_select_workspace_bytes(...) bytes, 256-byte aligned).
+ * Errors: those of h3attn_qk_norm_rope and of h3attn_subblock_select's workspace and size checks. */
+h3attn_status h3attn_qk_norm_rope_pool(const h3attn_bf16* q_in, const h3attn_bf16* k_in,
+                                       h3attn_bf16* q_out, h3attn_bf16* k_out,
+                                       const float* q_weight, const float* k_weight,
+                                       int32_t batch, int32_t heads, int32_t head_dim, h3attn_grid grid,
+                                       int32_t d_t, int32_t d_h, int32_t d_w,
+                                       float rope_theta, float eps, int32_t block_size,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The rest of h3attn_subblock_select [P3 "6.24 倍里…"] on a workspace that h3attn_qk_norm_rope_pool
+ * has just filled: the same kept sets, bit for bit, as h3attn_subblock_select on that call's
+ * q_out and k_out. Arguments and errors as h3attn_subblock_select without q and k; a workspace not
+ * filled that way gives undefined (but in-bounds) results. A filled workspace serves one call: the
+ * call rewrites the key blocks' exponents in it in place. */
+h3attn_status h3attn_subblock_select_pooled(int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                            int32_t block_size, double sparsity, int32_t keep,
+                                            int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
+
 /* Block-sparse attention [P3 "6.24 倍里…"]: the queries of block i attend only to the tokens of
  * the key blocks block_idx[b, head, i, 0..keep-1], with the softmax renormalised over those
  * tokens (a partial last key block contributes only its valid tokens). Same numerics and

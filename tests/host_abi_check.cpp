@@ -36,6 +36,10 @@ void launch_dense_fwd(const AttnArgs& a, hipStream_t) { g_attn = a; ++g_launches
 void launch_block_sparse_fwd(const AttnArgs& a, hipStream_t) { g_attn = a; ++g_launches; }
 void launch_block_sparse_csr_fwd(const AttnArgs& a, hipStream_t) { g_attn = a; ++g_launches; }
 void launch_subblock_select(const SelectArgs& a, hipStream_t) { g_sel = a; ++g_launches; }
+void launch_qk_norm_rope_pool(const NormRopeArgs& nr, const RopeTable& t, const SelectArgs& a, hipStream_t) {
+  g_nr = nr; g_tab = t; g_sel = a; ++g_launches;
+}
+void launch_subblock_select_pooled(const SelectArgs& a, hipStream_t) { g_sel = a; ++g_launches; }
 void launch_threshold_count(const SelectArgs& a, hipStream_t) { g_sel = a; ++g_launches; }
 void launch_threshold_fill(const SelectArgs& a, hipStream_t) { g_sel = a; ++g_launches; }
 void launch_check_topk_rows(const IndexCheckArgs& a, hipStream_t) { g_chk = a; ++g_launches; }
@@ -155,6 +159,35 @@ void check_select() {
   EXPECT(h3attn_subblock_select(Q, K, 1, 2, 640, 64, 64, 0.75, keep, idx, WS, ws - 1, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
   EXPECT(h3attn_subblock_select(Q, K, 1, 2, 640, 64, 64, 1.0, keep, idx, WS, ws, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
   EXPECT(h3attn_subblock_select(Q, K, 1, 2, 19969LL * 64, 64, 64, 0.75, keep, idx, WS, ws, nullptr) == H3ATTN_ERR_UNSUPPORTED);
+  // norm+RoPE with the pooling, then the pooled selection: the same workspace regions
+  {
+    const float* wq = P<const float>(0x50000);
+    const float* wk = P<const float>(0x60000);
+    h3attn_bf16* qo = P<h3attn_bf16>(0x70000);
+    h3attn_bf16* ko = P<h3attn_bf16>(0x80000);
+    const h3attn_grid g10{10, 8, 8};
+    const void* qmean = g_sel.q_mean;
+    n0 = g_launches;
+    EXPECT(launched(h3attn_qk_norm_rope_pool(Q, K, qo, ko, wq, wk, 1, 2, 64, g10, 16, 24, 24, 1e4f, 1e-6f, 64, WS,
+                                             ws, nullptr), n0));
+    EXPECT(g_nr.n_tokens == 640 && g_nr.q_out == qo && g_nr.k_out == ko && g_nr.heads == 2);
+    EXPECT(g_sel.n_blocks == 10 && g_sel.q == qo && g_sel.k == ko && (const void*)g_sel.q_mean == qmean);
+    EXPECT(h3attn_qk_norm_rope_pool(Q, K, qo, ko, wq, wk, 1, 2, 64, g10, 16, 24, 24, 1e4f, 1e-6f, 64, WS, ws - 1,
+                                    nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+    EXPECT(h3attn_qk_norm_rope_pool(Q, K, qo, ko, wq, wk, 1, 2, 64, g10, 16, 24, 24, 1e4f, 1e-6f, 32, WS, ws,
+                                    nullptr) == H3ATTN_ERR_UNSUPPORTED);
+    EXPECT(h3attn_qk_norm_rope_pool(Q, K, qo, ko, wq, wk, 1, 2, 64, g10, 16, 24, 22, 1e4f, 1e-6f, 64, WS, ws,
+                                    nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+    EXPECT(h3attn_qk_norm_rope_pool(Q, K, qo, ko, wq, wk, 1, 2, 64, g10, 16, 24, 24, 1e4f, 1e-6f, 64, nullptr, ws,
+                                    nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+    n0 = g_launches;
+    EXPECT(launched(h3attn_subblock_select_pooled(1, 2, 640, 64, 64, 0.75, keep, idx, WS, ws, nullptr), n0));
+    EXPECT(g_sel.n_blocks == 10 && g_sel.keep == 3 && g_sel.block_idx == idx && (const void*)g_sel.q_mean == qmean);
+    EXPECT(h3attn_subblock_select_pooled(1, 2, 640, 64, 64, 0.75, keep + 1, idx, WS, ws, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+    EXPECT(h3attn_subblock_select_pooled(1, 2, 640, 64, 64, 1.0, keep, idx, WS, ws, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+    EXPECT(h3attn_subblock_select_pooled(1, 2, 640, 64, 64, 0.75, keep, nullptr, WS, ws, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+    EXPECT(h3attn_subblock_select_pooled(1, 2, 640, 64, 64, 0.75, keep, idx, WS, ws - 1, nullptr) == H3ATTN_ERR_INVALID_ARGUMENT);
+  }
   // threshold mode
   const size_t tws = h3attn_threshold_workspace_bytes(1, 2, 640, 64, 64);
   int64_t* rp = P<int64_t>(0xB0000);

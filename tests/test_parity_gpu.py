@@ -119,6 +119,50 @@ def test_ragged_norm_rope_grids(h3):
         _full_norm_rope(h3, c["q"], c["k"], c["wq"], c["wk"], grid, sec, 1e4, 1e-6, f"grid {grid}", wl="ragged grids")
 
 
+def _pooled_matches_separate(h3, q, k, wq, wk, grid, sections, sparsity, what, inplace=False):
+    """qk_norm_rope_pool + subblock_select_pooled against qk_norm_rope + subblock_select: the same
+    q', k' and the same kept sets, bit for bit (the pooled path sums the same rounded outputs)."""
+    qa, ka = h3.qk_norm_rope(q, k, wq, wk, grid, sections)
+    ia = h3.subblock_select(qa, ka, sparsity)
+    if inplace:
+        q2, k2 = q.clone(), k.clone()
+        qb, kb, pooled = h3.qk_norm_rope_pool(q2, k2, wq, wk, grid, sections, inplace=True)
+        assert qb.data_ptr() == q2.data_ptr() and kb.data_ptr() == k2.data_ptr()
+    else:
+        qb, kb, pooled = h3.qk_norm_rope_pool(q, k, wq, wk, grid, sections)
+    ib = h3.subblock_select_pooled(pooled, sparsity)
+    _sync()
+    assert torch.equal(qa.view(torch.int16), qb.view(torch.int16)), f"{what}: q' differs"
+    assert torch.equal(ka.view(torch.int16), kb.view(torch.int16)), f"{what}: k' differs"
+    assert torch.equal(ia, ib), f"{what}: kept sets differ ({int((ia != ib).sum())} entries)"
+    log(f"{what}: pooled norm+rope and selection identical to the separate calls ({tuple(ib.shape)})")
+
+
+def test_norm_rope_pool_matches_separate_calls(h3):
+    cfg = TINY
+    x = make_inputs(cfg, DEV)
+    _pooled_matches_separate(h3, x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, 0.5, "tiny")
+    for grid, d, sec in (((3, 5, 7), 64, (16, 24, 24)), ((2, 3, 11), 128, (32, 48, 48)),
+                         ((1, 1, 9), 128, (0, 64, 64)), ((5, 2, 3), 64, (64, 0, 0)), ((4, 8, 9), 128, (32, 48, 48))):
+        n = grid[0] * grid[1] * grid[2]
+        c = random_case(2, n, 5, d, seed=7 + n, device=DEV, scale=3.0)
+        for s in (0.0, 0.5):
+            _pooled_matches_separate(h3, c["q"], c["k"], c["wq"], c["wk"], grid, sec, s, f"grid {grid} d={d} s={s}")
+    c = random_case(1, 288, 17, 128, seed=5, device=DEV)
+    _pooled_matches_separate(h3, c["q"], c["k"], c["wq"], c["wk"], (2, 12, 12), (32, 48, 48), 0.75,
+                             "17 heads, in place", inplace=True)
+    cfg = FRAME
+    x = make_inputs(cfg, DEV)
+    _pooled_matches_separate(h3, x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, 0.75, "frame")
+
+
+@pytest.mark.timeout(600)
+def test_norm_rope_pool_matches_separate_calls_video10s(h3):
+    cfg = VIDEO10S
+    x = make_inputs(cfg, DEV)
+    _pooled_matches_separate(h3, x["q"], x["k"], x["wq"], x["wk"], cfg.grid, cfg.sections, 0.75, "10s")
+
+
 def test_norm_rope_inplace_matches_out_of_place(h3):
     c = random_case(1, 96, 4, 128, seed=3, device=DEV)
     a, b = h3.qk_norm_rope(c["q"], c["k"], c["wq"], c["wk"], (2, 6, 8), (32, 48, 48))

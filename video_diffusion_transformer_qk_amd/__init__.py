@@ -2,6 +2,8 @@
 
 Four calls, each a hand-written HIP kernel behind a C ABI (include/h3attn.h):
   qk_norm_rope      fused per-head QK RMSNorm + 3D (t/h/w) RoPE
+                    (qk_norm_rope_pool also pools q', k' for the selection in the same pass, and
+                    subblock_select_pooled finishes the selection from that)
   dense_fwd         dense bf16 self-attention over the full latent sequence
   subblock_select   SubBlock 64-token block scores and per-query-block top-k
   block_sparse_fwd  attention over the kept key blocks only
@@ -15,9 +17,10 @@ from ._lib import (LIB_PATH, SIGNATURES, H3AttnError, block_sparse_csr_fwd, bloc
                    dense_fwd, keep_count, load_library, qk_norm_rope, select_workspace_bytes,
                    subblock_select, subblock_select_threshold, threshold_workspace_bytes, version,
                    adaln_modulate, swiglu, residual_change, CacheGate, Fp8QKV, fp8_workspace_bytes,
-                   fp8_quantize, fp8_dense_fwd, fp8_block_sparse_fwd, frame_group_stride, check_block_idx, check_csr)
+                   fp8_quantize, fp8_dense_fwd, fp8_block_sparse_fwd, frame_group_stride, check_block_idx, check_csr,
+                   qk_norm_rope_pool, subblock_select_pooled, PooledBlocks)
 
-__all__ = ["qk_norm_rope", "dense_fwd", "subblock_select", "block_sparse_fwd", "keep_count",
+__all__ = ["qk_norm_rope", "qk_norm_rope_pool", "subblock_select_pooled", "PooledBlocks", "dense_fwd", "subblock_select", "block_sparse_fwd", "keep_count",
            "select_workspace_bytes", "subblock_select_threshold", "block_sparse_csr_fwd",
            "threshold_workspace_bytes", "adaln_modulate", "swiglu",
            "residual_change", "CacheGate", "Fp8QKV", "fp8_workspace_bytes", "fp8_quantize",

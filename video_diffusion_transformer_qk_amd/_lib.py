@@ -34,6 +34,11 @@ SIGNATURES = {
     "h3attn_select_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I64, _I32, _I32]),
     "h3attn_qk_norm_rope": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, Grid,
                                            _I32, _I32, _I32, ctypes.c_float, ctypes.c_float, _P]),
+    "h3attn_qk_norm_rope_pool": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, Grid,
+                                                _I32, _I32, _I32, ctypes.c_float, ctypes.c_float, _I32,
+                                                _P, ctypes.c_size_t, _P]),
+    "h3attn_subblock_select_pooled": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.c_double,
+                                                     _I32, _P, _P, ctypes.c_size_t, _P]),
     "h3attn_dense_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I64, _I32, _P]),
     "h3attn_subblock_select": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32, _I32, ctypes.c_double,
                                               _I32, _P, _P, ctypes.c_size_t, _P]),
@@ -169,12 +174,7 @@ def select_workspace_bytes(batch: int, heads: int, n_tokens: int, head_dim: int,
     return int(load_library().h3attn_select_workspace_bytes(batch, heads, n_tokens, head_dim, block_size))
 
 
-def qk_norm_rope(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
-                 grid: Sequence[int], sections: Sequence[int], theta: float = 1e4, eps: float = 1e-6,
-                 out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-                 inplace: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Fused per-head RMSNorm + 3D RoPE of bf16 q, k [B, N, heads, D]; returns (q', k')."""
-    lib = load_library()
+def _norm_rope_args(q, k, w_q, w_k, grid, sections, out, inplace):
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(w_q, "w_q", torch.float32, 1)
@@ -199,10 +199,71 @@ def qk_norm_rope(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch
     if g.t * g.h * g.w != n:
         raise ValueError(f"grid {tuple(grid)} does not hold {n} tokens")
     d_t, d_h, d_w = [int(x) for x in sections]
+    return qo, ko, g, (d_t, d_h, d_w)
+
+
+def qk_norm_rope(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                 grid: Sequence[int], sections: Sequence[int], theta: float = 1e4, eps: float = 1e-6,
+                 out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                 inplace: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fused per-head RMSNorm + 3D RoPE of bf16 q, k [B, N, heads, D]; returns (q', k')."""
+    lib = load_library()
+    qo, ko, g, (d_t, d_h, d_w) = _norm_rope_args(q, k, w_q, w_k, grid, sections, out, inplace)
+    b, n, h, d = q.shape
     _check(lib.h3attn_qk_norm_rope(q.data_ptr(), k.data_ptr(), qo.data_ptr(), ko.data_ptr(),
                                    w_q.data_ptr(), w_k.data_ptr(), b, h, d, g, d_t, d_h, d_w,
                                    float(theta), float(eps), _stream()))
     return qo, ko
+
+
+class PooledBlocks(NamedTuple):
+    """The selection workspace as qk_norm_rope_pool left it, with the shape it was filled for."""
+    workspace: torch.Tensor
+    batch: int
+    n_tokens: int
+    heads: int
+    head_dim: int
+    block_size: int
+
+
+def qk_norm_rope_pool(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                      grid: Sequence[int], sections: Sequence[int], theta: float = 1e4, eps: float = 1e-6,
+                      block_size: int = 64, workspace: Optional[torch.Tensor] = None,
+                      out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                      inplace: bool = False) -> Tuple[torch.Tensor, torch.Tensor, PooledBlocks]:
+    """qk_norm_rope plus the selection's pooling of q', k' in the same pass; returns (q', k', pooled)
+    for subblock_select_pooled."""
+    lib = load_library()
+    qo, ko, g, (d_t, d_h, d_w) = _norm_rope_args(q, k, w_q, w_k, grid, sections, out, inplace)
+    b, n, h, d = q.shape
+    need = select_workspace_bytes(b, h, n, d, block_size)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _same_device(q, workspace=workspace)
+    _check(lib.h3attn_qk_norm_rope_pool(q.data_ptr(), k.data_ptr(), qo.data_ptr(), ko.data_ptr(),
+                                        w_q.data_ptr(), w_k.data_ptr(), b, h, d, g, d_t, d_h, d_w,
+                                        float(theta), float(eps), block_size, workspace.data_ptr(),
+                                        workspace.numel(), _stream()))
+    return qo, ko, PooledBlocks(workspace, b, n, h, d, block_size)
+
+
+def subblock_select_pooled(pooled: PooledBlocks, sparsity: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """subblock_select on the q', k' of the qk_norm_rope_pool call that returned `pooled` (the same kept
+    sets); int32 [B, heads, nB, keep], rows ascending. `pooled` serves one call (the selection rewrites
+    the key blocks' exponents in the workspace in place)."""
+    lib = load_library()
+    ws = pooled.workspace
+    _need(ws, "workspace", torch.uint8, 1)
+    b, n, h, d, bs = pooled.batch, pooled.n_tokens, pooled.heads, pooled.head_dim, pooled.block_size
+    nb = -(-n // bs)
+    keep = keep_count(nb, sparsity)
+    idx = torch.empty((b, h, nb, keep), dtype=torch.int32, device=ws.device) if out is None else out
+    _need(idx, "block_idx", torch.int32, 4)
+    _need_shape(idx, "block_idx", (b, h, nb, keep), ws)
+    _check(lib.h3attn_subblock_select_pooled(b, h, n, d, bs, float(sparsity), keep, idx.data_ptr(), ws.data_ptr(),
+                                             ws.numel(), _stream()))
+    return idx
 
 
 def dense_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, return_lse: bool = False,

@@ -125,12 +125,12 @@ size_t h3attn_select_workspace_bytes(int32_t batch, int32_t heads, int64_t n_tok
   return select_layout(batch, heads, n_tokens, head_dim, block_size).total;
 }
 
-h3attn_status h3attn_qk_norm_rope(const h3attn_bf16* q_in, const h3attn_bf16* k_in,
-                                  h3attn_bf16* q_out, h3attn_bf16* k_out,
-                                  const float* q_weight, const float* k_weight,
-                                  int32_t batch, int32_t heads, int32_t head_dim, h3attn_grid grid,
-                                  int32_t d_t, int32_t d_h, int32_t d_w,
-                                  float rope_theta, float eps, hipStream_t stream) {
+// Validates the norm+RoPE arguments and builds the kernel arguments and the rotation-rate table.
+static h3attn_status prepare_norm_rope(const h3attn_bf16* q_in, const h3attn_bf16* k_in, h3attn_bf16* q_out,
+                                       h3attn_bf16* k_out, const float* q_weight, const float* k_weight,
+                                       int32_t batch, int32_t heads, int32_t head_dim, h3attn_grid grid,
+                                       int32_t d_t, int32_t d_h, int32_t d_w, float rope_theta, float eps,
+                                       h3attn::NormRopeArgs& a, h3attn::RopeTable& tab) {
   CHECK_PTR(q_in); CHECK_PTR(k_in); CHECK_PTR(q_out); CHECK_PTR(k_out);
   CHECK_PTR(q_weight); CHECK_PTR(k_weight);
   if (grid.t <= 0 || grid.h <= 0 || grid.w <= 0)
@@ -151,7 +151,6 @@ h3attn_status h3attn_qk_norm_rope(const h3attn_bf16* q_in, const h3attn_bf16* k_
 
   if (((int64_t)batch * n_tokens / 8 + 1) * ((2 * (int64_t)heads + 3) / 4) >= ((int64_t)1 << 31))
     return fail(H3ATTN_ERR_UNSUPPORTED, "batch*n_tokens*heads too large for one launch");
-  h3attn::RopeTable tab;
   std::memset(&tab, 0, sizeof(tab));
   const int32_t secs[3] = {d_t, d_h, d_w};
   int pair = 0;
@@ -161,11 +160,25 @@ h3attn_status h3attn_qk_norm_rope(const h3attn_bf16* q_in, const h3attn_bf16* k_
       tab.axis[pair] = ax;
     }
   }
-  h3attn::NormRopeArgs a{};
+  a = h3attn::NormRopeArgs{};
   a.q_in = q_in; a.k_in = k_in; a.q_out = q_out; a.k_out = k_out;
   a.q_weight = q_weight; a.k_weight = k_weight;
   a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
   a.grid_h = grid.h; a.grid_w = grid.w; a.eps = eps;
+  return H3ATTN_OK;
+}
+
+h3attn_status h3attn_qk_norm_rope(const h3attn_bf16* q_in, const h3attn_bf16* k_in,
+                                  h3attn_bf16* q_out, h3attn_bf16* k_out,
+                                  const float* q_weight, const float* k_weight,
+                                  int32_t batch, int32_t heads, int32_t head_dim, h3attn_grid grid,
+                                  int32_t d_t, int32_t d_h, int32_t d_w,
+                                  float rope_theta, float eps, hipStream_t stream) {
+  h3attn::NormRopeArgs a;
+  h3attn::RopeTable tab;
+  const h3attn_status st = prepare_norm_rope(q_in, k_in, q_out, k_out, q_weight, k_weight, batch, heads, head_dim,
+                                             grid, d_t, d_h, d_w, rope_theta, eps, a, tab);
+  if (st != H3ATTN_OK) return st;
   h3attn::launch_qk_norm_rope(a, tab, stream);
   return check_launch("h3attn_qk_norm_rope");
 }
@@ -196,38 +209,91 @@ h3attn_status h3attn_dense_fwd(const h3attn_bf16* q, const h3attn_bf16* k, const
   return check_launch("h3attn_dense_fwd");
 }
 
+// Checks shared by the selection entry points (sizes, block size, the fallback's LDS limit, the
+// workspace) and the workspace pointers of the SelectArgs.
+static h3attn_status prepare_select(int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                    int32_t block_size, void* workspace, size_t workspace_bytes,
+                                    h3attn::SelectArgs& a) {
+  if (workspace == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  h3attn_status st = check_sizes(batch, heads, n_tokens, head_dim);
+  if (st != H3ATTN_OK) return st;
+  if (block_size != 64) return fail(H3ATTN_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", block_size);
+  if ((int64_t)batch * heads > 65535) return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads must be <= 65535");
+  const int64_t nb = (n_tokens + block_size - 1) / block_size;
+  if (nb * 8 > h3attn::kSelectRowLdsBytes)
+    return fail(H3ATTN_ERR_UNSUPPORTED, "%lld blocks exceed the per-row LDS budget of the selection kernels", (long long)nb);
+  const size_t need = h3attn_select_workspace_bytes(batch, heads, n_tokens, head_dim, block_size);
+  if (workspace_bytes < need)
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  a = h3attn::SelectArgs{};
+  a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
+  a.block_size = block_size; a.n_blocks = (int32_t)nb;
+  select_pointers(a, workspace, select_layout(batch, heads, n_tokens, head_dim, block_size));
+  return H3ATTN_OK;
+}
+
+// The top-k arguments: the output rows and keep = keep_count(nB, sparsity).
+static h3attn_status prepare_topk(double sparsity, int32_t keep, int32_t* block_idx, h3attn::SelectArgs& a) {
+  if (block_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is NULL");
+  if (reinterpret_cast<uintptr_t>(block_idx) & 3u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is not 4-byte aligned");
+  if (!(sparsity >= 0.0 && sparsity < 1.0)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "sparsity must be in [0, 1) (got %g)", sparsity);
+  const int32_t want = h3attn_keep_count(a.n_blocks, sparsity);
+  if (keep != want) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep %d does not match keep_count(%d, %g) = %d", keep, a.n_blocks, sparsity, want);
+  if ((uint64_t)a.batch * a.heads * (uint64_t)a.n_blocks * (uint64_t)keep > ((uint64_t)1 << 62))
+    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx too large");
+  a.keep = keep;
+  a.block_idx = block_idx;
+  return H3ATTN_OK;
+}
+
 h3attn_status h3attn_subblock_select(const h3attn_bf16* q, const h3attn_bf16* k,
                                      int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
                                      int32_t block_size, double sparsity, int32_t keep,
                                      int32_t* block_idx, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream) {
   CHECK_PTR(q); CHECK_PTR(k);
-  if (block_idx == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is NULL");
-  if (reinterpret_cast<uintptr_t>(block_idx) & 3u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx is not 4-byte aligned");
-  if (workspace == nullptr) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace is NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-  h3attn_status st = check_sizes(batch, heads, n_tokens, head_dim);
+  h3attn::SelectArgs a;
+  h3attn_status st = prepare_select(batch, heads, n_tokens, head_dim, block_size, workspace, workspace_bytes, a);
   if (st != H3ATTN_OK) return st;
-  if (block_size != 64) return fail(H3ATTN_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", block_size);
-  if (!(sparsity >= 0.0 && sparsity < 1.0)) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "sparsity must be in [0, 1) (got %g)", sparsity);
-  if ((int64_t)batch * heads > 65535) return fail(H3ATTN_ERR_UNSUPPORTED, "batch*heads must be <= 65535");
-  const int64_t nb = (n_tokens + block_size - 1) / block_size;
-  if (nb * 8 > h3attn::kSelectRowLdsBytes)
-    return fail(H3ATTN_ERR_UNSUPPORTED, "%lld blocks exceed the per-row LDS budget of the selection kernels", (long long)nb);
-  const int32_t want = h3attn_keep_count((int32_t)nb, sparsity);
-  if (keep != want) return fail(H3ATTN_ERR_INVALID_ARGUMENT, "keep %d does not match keep_count(%lld, %g) = %d", keep, (long long)nb, sparsity, want);
-  const size_t need = h3attn_select_workspace_bytes(batch, heads, n_tokens, head_dim, block_size);
-  if (workspace_bytes < need)
-    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
-  if ((uint64_t)batch * heads * (uint64_t)nb * (uint64_t)keep > ((uint64_t)1 << 62))
-    return fail(H3ATTN_ERR_INVALID_ARGUMENT, "block_idx too large");
-
-  h3attn::SelectArgs a{};
-  a.q = q; a.k = k; a.n_tokens = n_tokens; a.batch = batch; a.heads = heads; a.head_dim = head_dim;
-  a.block_size = block_size; a.n_blocks = (int32_t)nb; a.keep = keep; a.block_idx = block_idx;
-  select_pointers(a, workspace, select_layout(batch, heads, n_tokens, head_dim, block_size));
+  st = prepare_topk(sparsity, keep, block_idx, a);
+  if (st != H3ATTN_OK) return st;
+  a.q = q; a.k = k;
   h3attn::launch_subblock_select(a, stream);
   return check_launch("h3attn_subblock_select");
+}
+
+h3attn_status h3attn_qk_norm_rope_pool(const h3attn_bf16* q_in, const h3attn_bf16* k_in,
+                                       h3attn_bf16* q_out, h3attn_bf16* k_out,
+                                       const float* q_weight, const float* k_weight,
+                                       int32_t batch, int32_t heads, int32_t head_dim, h3attn_grid grid,
+                                       int32_t d_t, int32_t d_h, int32_t d_w,
+                                       float rope_theta, float eps, int32_t block_size,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  h3attn::NormRopeArgs nr;
+  h3attn::RopeTable tab;
+  h3attn_status st = prepare_norm_rope(q_in, k_in, q_out, k_out, q_weight, k_weight, batch, heads, head_dim,
+                                       grid, d_t, d_h, d_w, rope_theta, eps, nr, tab);
+  if (st != H3ATTN_OK) return st;
+  h3attn::SelectArgs a;
+  st = prepare_select(batch, heads, nr.n_tokens, head_dim, block_size, workspace, workspace_bytes, a);
+  if (st != H3ATTN_OK) return st;
+  a.q = q_out; a.k = k_out;  // what is pooled: the outputs
+  h3attn::launch_qk_norm_rope_pool(nr, tab, a, stream);
+  return check_launch("h3attn_qk_norm_rope_pool");
+}
+
+h3attn_status h3attn_subblock_select_pooled(int32_t batch, int32_t heads, int64_t n_tokens, int32_t head_dim,
+                                            int32_t block_size, double sparsity, int32_t keep,
+                                            int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  h3attn::SelectArgs a;
+  h3attn_status st = prepare_select(batch, heads, n_tokens, head_dim, block_size, workspace, workspace_bytes, a);
+  if (st != H3ATTN_OK) return st;
+  st = prepare_topk(sparsity, keep, block_idx, a);
+  if (st != H3ATTN_OK) return st;
+  h3attn::launch_subblock_select_pooled(a, stream);
+  return check_launch("h3attn_subblock_select_pooled");
 }
 
 static h3attn_status block_sparse_topk(const char* name, const h3attn_bf16* q, const h3attn_bf16* k,

@@ -81,6 +81,11 @@ struct SelectArgs {
 };
 
 void launch_subblock_select(const SelectArgs& a, hipStream_t stream);
+// norm+RoPE of (nr) with the pooling of its output into a's workspace (the selection's first step)
+void launch_qk_norm_rope_pool(const NormRopeArgs& nr, const RopeTable& table, const SelectArgs& a,
+                              hipStream_t stream);
+// the selection after launch_qk_norm_rope_pool: key statistics, top-k, fallback
+void launch_subblock_select_pooled(const SelectArgs& a, hipStream_t stream);
 void launch_threshold_count(const SelectArgs& a, hipStream_t stream);
 void launch_threshold_fill(const SelectArgs& a, hipStream_t stream);
 

@@ -13,6 +13,7 @@
 // flight. The sum of squares is reduced across the D/8 lanes of a row with cross-lane shuffles.
 #include "device_util.h"
 #include "kernels.h"
+#include "norm_rope_math.h"
 
 namespace h3attn {
 namespace {
@@ -59,20 +60,11 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(NormRopeArgs a, 
   }
 
   // Token coordinates on the latent grid (n = (t*H + h)*W + w).
-  const int64_t n = tok % a.n_tokens;
-  const int64_t hw = (int64_t)a.grid_h * a.grid_w;
-  const int64_t pos[3] = {n / hw, (n / a.grid_w) % a.grid_h, n % a.grid_w};
-
+  int64_t pos[3];
+  rope_position(tok % a.n_tokens, a.grid_h, a.grid_w, pos);
   float cs[4], sn[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int pair = 4 * c + p;
-    const double ang = (double)pos[tab.axis[pair]] * tab.rate[pair];
-    // reduce to [-pi, pi] in double so the float sincos stays on its accurate short path
-    const double turns = rint(ang * 0.15915494309189535);  // 1/(2 pi)
-    const float red = (float)fma(-turns, 6.283185307179586, ang);
-    sincosf(red, &sn[p], &cs[p]);
-  }
+  for (int p = 0; p < 4; ++p) rope_pair(pos, 4 * c + p, tab, cs[p], sn[p]);
 
   float wq[8], wk[8];
   {
@@ -89,24 +81,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(NormRopeArgs a, 
     const int r = r0 + i;
     if (r >= rows_total) break;  // uniform across the row group
     const bool is_k = r >= a.heads;
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { v[2 * j] = bf16_lo(x[i][j]); v[2 * j + 1] = bf16_hi(x[i][j]); }
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
-#pragma unroll
-    for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m, TPR);
-    const float rs = rsqrtf(fmaf(ss, inv_d, a.eps));
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float y0 = v[2 * p] * rs * (is_k ? wk[2 * p] : wq[2 * p]);
-      const float y1 = v[2 * p + 1] * rs * (is_k ? wk[2 * p + 1] : wq[2 * p + 1]);
-      const float z0 = fmaf(y0, cs[p], -y1 * sn[p]);
-      const float z1 = fmaf(y0, sn[p], y1 * cs[p]);
-      o[p] = pack_bf16x2(z0, z1);
-    }
+    const u32x4 o = norm_rope_chunk<TPR>(x[i], is_k ? wk : wq, cs, sn, inv_d, a.eps);
     const int head = is_k ? r - a.heads : r;
     uint16_t* dst = (is_k ? a.k_out : a.q_out) + ((tok * a.heads + head) * D + 8 * c);
     store_stream(reinterpret_cast<u32x4*>(dst), o);

@@ -41,6 +41,7 @@
 #include "device_util.h"
 #include "kernels.h"
 #include "launch_util.h"
+#include "norm_rope_math.h"
 
 namespace h3attn {
 namespace {
@@ -66,50 +67,15 @@ __device__ __forceinline__ int64_t n_pad(int32_t nb) { return ((int64_t)nb + kRo
 
 // ------------------------------------------------------------------------------------ pooling
 
-// One workgroup per (batch, tensor, block j, group of heads): thread t owns the 16-byte chunk t of
-// the group's slice of every token row (kPoolThreads * 16 bytes of consecutive heads), so each
-// wave reads 1 KB contiguous per row and the 64 rows stream in with 16 loads in flight per
-// thread. Each thread sums its 8 channels over the block in float64 (exact whenever a channel's
-// nonzero values in the block lie within a factor 2^39 of each other: 8-bit significands, 64
-// terms, 53 bits; always so for data of these workloads' ranges), then the
-// D / 8 threads of a head finish the block: means, max |x|, sum |x| and sum x^2 over the head's
-// channels (a fixed xor-shuffle tree), the digits, exponent and norms. No LDS, no barriers.
+// The end of a block's pooling, shared by pool_kernel and norm_rope_pool_kernel: from the thread's
+// float64 sums acc of its 8 channels over the block's rows (all D/8 threads of the head present),
+// the means, max |x|, sum |x| and sum x^2 over the head's channels (a fixed xor-shuffle tree), the
+// digits, exponent and norms, written to the workspace.
 template <int D>
-__global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
-  constexpr int CH = D / 8;                 // 16-byte chunks per head row
-  constexpr int HPW = kPoolThreads / CH;    // heads per workgroup
-  constexpr int KS = D / 32;                // MFMA k steps
-  constexpr int UNROLL = 16;                // rows in flight per thread
-  const int tid = threadIdx.x;
-  const int groups = (a.heads + HPW - 1) / HPW;
-  const int hg = (int)(blockIdx.x % (unsigned)groups), j = (int)(blockIdx.x / (unsigned)groups);
-  const int tensor = (int)(blockIdx.z & 1u), b = (int)(blockIdx.z >> 1);
-  const int head = hg * HPW + tid / CH, chunk = tid % CH;
-  if (head >= a.heads) return;  // whole heads drop out together (CH divides 64)
-  const int64_t N = a.n_tokens;
-  const int64_t row_stride = (int64_t)a.heads * D;
-  const int64_t t0 = (int64_t)j * a.block_size;
-  const int rows = (int)(t0 + a.block_size < N ? a.block_size : N - t0);
-  const uint16_t* src = (tensor == 0 ? a.q : a.k) + ((int64_t)b * N + t0) * row_stride + (int64_t)head * D + chunk * 8;
-
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  // blocks are 64 tokens (the entry points accept no other size)
-#pragma unroll 1
-  for (int g = 0; g < 64; g += UNROLL) {
-    u32x4 w[UNROLL];
-#pragma unroll
-    for (int i = 0; i < UNROLL; ++i) {
-      w[i] = u32x4{0u, 0u, 0u, 0u};
-      if (g + i < rows) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(g + i) * row_stride));
-    }
-#pragma unroll
-    for (int i = 0; i < UNROLL; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += (double)bf16_lo(w[i][e]);
-        acc[2 * e + 1] += (double)bf16_hi(w[i][e]);
-      }
-  }
+__device__ __forceinline__ void pool_store(const SelectArgs& a, int tensor, int b, int head, int chunk, int j,
+                                           int rows, const double (&acc)[8]) {
+  constexpr int CH = D / 8;
+  constexpr int KS = D / 32;
   const int64_t bh = (int64_t)b * a.heads + head;
   // a full block divides by 64 = 2^6: the product by 2^-6 is the same correctly rounded quotient
   const bool full = rows == 64;
@@ -167,6 +133,135 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
     const float n2 = __double2float_ru(sqrt(l2) * (1.0 + 0x1p-40));
     *reinterpret_cast<float2*>((tensor == 0 ? a.q_norm : a.k_norm) + 2 * r) = float2{n1, n2};
   }
+}
+
+// One workgroup per (batch, tensor, block j, group of heads): thread t owns the 16-byte chunk t of
+// the group's slice of every token row (kPoolThreads * 16 bytes of consecutive heads), so each
+// wave reads 1 KB contiguous per row and the 64 rows stream in with 16 loads in flight per
+// thread. Each thread sums its 8 channels over the block in float64 (exact whenever a channel's
+// nonzero values in the block lie within a factor 2^39 of each other: 8-bit significands, 64
+// terms, 53 bits; always so for data of these workloads' ranges), then the
+// D / 8 threads of a head finish the block (pool_store). No LDS, no barriers.
+template <int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(SelectArgs a) {
+  constexpr int CH = D / 8;                 // 16-byte chunks per head row
+  constexpr int HPW = kPoolThreads / CH;    // heads per workgroup
+  constexpr int UNROLL = 16;                // rows in flight per thread
+  const int tid = threadIdx.x;
+  const int groups = (a.heads + HPW - 1) / HPW;
+  const int hg = (int)(blockIdx.x % (unsigned)groups), j = (int)(blockIdx.x / (unsigned)groups);
+  const int tensor = (int)(blockIdx.z & 1u), b = (int)(blockIdx.z >> 1);
+  const int head = hg * HPW + tid / CH, chunk = tid % CH;
+  if (head >= a.heads) return;  // whole heads drop out together (CH divides 64)
+  const int64_t N = a.n_tokens;
+  const int64_t row_stride = (int64_t)a.heads * D;
+  const int64_t t0 = (int64_t)j * a.block_size;
+  const int rows = (int)(t0 + a.block_size < N ? a.block_size : N - t0);
+  const uint16_t* src = (tensor == 0 ? a.q : a.k) + ((int64_t)b * N + t0) * row_stride + (int64_t)head * D + chunk * 8;
+
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // blocks are 64 tokens (the entry points accept no other size)
+#pragma unroll 1
+  for (int g = 0; g < 64; g += UNROLL) {
+    u32x4 w[UNROLL];
+#pragma unroll
+    for (int i = 0; i < UNROLL; ++i) {
+      w[i] = u32x4{0u, 0u, 0u, 0u};
+      if (g + i < rows) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(g + i) * row_stride));
+    }
+#pragma unroll
+    for (int i = 0; i < UNROLL; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)bf16_lo(w[i][e]);
+        acc[2 * e + 1] += (double)bf16_hi(w[i][e]);
+      }
+  }
+  pool_store<D>(a, tensor, b, head, chunk, j, rows, acc);
+}
+
+// QK RMSNorm + 3D RoPE with the SubBlock pooling of its output in the same pass: the pooling's
+// own read of q' and k' (4 B N heads D bytes) disappears. Same workgroups and lanes as
+// pool_kernel; for every row of the block a thread loads its chunk of q (or k), normalises and
+// rotates it exactly as the stand-alone kernel does (norm_rope_chunk, so the bits are the same),
+// stores it, and adds the rounded bf16 outputs to its float64 sums. The rotation's cos and sin
+// depend on the token and the channel pair, not on the head, so the workgroup computes them once
+// for its 64 rows into LDS (64 x CH x 4 pairs), while the first 16 rows' loads are in flight
+// (measured 2 % faster than computing the table first; 8 rows in flight or a two-group prefetch
+// pipeline measured the same as the table first).
+template <int D>
+__global__ __launch_bounds__(kPoolThreads) void norm_rope_pool_kernel(NormRopeArgs nr, RopeTable tab, SelectArgs a) {
+  constexpr int CH = D / 8;
+  constexpr int HPW = kPoolThreads / CH;
+  constexpr int UNROLL = 16;                // rows in flight per thread
+  __shared__ float2 s_rot[64][CH][4];       // (cos, sin) per row, chunk and pair
+  const int tid = threadIdx.x;
+  const int groups = (a.heads + HPW - 1) / HPW;
+  const int hg = (int)(blockIdx.x % (unsigned)groups), j = (int)(blockIdx.x / (unsigned)groups);
+  const int tensor = (int)(blockIdx.z & 1u), b = (int)(blockIdx.z >> 1);
+  const int head = hg * HPW + tid / CH, chunk = tid % CH;
+  const int64_t N = a.n_tokens;
+  const int64_t row_stride = (int64_t)a.heads * D;
+  const int64_t t0 = (int64_t)j * a.block_size;
+  const int rows = (int)(t0 + a.block_size < N ? a.block_size : N - t0);
+  const bool live = head < a.heads;         // whole heads (CH lanes) are live or not
+  const int64_t off = ((int64_t)b * N + t0) * row_stride + (int64_t)(live ? head : 0) * D + chunk * 8;
+  const uint16_t* src = (tensor == 0 ? nr.q_in : nr.k_in) + off;
+  uint16_t* dst = (tensor == 0 ? nr.q_out : nr.k_out) + off;
+
+  u32x4 x[UNROLL];
+  auto load_rows = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < UNROLL; ++i) {
+      x[i] = u32x4{0u, 0u, 0u, 0u};
+      if (live && g + i < rows)
+        x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(g + i) * row_stride));
+    }
+  };
+  load_rows(0);
+  for (int i = tid; i < rows * CH * 4; i += kPoolThreads) {
+    const int r = i / (CH * 4), cc = (i / 4) % CH, p = i % 4;
+    int64_t pos[3];
+    rope_position(t0 + r, nr.grid_h, nr.grid_w, pos);
+    float cs, sn;
+    rope_pair(pos, 4 * cc + p, tab, cs, sn);
+    s_rot[r][cc][p] = float2{cs, sn};
+  }
+  __syncthreads();
+  if (!live) return;
+
+  float w[8];
+  {
+    const f32x4* wp = reinterpret_cast<const f32x4*>((tensor == 0 ? nr.q_weight : nr.k_weight) + 8 * chunk);
+    const f32x4 w0 = wp[0], w1 = wp[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { w[e] = w0[e]; w[4 + e] = w1[e]; }
+  }
+  const float inv_d = 1.0f / (float)D;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 1
+  for (int g = 0; g < 64; g += UNROLL) {
+    if (g > 0) load_rows(g);
+#pragma unroll
+    for (int i = 0; i < UNROLL; ++i) {
+      if (g + i >= rows) break;  // uniform across the workgroup
+      float cs[4], sn[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float2 t = s_rot[g + i][chunk][p];
+        cs[p] = t.x;
+        sn[p] = t.y;
+      }
+      const u32x4 o = norm_rope_chunk<CH>(x[i], w, cs, sn, inv_d, nr.eps);
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + (int64_t)(g + i) * row_stride));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)bf16_lo(o[e]);
+        acc[2 * e + 1] += (double)bf16_hi(o[e]);
+      }
+    }
+  }
+  pool_store<D>(a, tensor, b, head, chunk, j, rows, acc);
 }
 
 // Per (batch, head): the largest key exponent F and the largest key norms (for the bounds); then
@@ -1159,11 +1254,16 @@ __global__ __launch_bounds__(kScanThreads) void row_ptr_scan_kernel(SelectArgs a
   if (tid == 0) a.row_ptr[rows] = s_carry;
 }
 
+// pooling grid: (block, head group) x 1 x (batch, tensor)
+template <int D>
+dim3 pool_grid(const SelectArgs& a) {
+  const unsigned groups = (unsigned)((a.heads + kPoolThreads / (D / 8) - 1) / (kPoolThreads / (D / 8)));
+  return dim3((unsigned)a.n_blocks * groups, 1, 2u * (unsigned)a.batch);
+}
+
 template <int D>
 void launch_pool(const SelectArgs& a, hipStream_t stream) {
-  const unsigned groups = (unsigned)((a.heads + kPoolThreads / (D / 8) - 1) / (kPoolThreads / (D / 8)));
-  const dim3 g3((unsigned)a.n_blocks * groups, 1, 2u * (unsigned)a.batch);
-  hipLaunchKernelGGL(pool_kernel<D>, g3, dim3(kPoolThreads), 0, stream, a);
+  hipLaunchKernelGGL(pool_kernel<D>, pool_grid<D>(a), dim3(kPoolThreads), 0, stream, a);
   hipLaunchKernelGGL(key_stats_kernel, dim3((unsigned)(a.batch * a.heads)), dim3(256), 0, stream, a);
 }
 
@@ -1174,9 +1274,10 @@ size_t topk_dyn_lds(int32_t nb) {
   return hist > classify ? hist : classify;
 }
 
+// the selection after the pooling kernel: key statistics, top-k, fallback
 template <int D>
-void launch_topk(const SelectArgs& a, hipStream_t stream) {
-  launch_pool<D>(a, stream);
+void launch_topk_pooled(const SelectArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(key_stats_kernel, dim3((unsigned)(a.batch * a.heads)), dim3(256), 0, stream, a);
   const dim3 grid((unsigned)((a.n_blocks + kRows - 1) / kRows), (unsigned)(a.batch * a.heads));
   const size_t lds = topk_dyn_lds(a.n_blocks);
   // the dynamic-LDS limit plus the kernel's static LDS (RowState) must stay within a CU's 160 KB
@@ -1185,6 +1286,12 @@ void launch_topk(const SelectArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(topk_select_kernel<D>, grid, dim3(kSelThreads), lds, stream, a);
   allow_dynamic_lds(reinterpret_cast<const void*>(fallback_kernel<D>), (int)kSelectRowLdsBytes);
   hipLaunchKernelGGL(fallback_kernel<D>, dim3(256), dim3(kFbThreads), (size_t)a.n_blocks * 8, stream, a);
+}
+
+template <int D>
+void launch_topk(const SelectArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(pool_kernel<D>, pool_grid<D>(a), dim3(kPoolThreads), 0, stream, a);
+  launch_topk_pooled<D>(a, stream);
 }
 
 template <int D>
@@ -1209,6 +1316,19 @@ void launch_thr_fill(const SelectArgs& a, hipStream_t stream) {
 void launch_subblock_select(const SelectArgs& a, hipStream_t stream) {
   if (a.head_dim == 128) launch_topk<128>(a, stream);
   else launch_topk<64>(a, stream);
+}
+
+void launch_qk_norm_rope_pool(const NormRopeArgs& nr, const RopeTable& table, const SelectArgs& a,
+                              hipStream_t stream) {
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL(norm_rope_pool_kernel<128>, pool_grid<128>(a), dim3(kPoolThreads), 0, stream, nr, table, a);
+  else
+    hipLaunchKernelGGL(norm_rope_pool_kernel<64>, pool_grid<64>(a), dim3(kPoolThreads), 0, stream, nr, table, a);
+}
+
+void launch_subblock_select_pooled(const SelectArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) launch_topk_pooled<128>(a, stream);
+  else launch_topk_pooled<64>(a, stream);
 }
 
 void launch_threshold_count(const SelectArgs& a, hipStream_t stream) {
