@@ -132,7 +132,23 @@ int main(int argc, char** argv) {
   int32_t* didx = device_alloc<int32_t>(idx_count);
   H3_OK(h3attn_subblock_select(dqo, dko, batch, heads, n, head_dim, 64, sparsity, keep, didx, ws, ws_bytes, stream));
   H3_OK(h3attn_block_sparse_fwd(dqo, dko, dv, didx, keep, dsparse, nullptr, batch, heads, n, head_dim, 64, stream));
+
+  // the same selection with the pooling inside the norm+RoPE pass: q', k' and the kept sets must be
+  // the same bits as the stand-alone calls' above
+  h3attn_bf16* dqo2 = device_alloc<h3attn_bf16>(elems);
+  h3attn_bf16* dko2 = device_alloc<h3attn_bf16>(elems);
+  int32_t* didx2 = device_alloc<int32_t>(idx_count);
+  void* ws2 = device_alloc<unsigned char>(ws_bytes);
+  H3_OK(h3attn_qk_norm_rope_pool(dq, dk, dqo2, dko2, dwq, dwk, batch, heads, head_dim, grid, hdr[6], hdr[7], hdr[8],
+                                 theta_eps[0], theta_eps[1], 64, ws2, ws_bytes, stream));
+  H3_OK(h3attn_subblock_select_pooled(batch, heads, n, head_dim, 64, sparsity, keep, didx2, ws2, ws_bytes, stream));
   HIP_OK(hipStreamSynchronize(stream));
+  if (host_copy(dqo, elems) != host_copy(dqo2, elems) || host_copy(dko, elems) != host_copy(dko2, elems) ||
+      host_copy(didx, idx_count) != host_copy(didx2, idx_count)) {
+    std::fprintf(stderr, "the pooled path differs from the stand-alone calls\n");
+    return 4;
+  }
+  for (void* p : {(void*)dqo2, (void*)dko2, (void*)didx2, ws2}) HIP_OK(hipFree(p));
 
   FILE* out = std::fopen(argv[2], "wb");
   if (!out) {
@@ -152,7 +168,8 @@ int main(int argc, char** argv) {
                   (void*)dsparse, (void*)dlse, ws, (void*)didx})
     HIP_OK(hipFree(p));
   HIP_OK(hipStreamDestroy(stream));
-  std::printf("c_abi_consumer: %s ok (N=%lld, heads=%d, D=%d, keep=%d)\n", h3attn_version(), (long long)n, heads,
+  std::printf("c_abi_consumer: %s ok (N=%lld, heads=%d, D=%d, keep=%d; pooled path identical)\n", h3attn_version(),
+              (long long)n, heads,
               head_dim, keep);
   return 0;
 }

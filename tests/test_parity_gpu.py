@@ -1000,7 +1000,9 @@ def test_c_program_drives_the_path_through_the_c_abi(h3, tmp_path):
     """tests/c_abi_consumer.cpp (built by __graft_entry__.build()) is a host program with no Python
     or torch: it allocates its own device buffers and stream and runs norm+RoPE -> dense -> select ->
     block-sparse through the four entry points. Its outputs on a ragged two-batch case (N = 240,
-    a partial last block) are checked against the oracle."""
+    a partial last block) are checked against the oracle. It also runs the selection with the
+    pooling inside the norm+RoPE pass and exits nonzero unless q', k' and the kept sets are the
+    same bits as the stand-alone calls'."""
     import os
     import subprocess
     exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_build", "c_abi_consumer")
