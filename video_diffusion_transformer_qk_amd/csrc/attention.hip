@@ -5,19 +5,22 @@
 // (xiaodao.ai), section "6.24 倍里，真正有损的部分大约是三倍" — SubBlock sends only the kept
 // 64-token key blocks of each query block to a block-sparse attention kernel.
 //
-// Formulation. Each wave owns 32 query rows and computes the transposed score tile
+// Formulation. Each wave owns 32 query rows (two 16-query column tiles) and computes the
+// transposed score tile
 //   S^T (keys x queries) = K (keys x D) . Q^T (D x queries)
-// with v_mfma_f32_32x32x16_bf16, K as the A operand (read from LDS) and Q^T as the B operand
-// (held in registers for the whole loop). In the MFMA accumulator layout a lane holds one query
-// column and 16 key rows, so the softmax row statistics are mostly per-lane: the max needs one
-// exchange with the lane 32 away, and the row sum stays a per-lane partial until the epilogue.
-// The exponentials P^T are converted to bf16 in place and used directly as the B operand of
+// with v_mfma_f32_16x16x32_bf16 on 16x16 tiles, K as the A operand (read from LDS, each fragment
+// used for both query tiles) and Q^T as the B operand (held in registers for the whole loop). In
+// the accumulator layout a lane holds 4 keys of each 16-key tile for one query per query tile, so
+// a query's row statistics span the 4 lanes l, l^16, l^32, l^48 (two cross-lane swaps for the
+// max; the row sum stays a per-lane partial until the epilogue). The exponentials P^T are
+// converted to bf16 in place and used directly as the B operand of
 //   O^T (D x queries) += V^T (D x keys) . P^T (keys x queries),
 // whose A operand (V^T) is read from a row-major V tile with the gfx950 LDS transpose read
-// (ds_read_b64_tr_b16). The key order inside each 16-key MFMA step is permuted identically on
+// (ds_read_b64_tr_b16). The key order inside each 32-key MFMA step is permuted identically on
 // both operands so that it matches the registers that already hold P^T. The softmax uses exp2
 // with log2(e)/sqrt(D) folded into one FMA, and the running max only moves (with a wave-uniform
-// O rescale) when a tile exceeds it by more than 2^8.
+// O rescale) when a tile exceeds it by more than 2^8. (The same work on 32x32x16 tiles, one query
+// per lane, measured 2.5 % slower.)
 //
 // Pipeline: tile t+1 is loaded from global memory straight into the other half of a
 // double-buffered LDS tile while tile t is computed (one barrier per tile). Dense:
@@ -37,54 +40,19 @@ constexpr int kBN = 64;  // keys per tile (= SubBlock block size)
 
 #define kOnes2 (__builtin_bit_cast(bf16x2, 0x3f803f80u))  // bf16 pair (1.0, 1.0)
 
-// One wave's share of the forward pass: 32 query rows, their Q^T fragments (B operand, one
-// bf16x8 per 16-wide k step), the O^T accumulator and the running softmax statistics.
-template <int D>
-struct WaveRows {
-  static constexpr int KSTEPS = D / 16;
-  static constexpr int DT = D / 32;
-  bf16x8 qf[KSTEPS];
-  f32x16 o[DT];
-  float m_run;  // running max of s*sc (log2 units), shared by lanes l and l^32
-  float l_part[4];  // per-lane partial row sums, four independent chains across all tiles
-};
-
-template <int D>
-__device__ __forceinline__ void rows_begin(WaveRows<D>& w, const uint16_t* qp) {
-#pragma unroll
-  for (int ks = 0; ks < WaveRows<D>::KSTEPS; ++ks)
-    w.qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
-#pragma unroll
-  for (int dt = 0; dt < WaveRows<D>::DT; ++dt) w.o[dt] = f32x16{};
-  w.m_run = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) w.l_part[j] = 0.f;
-}
-
-// Where a lane's operands sit in a K/V tile in LDS, for the MFMA fragment reads.
-//
-// qk_tile's fragment i (k step i/2, 32-key half i%2): this lane's key row 32 (i%2) + lane%32 and
-// its 16-byte chunk 2 (i/2) + lane/32 of the K row. pv_tile's read (16-key step kk, 32-channel
-// step dt): within each group of 16 lanes, 4 rows x 4 8-byte pieces of V, the lane's row
-// 16 kk + 4 (lane/32) + (lane%16)/4 and channels 32 dt + 16 ((lane/16)%2) + 4 (lane%4); the second
-// read of the pair is 8 rows further.
-//
-// SwzLayout: unpadded rows of 2D bytes (CPR = D/8 chunks), filled by direct global -> LDS loads,
-// which write each wave instruction's 64 x 16 bytes to consecutive LDS addresses, so rows cannot
-// be padded. The chunks of a row are rotated instead, so that the chunks one read instruction
-// touches fall on distinct banks (the bank positions of rows padded to 17 (K) or 20 (V) chunks):
+// SwzLayout: the K and V tiles of 64 keys in LDS, unpadded rows of 2D bytes (CPR = D/8 chunks),
+// filled by direct global -> LDS loads, which write each wave instruction's 64 x 16 bytes to
+// consecutive LDS addresses, so rows cannot be padded. The chunks of a row are rotated instead,
+// so that the chunks one read instruction touches fall on distinct banks (the bank positions of
+// rows padded to 17 (K) or 20 (V) chunks):
 //   K: chunk c of row r at column (c + r) mod 16 (D = 128) or (c + r/2) mod 8 (D = 64);
 //   V: chunk c of row r at column (c + 4r) mod 16 (D = 128) or (c + 4 (r/2)) mod 8 (D = 64).
-// A lane's columns depend only on the lane and the k (channel) step, never on the 32-key half or
-// the 16-key step, so the offsets are computed once per kernel (D/16 for K, D/32 for V) and the
-// steps add constants.
 template <int D>
 struct SwzLayout {
   static constexpr int ROW = 2 * D;
   static constexpr int CPR = D / 8;
   static constexpr int K_BYTES = kBN * ROW;
   static constexpr int BUF_BYTES = 2 * K_BYTES;
-  static constexpr int V8 = 8 * ROW;
   __device__ static __forceinline__ int kcol(int r, int c) {
     return D == 128 ? (c + r) & 15 : (c + (r >> 1)) & 7;
   }
@@ -98,175 +66,188 @@ struct SwzLayout {
   __device__ static __forceinline__ int vchunk(int r, int col) {
     return D == 128 ? (col - 4 * r) & 15 : (col - 4 * (r >> 1)) & 7;
   }
-  int koff[D / 16], voff[D / 32];
-  __device__ __forceinline__ explicit SwzLayout(int lane) {
-    const int l32 = lane & 31, hi = lane >> 5, ig = lane & 15, g16 = (lane >> 4) & 1;
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) koff[k] = l32 * ROW + kcol(l32, 2 * k + hi) * 16;
-    const int r = 4 * hi + (ig >> 2);  // the row inside the 16-key step; 16 kk adds whole rotations
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const int byte = (32 * dt + 16 * g16 + 4 * (ig & 3)) * 2;
-      voff[dt] = r * ROW + vcol(r, byte / 16) * 16 + byte % 16;
-    }
-  }
-  __device__ __forceinline__ int kfrag(int i) const { return koff[i >> 1] + (i & 1) * 32 * ROW; }
-  __device__ __forceinline__ int vfrag(int kk, int dt) const { return 16 * kk * ROW + voff[dt]; }
 };
 
-// The three parts of one 64-key tile for one wave. qk_tile: S^T = K . Q^T from the K tile at kb.
-// The K fragments (k step ks, 32-key half m) are read in MFMA order through a ring of kQkInFlight
-// registers, and the schedule is pinned (kQkInFlight reads, then one MFMA per read, then the
-// last MFMAs): left alone, the compiler reuses one register quad and every MFMA waits for its
-// own LDS read (3 % slower at 4 reads in flight).
-constexpr int kQkInFlight = 4;
-template <int D, typename L>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const bf16x8 (&qf)[D / 16], const unsigned char* kb,
-                                        const L& lay) {
-  constexpr int NF = 2 * (D / 16);  // fragments i = 2 ks + m
-  constexpr int PF = kQkInFlight;
-  auto frag = [&](int i) { return *reinterpret_cast<const bf16x8*>(kb + lay.kfrag(i)); };
-  s[0] = f32x16{};
-  s[1] = f32x16{};
-  bf16x8 kf[PF];
-#pragma unroll
-  for (int i = 0; i < PF; ++i) kf[i] = frag(i);
-#pragma unroll
-  for (int i = 0; i < NF; ++i) {
-    s[i & 1] = mfma32x32x16(kf[i % PF], qf[i >> 1], s[i & 1]);
-    if (i + PF < NF) kf[i % PF] = frag(i + PF);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // LDS reads
-#pragma unroll
-  for (int i = 0; i < NF - PF; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// max and sum over the lanes l, l^16, l^32 and l^48 (the four lanes that hold one query)
+__device__ __forceinline__ float quad_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return pair_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return pair_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
-// Keys at or past N get a score of -inf; only called for the tile that holds the last token,
-// so the number of valid keys in it, N - key0, is below 64.
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int64_t key0, int64_t N, int lane) {
-  const int valid = (int)(N - key0) - 4 * (lane >> 5);  // valid keys counted from this lane's first row
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (32 * m + 8 * (r / 4) + (r % 4) >= valid) s[m][r] = -INFINITY;
-}
-
-// Online softmax of one score tile in the log2 domain (sc = log2(e)/sqrt(D)), in two parts.
-// softmax_max moves the running max and rescales O and the row sum. The running max only moves
-// when the tile max exceeds it by more than 8 (a factor 256): until then exp2 values stay <= 256,
-// which fp32 sums and bf16 P hold exactly enough, and the rescale (a wave-uniform branch) is
-// skipped.
+// One wave's share of the forward pass: 32 query rows q0 .. q0+31 as two 16-query tiles, their
+// Q^T fragments (B operand: [query tile][32-channel step]), the O^T accumulators ([16-channel
+// tile][query tile]), the running softmax statistics per query tile, and the lane's LDS read
+// offsets. Lane l holds query 16 qt + l%16 of each tile; within a 16-key (16-channel) MFMA tile,
+// rows 4 (l/16) .. +3.
+// K fragment of k step ks, 16-key tile kt: key row 16 kt + l%16, chunk 4 ks + l/16 (koff[ks]; kt
+// adds whole rotations). V transpose reads of 32-key step s, 16-channel tile dt: within each group
+// of 16 lanes, rows 32 s + 4 (l/16) + s' (s' = 0..3, then the same + 16) at channels 16 dt + l%16
+// (voff[dt]).
 template <int D>
-__device__ __forceinline__ void softmax_max(WaveRows<D>& w, const f32x16 (&s)[2], float sc) {
-  // tile max as a shallow tree (independent partial maxima) rather than one long chain
-  float mp[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) mp[j] = fmaxf(s[0][4 * j], s[0][4 * j + 1]);
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (m > 0 || (r % 4) >= 2) mp[r / 4] = fmaxf(mp[r / 4], s[m][r]);
-  float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-  mx = pair_max(mx) * sc;
-  if (__any(mx > w.m_run + 8.0f)) {
-    const float m_new = fmaxf(w.m_run, mx);
-    const float alpha = fast_exp2(w.m_run - m_new);
-    w.m_run = m_new;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w.l_part[j] *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) w.o[dt][r] *= alpha;
-  }
-}
+struct WaveRows {
+  bf16x8 qf[2][D / 32];
+  f32x4 o[D / 16][2];
+  float m_run[2];     // running max of s*sc (log2 units) per query tile, shared by the query's 4 lanes
+  float l_part[2][2]; // per-lane partial row sums, two chains per query tile across all tiles
+  int koff[D / 32];
+  int voff[D / 16];
+};
 
-// softmax_exp: P^T = exp2(s*sc - m_run) as bf16 (pk, 8 values per 16-key step: step kk covers
-// s[kk/2] regs 8*(kk%2) .. +7). The row sum of the bf16-rounded P that P.V uses is accumulated
-// with packed dot products against (1, 1) straight into the wave's four running per-lane
-// chains, which are added up only in the epilogue.
-__device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2], u32x4 (&pk)[4], float m_run, float sc,
-                                                float (&lp)[4]) {
+template <int D>
+__device__ __forceinline__ void rows_begin(WaveRows<D>& w, const uint16_t* q, int64_t base, int64_t q0, int64_t N,
+                                           int64_t row_stride, int lane) {
+  using L = SwzLayout<D>;
+  const int i16 = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int qt = 0; qt < 2; ++qt) {
+    int64_t my = q0 + 16 * qt + i16;
+    my = my < N ? my : N - 1;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(fmaf(s[m][r], sc, -m_run));
-      const float p1 = fast_exp2(fmaf(s[m][r + 1], sc, -m_run));
-      const uint32_t pp = pack_bf16x2(p0, p1);
-      pk[2 * m + r / 8][(r % 8) / 2] = pp;
-      lp[(r / 2) % 4] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnes2, lp[(r / 2) % 4], false);
-    }
+    for (int ks = 0; ks < D / 32; ++ks)
+      w.qf[qt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + base + my * row_stride + 32 * ks + 8 * g));
   }
-}
-
-// O^T += V^T . P^T with V^T read from the row-major V tile at vb through the LDS transpose read;
-// the key order inside each 16-key step matches the registers that hold P^T.
-template <int D, typename L>
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const u32x4 (&pk)[4], const unsigned char* vb,
-                                        const L& lay) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[kk]);
+  for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const unsigned char* p1 = vb + lay.vfrag(kk, dt);
-      const i16x4 lo = lds_read_tr16(p1);
-      const i16x4 hi4 = lds_read_tr16(p1 + L::V8);
-      typedef __attribute__((ext_vector_type(8))) short i16x8;
-      const i16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, vv), pb, o[dt]);
-    }
+    for (int qt = 0; qt < 2; ++qt) w.o[dt][qt] = f32x4{};
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    w.m_run[qt] = -INFINITY;
+    w.l_part[qt][0] = w.l_part[qt][1] = 0.f;
+  }
+  // the rotations depend on bits of the row that 16-key and 32-key steps leave unchanged
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) w.koff[ks] = i16 * L::ROW + L::kcol(i16, 4 * ks + g) * 16;
+  const int r = 4 * g + (i16 >> 2);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const int byte = 32 * dt + 8 * (i16 & 3);
+    w.voff[dt] = r * L::ROW + L::vcol(r, byte / 16) * 16 + byte % 16;
   }
 }
 
 // One K/V tile of 64 keys (K rows at kb, V rows at vb in LDS; first key key0) applied to the
 // wave's rows: S^T = K . Q^T, online softmax, O^T += V^T . P^T. `partial` (wave-uniform) marks
-// the tile that holds the last token when N is not a multiple of 64.
-template <int D, int BN, typename L>
+// the tile that holds the last token when N is not a multiple of 64: keys at or past N get a
+// score of -inf. The running max only moves when the tile max exceeds it by more than 8 (a factor
+// 256): until then exp2 values stay <= 256, which fp32 sums and bf16 P hold exactly enough, and
+// the rescale (a wave-uniform branch) is skipped. The row sum of the bf16-rounded P that P.V uses
+// is accumulated with packed dot products against (1, 1).
+template <int D>
 __device__ __forceinline__ void rows_tile(WaveRows<D>& w, const unsigned char* kb, const unsigned char* vb,
-                                          int64_t key0, int64_t N, bool partial, int lane, float sc, const L& lay) {
-  static_assert(BN == kBN, "64-key tiles");
-  f32x16 s[2];
-  qk_tile<D>(s, w.qf, kb, lay);
-  if (partial) mask_tile(s, key0, N, lane);
-  softmax_max(w, s, sc);
-  u32x4 pk[4];
-  softmax_exp(s, pk, w.m_run, sc, w.l_part);
-  pv_tile<D>(w.o, pk, vb, lay);
+                                          int64_t key0, int64_t N, bool partial, int lane, float sc) {
+  using L = SwzLayout<D>;
+  const int g = lane >> 4;
+  f32x4 s[4][2];  // [16-key tile][query tile]
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) s[kt][qt] = f32x4{};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    bf16x8 a[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) a[kt] = *reinterpret_cast<const bf16x8*>(kb + 16 * kt * L::ROW + w.koff[ks]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma16x16x32(a[kt], w.qf[qt][ks], s[kt][qt]);
+  }
+  if (partial) {
+    const int valid = (int)(N - key0);  // below 64
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * kt + 4 * g + i >= valid) {
+          s[kt][0][i] = -INFINITY;
+          s[kt][1][i] = -INFINITY;
+        }
+  }
+  bf16x8 pb[2][2];  // P^T B operands [query tile][32-key step]
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float mt[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) mt[kt] = fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3]));
+    const float mx = quad_max(fmaxf(fmaxf(mt[0], mt[1]), fmaxf(mt[2], mt[3]))) * sc;
+    if (__any(mx > w.m_run[qt] + 8.0f)) {
+      const float m_new = fmaxf(w.m_run[qt], mx);
+      const float alpha = fast_exp2(w.m_run[qt] - m_new);
+      w.m_run[qt] = m_new;
+      w.l_part[qt][0] *= alpha;
+      w.l_part[qt][1] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w.o[dt][qt][i] *= alpha;
+    }
+    const float mr = w.m_run[qt];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      u32x4 pk;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // operand bytes 0..7: keys 32 ks2 + 4 g + i; 8..15: the same + 16
+        const f32x4 t = s[2 * ks2 + h][qt];
+        const uint32_t p01 = pack_bf16x2(fast_exp2(fmaf(t[0], sc, -mr)), fast_exp2(fmaf(t[1], sc, -mr)));
+        const uint32_t p23 = pack_bf16x2(fast_exp2(fmaf(t[2], sc, -mr)), fast_exp2(fmaf(t[3], sc, -mr)));
+        pk[2 * h] = p01;
+        pk[2 * h + 1] = p23;
+        w.l_part[qt][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p01), kOnes2, w.l_part[qt][0], false);
+        w.l_part[qt][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p23), kOnes2, w.l_part[qt][1], false);
+      }
+      pb[qt][ks2] = __builtin_bit_cast(bf16x8, pk);
+    }
+  }
+#pragma unroll
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const unsigned char* p1 = vb + 32 * ks2 * L::ROW + w.voff[dt];
+      const i16x4 lo = lds_read_tr16(p1);
+      const i16x4 hi4 = lds_read_tr16(p1 + 16 * L::ROW);
+      typedef __attribute__((ext_vector_type(8))) short i16x8;
+      const i16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      const bf16x8 av = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) w.o[dt][qt] = mfma16x16x32(av, pb[qt][ks2], w.o[dt][qt]);
+    }
+  }
 }
 
-// Epilogue: combine the two lane-partial sums, normalise and store query row my_q if it is
+// Epilogue: combine the lane-partial sums over the query's 4 lanes, normalise and store the rows
 // inside the sequence (out: the output tensor at the (batch, head) base; lse_row: the LSE row of
-// the (batch, head), or null). A row that saw no key (an empty kept set) is written as zeros
-// with LSE -inf.
+// the (batch, head), or null). Rows that saw no key (an empty kept set) are written as zeros with
+// LSE -inf.
 template <int D>
-__device__ __forceinline__ void rows_end(const WaveRows<D>& w, uint16_t* out, float* lse_row, int64_t my_q,
-                                         int64_t N, int64_t row_stride, bool empty, int hi) {
-  constexpr int DT = D / 32;
-  const float l_tot = pair_sum((w.l_part[0] + w.l_part[1]) + (w.l_part[2] + w.l_part[3]));
-  const float inv = empty ? 0.f : 1.0f / l_tot;
-  if (my_q >= N) return;
-  uint16_t* op = out + my_q * row_stride;
-  float* lse_p = lse_row != nullptr ? lse_row + my_q : nullptr;
+__device__ __forceinline__ void rows_end(const WaveRows<D>& w, uint16_t* out, float* lse_row, int64_t q0,
+                                         int64_t N, int64_t row_stride, bool empty, int lane) {
+  const int i16 = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int qt = 0; qt < 2; ++qt) {
+    const float l_tot = quad_sum(w.l_part[qt][0] + w.l_part[qt][1]);
+    const float inv = empty ? 0.f : 1.0f / l_tot;
+    const int64_t my = q0 + 16 * qt + i16;
+    if (my < N) {
+      uint16_t* op = out + my * row_stride;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = 32 * dt + 8 * g + 4 * hi;
-      u32x2 v;
-      v[0] = pack_bf16x2(w.o[dt][4 * g + 0] * inv, w.o[dt][4 * g + 1] * inv);
-      v[1] = pack_bf16x2(w.o[dt][4 * g + 2] * inv, w.o[dt][4 * g + 3] * inv);
-      *reinterpret_cast<u32x2*>(op + d) = v;
+      for (int dt = 0; dt < D / 16; ++dt) {
+        u32x2 v;
+        v[0] = pack_bf16x2(w.o[dt][qt][0] * inv, w.o[dt][qt][1] * inv);
+        v[1] = pack_bf16x2(w.o[dt][qt][2] * inv, w.o[dt][qt][3] * inv);
+        *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * g) = v;
+      }
+      if (lse_row != nullptr && g == 0)
+        lse_row[my] = empty ? -INFINITY : (w.m_run[qt] + __log2f(l_tot)) * 0.6931471805599453f;
     }
-  if (lse_p != nullptr && hi == 0)
-    *lse_p = empty ? -INFINITY : (w.m_run + __log2f(l_tot)) * 0.6931471805599453f;
+  }
 }
 
 // Direct global -> LDS staging of one K/V tile into the SwzLayout (gfx950 global_load_lds_dwordx4:
@@ -333,8 +314,6 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
 
   const int64_t N = a.n_tokens;
   const int64_t qtile = blockIdx.x;
@@ -342,16 +321,14 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
   const int64_t row_stride = (int64_t)a.heads * D;  // elements between consecutive tokens
   const int64_t base = ((int64_t)b * N) * row_stride + (int64_t)head * D;
 
-  const int64_t my_q = qtile * (WAVES * 32) + wave * 32 + l32;
-  const int64_t my_q_c = my_q < N ? my_q : N - 1;
+  const int64_t q0 = qtile * (WAVES * 32) + wave * 32;  // the wave's first query row
   WaveRows<D> w;
-  rows_begin(w, a.q + base + my_q_c * row_stride + 8 * hi);
+  rows_begin(w, a.q, base, q0, N, row_stride, lane);
 
   const int n_tiles = (int)((N + kBN - 1) / kBN);
   const int last_partial = N % kBN ? n_tiles - 1 : -1;  // the tile to mask, if any
   TileDma<D, NT> dma;
   dma.init(tid, row_stride);
-  const L lay(lane);
   const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
 
   // LDS byte address of the tile buffers
@@ -365,12 +342,12 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
     if (t + 1 < n_tiles)
       dma.fetch(a.k, a.v, base, (int64_t)(t + 1) * kBN, N, row_stride, smem_lds + (buf ^ 1) * L::BUF_BYTES);
     const unsigned char* kb = smem + buf * L::BUF_BYTES;
-    rows_tile<D, kBN>(w, kb, kb + L::K_BYTES, (int64_t)t * kBN, N, t == last_partial, lane, sc, lay);
+    rows_tile<D>(w, kb, kb + L::K_BYTES, (int64_t)t * kBN, N, t == last_partial, lane, sc);
     wait_dma();
     __syncthreads();
   }
-  rows_end(w, a.out + base, a.lse != nullptr ? a.lse + ((int64_t)b * a.heads + head) * N : nullptr, my_q, N,
-           row_stride, false, hi);
+  rows_end(w, a.out + base, a.lse != nullptr ? a.lse + ((int64_t)b * a.heads + head) * N : nullptr, q0, N,
+           row_stride, false, lane);
 }
 
 // Block-sparse attention over groups of G query blocks per workgroup (2 waves per block, 32
@@ -399,8 +376,6 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
 
   const int64_t N = a.n_tokens;
   const int64_t nb = a.n_blocks;
@@ -412,8 +387,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
   const int half = (wave >> 1) & 1;               // and its 32-query half
   const int64_t row0 = ((int64_t)b * a.heads + head) * nb;
   const int64_t qb = group_block<G>(blockIdx.x, gblk, a.group_stride, nb);
-  const int64_t my_q = (qb < 0 ? 0 : qb) * kBN + half * 32 + l32;
-  const int64_t my_q_c = my_q < N ? my_q : N - 1;
+  const int64_t q0 = (qb < 0 ? 0 : qb) * kBN + half * 32;  // the wave's first query row
 
   // the kept list of each block of the group inside block_idx, in LDS; this wave's own length
   __shared__ int64_t s_range[2 * G];
@@ -423,10 +397,9 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
   const int64_t my_count = my_end - my_beg;
 
   WaveRows<D> w;
-  rows_begin(w, a.q + base + my_q_c * row_stride + 8 * hi);
+  rows_begin(w, a.q, base, q0, N, row_stride, lane);
   TileDma<D, NT> dma;
   dma.init(tid, row_stride);
-  const L lay(lane);
   const uint32_t smem_lds = lds_address(smem);
   const float sc = 1.4426950408889634f / sqrtf((float)D);
   const uint32_t my_bit = 1u << gblk;
@@ -450,15 +423,15 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
         // a 64-bit compare here: the 32-bit block-index compare of the dense kernel measured 8 %
         // slower in this kernel
         const int64_t key0 = (j0 + (int64_t)(e >> 8)) * kBN;
-        rows_tile<D, kBN>(w, kb, kb + L::K_BYTES, key0, N, key0 + kBN > N, lane, sc, lay);
+        rows_tile<D>(w, kb, kb + L::K_BYTES, key0, N, key0 + kBN > N, lane, sc);
       }
       wait_dma();
       __syncthreads();
     }
   }
   if (qb >= 0)
-    rows_end(w, a.out + base, a.lse != nullptr ? a.lse + ((int64_t)b * a.heads + head) * N : nullptr, my_q, N,
-             row_stride, my_count <= 0, hi);
+    rows_end(w, a.out + base, a.lse != nullptr ? a.lse + ((int64_t)b * a.heads + head) * N : nullptr, q0, N,
+             row_stride, my_count <= 0, lane);
 }
 
 template <int D, int WAVES, int OCC>
