@@ -43,29 +43,29 @@ constexpr int kBN = 64;  // keys per tile (= SubBlock block size)
 // SwzLayout: the K and V tiles of 64 keys in LDS, unpadded rows of 2D bytes (CPR = D/8 chunks),
 // filled by direct global -> LDS loads, which write each wave instruction's 64 x 16 bytes to
 // consecutive LDS addresses, so rows cannot be padded. The chunks of a row are rotated instead,
-// so that the chunks one read instruction touches fall on distinct banks (the bank positions of
-// rows padded to 17 (K) or 20 (V) chunks):
-//   K: chunk c of row r at column (c + r) mod 16 (D = 128) or (c + r/2) mod 8 (D = 64);
-//   V: chunk c of row r at column (c + 4r) mod 16 (D = 128) or (c + 4 (r/2)) mod 8 (D = 64).
+// by a function of the row, so that the chunks one read instruction touches fall on distinct
+// banks whether a read cycle serves 256 or 128 bytes. A K read takes one chunk of 16 consecutive
+// rows per 16 lanes; a V transpose read takes 2 adjacent chunks of 4 consecutive rows per 16 lanes
+// (8 rows per 32 lanes):
+//   D = 128 (16 chunks per row): K chunk c of row r at column (c + r) mod 16, V at (c + 2r) mod 16;
+//   D = 64 (8 chunks, two rows per 256 bytes): K at (c + (r xor bit3(r))) mod 8, V at
+//   (c + 2 ((r mod 4) xor bit2(r))) mod 8.
+// The rotations only use the row's low 4 bits, so a lane's columns do not change with the 16-key
+// tile or the 32-key step. (V rotated by 4r, as for reads of 4 rows x 4 chunks, conflicted 2-way
+// here: 1.0 bank conflicts per LDS access in the PMC counters.)
 template <int D>
 struct SwzLayout {
   static constexpr int ROW = 2 * D;
   static constexpr int CPR = D / 8;
   static constexpr int K_BYTES = kBN * ROW;
   static constexpr int BUF_BYTES = 2 * K_BYTES;
-  __device__ static __forceinline__ int kcol(int r, int c) {
-    return D == 128 ? (c + r) & 15 : (c + (r >> 1)) & 7;
-  }
-  __device__ static __forceinline__ int vcol(int r, int c) {
-    return D == 128 ? (c + 4 * r) & 15 : (c + 4 * (r >> 1)) & 7;
-  }
+  __device__ static __forceinline__ int krot(int r) { return D == 128 ? r : r ^ ((r >> 3) & 1); }
+  __device__ static __forceinline__ int vrot(int r) { return D == 128 ? 2 * r : 2 * ((r & 3) ^ ((r >> 2) & 1)); }
+  __device__ static __forceinline__ int kcol(int r, int c) { return (c + krot(r)) & (CPR - 1); }
+  __device__ static __forceinline__ int vcol(int r, int c) { return (c + vrot(r)) & (CPR - 1); }
   // logical chunk stored at column col of row r (the inverses)
-  __device__ static __forceinline__ int kchunk(int r, int col) {
-    return D == 128 ? (col - r) & 15 : (col - (r >> 1)) & 7;
-  }
-  __device__ static __forceinline__ int vchunk(int r, int col) {
-    return D == 128 ? (col - 4 * r) & 15 : (col - 4 * (r >> 1)) & 7;
-  }
+  __device__ static __forceinline__ int kchunk(int r, int col) { return (col - krot(r)) & (CPR - 1); }
+  __device__ static __forceinline__ int vchunk(int r, int col) { return (col - vrot(r)) & (CPR - 1); }
 };
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
