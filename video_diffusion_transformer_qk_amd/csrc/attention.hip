@@ -95,6 +95,7 @@ struct WaveRows {
   bf16x8 qf[2][D / 32];
   f32x4 o[D / 16][2];
   float m_run[2];     // running max of s*sc (log2 units) per query tile, shared by the query's 4 lanes
+  float m_thr[2];     // m_run + 8: a tile max above it moves the running max
   float l_part[2][2]; // per-lane partial row sums, two chains per query tile across all tiles
   int koff[D / 32];
   int voff[D / 16];
@@ -120,6 +121,7 @@ __device__ __forceinline__ void rows_begin(WaveRows<D>& w, const uint16_t* q, in
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     w.m_run[qt] = -INFINITY;
+    w.m_thr[qt] = -INFINITY;
     w.l_part[qt][0] = w.l_part[qt][1] = 0.f;
   }
   // the rotations depend on bits of the row that 16-key and 32-key steps leave unchanged
@@ -174,14 +176,17 @@ __device__ __forceinline__ void rows_tile(WaveRows<D>& w, const unsigned char* k
   bf16x8 pb[2][2];  // P^T B operands [query tile][32-key step]
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    float mt[4];
+    // the lane's 16 scores of the query tile as one chain of 3-input maxima (8 instructions)
+    float ml = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), s[0][qt][2]);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) mt[kt] = fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3]));
-    const float mx = quad_max(fmaxf(fmaxf(mt[0], mt[1]), fmaxf(mt[2], mt[3]))) * sc;
-    if (__any(mx > w.m_run[qt] + 8.0f)) {
+    for (int i = 3; i + 1 < 16; i += 2) ml = fmaxf(fmaxf(ml, s[i / 4][qt][i % 4]), s[(i + 1) / 4][qt][(i + 1) % 4]);
+    ml = fmaxf(ml, s[3][qt][3]);
+    const float mx = quad_max(ml) * sc;
+    if (__any(mx > w.m_thr[qt])) {
       const float m_new = fmaxf(w.m_run[qt], mx);
       const float alpha = fast_exp2(w.m_run[qt] - m_new);
       w.m_run[qt] = m_new;
+      w.m_thr[qt] = m_new + 8.0f;
       w.l_part[qt][0] *= alpha;
       w.l_part[qt][1] *= alpha;
 #pragma unroll
@@ -254,49 +259,55 @@ __device__ __forceinline__ void rows_end(const WaveRows<D>& w, uint16_t* out, fl
 // no staging registers, no LDS write instructions). A wave instruction writes 64 lanes x 16 bytes
 // to consecutive LDS addresses, so LDS slot p = 64 (J w + j) + lane of wave w's instruction j is
 // row p / CPR, column p % CPR of the tile, and the lane fetches the logical chunk that the
-// rotation puts at that column. Rows past the end of the sequence are clamped to the last token,
-// only in the tile that holds it. The loads are counted by vmcnt: a wave waits for its own
-// (wait_dma) before the barrier that hands the tile to the other waves.
+// rotation puts at that column. The loads take the tile's first K and V rows as wave-uniform
+// scalar bases and the lane's byte offset inside the tile (fixed for the whole kernel), so moving
+// to another tile costs scalar adds only. Rows past the end of the sequence are clamped to the
+// last token, only in the tile that holds it (the clamped offsets stay non-negative). The loads
+// are counted by vmcnt: a wave waits for its own (wait_dma) before the barrier that hands the
+// tile to the other waves.
 template <int D, int NT>
 struct TileDma {
   using L = SwzLayout<D>;
   static constexpr int WAVES = NT / 64;
   static constexpr int J = L::CPR / WAVES;  // instructions per wave and tensor
   static_assert(L::CPR % WAVES == 0, "the tile's 1 KB slices must split evenly over the waves");
-  int krow[J], koff[J], voff[J];
-  int lds0;  // byte offset of the wave's first slice (wave-uniform)
+  int krow[J];
+  uint32_t koff[J], voff[J];  // byte offsets inside the tile: below 2^31 (rows < 64, heads <= 65535)
+  int rs_bytes;               // bytes between consecutive tokens
+  int lds0;                   // byte offset of the wave's first slice (wave-uniform)
 
   __device__ __forceinline__ void init(int tid, int64_t row_stride) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     lds0 = wave * J * 1024;
+    rs_bytes = 2 * (int)row_stride;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int p = 64 * (J * wave + j) + lane;
       const int r = p / L::CPR, col = p % L::CPR;
       krow[j] = r;
-      koff[j] = r * (int)row_stride + 8 * L::kchunk(r, col);
-      voff[j] = r * (int)row_stride + 8 * L::vchunk(r, col);
+      koff[j] = (uint32_t)(r * rs_bytes + 16 * L::kchunk(r, col));
+      voff[j] = (uint32_t)(r * rs_bytes + 16 * L::vchunk(r, col));
     }
   }
-  // buf: LDS byte address of the tile buffer (wave-uniform)
-  __device__ __forceinline__ void fetch(const uint16_t* k, const uint16_t* v, int64_t base, int64_t key0,
-                                        int64_t N, int64_t row_stride, uint32_t buf) const {
-    const int64_t tile = base + key0 * row_stride;
+  // tk, tv: the tile's first K and V rows (wave-uniform); whole: all 64 rows lie inside the
+  // sequence, else last = index of the last valid row in the tile; buf: LDS byte address of the
+  // tile buffer (wave-uniform)
+  __device__ __forceinline__ void fetch(const unsigned char* tk, const unsigned char* tv, bool whole, int last,
+                                        uint32_t buf) const {
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(buf + lds0);
-    if (key0 + kBN <= N) {
+    if (whole) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        lds_dma16(k + tile + koff[j], l0 + 1024 * j);
-        lds_dma16(v + tile + voff[j], l0 + L::K_BYTES + 1024 * j);
+        lds_dma16_s(tk, koff[j], l0 + 1024 * j);
+        lds_dma16_s(tv, voff[j], l0 + L::K_BYTES + 1024 * j);
       }
     } else {
-      const int last = (int)(N - 1 - key0);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const int64_t adj = krow[j] < last ? 0 : (int64_t)(last - krow[j]) * row_stride;
-        lds_dma16(k + tile + koff[j] + adj, l0 + 1024 * j);
-        lds_dma16(v + tile + voff[j] + adj, l0 + L::K_BYTES + 1024 * j);
+        const int adj = krow[j] < last ? 0 : (last - krow[j]) * rs_bytes;  // row min(r, last)
+        lds_dma16_s(tk, (uint32_t)((int)koff[j] + adj), l0 + 1024 * j);
+        lds_dma16_s(tv, (uint32_t)((int)voff[j] + adj), l0 + L::K_BYTES + 1024 * j);
       }
     }
   }
@@ -330,17 +341,23 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
   TileDma<D, NT> dma;
   dma.init(tid, row_stride);
   const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k + base);
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v + base);
+  const int64_t tile_bytes = (int64_t)kBN * 2 * row_stride;
+  const int n_full = (int)(N / kBN);  // tiles that lie inside the sequence
+  auto fetch_tile = [&](int tt, uint32_t buf) {
+    dma.fetch(kbase + tt * tile_bytes, vbase + tt * tile_bytes, tt < n_full, (int)(N - 1 - (int64_t)tt * kBN), buf);
+  };
 
   // LDS byte address of the tile buffers
   const uint32_t smem_lds = lds_address(smem);
   wait_own_loads();  // the Q fragments
-  dma.fetch(a.k, a.v, base, 0, N, row_stride, smem_lds);
+  fetch_tile(0, smem_lds);
   wait_dma();
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles)
-      dma.fetch(a.k, a.v, base, (int64_t)(t + 1) * kBN, N, row_stride, smem_lds + (buf ^ 1) * L::BUF_BYTES);
+    if (t + 1 < n_tiles) fetch_tile(t + 1, smem_lds + (buf ^ 1) * L::BUF_BYTES);
     const unsigned char* kb = smem + buf * L::BUF_BYTES;
     rows_tile<D>(w, kb, kb + L::K_BYTES, (int64_t)t * kBN, N, t == last_partial, lane, sc);
     wait_dma();
@@ -404,20 +421,30 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
   const float sc = 1.4426950408889634f / sqrtf((float)D);
   const uint32_t my_bit = 1u << gblk;
 
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k + base);
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v + base);
+  const int64_t tile_bytes = (int64_t)kBN * 2 * row_stride;
+  const int n_full = (int)(N / kBN);  // key blocks that lie inside the sequence
+  auto fetch_block = [&](int kblk, uint32_t buf) {  // kblk wave-uniform
+    dma.fetch(kbase + kblk * tile_bytes, vbase + kblk * tile_bytes, kblk < n_full, (int)(N - 1 - (int64_t)kblk * kBN),
+              buf);
+  };
+
   for (int64_t j0 = 0; j0 < nb; j0 += KW) {
     const int nw = (int)(nb - j0 < KW ? nb - j0 : KW);
     const int nu = build_union_window<G, KW, NT>(ulist, s_wave_tot, &s_nu, a.block_idx, s_range, j0, nw);
     if (nu == 0) continue;
 
-    auto key0_of = [&](int t) -> int64_t { return (j0 + (int64_t)(ulist[t] >> 8)) * kBN; };
+    // union entry t: (slot << 8) | (bit per block of the group that keeps it), read wave-uniform
+    auto entry = [&](int t) -> uint32_t { return __builtin_amdgcn_readfirstlane(ulist[t]); };
     wait_own_loads();  // Q fragments, kept ranges and block lists
-    dma.fetch(a.k, a.v, base, key0_of(0), N, row_stride, smem_lds);
+    fetch_block((int)j0 + (int)(entry(0) >> 8), smem_lds);
     wait_dma();
     __syncthreads();
     for (int t = 0; t < nu; ++t) {
       const int buf = t & 1;
-      const uint32_t e = __builtin_amdgcn_readfirstlane(ulist[t]);  // uniform: scalar tests and loads
-      if (t + 1 < nu) dma.fetch(a.k, a.v, base, key0_of(t + 1), N, row_stride, smem_lds + (buf ^ 1) * L::BUF_BYTES);
+      const uint32_t e = entry(t);
+      if (t + 1 < nu) fetch_block((int)j0 + (int)(entry(t + 1) >> 8), smem_lds + (buf ^ 1) * L::BUF_BYTES);
       if (e & my_bit) {
         const unsigned char* kb = smem + buf * L::BUF_BYTES;
         // a 64-bit compare here: the 32-bit block-index compare of the dense kernel measured 8 %

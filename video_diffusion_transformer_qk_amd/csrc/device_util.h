@@ -45,6 +45,21 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
       : "v"(g), "s"(lds));
 }
 
+// The same load addressed as a wave-uniform 64-bit base (held in scalar registers) plus the lane's
+// unsigned 32-bit byte offset, so that moving to the next tile is a scalar add and the per-lane
+// offsets stay fixed.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds));
+}
+
 // Waits for this wave's direct loads: all of them (wait_dma) or all but the last N (wait_dma_keep).
 // They are asm, not the s_waitcnt builtin: the compiler's wait pass does not know of the loads
 // issued by lds_dma16 and dropped a builtin wait it took for redundant. For the same reason the
