@@ -71,11 +71,7 @@ struct SwzLayout {
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// max and sum over the lanes l, l^16, l^32 and l^48 (the four lanes that hold one query)
-__device__ __forceinline__ float quad_max(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return pair_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
-}
+// sum over the lanes l, l^16, l^32 and l^48 (the four lanes that hold one query)
 __device__ __forceinline__ float quad_sum(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return pair_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
@@ -138,16 +134,16 @@ __device__ __forceinline__ void rows_begin(WaveRows<D>& w, const uint16_t* q, in
 }
 
 // One K/V tile of 64 keys (K rows at kb, V rows at vb in LDS; first key key0) applied to the
-// wave's rows: S^T = K . Q^T, online softmax, O^T += V^T . P^T. `partial` (wave-uniform) marks
-// the tile that holds the last token when N is not a multiple of 64: keys at or past N get a
-// score of -inf. The running max only moves when the tile max exceeds it by more than 8 (a factor
+// wave's rows: S^T = K . Q^T, online softmax, O^T += V^T . P^T. In the tile that holds the last
+// token when N is not a multiple of 64, keys at or past N get a score of -inf. MASK selects how
+// that tile is told apart: 0 (the tile is whole) and 1 (it is the partial tile) are separate
+// instances, so that the dense loop's tile code has no branch between the score MFMAs and the
+// softmax; 2 tests `partial` (wave-uniform) at run time, which the block-sparse kernel keeps (two
+// instances inside its loop needed more than 256 registers). The running max only moves when the tile max exceeds it by more than 8 (a factor
 // 256): until then exp2 values stay <= 256, which fp32 sums and bf16 P hold exactly enough, and
 // the rescale (a wave-uniform branch) is skipped. The row sum of the bf16-rounded P that P.V uses
-// is accumulated with packed dot products against (1, 1). MERGED_MAX takes both query tiles'
-// row maxima across lanes in one pass (9 fewer VALU instructions per tile): the block-sparse
-// kernel uses it (2.4 % faster there); in the dense kernel, whose two waves per SIMD run the same
-// phase together, the longer dependency chain before the exponentials measured 2.3 % slower.
-template <int D, bool MERGED_MAX>
+// is accumulated with packed dot products against (1, 1).
+template <int D, int MASK>
 __device__ __forceinline__ void rows_tile(WaveRows<D>& w, const unsigned char* kb, const unsigned char* vb,
                                           int64_t key0, int64_t N, bool partial, int lane, float sc) {
   using L = SwzLayout<D>;
@@ -162,12 +158,13 @@ __device__ __forceinline__ void rows_tile(WaveRows<D>& w, const unsigned char* k
     bf16x8 a[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) a[kt] = *reinterpret_cast<const bf16x8*>(kb + 16 * kt * L::ROW + w.koff[ks]);
+    // query-tile-major: in the last k step query tile 0's scores are complete four MFMAs early
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma16x16x32(a[kt], w.qf[qt][ks], s[kt][qt]);
+      for (int kt = 0; kt < 4; ++kt) s[kt][qt] = mfma16x16x32(a[kt], w.qf[qt][ks], s[kt][qt]);
   }
-  if (partial) {
+  if (MASK == 1 || (MASK == 2 && partial)) {
     const int valid = (int)(N - key0);  // below 64
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -202,29 +199,21 @@ __device__ __forceinline__ void rows_tile(WaveRows<D>& w, const unsigned char* k
 #pragma unroll
       for (int i = 0; i < 4; ++i) w.o[dt][qt][i] *= alpha;
   };
-  if constexpr (MERGED_MAX) {
-    // Both query tiles in one cross-lane pass: one v_permlane16_swap of the two partial maxima and
-    // a max leave, in 16-lane rows 0 and 2, query tile 0's maximum over the lane pair (l, l^16)
-    // and, in rows 1 and 3, query tile 1's; v_permlane32_swap completes the four-lane maximum. So
-    // z is the scaled tile max of query l%16 of query tile (l/16)&1, compared with that tile's
-    // threshold (thr_mix) in one instruction. Only when a running max moves (rare) is z swapped
-    // once more, which gives every lane both tiles' maxima.
-    const auto rr = __builtin_amdgcn_permlane16_swap(__float_as_uint(ml[0]), __float_as_uint(ml[1]), false, false);
-    const float z = pair_max(fmaxf(__uint_as_float(rr[0]), __uint_as_float(rr[1]))) * sc;
-    const uint64_t over = __ballot(z > w.thr_mix);
-    if (over) {
-      const auto zz = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+  // Both query tiles in one cross-lane pass: one v_permlane16_swap of the two partial maxima and
+  // a max leave, in 16-lane rows 0 and 2, query tile 0's maximum over the lane pair (l, l^16)
+  // and, in rows 1 and 3, query tile 1's; v_permlane32_swap completes the four-lane maximum. So
+  // z is the scaled tile max of query l%16 of query tile (l/16)&1, compared with that tile's
+  // threshold (thr_mix) in one instruction. Only when a running max moves (rare) is z swapped
+  // once more, which gives every lane both tiles' maxima.
+  const auto rr = __builtin_amdgcn_permlane16_swap(__float_as_uint(ml[0]), __float_as_uint(ml[1]), false, false);
+  const float z = pair_max(fmaxf(__uint_as_float(rr[0]), __uint_as_float(rr[1]))) * sc;
+  const uint64_t over = __ballot(z > w.thr_mix);
+  if (over) {
+    const auto zz = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-        if (over & (qt ? 0xFFFF0000FFFF0000ull : 0x0000FFFF0000FFFFull)) rescale(qt, __uint_as_float(zz[qt]));
-      w.thr_mix = (g & 1) ? w.m_thr[1] : w.m_thr[0];
-    }
-  } else {
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const float mx = quad_max(ml[qt]) * sc;
-      if (__any(mx > w.m_thr[qt])) rescale(qt, mx);
-    }
+    for (int qt = 0; qt < 2; ++qt)
+      if (over & (qt ? 0xFFFF0000FFFF0000ull : 0x0000FFFF0000FFFFull)) rescale(qt, __uint_as_float(zz[qt]));
+    w.thr_mix = (g & 1) ? w.m_thr[1] : w.m_thr[0];
   }
   bf16x8 pb[2][2];  // P^T B operands [query tile][32-key step]
 #pragma unroll
@@ -390,13 +379,20 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void attn_fwd_kernel(AttnArgs a) {
   fetch_tile(0, smem_lds);
   wait_dma();
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
+  // the tiles that lie inside the sequence, then the one that holds the last token (if partial),
+  // so that the loop's tile code has no masking branch between the score MFMAs and the softmax
+  const int n_loop = last_partial >= 0 ? n_tiles - 1 : n_tiles;
+  for (int t = 0; t < n_loop; ++t) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) fetch_tile(t + 1, smem_lds + (buf ^ 1) * L::BUF_BYTES);
     const unsigned char* kb = smem + buf * L::BUF_BYTES;
-    rows_tile<D, false>(w, kb, kb + L::K_BYTES, (int64_t)t * kBN, N, t == last_partial, lane, sc);
+    rows_tile<D, 0>(w, kb, kb + L::K_BYTES, (int64_t)t * kBN, N, false, lane, sc);
     wait_dma();
     __syncthreads();
+  }
+  if (last_partial >= 0) {
+    const unsigned char* kb = smem + (last_partial & 1) * L::BUF_BYTES;
+    rows_tile<D, 1>(w, kb, kb + L::K_BYTES, (int64_t)last_partial * kBN, N, true, lane, sc);
   }
   rows_end(w, a.out + base, a.lse != nullptr ? a.lse + ((int64_t)b * a.heads + head) * N : nullptr, q0, N,
            row_stride, false, lane);
@@ -485,7 +481,7 @@ __global__ __launch_bounds__(G * 128, 2) void attn_sparse_group_kernel(AttnArgs 
         // a 64-bit compare here: the 32-bit block-index compare of the dense kernel measured 8 %
         // slower in this kernel
         const int64_t key0 = (j0 + (int64_t)(e >> 8)) * kBN;
-        rows_tile<D, true>(w, kb, kb + L::K_BYTES, key0, N, key0 + kBN > N, lane, sc);
+        rows_tile<D, 2>(w, kb, kb + L::K_BYTES, key0, N, key0 + kBN > N, lane, sc);
       }
       wait_dma();
       __syncthreads();
