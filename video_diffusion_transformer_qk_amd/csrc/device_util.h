@@ -1,4 +1,5 @@
-// Small device helpers shared by the gfx950 kernels: bf16 packing, vector types, MFMA wrappers.
+// Small device helpers shared by the gfx950 kernels: bf16 packing, vector types, direct LDS loads,
+// cross-lane combines.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,30 +25,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-// Direct global -> LDS load (gfx950 global_load_lds_dwordx4): 16 bytes per lane from g to the
-// LDS byte address lds + 16 * lane, lds wave-uniform; no register receives the data. The load is
-// counted by vmcnt like any global load: wait_dma before the LDS is read.
+// Direct global -> LDS load (gfx950 global_load_lds_dwordx4): 16 bytes per lane from
+// sbase + voff to the LDS byte address lds + 16 * lane; sbase (a 64-bit base held in scalar
+// registers) and lds are wave-uniform, voff is the lane's unsigned 32-bit byte offset, so moving
+// to the next tile is a scalar add and the per-lane offsets stay fixed. No register receives the
+// data. The load is counted by vmcnt like any global load: wait_dma before the LDS is read.
 //
 // It is issued from an asm block: through the compiler builtin, the compiler put a vmcnt(0) wait in
 // front of LDS reads issued while such a load is in flight, also where they read another buffer
 // (a tile is computed while the next one arrives). The block has no output that the load writes;
 // it saves and restores M0 (which the load takes its LDS address from), with the one wait state
 // the hardware needs between writing M0 and the load.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(lds));
-}
-
-// The same load addressed as a wave-uniform 64-bit base (held in scalar registers) plus the lane's
-// unsigned 32-bit byte offset, so that moving to the next tile is a scalar add and the per-lane
-// offsets stay fixed.
 __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
   uint32_t saved;
   asm volatile(
@@ -60,30 +48,18 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, ui
       : "v"(voff), "s"(sbase), "s"(lds));
 }
 
-// Waits for this wave's direct loads: all of them (wait_dma) or all but the last N (wait_dma_keep).
-// They are asm, not the s_waitcnt builtin: the compiler's wait pass does not know of the loads
-// issued by lds_dma16 and dropped a builtin wait it took for redundant. For the same reason the
-// compiler's own waits (for loads it issued itself) must not be left open across a direct load:
-// a kernel waits for its ordinary loads with the builtin before its first lds_dma16
-// (wait_own_loads), so that no compiler wait inside the tile loop counts the direct loads.
+// Waits for all of this wave's direct loads. It is asm, not the s_waitcnt builtin: the compiler's
+// wait pass does not know of the loads issued by lds_dma16_s and dropped a builtin wait it took
+// for redundant. For the same reason the compiler's own waits (for loads it issued itself) must
+// not be left open across a direct load: a kernel waits for its ordinary loads with the builtin
+// before its first lds_dma16_s (wait_own_loads), so that no compiler wait inside the tile loop
+// counts the direct loads.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-template <int N>
-__device__ __forceinline__ void wait_dma_keep() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 __device__ __forceinline__ void wait_own_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // LDS byte address of a pointer into shared memory
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-
-// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
-// Lane l holds A[l%32][8*(l/32) .. +7], B[8*(l/32) .. +7][l%32];
-// accumulator register r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // LDS transpose read of 4 x 16-bit values (ds_read_b64_tr_b16). Within each group of 16 lanes,
