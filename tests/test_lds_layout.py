@@ -12,7 +12,8 @@ rely on, for D = 64 and 128:
   * the per-lane byte offsets of the loads stay non-negative and below 2^31 at the largest head
     count the library accepts, also in the tile that holds the last token.
 A wrong rotation is caught: rotating V rows by 4r (D = 128) or leaving K rows unrotated puts lanes
-on the same banks."""
+on the same banks. The padded tiles of the fp8 kernels (attention_fp8.hip) are checked the same
+way: every staged chunk read back where the MFMA operands expect it, no bank conflicts."""
 import pytest
 
 TILE_ROWS = 64
@@ -138,3 +139,29 @@ def test_load_offsets_fit_32_bits(D):
         for last in range(TILE_ROWS):  # the tile that holds the last token: rows clamped to it
             adj = 0 if r < last else (last - r) * rs_bytes
             assert koff + adj == min(r, last) * rs_bytes + 16 * kc >= 0
+
+
+# fp8 kernels (attention_fp8.hip: Fp8Tile, Fp8Stage::stash, fp8_qk, fp8_soft_pv): padded rows,
+# K rows of D + 16 bytes and V^T rows of 64 + 16 bytes, written by 16-byte stores and read as two
+# 16-byte halves of each lane's 32-byte MFMA operand.
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_tiles_round_trip_and_reads_are_conflict_free(D):
+    KS, VS = D + 16, 64 + 16
+    k_store = {ci: ((ci // (D // 16)) * KS + (ci % (D // 16)) * 16) for ci in range(64 * D // 16)}
+    v_store = {ci: ((ci >> 2) * VS + (ci & 3) * 16) for ci in range(D * 64 // 16)}
+    assert len(set(k_store.values())) == len(k_store) and len(set(v_store.values())) == len(v_store)
+    k_chunk_at = {a: (ci // (D // 16), ci % (D // 16)) for ci, a in k_store.items()}  # (key, chunk)
+    v_chunk_at = {a: (ci >> 2, ci & 3) for ci, a in v_store.items()}                  # (channel, chunk)
+    for m in range(2):
+        for ks in range(D // 64):
+            for half in (0, 16):
+                addrs = [(32 * m + (l & 31)) * KS + 64 * ks + 32 * (l >> 5) + half for l in range(64)]
+                for l, a in enumerate(addrs):
+                    assert k_chunk_at[a] == (32 * m + (l & 31), (64 * ks + 32 * (l >> 5) + half) // 16)
+                assert conflicts(addrs, 16, 256, 16) == 0 and conflicts(addrs, 8, 128, 16) == 0
+    for dt in range(D // 32):
+        for half in (0, 16):
+            addrs = [(32 * dt + (l & 31)) * VS + 32 * (l >> 5) + half for l in range(64)]
+            for l, a in enumerate(addrs):
+                assert v_chunk_at[a] == (32 * dt + (l & 31), (32 * (l >> 5) + half) // 16)
+            assert conflicts(addrs, 16, 256, 16) == 0 and conflicts(addrs, 8, 128, 16) == 0
